@@ -1,0 +1,33 @@
+"""CPU oracle for FlashHead inference — TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously correct float64 implementation of what the FlashHead
+retrieval head computes, written stage by stage from the method's description
+(FlashHead explainer, framerc.cn, §1.2 and §2.2.2; arXiv 2603.14591 abstract).
+It shares no code with the HIP path and imports nothing from it.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path never routes through it: the HIP
+library fails loudly when it is missing instead of falling back here.
+
+Every function is pinned by a ``-m "not gpu"`` test against something other
+than itself (closed forms, brute force, library routines, rocRAND's Philox);
+see ``tests/test_oracle_*.py``.
+"""
+
+from .flashhead_oracle import (  # noqa: F401
+    MODE_PROBE_SAMPLE,
+    MODE_TOKEN_SAMPLE,
+    OracleHead,
+    dense,
+    dequantize_int4,
+    finish,
+    forward,
+    gather,
+    pack_int4,
+    quantize_int4_g32,
+    score,
+    select,
+    unpack_int4,
+    validate_c2t,
+)
+from .philox import gumbel, philox4x32_10, uniform_from_word  # noqa: F401

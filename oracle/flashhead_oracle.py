@@ -1,0 +1,322 @@
+"""FlashHead inference, stage by stage, in float64 numpy.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What the method computes (FlashHead explainer, framerc.cn, §1.1, §1.2 and
+§2.2.2; arXiv 2603.14591 abstract): a dense head scores every token,
+z = E h.  FlashHead replaces this with a two-stage retrieval over a balanced
+clustering of E's rows:
+
+1. score h against the c centroids (optionally INT4-quantised, §1.2.4);
+2. choose p probe clusters, by top-p score (§1.2.2) or by multinomial
+   sampling with temperature (§1.2.3);
+3. score only the b = v/c tokens of each chosen cluster, found through the
+   dense cluster-to-token table C2T[c x b] (§1.2.1), in the embedding's own
+   precision (§1.2.4);
+4. finish with argmax or temperature sampling over the retrieved tokens.
+
+Inside a stage nothing is approximated, so each stage is its plain
+definition: float64 dot products over the exact stored values (bfloat16
+widened exactly, or dequantised INT4), a full lexicographic sort for
+selection, and Gumbel-max for every draw.  Readings where the pages are
+silent (the INT4 scheme, tie-breaks, output order, sampling without
+replacement, one temperature for both stages) are the ones listed under
+"Readings" in the design notes and restated at each function.
+
+Where a floating-point value decides an integer (a top-p cut, an argmax, an
+INT4 code), the decision is taken in float32, the precision the kernels
+decide in; all other arithmetic is float64.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .philox import gumbel
+
+# mode bits: probe stage (0 = top-p by score, 1 = sampled) | token stage
+# (0 = argmax, 2 = sampled)
+MODE_PROBE_SAMPLE = 1
+MODE_TOKEN_SAMPLE = 2
+
+
+# ---------------------------------------------------------------------------
+# Data structures (§1.2.1 balanced clustering; C2T is a dense c x b table)
+# ---------------------------------------------------------------------------
+
+def validate_c2t(c2t, v: int, c: int, b: int) -> np.ndarray:
+    """Check C2T: c clusters of exactly b tokens covering [0, v) once each.
+
+    Balanced clustering (explainer §1.2.1) gives every cluster exactly v/c
+    tokens, stored as a dense [c x b] table; a token belongs to one cluster.
+    Raises ValueError otherwise; returns C2T as int64 [c x b].
+    """
+    if c <= 0 or b <= 0 or c * b != v:
+        raise ValueError(f"v={v} must equal c*b={c}*{b}")
+    t = np.asarray(c2t)
+    if t.shape != (c, b):
+        raise ValueError(f"C2T shape {t.shape} != ({c}, {b})")
+    flat = t.reshape(-1).astype(np.int64)
+    if flat.min() < 0 or flat.max() >= v:
+        raise ValueError("C2T holds a token id outside [0, v)")
+    if np.bincount(flat, minlength=v).max() != 1:
+        raise ValueError("C2T is not a permutation of [0, v)")
+    return flat.reshape(c, b)
+
+
+# ---------------------------------------------------------------------------
+# Stage-1 quantisation (§1.2.4 selective quantisation; §2.3 quant config)
+# ---------------------------------------------------------------------------
+
+def quantize_int4_g32(C: np.ndarray):
+    """Symmetric INT4 with one fp16 scale per 32 consecutive row elements.
+
+    For each centroid row k and group g (elements 32g..32g+31):
+    sigma = fp16(amax / 7) with the division in float32 and round-to-nearest-
+    even to fp16; q = clamp(rint(x / sigma), -7, 7) with float32 division and
+    ties to even; q = 0 where sigma = 0.  Returns (q int8 [c x d],
+    sigma float16 [c x d/32]).  Raises OverflowError if a scale is not a
+    finite fp16 number and ValueError if d is not a multiple of 32.
+    """
+    C = np.asarray(C, dtype=np.float32)
+    c, d = C.shape
+    if d % 32 != 0:
+        raise ValueError("INT4 g32 needs d % 32 == 0")
+    g = C.reshape(c, d // 32, 32)
+    amax = np.abs(g).max(axis=2)
+    with np.errstate(over="ignore"):
+        sigma = (amax / np.float32(7.0)).astype(np.float16)
+    if not np.all(np.isfinite(sigma)):
+        raise OverflowError("a centroid group's scale overflows fp16")
+    s = sigma.astype(np.float32)[..., None]
+    nz = s > 0
+    q = np.rint(g / np.where(nz, s, np.float32(1.0)))
+    q = np.where(nz, np.clip(q, -7, 7), 0).astype(np.int8)
+    return q.reshape(c, d), sigma
+
+
+def dequantize_int4(q: np.ndarray, sigma: np.ndarray) -> np.ndarray:
+    """C_hat = sigma * q in float64 (exact)."""
+    c, d = q.shape
+    return (sigma.astype(np.float64)[:, :, None]
+            * q.reshape(c, d // 32, 32).astype(np.float64)).reshape(c, d)
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Two's-complement nibbles, element 2m in the low nibble of byte m."""
+    q = np.asarray(q, dtype=np.int8)
+    lo = q[..., 0::2].astype(np.uint8) & np.uint8(0xF)
+    hi = q[..., 1::2].astype(np.uint8) & np.uint8(0xF)
+    return (lo | (hi << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_int4."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lo = (p & np.uint8(0xF)).astype(np.int16)
+    hi = (p >> np.uint8(4)).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Stage 1: centroid scores (explainer §1.2.2, §1.2.4: c_logits = quantize(C) h)
+# ---------------------------------------------------------------------------
+
+def score(C_hat: np.ndarray, H: np.ndarray) -> np.ndarray:
+    """s[b, k] = sum_i C_hat[k, i] * h[b, i] in float64 (a plain dot product)."""
+    C_hat = np.asarray(C_hat, dtype=np.float64)
+    H = np.atleast_2d(np.asarray(H, dtype=np.float64))
+    return H @ C_hat.T
+
+
+# ---------------------------------------------------------------------------
+# Probe selection (explainer §1.2.2 multi-probe; §1.2.3 multinomial probes)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Selection:
+    S: np.ndarray  # int64 [B x p], ascending cluster ids per row
+    key: np.ndarray  # float64 [B x c] selection keys
+    key32: np.ndarray  # float32 [B x c] the keys the decision is taken on
+    theta: np.ndarray  # float32 [B] the p-th largest key32 per row
+
+
+def probe_keys(s: np.ndarray, mode: int, temperature: float, seed: int) -> np.ndarray:
+    """Selection keys: the score itself, or score/T plus Gumbel noise.
+
+    Drawing p distinct clusters one after another from softmax(s/T) without
+    replacement is the same as taking the top p of s/T + G with independent
+    standard Gumbel G (Gumbel-top-k: Yellott 1977; Kool, van Hoof and
+    Welling 2019).  Noise for row b, cluster k is gumbel(seed, b, k, stage 0).
+    """
+    s = np.atleast_2d(np.asarray(s, dtype=np.float64))
+    if not (mode & MODE_PROBE_SAMPLE):
+        return s.copy()
+    if not temperature > 0:
+        raise ValueError("sampling needs temperature > 0")
+    B, c = s.shape
+    g = gumbel(seed, np.arange(B)[:, None], np.arange(c)[None, :], 0)
+    return s / float(temperature) + g
+
+
+def _top_ids(key32_row: np.ndarray, ids_row: np.ndarray, n: int) -> np.ndarray:
+    """Positions of the n best entries: key descending, ties to the smaller id."""
+    order = np.lexsort((ids_row, -key32_row.astype(np.float64)))
+    return order[:n]
+
+
+def select(s: np.ndarray, p: int, mode: int = 0, temperature: float = 1.0,
+           seed: int = 0) -> Selection:
+    """Pick p clusters per row: the p largest keys, returned in ascending id.
+
+    Top-p here counts clusters (the pages' p probes), not nucleus mass.  Keys
+    are compared in float32; equal keys go to the smaller cluster id.
+    """
+    key = probe_keys(s, mode, temperature, seed)
+    B, c = key.shape
+    if not 1 <= p <= c:
+        raise ValueError(f"p={p} outside [1, c={c}]")
+    key32 = key.astype(np.float32)
+    ids = np.arange(c)
+    S = np.empty((B, p), dtype=np.int64)
+    theta = np.empty(B, dtype=np.float32)
+    for r in range(B):
+        top = _top_ids(key32[r], ids, p)
+        theta[r] = key32[r, top[-1]]
+        S[r] = np.sort(top)
+    return Selection(S, key, key32, theta)
+
+
+# ---------------------------------------------------------------------------
+# Stage 2: token scores of the probed clusters (explainer §1.2.4: E[top] h)
+# ---------------------------------------------------------------------------
+
+def gather(E: np.ndarray, c2t: np.ndarray, S: np.ndarray, H: np.ndarray):
+    """Retrieved ids and logits per row.
+
+    For row b, clusters k in S[b] (ascending) and slots j = 0..b-1 (that
+    order): t = C2T[k, j], z = E[t] . h_b in float64.  Returns (ids int64
+    [B x p*b], z float64 [B x p*b]).
+    """
+    c2t = np.asarray(c2t, dtype=np.int64)
+    H = np.atleast_2d(np.asarray(H, dtype=np.float64))
+    S = np.atleast_2d(S)
+    B = S.shape[0]
+    ids = c2t[S].reshape(B, -1)
+    z = np.empty(ids.shape, dtype=np.float64)
+    for r in range(B):
+        z[r] = np.asarray(E[ids[r]], dtype=np.float64) @ H[r]
+    return ids, z
+
+
+@dataclass
+class Finish:
+    token: np.ndarray  # int64 [B]
+    token_logit: np.ndarray  # float64 [B] z of the chosen token
+    lse: np.ndarray  # float64 [B] log sum exp(z / T') over the candidates
+    key: np.ndarray  # float64 [B x n] the keys the choice maximised
+    key32: np.ndarray  # float32 [B x n]
+
+
+def finish(ids: np.ndarray, z: np.ndarray, mode: int = 0, temperature: float = 1.0,
+           seed: int = 0) -> Finish:
+    """Argmax, or one draw from softmax(z/T), over each row's candidates.
+
+    Sampling is Gumbel-max: argmax of z/T + gumbel(seed, b, t, stage 1),
+    keyed by the token id t so that the draw does not depend on where t sits
+    in the candidate list.  The choice is taken on float32 keys, ties to the
+    smaller token id.  LSE = log sum_t exp(z_t / T') with T' = T when the
+    token is sampled and 1 otherwise, computed with the max shifted out.
+    """
+    ids = np.atleast_2d(np.asarray(ids, dtype=np.int64))
+    z = np.atleast_2d(np.asarray(z, dtype=np.float64))
+    B, n = z.shape
+    sample = bool(mode & MODE_TOKEN_SAMPLE)
+    if sample and not temperature > 0:
+        raise ValueError("sampling needs temperature > 0")
+    tp = float(temperature) if sample else 1.0
+    if sample:
+        key = z / tp + gumbel(seed, np.arange(B)[:, None], ids, 1)
+    else:
+        key = z.copy()
+    key32 = key.astype(np.float32)
+    token = np.empty(B, dtype=np.int64)
+    token_logit = np.empty(B, dtype=np.float64)
+    lse = np.empty(B, dtype=np.float64)
+    for r in range(B):
+        best = _top_ids(key32[r], ids[r], 1)[0]
+        token[r] = ids[r, best]
+        token_logit[r] = z[r, best]
+        x = z[r] / tp
+        m = x.max()
+        lse[r] = m + np.log(np.exp(x - m).sum())
+    return Finish(token, token_logit, lse, key, key32)
+
+
+# ---------------------------------------------------------------------------
+# Whole paths
+# ---------------------------------------------------------------------------
+
+@dataclass
+class ForwardResult:
+    scores: np.ndarray  # float64 [B x c]
+    sel: Selection
+    ids: np.ndarray  # int64 [B x p*b]
+    z: np.ndarray  # float64 [B x p*b]
+    fin: Finish
+
+
+class OracleHead:
+    """The engine's state: E, C (or its INT4 form) and C2T, validated once."""
+
+    def __init__(self, E, C, c2t, quant: str = "none"):
+        E = np.asarray(E)
+        C = np.asarray(C, dtype=np.float32)
+        self.v, self.d = E.shape
+        self.c = C.shape[0]
+        if self.v % self.c:
+            raise ValueError("v must be a multiple of c")
+        self.b = self.v // self.c
+        self.c2t = validate_c2t(c2t, self.v, self.c, self.b)
+        self.E = E
+        self.quant = quant
+        if quant == "none":
+            self.q = self.sigma = None
+            self.C_hat = C.astype(np.float64)
+        elif quant == "int4":
+            self.q, self.sigma = quantize_int4_g32(C)
+            self.C_hat = dequantize_int4(self.q, self.sigma)
+        else:
+            raise ValueError(f"unknown quant {quant}")
+
+    def forward(self, H, p: int, mode: int = 0, temperature: float = 1.0,
+                seed: int = 0) -> ForwardResult:
+        s = score(self.C_hat, H)
+        sel = select(s, p, mode, temperature, seed)
+        ids, z = gather(self.E, self.c2t, sel.S, H)
+        fin = finish(ids, z, mode, temperature, seed)
+        return ForwardResult(s, sel, ids, z, fin)
+
+    def dense(self, H, mode: int = 0, temperature: float = 1.0, seed: int = 0) -> Finish:
+        return dense(self.E, H, mode, temperature, seed)
+
+
+def forward(E, C, c2t, H, p: int, mode: int = 0, temperature: float = 1.0,
+            seed: int = 0, quant: str = "none") -> ForwardResult:
+    """One FlashHead call on the CPU (see OracleHead.forward)."""
+    return OracleHead(E, C, c2t, quant).forward(H, p, mode, temperature, seed)
+
+
+def dense(E, H, mode: int = 0, temperature: float = 1.0, seed: int = 0) -> Finish:
+    """The dense head z = E h over all v tokens, finished like FlashHead (§1.1)."""
+    H = np.atleast_2d(np.asarray(H, dtype=np.float64))
+    z = H @ np.asarray(E, dtype=np.float64).T
+    ids = np.broadcast_to(np.arange(z.shape[1]), z.shape)
+    return finish(ids, z, mode, temperature, seed)
