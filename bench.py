@@ -1,0 +1,271 @@
+"""FlashHead throughput on one MI355X: calls/s and achieved HBM GB/s of the
+retrieval head at (v=128256, d=2048, c=8016, p=512, bf16, batch 1), beside
+the dense head z = E h on the same inputs and the CPU oracle.
+
+One step is one fh_forward call (stage-1 scores, probe selection,
+gather-score of the p*b retrieved tokens, argmax epilogue) over one batch of
+B synthetic queries.  Inputs are resident in HBM before timing starts.  The
+engine is replicated R times (default 8) and consecutive steps rotate over
+the replicas and over 256 queries, so that the bytes a call touches are not
+still in the 256 MB Infinity Cache from the previous call: the working set
+between two uses of one replica is R * (|C| + |E rows read|), several times
+the cache.
+
+Output: one JSON line (see the keys below).  --gpus N > 1 is not supported:
+this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--shape", default="llama32_1b")
+    ap.add_argument("--B", type=int, default=1)
+    ap.add_argument("--p", type=int, default=512)
+    ap.add_argument("--quant", default="none", choices=["none", "int4"])
+    ap.add_argument("--mode", type=int, default=0)
+    ap.add_argument("--temperature", type=float, default=1.0)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--dense-steps", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lm_output_head_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(shape, B, p, quant, elem):
+    """Bytes each kernel must move per launch (the minimum the method reads
+    and writes), by kernel name."""
+    v, d, c, b = shape.v, shape.d, shape.c, shape.b
+    if quant == "int4":
+        c_bytes = c * d // 2 + c * (d // 32) * 2
+    else:
+        c_bytes = c * d * elem
+    score = c_bytes + B * d * elem + B * c * 4
+    select = B * c * 4 + B * p * 4
+    # stage 2: the embedding rows of the retrieved tokens, their C2T entries,
+    # the probe lists and h; writes nothing but per-workgroup partials (not
+    # counted), the retrieved ids/logits are optional outputs (off here)
+    gather = B * p * b * d * elem + B * p * b * 4 + B * p * 4 + B * d * elem
+    dense = v * d * elem + B * d * elem
+    return {"score": score, "score_int4": score, "select": select, "gather": gather,
+            "dense": dense}
+
+
+def traffic_from_profiles(kernel: str, src_hash: str):
+    """HBM bytes per launch measured by rocprofv3 PMC counters, if a summary
+    for the current kernel sources exists under profiles/."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != src_hash:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(pb, p, quant, mode, temperature, seconds):
+    """The oracle as it stands, on host cores, over a bounded query sample."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    head = oracle.OracleHead(pb.E, pb.C, pb.C2T, quant)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        q = n % pb.H.shape[0]
+        head.forward(pb.H[q:q + 1], p, mode, temperature, 0x5EED + n)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(n / el, 3), "unit": "calls/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} single-query calls of the same workload in {el:.1f} s "
+                      f"(float64 numpy oracle, BLAS threads={cores})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lm_output_head_amd import flashhead as fhb
+    from synth import SHAPES, make_problem
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    shape = SHAPES[args.shape]
+    B, p = args.B, args.p
+    print(f"[bench] generating {shape.name} workload", file=sys.stderr, flush=True)
+    pb = make_problem(shape)
+    bf16 = shape.dtype == "bf16"
+    elem = 2 if bf16 else 4
+    tdt = torch.bfloat16 if bf16 else torch.float32
+
+    def dev(bits_or_f32):
+        a = np.ascontiguousarray(bits_or_f32)
+        if bf16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a.astype(np.float32)).cuda()
+
+    E0 = dev(pb.E_bits if bf16 else pb.E)
+    C0 = dev(pb.C_bits if bf16 else pb.C)
+    Hall = dev(pb.H_bits if bf16 else pb.H)
+    nq = Hall.shape[0]
+    R = max(1, args.replicas)
+    heads = []
+    for r in range(R):
+        E = E0 if r == 0 else E0.clone()
+        C = C0 if r == 0 else C0.clone()
+        heads.append(fhb.FlashHead(E, C, pb.C2T, quant=args.quant, max_batch=B))
+    # query batches: B consecutive queries, rotating
+    hb = [Hall[(i * B) % nq:(i * B) % nq + B].contiguous() for i in range(max(1, nq // B))]
+    out_tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    out_logit = torch.empty(B, dtype=torch.float32, device="cuda")
+    out_lse = torch.empty(B, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    lib = fhb._abi.load()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    hptr = [ptr(h) for h in hb]
+    engs = [h.eng for h in heads]
+    otok, olog, olse = ptr(out_tok), ptr(out_logit), ptr(out_lse)
+
+    def step(i):
+        st = lib.fh_forward(engs[i % R], hptr[i % len(hptr)], B, p, args.mode,
+                            args.temperature, 0x5EED + i, otok, olog, olse, None, None, None, sp)
+        if st != 0:
+            raise RuntimeError(lib.fh_last_error().decode())
+
+    def dense_step(i):
+        st = lib.fh_dense_forward(engs[i % R], hptr[i % len(hptr)], B, args.mode & 2,
+                                  args.temperature, 0x5EED + i, otok, olog, olse, None, sp)
+        if st != 0:
+            raise RuntimeError(lib.fh_last_error().decode())
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            fn(warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3
+
+    print(f"[bench] timing {args.steps} FlashHead steps", file=sys.stderr, flush=True)
+    ms, wall_ms = timed(step, args.steps, args.warmup)
+
+    # the same steps again with per-kernel HIP events on the launch stream
+    n_launch = 4 * args.steps
+    for eng in engs:
+        fhb.fh_profile_begin(eng, n_launch)
+    ms_prof, _ = timed(step, args.steps, 0)
+    per = {}
+    for eng in engs:
+        for name, (n, tot) in fhb.fh_profile_end(eng).items():
+            a = per.setdefault(name, [0, 0.0])
+            a[0] += n
+            a[1] += tot
+    kern = {k: {"launches": n, "avg_us": round(tot / n * 1e3, 3)} for k, (n, tot) in per.items()}
+    algo = algorithmic_bytes(shape, B, p, args.quant, elem)
+    dominant = max(kern, key=lambda k: kern[k]["avg_us"] * kern[k]["launches"])
+    dom_bytes = algo[dominant]
+    dom_us = kern[dominant]["avg_us"]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profiles(dominant, src_hash)
+    total_bytes = sum(algo[k] for k in kern if k in algo)
+
+    res = {
+        "metric": "FlashHead calls/s & achieved HBM GB/s (v=128256,d=2048,p=512) vs dense head",
+        "value": round(1000.0 / ms, 2),
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic seeded clustered embeddings (no trained weights)",
+        "config": {"workload": f"flashhead_{shape.name}", "v": shape.v, "d": shape.d,
+                   "c": shape.c, "b": shape.b, "p": p, "batch": B, "quant": args.quant,
+                   "mode": args.mode, "replicas": R, "parallelism": "single-gpu"},
+        "tokens_per_s": round(1000.0 / ms * B, 2),
+        "call_algorithmic_bytes": total_bytes,
+        "call_achieved_gbs": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+        "call_roofline_frac": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "host_wall_ms_per_step": round(wall_ms, 5),
+        "profiled_ms_per_step": round(ms_prof, 5),
+        "kernels": kern,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": dom_bytes, "source_hash": src_hash},
+    }
+    if not args.no_dense:
+        print(f"[bench] timing {args.dense_steps} dense steps", file=sys.stderr, flush=True)
+        dms, _ = timed(dense_step, args.dense_steps, 10)
+        dense_bytes = algo["dense"]
+        res["dense"] = {"calls_per_s": round(1000.0 / dms, 2), "ms_per_call": round(dms, 5),
+                        "achieved_gbs": round(dense_bytes / (dms * 1e-3) / 1e9, 1),
+                        "speedup_flashhead_vs_dense": round(dms / ms, 3)}
+    for hd in heads:
+        hd.close()
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(pb, p, args.quant, args.mode, args.temperature,
+                                           args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

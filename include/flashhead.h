@@ -1,0 +1,189 @@
+/*
+ * flashhead.h — C ABI of libflashhead, an MI355X (gfx950) implementation of
+ * FlashHead inference: a drop-in replacement for a language model's dense
+ * output head z = E h by two-stage retrieval over a balanced clustering of
+ * E's rows.
+ *
+ * Sources, cited by page title and section:
+ *   [X]  FlashHead technical explainer (framerc.cn), §1.1 dense head cost,
+ *        §1.2.1 balanced clustering and the dense C2T table, §1.2.2 multi-probe
+ *        top-p retrieval, §1.2.3 multinomial probe sampling with temperature,
+ *        §1.2.4 selective (INT4 stage-1) quantisation, §2.2.2 the computation
+ *        graph h -> centroid scores -> top-p clusters -> token scores,
+ *        §2.3 the quantisation config (centroid int4, token bf16).
+ *   [A]  "FlashHead: Efficient Drop-In Replacement for the Classification Head
+ *        in Language Model Inference" (arXiv 2603.14591), abstract,
+ *        innovations (1)-(4).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense and row-major.  "Device" pointers address GPU memory
+ *     on the engine's device; "host" pointers address CPU memory.
+ *   - Work is enqueued on the HIP stream passed as `stream` (NULL = the
+ *     default stream) and the call returns without waiting for it, except
+ *     fh_create, which waits for its own set-up work.  Outputs are valid once
+ *     that stream has reached the call.
+ *   - Argument errors are detected before anything is enqueued: the call
+ *     returns FH_EINVAL or FH_EUNSUPPORTED, writes nothing, and
+ *     fh_last_error() describes the problem.  A failing HIP call returns
+ *     FH_EHIP; allocation failure returns FH_ENOMEM.
+ *   - Results are deterministic: the same inputs, p, mode, temperature and
+ *     seed give bit-identical outputs on the same device.
+ *   - One engine may be used from several threads only if the calls do not
+ *     overlap: calls share the engine's workspace.
+ */
+#ifndef FLASHHEAD_H
+#define FLASHHEAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fh_engine fh_engine; /* opaque */
+
+typedef enum {
+  FH_OK = 0,
+  FH_EINVAL = -1,       /* invalid argument                                 */
+  FH_ENOMEM = -2,       /* device or host allocation failed                 */
+  FH_EHIP = -3,         /* a HIP runtime call or kernel launch failed       */
+  FH_EUNSUPPORTED = -4  /* valid, but outside what this build implements    */
+} fh_status;
+
+/* Storage type shared by E, C and h. */
+typedef enum { FH_F32 = 0, FH_BF16 = 1 } fh_dtype;
+
+/* Stage-1 centroid storage ([X] §1.2.4, §2.3). */
+typedef enum {
+  FH_QUANT_NONE = 0,     /* centroids used as given                          */
+  FH_QUANT_INT4_G32 = 1  /* symmetric INT4, one fp16 scale per 32 elements   */
+} fh_quant;
+
+/* `mode` is the OR of one probe flag and one token flag. */
+enum {
+  FH_PROBE_TOPK = 0,   /* the p highest-scoring clusters ([X] §1.2.2)       */
+  FH_PROBE_SAMPLE = 1, /* p distinct clusters drawn from softmax(s/T)
+                          without replacement ([X] §1.2.3)                  */
+  FH_TOKEN_ARGMAX = 0, /* highest logit among retrieved tokens              */
+  FH_TOKEN_SAMPLE = 2  /* one draw from softmax(z/T) over retrieved tokens  */
+};
+
+/*
+ * fh_create — build an engine over one output head.
+ *
+ *   E        device, [v x d] of `dtype`: output embeddings, one row per token
+ *            ([X] §1.1).  BORROWED: not copied; keep it alive and unchanged
+ *            until fh_destroy.
+ *   C        device, [c x d] of `dtype`: cluster centroids ([X] §1.2.1).
+ *            Borrowed for FH_QUANT_NONE.  For FH_QUANT_INT4_G32 it is read
+ *            once here and may be freed after the call returns.
+ *   C2T      HOST, [c x b] int32 with b = v / c: C2T[k*b + j] is the token in
+ *            slot j of cluster k ([X] §1.2.1, [A] (1)).  Copied.  Must hold
+ *            every token of [0, v) exactly once (balanced clustering).
+ *   v, d, c  vocabulary size, hidden size, cluster count; v % c == 0.
+ *            d % 4 == 0 for FH_F32, d % 8 == 0 for FH_BF16, and
+ *            d % 32 == 0 with FH_QUANT_INT4_G32.  c <= 16384, d <= 8192.
+ *   quant    FH_QUANT_INT4_G32 quantises C here: per row k and group g of 32
+ *            consecutive elements, sigma = fp16(amax / 7) (float32 division,
+ *            round to nearest even), q = clamp(rint(x / sigma), -7, 7), q = 0
+ *            where sigma = 0 ([X] §1.2.4).  A scale that overflows fp16 gives
+ *            FH_EINVAL.
+ *   max_batch largest B any later call will use (sizes the workspace).
+ *   stream   stream for the set-up work; fh_create waits for it.
+ *   out      receives the engine (set only on FH_OK).
+ */
+fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype dtype,
+                    int64_t v, int64_t d, int64_t c, fh_quant quant, int64_t max_batch,
+                    void* stream, fh_engine** out);
+
+/* fh_destroy — release everything the engine owns (NULL is a no-op).  Waits
+ * for the device to finish work that may still use it. */
+void fh_destroy(fh_engine* e);
+
+/*
+ * fh_forward — one FlashHead call over B hidden states ([X] §2.2.2).
+ *
+ *   h        device, [B x d] of the engine's dtype.
+ *   B        1 <= B <= max_batch.
+ *   p        probes per query, 1 <= p <= c ([X] §1.2.2).
+ *   mode     FH_PROBE_* | FH_TOKEN_*.
+ *   temperature  > 0 when either stage samples ([X] §1.2.3); otherwise
+ *            ignored.  One temperature serves both stages.
+ *   seed     keys the Philox4x32-10 stream of every draw: probe k of row b
+ *            uses counter (k/4, b, 0, 0), token t uses (t/4, b, 1, 0), key
+ *            (seed mod 2^32, seed >> 32), word k mod 4 (resp. t mod 4),
+ *            u = ((w >> 9) + 1/2) 2^-23, Gumbel noise -ln(-ln u).
+ *
+ * Outputs (device; any of the last four may be NULL to skip it):
+ *   out_token        [B] int32: the chosen token id.
+ *   out_token_logit  [B] float: its logit z = E[token] . h.
+ *   out_lse          [B] float: log sum exp(z / T') over the retrieved
+ *                    tokens, T' = temperature if tokens are sampled, else 1.
+ *   out_clusters     [B x p] int32: the probed clusters, ascending id.
+ *   out_ids          [B x p*b] int32: retrieved token ids, in cluster order
+ *                    (ascending id) then slot order.
+ *   out_logits       [B x p*b] float: their logits z = E[t] . h (float32
+ *                    accumulation of the stored values).
+ * Selection keys are compared in float32; equal keys go to the smaller
+ * cluster / token id.
+ */
+fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode,
+                     float temperature, uint64_t seed, int32_t* out_token,
+                     float* out_token_logit, float* out_lse, int32_t* out_clusters,
+                     int32_t* out_ids, float* out_logits, void* stream);
+
+/*
+ * fh_score — stage 1 alone: out_scores[b*c + k] = C_hat[k] . h[b] in float32
+ * accumulation, with C_hat the centroids as stored (INT4: sigma * q)
+ * ([X] §1.2.4 stage 1).
+ *   h device [B x d]; out_scores device [B x c] float.  1 <= B <= max_batch.
+ */
+fh_status fh_score(fh_engine* e, const void* h, int64_t B, float* out_scores, void* stream);
+
+/*
+ * fh_dense_forward — the dense head z = E h over all v tokens ([X] §1.1),
+ * finished exactly like fh_forward (argmax or one draw from softmax(z/T), the
+ * same Philox stream for tokens, LSE over all v).  The comparison baseline.
+ *   out_logits may be NULL; otherwise device [B x v] float.
+ */
+fh_status fh_dense_forward(fh_engine* e, const void* h, int64_t B, int mode,
+                           float temperature, uint64_t seed, int32_t* out_token,
+                           float* out_token_logit, float* out_lse, float* out_logits,
+                           void* stream);
+
+/*
+ * fh_get_int4 — copy the engine's quantised centroids out (FH_QUANT_INT4_G32
+ * only, else FH_EINVAL).
+ *   packed  device [c x d/2] uint8: two's-complement nibbles, element 2m in
+ *           the low nibble of byte m.
+ *   scales  device [c x d/32] uint16: fp16 bit patterns of sigma.
+ */
+fh_status fh_get_int4(fh_engine* e, uint8_t* packed, uint16_t* scales, void* stream);
+
+/*
+ * Per-kernel timing.  fh_profile_begin(e, n) makes the engine record a HIP
+ * event pair on the launch stream around each of its next n kernel launches.
+ * fh_profile_end waits for those events and fills up to `max` records
+ * (kernel name, launches, total milliseconds) aggregated by kernel, returning
+ * how many it wrote in *count.  Names point to static strings.
+ */
+typedef struct {
+  const char* name;
+  int64_t launches;
+  double total_ms;
+} fh_kernel_time;
+
+fh_status fh_profile_begin(fh_engine* e, int64_t max_launches);
+fh_status fh_profile_end(fh_engine* e, fh_kernel_time* out, int max, int* count);
+
+/* Thread-local description of the last error on this thread ("" if none). */
+const char* fh_last_error(void);
+
+/* Library version string. */
+const char* fh_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHHEAD_H */

@@ -1,0 +1,85 @@
+"""ctypes declarations of libflashhead's C ABI (include/flashhead.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation of any step.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashhead.so")
+
+FH_OK, FH_EINVAL, FH_ENOMEM, FH_EHIP, FH_EUNSUPPORTED = 0, -1, -2, -3, -4
+FH_F32, FH_BF16 = 0, 1
+FH_QUANT_NONE, FH_QUANT_INT4_G32 = 0, 1
+FH_PROBE_TOPK, FH_PROBE_SAMPLE, FH_TOKEN_ARGMAX, FH_TOKEN_SAMPLE = 0, 1, 0, 2
+
+# Every symbol the header declares.
+EXPORTS = (
+    "fh_create", "fh_destroy", "fh_forward", "fh_score", "fh_dense_forward",
+    "fh_get_int4", "fh_profile_begin", "fh_profile_end", "fh_last_error", "fh_version",
+)
+
+
+class FhKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
+
+
+class FlashHeadError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"flashhead status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_u64 = ctypes.c_uint64
+_int = ctypes.c_int
+_f = ctypes.c_float
+
+_SIGS = {
+    "fh_create": ([_p, _p, _p, _int, _i64, _i64, _i64, _int, _i64, _p, ctypes.POINTER(_p)], _int),
+    "fh_destroy": ([_p], None),
+    "fh_forward": ([_p, _p, _i64, _i64, _int, _f, _u64, _p, _p, _p, _p, _p, _p, _p], _int),
+    "fh_score": ([_p, _p, _i64, _p, _p], _int),
+    "fh_dense_forward": ([_p, _p, _i64, _int, _f, _u64, _p, _p, _p, _p, _p], _int),
+    "fh_get_int4": ([_p, _p, _p, _p], _int),
+    "fh_profile_begin": ([_p, _i64], _int),
+    "fh_profile_end": ([_p, ctypes.POINTER(FhKernelTime), _int, ctypes.POINTER(_int)], _int),
+    "fh_last_error": ([], ctypes.c_char_p),
+    "fh_version": ([], ctypes.c_char_p),
+}
+
+
+def lib_path() -> str:
+    return os.environ.get("FLASHHEAD_LIB", LIB)
+
+
+def load() -> ctypes.CDLL:
+    """Load libflashhead.so (built in-tree) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m lm_output_head_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != FH_OK:
+        msg = load().fh_last_error().decode(errors="replace")
+        raise FlashHeadError(status, msg)

@@ -1,0 +1,170 @@
+// Device-side helpers shared by the FlashHead kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cfloat>
+
+#include "fh_internal.hpp"
+
+namespace fh {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- numerics --
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// a.x*b.x + a.y*b.y + acc over packed bfloat16 pairs, float32 accumulate.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Dot product of one 16-byte chunk: 8 bfloat16 or 4 float32 elements.
+template <typename T>
+struct Chunk;
+
+template <>
+struct Chunk<uint16_t> {  // bfloat16 bit patterns
+  static constexpr int kElems = 8;
+  __device__ __forceinline__ static float dot(const uint4& a, const uint4& b, float acc) {
+    acc = dot2_bf16(a.x, b.x, acc);
+    acc = dot2_bf16(a.y, b.y, acc);
+    acc = dot2_bf16(a.z, b.z, acc);
+    acc = dot2_bf16(a.w, b.w, acc);
+    return acc;
+  }
+};
+
+template <>
+struct Chunk<float> {
+  static constexpr int kElems = 4;
+  __device__ __forceinline__ static float dot(const uint4& a, const uint4& b, float acc) {
+    acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+    acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+    acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+    acc = fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+    return acc;
+  }
+};
+
+// ------------------------------------------------------------ wave helpers --
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_min(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fminf(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+
+// Inclusive prefix sum across the wave (lane order).
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// ------------------------------------------------------------------ Philox --
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds over a
+// 128-bit counter with a 64-bit key; counter words 0 and 2 are multiplied by
+// two fixed odd constants, the product halves are mixed with the other
+// words and the key, and the key advances by two Weyl increments per round.
+
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 philox4x32_10(U4 ctr, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t a = 0xD2511F53u * ctr.x;
+    const uint32_t ah = __umulhi(0xD2511F53u, ctr.x);
+    const uint32_t c = 0xCD9E8D57u * ctr.z;
+    const uint32_t ch = __umulhi(0xCD9E8D57u, ctr.z);
+    ctr = U4{ch ^ ctr.y ^ k0, c, ah ^ ctr.w ^ k1, a};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return ctr;
+}
+
+// The four Philox words of block `blk` (= index / 4) for (seed, row, stage).
+__device__ __forceinline__ U4 philox_block(uint64_t seed, uint32_t row, uint32_t blk,
+                                           uint32_t stage) {
+  return philox4x32_10(U4{blk, row, stage, 0u}, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t u4_word(const U4& u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+// Standard Gumbel variate from one 32-bit word: u = ((w >> 9) + 1/2) 2^-23
+// lies in (0, 1) and is exact in float32; G = -ln(-ln u).
+__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
+  const float u = ((float)(w >> 9) + 0.5f) * 1.1920928955078125e-07f;
+  return -logf(-logf(u));
+}
+
+__device__ __forceinline__ float gumbel_at(uint64_t seed, uint32_t row, uint32_t index,
+                                           uint32_t stage) {
+  const U4 blk = philox_block(seed, row, index >> 2, stage);
+  return gumbel_from_word(u4_word(blk, index & 3));
+}
+
+// ------------------------------------------------------ epilogue partials --
+// A partial result over a set of candidate tokens: the best (key, id) pair
+// with the logit of that token, and (m, s) with m = max x, s = sum exp(x - m)
+// for x = z / T'.
+
+
+__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+__device__ __forceinline__ Part part_empty() {
+  return Part{-INFINITY, 0.f, -INFINITY, 0.f, 0x7FFFFFFF};
+}
+
+__device__ __forceinline__ Part part_merge(const Part& a, const Part& b) {
+  Part r;
+  if (better(b.key, b.id, a.key, a.id)) {
+    r.key = b.key; r.id = b.id; r.z = b.z;
+  } else {
+    r.key = a.key; r.id = a.id; r.z = a.z;
+  }
+  const float m = fmaxf(a.m, b.m);
+  if (m == -INFINITY) {
+    r.m = m; r.s = 0.f;
+  } else {
+    r.m = m;
+    r.s = a.s * expf(a.m - m) + b.s * expf(b.m - m);
+  }
+  return r;
+}
+
+}  // namespace fh

@@ -1,0 +1,394 @@
+// libflashhead C ABI: argument checking, ownership and launch sequencing.
+//
+// The path per call follows the FlashHead computation graph (explainer,
+// framerc.cn, §2.2.2): centroid scores -> top-p (or sampled) clusters ->
+// retrieved-token scores -> argmax / sample.  Every step runs in the HIP
+// kernels of fh_kernels.hip; this file only checks arguments, owns device
+// buffers and enqueues work on the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <algorithm>
+#include <new>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "fh_internal.hpp"
+#include "flashhead.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+fh_status fail(fh_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+fh_status hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return e == hipErrorOutOfMemory ? FH_ENOMEM : FH_EHIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxC = 16384;
+
+}  // namespace
+
+struct fh_engine {
+  int device = 0;
+  fh_dtype dtype = FH_BF16;
+  fh_quant quant = FH_QUANT_NONE;
+  int64_t v = 0, d = 0, c = 0, b = 0, max_batch = 0;
+  const void* E = nullptr;
+  const void* C = nullptr;
+  int32_t* c2t = nullptr;
+  uint8_t* cq = nullptr;
+  uint16_t* csig = nullptr;
+  float* scores = nullptr;   // [max_batch x c]
+  int32_t* sel = nullptr;    // [max_batch x c]
+  fh::Part* parts = nullptr;  // [max_batch x parts_per_q]
+  int64_t parts_per_q = 0;
+  // per-kernel timing
+  bool prof = false;
+  int64_t prof_cap = 0, prof_n = 0;
+  std::vector<hipEvent_t> prof_ev;
+  std::vector<const char*> prof_name;
+
+  fh::KernelCtx ctx(hipStream_t st) const {
+    fh::KernelCtx k;
+    k.bf16 = dtype == FH_BF16;
+    k.E = E;
+    k.C = C;
+    k.c2t = c2t;
+    k.cq = cq;
+    k.csig = csig;
+    k.v = v;
+    k.c = c;
+    k.b = b;
+    k.d = (int)d;
+    k.stream = st;
+    return k;
+  }
+};
+
+namespace {
+
+// Run one launcher, bracketed by profiling events when profiling is on.
+template <typename F>
+hipError_t timed(fh_engine* e, hipStream_t st, const char* name, F&& launch) {
+  const bool rec = e->prof && e->prof_n < e->prof_cap;
+  if (rec) {
+    hipError_t r = hipEventRecord(e->prof_ev[2 * e->prof_n], st);
+    if (r != hipSuccess) return r;
+  }
+  hipError_t r = launch();
+  if (r != hipSuccess) return r;
+  if (rec) {
+    r = hipEventRecord(e->prof_ev[2 * e->prof_n + 1], st);
+    if (r != hipSuccess) return r;
+    e->prof_name[e->prof_n] = name;
+    e->prof_n++;
+  }
+  return hipSuccess;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+void free_engine(fh_engine* e) {
+  if (!e) return;
+  (void)hipFree(e->c2t);
+  (void)hipFree(e->cq);
+  (void)hipFree(e->csig);
+  (void)hipFree(e->scores);
+  (void)hipFree(e->sel);
+  (void)hipFree(e->parts);
+  for (hipEvent_t ev : e->prof_ev) (void)hipEventDestroy(ev);
+  delete e;
+}
+
+fh_status check_common(const fh_engine* e, const void* h, int64_t B) {
+  if (!e) return fail(FH_EINVAL, "engine is NULL");
+  if (!h) return fail(FH_EINVAL, "h is NULL");
+  if (!aligned16(h)) return fail(FH_EINVAL, "h must be 16-byte aligned");
+  if (B < 1 || B > e->max_batch)
+    return fail(FH_EINVAL, "B=" + std::to_string(B) + " outside [1, max_batch=" +
+                               std::to_string(e->max_batch) + "]");
+  return FH_OK;
+}
+
+fh_status check_mode(int mode, float temperature) {
+  if (mode < 0 || mode > 3) return fail(FH_EINVAL, "mode must be FH_PROBE_* | FH_TOKEN_*");
+  if (mode != 0 && !(temperature > 0.f && std::isfinite(temperature)))
+    return fail(FH_EINVAL, "sampling needs a finite temperature > 0");
+  return FH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fh_last_error(void) { return g_err.c_str(); }
+
+const char* fh_version(void) { return "flashhead-mi355x 0.1.0 (gfx950)"; }
+
+fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype dtype, int64_t v,
+                    int64_t d, int64_t c, fh_quant quant, int64_t max_batch, void* stream,
+                    fh_engine** out) {
+  g_err.clear();
+  if (!out) return fail(FH_EINVAL, "out is NULL");
+  if (!E || !C || !C2T) return fail(FH_EINVAL, "E, C and C2T must be non-NULL");
+  if (dtype != FH_F32 && dtype != FH_BF16) return fail(FH_EINVAL, "unknown dtype");
+  if (quant != FH_QUANT_NONE && quant != FH_QUANT_INT4_G32) return fail(FH_EINVAL, "unknown quant");
+  if (v <= 0 || d <= 0 || c <= 0) return fail(FH_EINVAL, "v, d and c must be positive");
+  if (v % c != 0) return fail(FH_EINVAL, "v must be a multiple of c (balanced clusters)");
+  if (v >= (int64_t(1) << 31)) return fail(FH_EUNSUPPORTED, "v must be below 2^31");
+  if (c > kMaxC) return fail(FH_EUNSUPPORTED, "c above 16384 is not supported");
+  const int epc = dtype == FH_BF16 ? 8 : 4;
+  if (d % epc != 0)
+    return fail(FH_EINVAL, dtype == FH_BF16 ? "bf16 needs d % 8 == 0" : "f32 needs d % 4 == 0");
+  if (d > 64 * 8 * epc) return fail(FH_EUNSUPPORTED, "d too large for this build");
+  if (quant == FH_QUANT_INT4_G32 && d % 32 != 0)
+    return fail(FH_EUNSUPPORTED, "INT4 g32 needs d % 32 == 0");
+  if (max_batch < 1 || max_batch > 65535) return fail(FH_EINVAL, "max_batch outside [1, 65535]");
+  if (!aligned16(E) || !aligned16(C)) return fail(FH_EINVAL, "E and C must be 16-byte aligned");
+  const int64_t b = v / c;
+  {  // balanced clustering: C2T is a permutation of [0, v)
+    std::vector<uint8_t> seen((size_t)v, 0);
+    for (int64_t i = 0; i < v; ++i) {
+      const int32_t t = C2T[i];
+      if (t < 0 || t >= v) return fail(FH_EINVAL, "C2T holds a token id outside [0, v)");
+      if (seen[(size_t)t]) return fail(FH_EINVAL, "C2T lists a token twice (not a permutation)");
+      seen[(size_t)t] = 1;
+    }
+  }
+
+  fh_engine* e = new (std::nothrow) fh_engine();
+  if (!e) return fail(FH_ENOMEM, "host allocation failed");
+  e->dtype = dtype;
+  e->quant = quant;
+  e->v = v;
+  e->d = d;
+  e->c = c;
+  e->b = b;
+  e->max_batch = max_batch;
+  e->E = E;
+  e->C = C;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t r = hipGetDevice(&e->device);
+  if (r != hipSuccess) { free_engine(e); return hip_fail(r, "hipGetDevice"); }
+
+  e->parts_per_q = std::max(fh::rows_blocks(v, fh::kGatherRPW), fh::rows_blocks(v, fh::kDenseRPW));
+  struct Alloc { void** p; size_t bytes; const char* what; };
+  const Alloc allocs[] = {
+      {(void**)&e->c2t, sizeof(int32_t) * (size_t)v, "C2T"},
+      {(void**)&e->scores, sizeof(float) * (size_t)(max_batch * c), "scores"},
+      {(void**)&e->sel, sizeof(int32_t) * (size_t)(max_batch * c), "selection"},
+      {(void**)&e->parts, sizeof(fh::Part) * (size_t)(max_batch * e->parts_per_q), "partials"},
+  };
+  for (const Alloc& a : allocs) {
+    r = hipMalloc(a.p, a.bytes);
+    if (r != hipSuccess) { free_engine(e); return hip_fail(r, a.what); }
+  }
+  r = hipMemcpyAsync(e->c2t, C2T, sizeof(int32_t) * (size_t)v, hipMemcpyHostToDevice, st);
+  if (r != hipSuccess) { free_engine(e); return hip_fail(r, "copy C2T"); }
+
+  if (quant == FH_QUANT_INT4_G32) {
+    int* bad = nullptr;
+    r = hipMalloc((void**)&e->cq, (size_t)(c * d / 2));
+    if (r == hipSuccess) r = hipMalloc((void**)&e->csig, sizeof(uint16_t) * (size_t)(c * d / 32));
+    if (r == hipSuccess) r = hipMalloc((void**)&bad, sizeof(int));
+    if (r == hipSuccess) r = hipMemsetAsync(bad, 0, sizeof(int), st);
+    if (r == hipSuccess) r = fh::launch_quant_int4(e->ctx(st), bad);
+    int hbad = 0;
+    if (r == hipSuccess) r = hipMemcpyAsync(&hbad, bad, sizeof(int), hipMemcpyDeviceToHost, st);
+    if (r == hipSuccess) r = hipStreamSynchronize(st);
+    (void)hipFree(bad);
+    if (r != hipSuccess) { free_engine(e); return hip_fail(r, "INT4 quantisation"); }
+    if (hbad) { free_engine(e); return fail(FH_EINVAL, "a centroid group's INT4 scale overflows fp16"); }
+    e->C = nullptr;  // not borrowed in INT4 mode
+  } else {
+    r = hipStreamSynchronize(st);
+    if (r != hipSuccess) { free_engine(e); return hip_fail(r, "create"); }
+  }
+  *out = e;
+  return FH_OK;
+}
+
+void fh_destroy(fh_engine* e) {
+  if (!e) return;
+  DeviceGuard g(e->device);
+  (void)hipDeviceSynchronize();
+  free_engine(e);
+}
+
+fh_status fh_score(fh_engine* e, const void* h, int64_t B, float* out_scores, void* stream) {
+  g_err.clear();
+  fh_status s = check_common(e, h, B);
+  if (s != FH_OK) return s;
+  if (!out_scores) return fail(FH_EINVAL, "out_scores is NULL");
+  DeviceGuard g(e->device);
+  if (!g.ok) return fail(FH_EHIP, "cannot select the engine's device");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const fh::KernelCtx k = e->ctx(st);
+  hipError_t r = timed(e, st, e->quant == FH_QUANT_INT4_G32 ? "score_int4" : "score", [&] {
+    return e->quant == FH_QUANT_INT4_G32 ? fh::launch_score_int4(k, h, (int)B, out_scores)
+                                         : fh::launch_score(k, h, (int)B, out_scores);
+  });
+  return r == hipSuccess ? FH_OK : hip_fail(r, "score launch");
+}
+
+fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode, float temperature,
+                     uint64_t seed, int32_t* out_token, float* out_token_logit, float* out_lse,
+                     int32_t* out_clusters, int32_t* out_ids, float* out_logits, void* stream) {
+  g_err.clear();
+  fh_status s = check_common(e, h, B);
+  if (s != FH_OK) return s;
+  if (p < 1 || p > e->c)
+    return fail(FH_EINVAL, "p=" + std::to_string(p) + " outside [1, c=" + std::to_string(e->c) + "]");
+  s = check_mode(mode, temperature);
+  if (s != FH_OK) return s;
+  DeviceGuard g(e->device);
+  if (!g.ok) return fail(FH_EHIP, "cannot select the engine's device");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const fh::KernelCtx k = e->ctx(st);
+  const int probe_sample = mode & FH_PROBE_SAMPLE;
+  const int token_sample = (mode & FH_TOKEN_SAMPLE) ? 1 : 0;
+  const float tprime = token_sample ? temperature : 1.f;
+  int32_t* S = out_clusters ? out_clusters : e->sel;
+
+  hipError_t r = timed(e, st, e->quant == FH_QUANT_INT4_G32 ? "score_int4" : "score", [&] {
+    return e->quant == FH_QUANT_INT4_G32 ? fh::launch_score_int4(k, h, (int)B, e->scores)
+                                         : fh::launch_score(k, h, (int)B, e->scores);
+  });
+  if (r != hipSuccess) return hip_fail(r, "score launch");
+  r = timed(e, st, "select", [&] {
+    return fh::launch_select(k, e->scores, (int)B, (int)p, probe_sample, temperature, seed, S, (int)p);
+  });
+  if (r != hipSuccess) return hip_fail(r, "select launch");
+  int64_t nparts = 0;
+  r = timed(e, st, "gather", [&] {
+    return fh::launch_gather(k, h, (int)B, S, (int)p, token_sample, tprime, seed, out_ids,
+                             out_logits, e->parts, &nparts);
+  });
+  if (r != hipSuccess) return hip_fail(r, "gather launch");
+  r = timed(e, st, "finish", [&] {
+    return fh::launch_finish(k, e->parts, (int)B, nparts, out_token, out_token_logit, out_lse);
+  });
+  if (r != hipSuccess) return hip_fail(r, "finish launch");
+  return FH_OK;
+}
+
+fh_status fh_dense_forward(fh_engine* e, const void* h, int64_t B, int mode, float temperature,
+                           uint64_t seed, int32_t* out_token, float* out_token_logit,
+                           float* out_lse, float* out_logits, void* stream) {
+  g_err.clear();
+  fh_status s = check_common(e, h, B);
+  if (s != FH_OK) return s;
+  if (mode & FH_PROBE_SAMPLE) return fail(FH_EINVAL, "the dense head has no probe stage");
+  s = check_mode(mode, temperature);
+  if (s != FH_OK) return s;
+  DeviceGuard g(e->device);
+  if (!g.ok) return fail(FH_EHIP, "cannot select the engine's device");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const fh::KernelCtx k = e->ctx(st);
+  const int token_sample = (mode & FH_TOKEN_SAMPLE) ? 1 : 0;
+  const float tprime = token_sample ? temperature : 1.f;
+  int64_t nparts = 0;
+  hipError_t r = timed(e, st, "dense", [&] {
+    return fh::launch_dense(k, h, (int)B, token_sample, tprime, seed, out_logits, e->parts, &nparts);
+  });
+  if (r != hipSuccess) return hip_fail(r, "dense launch");
+  r = timed(e, st, "finish", [&] {
+    return fh::launch_finish(k, e->parts, (int)B, nparts, out_token, out_token_logit, out_lse);
+  });
+  if (r != hipSuccess) return hip_fail(r, "finish launch");
+  return FH_OK;
+}
+
+fh_status fh_get_int4(fh_engine* e, uint8_t* packed, uint16_t* scales, void* stream) {
+  g_err.clear();
+  if (!e) return fail(FH_EINVAL, "engine is NULL");
+  if (e->quant != FH_QUANT_INT4_G32) return fail(FH_EINVAL, "engine is not INT4");
+  if (!packed || !scales) return fail(FH_EINVAL, "NULL output");
+  DeviceGuard g(e->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t r = hipMemcpyAsync(packed, e->cq, (size_t)(e->c * e->d / 2), hipMemcpyDeviceToDevice, st);
+  if (r == hipSuccess)
+    r = hipMemcpyAsync(scales, e->csig, sizeof(uint16_t) * (size_t)(e->c * e->d / 32),
+                       hipMemcpyDeviceToDevice, st);
+  return r == hipSuccess ? FH_OK : hip_fail(r, "copy INT4 centroids");
+}
+
+fh_status fh_profile_begin(fh_engine* e, int64_t max_launches) {
+  g_err.clear();
+  if (!e) return fail(FH_EINVAL, "engine is NULL");
+  if (max_launches < 1 || max_launches > (1 << 20)) return fail(FH_EINVAL, "max_launches outside [1, 2^20]");
+  DeviceGuard g(e->device);
+  for (hipEvent_t ev : e->prof_ev) (void)hipEventDestroy(ev);
+  e->prof_ev.assign((size_t)(2 * max_launches), nullptr);
+  e->prof_name.assign((size_t)max_launches, nullptr);
+  for (auto& ev : e->prof_ev) {
+    hipError_t r = hipEventCreate(&ev);
+    if (r != hipSuccess) {
+      e->prof = false;
+      return hip_fail(r, "hipEventCreate");
+    }
+  }
+  e->prof_cap = max_launches;
+  e->prof_n = 0;
+  e->prof = true;
+  return FH_OK;
+}
+
+fh_status fh_profile_end(fh_engine* e, fh_kernel_time* out, int max, int* count) {
+  g_err.clear();
+  if (!e) return fail(FH_EINVAL, "engine is NULL");
+  if (!e->prof) return fail(FH_EINVAL, "profiling was not started");
+  DeviceGuard g(e->device);
+  e->prof = false;
+  std::vector<std::pair<const char*, std::pair<int64_t, double>>> agg;
+  for (int64_t i = 0; i < e->prof_n; ++i) {
+    hipError_t r = hipEventSynchronize(e->prof_ev[2 * i + 1]);
+    if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
+    float ms = 0.f;
+    r = hipEventElapsedTime(&ms, e->prof_ev[2 * i], e->prof_ev[2 * i + 1]);
+    if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");
+    const char* nm = e->prof_name[i];
+    size_t j = 0;
+    while (j < agg.size() && std::strcmp(agg[j].first, nm) != 0) ++j;
+    if (j == agg.size()) agg.push_back({nm, {0, 0.0}});
+    agg[j].second.first += 1;
+    agg[j].second.second += ms;
+  }
+  int n = 0;
+  for (size_t j = 0; j < agg.size() && n < max; ++j, ++n) {
+    out[n].name = agg[j].first;
+    out[n].launches = agg[j].second.first;
+    out[n].total_ms = agg[j].second.second;
+  }
+  if (count) *count = n;
+  for (hipEvent_t ev : e->prof_ev) (void)hipEventDestroy(ev);
+  e->prof_ev.clear();
+  e->prof_name.clear();
+  e->prof_n = e->prof_cap = 0;
+  return FH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal interface between the C-ABI engine and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fh {
+
+// A partial epilogue result over a set of candidate tokens: the best
+// (key, id) pair with the logit z of that token, and (m, s) with
+// m = max x, s = sum exp(x - m) over x = z / T'.
+struct Part {
+  float key;
+  float z;
+  float m;
+  float s;
+  int32_t id;
+};
+
+// Rows per wave of each row-GEMV launch.
+constexpr int kScoreRPW = 2;
+constexpr int kGatherRPW = 2;
+constexpr int kDenseRPW = 4;
+constexpr int kInt4RPW = 2;
+
+// What every launcher needs to know about the engine and the call.
+struct KernelCtx {
+  bool bf16;
+  const void* E;
+  const void* C;
+  const int32_t* c2t;
+  const uint8_t* cq;
+  const uint16_t* csig;
+  int64_t v, c, b;
+  int d;
+  hipStream_t stream;
+};
+
+int64_t rows_blocks(int64_t nrows, int rpw);
+
+hipError_t launch_quant_int4(const KernelCtx& k, int* bad);
+hipError_t launch_score(const KernelCtx& k, const void* h, int B, float* out);
+hipError_t launch_score_int4(const KernelCtx& k, const void* h, int B, float* out);
+hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, int sample,
+                         float temperature, uint64_t seed, int32_t* S, int ldS);
+hipError_t launch_gather(const KernelCtx& k, const void* h, int B, const int32_t* S, int p,
+                         int token_sample, float tprime, uint64_t seed, int32_t* out_ids,
+                         float* out_logits, Part* parts, int64_t* nparts);
+hipError_t launch_dense(const KernelCtx& k, const void* h, int B, int token_sample, float tprime,
+                        uint64_t seed, float* out_logits, Part* parts, int64_t* nparts);
+hipError_t launch_finish(const KernelCtx& k, const Part* parts, int B, int64_t nparts,
+                         int32_t* out_token, float* out_logit, float* out_lse);
+
+}  // namespace fh

@@ -1,0 +1,180 @@
+"""Thin Python binding of libflashhead: torch tensors in, C-ABI calls out.
+
+Functions named like the C entry points (``fh_create``, ``fh_forward`` ...)
+only marshal arguments: they check tensor placement and dtype, pass raw
+pointers and the current HIP stream, and raise on a non-OK status.  All
+computation runs in the library's HIP kernels.  ``FlashHead`` wraps an engine
+with output allocation for convenience.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _abi
+from ._abi import (FH_BF16, FH_F32, FH_PROBE_SAMPLE, FH_PROBE_TOPK, FH_QUANT_INT4_G32,  # noqa: F401
+                   FH_QUANT_NONE, FH_TOKEN_ARGMAX, FH_TOKEN_SAMPLE, FlashHeadError, check)
+
+_DTYPES = {torch.float32: FH_F32, torch.bfloat16: FH_BF16}
+_QUANTS = {"none": FH_QUANT_NONE, "int4": FH_QUANT_INT4_G32}
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors passed to libflashhead must be contiguous GPU tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(t, dtype, shape, name):
+    if t is None:
+        return
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def fh_version() -> str:
+    return _abi.load().fh_version().decode()
+
+
+def fh_last_error() -> str:
+    return _abi.load().fh_last_error().decode()
+
+
+def fh_create(E: torch.Tensor, C: torch.Tensor, C2T, quant: str = "none", max_batch: int = 1,
+              stream=None) -> ctypes.c_void_p:
+    """Create an engine.  E [v x d] and C [c x d] on the GPU (float32 or
+    bfloat16, same dtype); C2T [c x b] int32 on the host (numpy or CPU tensor)."""
+    lib = _abi.load()
+    if E.dtype not in _DTYPES or C.dtype != E.dtype:
+        raise ValueError("E and C must share dtype float32 or bfloat16")
+    c2t = np.ascontiguousarray(np.asarray(C2T), dtype=np.int32)
+    v, d = E.shape
+    c = C.shape[0]
+    if C.shape[1] != d or c2t.size != v:
+        raise ValueError("inconsistent shapes of E, C and C2T")
+    eng = ctypes.c_void_p()
+    check(lib.fh_create(_ptr(E), _ptr(C), c2t.ctypes.data_as(ctypes.c_void_p), _DTYPES[E.dtype],
+                        v, d, c, _QUANTS[quant], max_batch, _stream(stream), ctypes.byref(eng)))
+    return eng
+
+
+def fh_destroy(eng) -> None:
+    _abi.load().fh_destroy(eng)
+
+
+def fh_forward(eng, h, p, mode, temperature, seed, out_token, out_token_logit=None, out_lse=None,
+               out_clusters=None, out_ids=None, out_logits=None, stream=None) -> None:
+    check(_abi.load().fh_forward(eng, _ptr(h), h.shape[0], p, mode, temperature, seed,
+                                 _ptr(out_token), _ptr(out_token_logit), _ptr(out_lse),
+                                 _ptr(out_clusters), _ptr(out_ids), _ptr(out_logits),
+                                 _stream(stream)))
+
+
+def fh_score(eng, h, out_scores, stream=None) -> None:
+    check(_abi.load().fh_score(eng, _ptr(h), h.shape[0], _ptr(out_scores), _stream(stream)))
+
+
+def fh_dense_forward(eng, h, mode, temperature, seed, out_token, out_token_logit=None,
+                     out_lse=None, out_logits=None, stream=None) -> None:
+    check(_abi.load().fh_dense_forward(eng, _ptr(h), h.shape[0], mode, temperature, seed,
+                                       _ptr(out_token), _ptr(out_token_logit), _ptr(out_lse),
+                                       _ptr(out_logits), _stream(stream)))
+
+
+def fh_get_int4(eng, packed, scales, stream=None) -> None:
+    check(_abi.load().fh_get_int4(eng, _ptr(packed), _ptr(scales), _stream(stream)))
+
+
+def fh_profile_begin(eng, max_launches: int) -> None:
+    check(_abi.load().fh_profile_begin(eng, max_launches))
+
+
+def fh_profile_end(eng) -> dict:
+    """Per-kernel {name: (launches, total_ms)} since fh_profile_begin."""
+    recs = (_abi.FhKernelTime * 64)()
+    n = ctypes.c_int(0)
+    check(_abi.load().fh_profile_end(eng, recs, 64, ctypes.byref(n)))
+    return {recs[i].name.decode(): (recs[i].launches, recs[i].total_ms) for i in range(n.value)}
+
+
+class FlashHead:
+    """An engine over one head, with output allocation.
+
+    ``E`` and ``C`` stay borrowed by the engine; this object keeps references
+    to them so they outlive it.
+    """
+
+    def __init__(self, E: torch.Tensor, C: torch.Tensor, C2T, quant: str = "none",
+                 max_batch: int = 1, stream=None):
+        self.v, self.d = E.shape
+        self.c = C.shape[0]
+        self.b = self.v // self.c
+        self.quant = quant
+        self.max_batch = max_batch
+        self.device = E.device
+        self._E = E
+        self._C = C if quant == "none" else None
+        self.eng = fh_create(E, C, C2T, quant, max_batch, stream)
+
+    def close(self):
+        if getattr(self, "eng", None) is not None:
+            fh_destroy(self.eng)
+            self.eng = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _alloc(self, shape, dtype):
+        return torch.empty(shape, dtype=dtype, device=self.device)
+
+    def forward(self, h: torch.Tensor, p: int, mode: int = 0, temperature: float = 1.0,
+                seed: int = 0, want_clusters: bool = False, want_retrieved: bool = False,
+                stream=None) -> dict:
+        B = h.shape[0]
+        out = {"token": self._alloc((B,), torch.int32),
+               "token_logit": self._alloc((B,), torch.float32),
+               "lse": self._alloc((B,), torch.float32)}
+        if want_clusters:
+            out["clusters"] = self._alloc((B, p), torch.int32)
+        if want_retrieved:
+            out["ids"] = self._alloc((B, p * self.b), torch.int32)
+            out["logits"] = self._alloc((B, p * self.b), torch.float32)
+        fh_forward(self.eng, h, p, mode, temperature, seed, out["token"], out["token_logit"],
+                   out["lse"], out.get("clusters"), out.get("ids"), out.get("logits"), stream)
+        return out
+
+    def score(self, h: torch.Tensor, stream=None) -> torch.Tensor:
+        out = self._alloc((h.shape[0], self.c), torch.float32)
+        fh_score(self.eng, h, out, stream)
+        return out
+
+    def dense(self, h: torch.Tensor, mode: int = 0, temperature: float = 1.0, seed: int = 0,
+              want_logits: bool = False, stream=None) -> dict:
+        B = h.shape[0]
+        out = {"token": self._alloc((B,), torch.int32),
+               "token_logit": self._alloc((B,), torch.float32),
+               "lse": self._alloc((B,), torch.float32)}
+        if want_logits:
+            out["logits"] = self._alloc((B, self.v), torch.float32)
+        fh_dense_forward(self.eng, h, mode, temperature, seed, out["token"], out["token_logit"],
+                         out["lse"], out.get("logits"), stream)
+        return out
+
+    def int4(self, stream=None):
+        packed = self._alloc((self.c, self.d // 2), torch.uint8)
+        scales = self._alloc((self.c, self.d // 32), torch.int16)
+        fh_get_int4(self.eng, packed, scales, stream)
+        return packed, scales

@@ -148,13 +148,15 @@ class Selection:
     theta: np.ndarray  # float32 [B] the p-th largest key32 per row
 
 
-def probe_keys(s: np.ndarray, mode: int, temperature: float, seed: int) -> np.ndarray:
+def probe_keys(s: np.ndarray, mode: int, temperature: float, seed: int,
+               rows=None) -> np.ndarray:
     """Selection keys: the score itself, or score/T plus Gumbel noise.
 
     Drawing p distinct clusters one after another from softmax(s/T) without
     replacement is the same as taking the top p of s/T + G with independent
     standard Gumbel G (Gumbel-top-k: Yellott 1977; Kool, van Hoof and
-    Welling 2019).  Noise for row b, cluster k is gumbel(seed, b, k, stage 0).
+    Welling 2019).  Noise for row b, cluster k is gumbel(seed, b, k, stage 0);
+    ``rows`` gives the row indices b of s's rows (default 0..B-1).
     """
     s = np.atleast_2d(np.asarray(s, dtype=np.float64))
     if not (mode & MODE_PROBE_SAMPLE):
@@ -162,7 +164,8 @@ def probe_keys(s: np.ndarray, mode: int, temperature: float, seed: int) -> np.nd
     if not temperature > 0:
         raise ValueError("sampling needs temperature > 0")
     B, c = s.shape
-    g = gumbel(seed, np.arange(B)[:, None], np.arange(c)[None, :], 0)
+    rows = np.arange(B) if rows is None else np.asarray(rows)
+    g = gumbel(seed, rows[:, None], np.arange(c)[None, :], 0)
     return s / float(temperature) + g
 
 
@@ -173,13 +176,13 @@ def _top_ids(key32_row: np.ndarray, ids_row: np.ndarray, n: int) -> np.ndarray:
 
 
 def select(s: np.ndarray, p: int, mode: int = 0, temperature: float = 1.0,
-           seed: int = 0) -> Selection:
+           seed: int = 0, rows=None) -> Selection:
     """Pick p clusters per row: the p largest keys, returned in ascending id.
 
     Top-p here counts clusters (the pages' p probes), not nucleus mass.  Keys
     are compared in float32; equal keys go to the smaller cluster id.
     """
-    key = probe_keys(s, mode, temperature, seed)
+    key = probe_keys(s, mode, temperature, seed, rows)
     B, c = key.shape
     if not 1 <= p <= c:
         raise ValueError(f"p={p} outside [1, c={c}]")
@@ -226,7 +229,7 @@ class Finish:
 
 
 def finish(ids: np.ndarray, z: np.ndarray, mode: int = 0, temperature: float = 1.0,
-           seed: int = 0) -> Finish:
+           seed: int = 0, rows=None) -> Finish:
     """Argmax, or one draw from softmax(z/T), over each row's candidates.
 
     Sampling is Gumbel-max: argmax of z/T + gumbel(seed, b, t, stage 1),
@@ -234,6 +237,7 @@ def finish(ids: np.ndarray, z: np.ndarray, mode: int = 0, temperature: float = 1
     in the candidate list.  The choice is taken on float32 keys, ties to the
     smaller token id.  LSE = log sum_t exp(z_t / T') with T' = T when the
     token is sampled and 1 otherwise, computed with the max shifted out.
+    ``rows`` gives the row indices b of the rows (default 0..B-1).
     """
     ids = np.atleast_2d(np.asarray(ids, dtype=np.int64))
     z = np.atleast_2d(np.asarray(z, dtype=np.float64))
@@ -243,7 +247,8 @@ def finish(ids: np.ndarray, z: np.ndarray, mode: int = 0, temperature: float = 1
         raise ValueError("sampling needs temperature > 0")
     tp = float(temperature) if sample else 1.0
     if sample:
-        key = z / tp + gumbel(seed, np.arange(B)[:, None], ids, 1)
+        rows = np.arange(B) if rows is None else np.asarray(rows)
+        key = z / tp + gumbel(seed, rows[:, None], ids, 1)
     else:
         key = z.copy()
     key32 = key.astype(np.float32)

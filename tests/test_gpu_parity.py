@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case runs the engine (libflashhead via the thin binding) and the
+float64 oracle on the same seeded inputs and applies the parity rule of
+oracle/parity.py: exact ids up to certified near-ties (gap < 1e-3), logits
+within 2e-3 relative (with a one-bfloat16-quantum Cauchy-Schwarz floor).
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import parity
+from synth import SHAPES, Shape, make_problem
+
+from _gpu import assert_report, host, need_gpu, problem_tensors, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOPK, PSAMPLE, TSAMPLE = 0, 1, 2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    from lm_output_head_amd import load_library
+    load_library()
+
+
+def _engine(pb, quant="none", max_batch=1):
+    from lm_output_head_amd import FlashHead
+    E, C, H = problem_tensors(pb)
+    return FlashHead(E, C, pb.C2T, quant=quant, max_batch=max_batch), H
+
+
+def _oracle(pb, quant="none"):
+    return oracle.OracleHead(pb.E, pb.C, pb.C2T, quant)
+
+
+# ---------------------------------------------------------------- fixture ---
+
+def test_toy_fixture_on_gpu():
+    """The hand-worked toy head, padded to d = 4 with zero columns (fp32)."""
+    from lm_output_head_amd import FlashHead
+    with open(os.path.join(os.path.dirname(__file__), "golden", "toy_two_stage.json")) as f:
+        g = json.load(f)
+    pad = lambda a: np.pad(np.array(a, dtype=np.float32), ((0, 0), (0, 2)))  # noqa: E731
+    E, C = torch.from_numpy(pad(g["E"])).cuda(), torch.from_numpy(pad(g["C"])).cuda()
+    head = FlashHead(E, C, np.array(g["C2T"], dtype=np.int32), max_batch=1)
+    for case in g["cases"]:
+        h = torch.from_numpy(pad([case["h"]])).cuda()
+        say("toy", case["h"])
+        assert host({"s": head.score(h)})["s"][0].tolist() == case["scores"]
+        dn = host(head.dense(h, want_logits=True))
+        assert dn["token"][0] == case["dense_token"]
+        assert dn["logits"][0].tolist() == case["dense_z"]
+        for p, want in case["by_p"].items():
+            out = host(head.forward(h, int(p), want_clusters=True, want_retrieved=True))
+            assert out["clusters"][0].tolist() == want["S"]
+            assert out["ids"][0].tolist() == want["ids"]
+            assert out["logits"][0].tolist() == want["z"]
+            assert out["token"][0] == want["token"]
+            assert out["token_logit"][0] == want["token_logit"]
+    head.close()
+
+
+# -------------------------------------------------------------- tiny (fp32) --
+
+def test_tiny_greedy_batch1_all_queries():
+    pb = make_problem("tiny")
+    head, H = _engine(pb)
+    ref = _oracle(pb)
+    outs = {k: [] for k in ("token", "token_logit", "lse", "clusters", "ids", "logits")}
+    for q in range(H.shape[0]):
+        o = host(head.forward(H[q:q + 1], 16, want_clusters=True, want_retrieved=True))
+        for k in outs:
+            outs[k].append(o[k][0])
+    gpu = {k: np.stack(v) for k, v in outs.items()}
+    say("tiny B=1 x 64")
+    assert_report(parity.check_forward(ref, pb.H, 16, TOPK, 1.0, 0, gpu), "tiny greedy B=1")
+
+
+def test_tiny_batched_scores_dense_and_determinism():
+    pb = make_problem("tiny")
+    head, H = _engine(pb, max_batch=64)
+    ref = _oracle(pb)
+    say("tiny scores B=64")
+    s = host({"s": head.score(H)})["s"]
+    assert_report(parity.check_scores(ref.C_hat, pb.H, s), "tiny scores")
+    say("tiny forward B=64")
+    a = host(head.forward(H, 16, want_clusters=True, want_retrieved=True))
+    b = host(head.forward(H, 16, want_clusters=True, want_retrieved=True))
+    for k in a:
+        assert np.array_equal(a[k], b[k]), f"{k} not bit-identical across runs"
+    assert_report(parity.check_forward(ref, pb.H, 16, TOPK, 1.0, 0, a), "tiny greedy B=64")
+    say("tiny dense B=64")
+    d = host(head.dense(H, want_logits=True))
+    assert_report(parity.check_dense(pb.E, pb.H, TOPK, 1.0, 0, d), "tiny dense")
+
+
+@pytest.mark.parametrize("p", [1, 2, 255, 256])
+def test_tiny_probe_counts_including_p_equals_c(p):
+    pb = make_problem("tiny")
+    head, H = _engine(pb, max_batch=8)
+    say("tiny p", p)
+    out = host(head.forward(H[:8], p, want_clusters=True, want_retrieved=True))
+    assert_report(parity.check_forward(_oracle(pb), pb.H[:8], p, TOPK, 1.0, 0, out), f"tiny p={p}")
+    if p == 256:  # every cluster probed: the dense head's token
+        d = host(head.dense(H[:8]))
+        assert np.array_equal(d["token"], out["token"])
+
+
+# ------------------------------------------------------- ragged / edge cases --
+
+def _custom_problem(v, d, c, dtype, nq, seed=5):
+    sh = Shape(f"custom{v}_{d}_{c}", v, d, c, 4, dtype, 4.0, nq)
+    return make_problem(sh, seed_data=seed, seed_query=seed + 1)
+
+
+@pytest.mark.parametrize("v,d,c,dtype", [
+    (1500, 40, 300, "bf16"),     # d = 5 chunks: lanes 5..63 idle; c not a multiple of 1024
+    (3000, 1032, 1000, "bf16"),  # d = 129 chunks: a ragged second chunk per lane
+    (1200, 36, 100, "f32"),      # fp32, 9 chunks
+    (20000, 264, 2000, "f32"),   # 66 chunks, b = 10
+])
+def test_ragged_shapes(v, d, c, dtype):
+    pb = _custom_problem(v, d, c, dtype, 12)
+    head, H = _engine(pb, max_batch=12)
+    ref = _oracle(pb)
+    for p in (1, 7, c // 3, c):
+        say("ragged", v, d, c, dtype, "p", p)
+        out = host(head.forward(H, p, want_clusters=True, want_retrieved=True))
+        assert_report(parity.check_forward(ref, pb.H, p, TOPK, 1.0, 0, out), f"ragged p={p}")
+    s = host({"s": head.score(H)})["s"]
+    assert_report(parity.check_scores(ref.C_hat, pb.H, s), "ragged scores")
+    dn = host(head.dense(H, want_logits=True))
+    assert_report(parity.check_dense(pb.E, pb.H, TOPK, 1.0, 0, dn), "ragged dense")
+
+
+def test_all_equal_scores_take_smallest_cluster_ids():
+    """Degenerate: identical centroids give equal scores; ties go to small ids."""
+    from lm_output_head_amd import FlashHead
+    v, d, c = 640, 64, 40
+    rng = np.random.default_rng(2)
+    E = rng.standard_normal((v, d)).astype(np.float32)
+    C = np.tile(rng.standard_normal((1, d)).astype(np.float32), (c, 1))
+    c2t = rng.permutation(v).reshape(c, v // c).astype(np.int32)
+    head = FlashHead(torch.from_numpy(E).cuda(), torch.from_numpy(C).cuda(), c2t, max_batch=3)
+    H = rng.standard_normal((3, d)).astype(np.float32)
+    for p in (1, 13, 39):
+        say("all-equal p", p)
+        out = host(head.forward(torch.from_numpy(H).cuda(), p, want_clusters=True))
+        assert np.array_equal(out["clusters"], np.tile(np.arange(p), (3, 1)))
+
+
+# -------------------------------------------------------- Llama-3.2-1B shape --
+
+@pytest.fixture(scope="module")
+def llama():
+    pb = make_problem("llama32_1b", nq=64)
+    return pb
+
+
+def test_llama_greedy_batch1(llama):
+    pb = llama
+    head, H = _engine(pb)
+    ref = _oracle(pb)
+    outs = {k: [] for k in ("token", "token_logit", "lse", "clusters", "ids", "logits")}
+    nq = 16
+    for q in range(nq):
+        say("llama B=1 q", q)
+        o = host(head.forward(H[q:q + 1], 512, want_clusters=True, want_retrieved=True))
+        for k in outs:
+            outs[k].append(o[k][0])
+    gpu = {k: np.stack(v) for k, v in outs.items()}
+    assert_report(parity.check_forward(ref, pb.H[:nq], 512, TOPK, 1.0, 0, gpu), "llama greedy")
+    head.close()
+
+
+def test_llama_scores_and_dense(llama):
+    pb = llama
+    head, H = _engine(pb, max_batch=4)
+    ref = _oracle(pb)
+    say("llama scores B=4")
+    s = host({"s": head.score(H[:4])})["s"]
+    assert_report(parity.check_scores(ref.C_hat, pb.H[:4], s), "llama scores")
+    say("llama dense B=4")
+    d = host(head.dense(H[:4], want_logits=True))
+    assert_report(parity.check_dense(pb.E, pb.H[:4], TOPK, 1.0, 0, d), "llama dense")
+    head.close()
+
+
+# --------------------------------------------------------------- INT4 (cfg3) --
+
+def test_int4_codes_bit_exact(llama):
+    pb = llama
+    head, _ = _engine(pb, quant="int4")
+    say("int4 codes")
+    packed, scales = head.int4()
+    packed, scales = packed.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
+    q, sigma = oracle.quantize_int4_g32(pb.C)
+    assert np.array_equal(scales, sigma.view(np.uint16))
+    assert np.array_equal(packed, oracle.pack_int4(q))
+    head.close()
+
+
+@pytest.mark.parametrize("B,p", [(1, 128), (1, 1024), (8, 256), (8, 512)])
+def test_int4_batched_probe_sweep(llama, B, p):
+    pb = llama
+    head, H = _engine(pb, quant="int4", max_batch=8)
+    ref = _oracle(pb, "int4")
+    say("int4 B", B, "p", p)
+    out = host(head.forward(H[:B], p, want_clusters=True, want_retrieved=True))
+    assert_report(parity.check_forward(ref, pb.H[:B], p, TOPK, 1.0, 0, out), f"int4 B={B} p={p}")
+    s = host({"s": head.score(H[:B])})["s"]
+    assert_report(parity.check_scores(ref.C_hat, pb.H[:B], s), "int4 scores")
+    head.close()
+
+
+# ------------------------------------------------ Gemma-3-1B shape (cfg4) ---
+
+def test_gemma_sampled_probes_and_tokens():
+    pb = make_problem("gemma3_1b", nq=16)
+    head, H = _engine(pb, max_batch=16)
+    ref = _oracle(pb)
+    mode = PSAMPLE | TSAMPLE
+    say("gemma B=16 sampled")
+    out = host(head.forward(H, 512, mode=mode, temperature=1.0, seed=0x5EED,
+                            want_clusters=True, want_retrieved=True))
+    assert_report(parity.check_forward(ref, pb.H, 512, mode, 1.0, 0x5EED, out), "gemma sampled")
+    say("gemma dense sampled B=4")
+    d = host(head.dense(H[:4], mode=TSAMPLE, temperature=1.0, seed=0x5EED))
+    assert_report(parity.check_dense(pb.E, pb.H[:4], TSAMPLE, 1.0, 0x5EED, d), "gemma dense")
+    head.close()
+
+
+# ------------------------------------------------- Qwen-3-4B shape (cfg5) ---
+
+def test_qwen_int4_batch128_greedy_and_t07():
+    pb = make_problem("qwen3_4b", nq=128)
+    head, H = _engine(pb, quant="int4", max_batch=128)
+    ref = _oracle(pb, "int4")
+    rows = list(range(0, 128, 9))
+    say("qwen B=128 greedy")
+    out = host(head.forward(H, 1024, want_clusters=True, want_retrieved=True))
+    assert_report(parity.check_forward(ref, pb.H, 1024, TOPK, 1.0, 0, out, queries=rows),
+                  "qwen greedy")
+    say("qwen B=128 T=0.7")
+    out = host(head.forward(H, 1024, mode=TSAMPLE, temperature=0.7, seed=0x5EED + 1,
+                            want_clusters=True, want_retrieved=True))
+    assert_report(parity.check_forward(ref, pb.H, 1024, TSAMPLE, 0.7, 0x5EED + 1, out,
+                                       queries=rows), "qwen T=0.7")
+    head.close()
+
+
+# ------------------------------------------------------------ argument errors --
+
+def test_argument_errors_are_reported():
+    from lm_output_head_amd import FlashHeadError
+    pb = make_problem("tiny")
+    head, H = _engine(pb, max_batch=2)
+    for kwargs in ({"p": 0}, {"p": 257}, {"p": 4, "mode": TSAMPLE, "temperature": 0.0},
+                   {"p": 4, "mode": 5}):
+        with pytest.raises(FlashHeadError) as ei:
+            head.forward(H[:1], **kwargs)
+        assert ei.value.status == -1
+    with pytest.raises(FlashHeadError):
+        head.forward(H[:3], 4)  # B > max_batch
+    from lm_output_head_amd import FlashHead
+    E, C, _ = problem_tensors(pb)
+    bad = pb.C2T.copy()
+    bad[0, 0] = bad[0, 1]
+    with pytest.raises(FlashHeadError):
+        FlashHead(E, C, bad)
+    head.close()
