@@ -176,6 +176,27 @@ typedef struct {
 fh_status fh_profile_begin(fh_engine* e, int64_t max_launches);
 fh_status fh_profile_end(fh_engine* e, fh_kernel_time* out, int max, int* count);
 
+/*
+ * fh_set_path — choose how fh_forward runs a batch-1 call.
+ *   FH_PATH_AUTO  (default) two launches: stage 1 with the probe selection
+ *                 done by its first workgroup, then stage 2 with the
+ *                 epilogue merged by its first workgroup.  Batches of B > 1
+ *                 use one launch per stage.
+ *   FH_PATH_MULTI always one launch per stage.
+ * Both paths return the same ids and logits; the LSE may differ in the last
+ * bits (a different merge order).
+ */
+enum { FH_PATH_AUTO = 0, FH_PATH_MULTI = 1 };
+fh_status fh_set_path(fh_engine* e, int path);
+
+/*
+ * fh_sync_status — wait for `stream`, then report FH_OK, or FH_EHIP if a
+ * bounded wait inside a batch-1 call ever gave up (that call's outputs are
+ * invalid; the flag stays set).  Calls that overlap on one engine (see
+ * above) are what can cause it.
+ */
+fh_status fh_sync_status(fh_engine* e, void* stream);
+
 /* Thread-local description of the last error on this thread ("" if none). */
 const char* fh_last_error(void);
 

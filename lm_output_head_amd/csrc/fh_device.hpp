@@ -54,39 +54,60 @@ struct Chunk<float> {
 };
 
 // ------------------------------------------------------------ wave helpers --
+// Cross-lane work uses DPP: four row-local steps (quad swaps, half-row and
+// row mirrors) combine the 16 lanes of each row with VALU latency, and the
+// four row results are read back as scalars.  The combination order is
+// fixed, so results are deterministic.
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+template <typename Op>
+__device__ __forceinline__ float row_allreduce(float v, Op op) {
+  v = op(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_f<0x140>(v));  // row_mirror
+  return v;
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-  return x;
+  x = row_allreduce(x, [](float a, float b) { return a + b; });
+  return (readlane_f(x, 0) + readlane_f(x, 16)) + (readlane_f(x, 32) + readlane_f(x, 48));
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
-  return x;
+  x = row_allreduce(x, [](float a, float b) { return fmaxf(a, b); });
+  return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
 }
 
 __device__ __forceinline__ float wave_min(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fminf(x, __shfl_xor(x, m, kWave));
-  return x;
+  x = row_allreduce(x, [](float a, float b) { return fminf(a, b); });
+  return fminf(fminf(readlane_f(x, 0), readlane_f(x, 16)), fminf(readlane_f(x, 32), readlane_f(x, 48)));
 }
 
-__device__ __forceinline__ int wave_sum_int(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-  return x;
-}
-
-// Inclusive prefix sum across the wave (lane order).
+// Inclusive prefix sum across the wave (lane order): a Hillis-Steele scan
+// inside each row (row_shr 1, 2, 4, 8 with zero fill), then the totals of
+// earlier rows added from scalar reads.
 __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  return x;
+  x += dpp_i<0x111>(x);
+  x += dpp_i<0x112>(x);
+  x += dpp_i<0x114>(x);
+  x += dpp_i<0x118>(x);
+  const int t0 = __builtin_amdgcn_readlane(x, 15);
+  const int t1 = __builtin_amdgcn_readlane(x, 31);
+  const int t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
 }
 
 // ------------------------------------------------------------------ Philox --
@@ -136,6 +157,21 @@ __device__ __forceinline__ float gumbel_at(uint64_t seed, uint32_t row, uint32_t
   return gumbel_from_word(u4_word(blk, index & 3));
 }
 
+// -------------------------------------------- device-coherent accesses ----
+// Agent-scope relaxed atomics compile to sc1 loads/stores on gfx950: they
+// reach the device coherence point, so workgroups on other XCDs see them
+// without an L2-wide writeback or invalidate.
+
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent_u32(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------ epilogue partials --
 // A partial result over a set of candidate tokens: the best (key, id) pair
 // with the logit of that token, and (m, s) with m = max x, s = sum exp(x - m)
@@ -165,6 +201,45 @@ __device__ __forceinline__ Part part_merge(const Part& a, const Part& b) {
     r.s = a.s * expf(a.m - m) + b.s * expf(b.m - m);
   }
   return r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ Part dpp_part(const Part& p) {
+  return Part{dpp_f<CTRL>(p.key), dpp_f<CTRL>(p.z), dpp_f<CTRL>(p.m), dpp_f<CTRL>(p.s),
+              dpp_i<CTRL>(p.id)};
+}
+
+__device__ __forceinline__ Part readlane_part(const Part& p, int l) {
+  return Part{readlane_f(p.key, l), readlane_f(p.z, l), readlane_f(p.m, l), readlane_f(p.s, l),
+              __builtin_amdgcn_readlane(p.id, l)};
+}
+
+// Merge the Parts of all 64 lanes; every lane gets the result.
+__device__ __forceinline__ Part wave_merge_part(Part p) {
+  p = part_merge(p, dpp_part<0xB1>(p));
+  p = part_merge(p, dpp_part<0x4E>(p));
+  p = part_merge(p, dpp_part<0x141>(p));
+  p = part_merge(p, dpp_part<0x140>(p));
+  return part_merge(part_merge(readlane_part(p, 0), readlane_part(p, 16)),
+                    part_merge(readlane_part(p, 32), readlane_part(p, 48)));
+}
+
+__device__ __forceinline__ void st_coherent_part(Part* p, const Part& v) {
+  st_coherent(&p->key, v.key);
+  st_coherent(&p->z, v.z);
+  st_coherent(&p->m, v.m);
+  st_coherent(&p->s, v.s);
+  __hip_atomic_store(&p->id, v.id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ Part ld_coherent_part(const Part* p) {
+  Part v;
+  v.key = ld_coherent(&p->key);
+  v.z = ld_coherent(&p->z);
+  v.m = ld_coherent(&p->m);
+  v.s = ld_coherent(&p->s);
+  v.id = __hip_atomic_load(const_cast<int32_t*>(&p->id), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
 }
 
 }  // namespace fh

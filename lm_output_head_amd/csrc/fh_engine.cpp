@@ -54,6 +54,11 @@ struct fh_engine {
   int32_t* sel = nullptr;    // [max_batch x c]
   fh::Part* parts = nullptr;  // [max_batch x parts_per_q]
   int64_t parts_per_q = 0;
+  unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up
+  unsigned long long* tagged = nullptr;  // batch-1 hand-over words: c scores + 5 per partial
+  unsigned epoch = 0;
+  int cus = 0;                // compute units of the device
+  int path = FH_PATH_AUTO;
   // per-kernel timing
   bool prof = false;
   int64_t prof_cap = 0, prof_n = 0;
@@ -119,6 +124,8 @@ void free_engine(fh_engine* e) {
   (void)hipFree(e->scores);
   (void)hipFree(e->sel);
   (void)hipFree(e->parts);
+  (void)hipFree(e->sync);
+  (void)hipFree(e->tagged);
   for (hipEvent_t ev : e->prof_ev) (void)hipEventDestroy(ev);
   delete e;
 }
@@ -193,20 +200,29 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t r = hipGetDevice(&e->device);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "hipGetDevice"); }
+  r = hipDeviceGetAttribute(&e->cus, hipDeviceAttributeMultiprocessorCount, e->device);
+  if (r != hipSuccess || e->cus <= 0) { free_engine(e); return hip_fail(r, "device attributes"); }
+  const int64_t ntag = 2 * c + 5 * (int64_t)fh::batch1_stage2_blocks(c, b, e->cus);
 
-  e->parts_per_q = std::max(fh::rows_blocks(v, fh::kGatherRPW), fh::rows_blocks(v, fh::kDenseRPW));
+  e->parts_per_q = std::max<int64_t>(
+      {fh::rows_blocks(v, fh::kGatherRPW), fh::rows_blocks(v, fh::kDenseRPW), 4096});
   struct Alloc { void** p; size_t bytes; const char* what; };
   const Alloc allocs[] = {
       {(void**)&e->c2t, sizeof(int32_t) * (size_t)v, "C2T"},
       {(void**)&e->scores, sizeof(float) * (size_t)(max_batch * c), "scores"},
       {(void**)&e->sel, sizeof(int32_t) * (size_t)(max_batch * c), "selection"},
       {(void**)&e->parts, sizeof(fh::Part) * (size_t)(max_batch * e->parts_per_q), "partials"},
+      {(void**)&e->sync, 4 * sizeof(unsigned), "sync flags"},
+      {(void**)&e->tagged, sizeof(unsigned long long) * (size_t)ntag, "tagged hand-over words"},
   };
   for (const Alloc& a : allocs) {
     r = hipMalloc(a.p, a.bytes);
     if (r != hipSuccess) { free_engine(e); return hip_fail(r, a.what); }
   }
   r = hipMemcpyAsync(e->c2t, C2T, sizeof(int32_t) * (size_t)v, hipMemcpyHostToDevice, st);
+  if (r == hipSuccess) r = hipMemsetAsync(e->sync, 0, 4 * sizeof(unsigned), st);
+  if (r == hipSuccess)
+    r = hipMemsetAsync(e->tagged, 0, sizeof(unsigned long long) * (size_t)ntag, st);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "copy C2T"); }
 
   if (quant == FH_QUANT_INT4_G32) {
@@ -273,6 +289,34 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
   const float tprime = token_sample ? temperature : 1.f;
   int32_t* S = out_clusters ? out_clusters : e->sel;
 
+  if (B == 1 && e->path == FH_PATH_AUTO) {
+    fh::FusedLaunch f{};
+    f.ctx = &k;
+    f.int4 = e->quant == FH_QUANT_INT4_G32;
+    f.cus = e->cus;
+    f.h = h;
+    f.p = (int)p;
+    f.probe_sample = probe_sample;
+    f.token_sample = token_sample;
+    f.temperature = temperature;
+    f.tprime = tprime;
+    f.seed = seed;
+    e->epoch = e->epoch == 0xFFFFFFFFu ? 1u : e->epoch + 1u;
+    f.epoch = e->epoch;
+    f.tscores = e->tagged;
+    f.tsel = e->tagged + e->c;
+    f.tparts = e->tagged + 2 * e->c;
+    f.out_clusters = out_clusters;
+    f.out_ids = out_ids;
+    f.out_logits = out_logits;
+    f.out_token = out_token;
+    f.out_logit = out_token_logit;
+    f.out_lse = out_lse;
+    f.err = e->sync;
+    hipError_t r = timed(e, st, "batch1", [&] { return fh::launch_batch1(f); });
+    return r == hipSuccess ? FH_OK : hip_fail(r, "batch-1 launch");
+  }
+
   hipError_t r = timed(e, st, e->quant == FH_QUANT_INT4_G32 ? "score_int4" : "score", [&] {
     return e->quant == FH_QUANT_INT4_G32 ? fh::launch_score_int4(k, h, (int)B, e->scores)
                                          : fh::launch_score(k, h, (int)B, e->scores);
@@ -319,6 +363,27 @@ fh_status fh_dense_forward(fh_engine* e, const void* h, int64_t B, int mode, flo
     return fh::launch_finish(k, e->parts, (int)B, nparts, out_token, out_token_logit, out_lse);
   });
   if (r != hipSuccess) return hip_fail(r, "finish launch");
+  return FH_OK;
+}
+
+fh_status fh_set_path(fh_engine* e, int path) {
+  g_err.clear();
+  if (!e) return fail(FH_EINVAL, "engine is NULL");
+  if (path != FH_PATH_AUTO && path != FH_PATH_MULTI) return fail(FH_EINVAL, "unknown path");
+  e->path = path;
+  return FH_OK;
+}
+
+fh_status fh_sync_status(fh_engine* e, void* stream) {
+  g_err.clear();
+  if (!e) return fail(FH_EINVAL, "engine is NULL");
+  DeviceGuard g(e->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  unsigned flags[4] = {0, 0, 0, 0};
+  hipError_t r = hipMemcpyAsync(flags, e->sync, sizeof(flags), hipMemcpyDeviceToHost, st);
+  if (r == hipSuccess) r = hipStreamSynchronize(st);
+  if (r != hipSuccess) return hip_fail(r, "sync status");
+  if (flags[0]) return fail(FH_EHIP, "a batch-1 hand-over poll gave up (outputs invalid)");
   return FH_OK;
 }
 

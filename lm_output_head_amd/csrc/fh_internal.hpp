@@ -51,4 +51,31 @@ hipError_t launch_dense(const KernelCtx& k, const void* h, int B, int token_samp
 hipError_t launch_finish(const KernelCtx& k, const Part* parts, int B, int64_t nparts,
                          int32_t* out_token, float* out_logit, float* out_lse);
 
+// The single-launch batch-1 path (stage 1, selection, stage 2 and the
+// finish by workgroups in dispatch order, handed over through tagged words).
+struct FusedLaunch {
+  const KernelCtx* ctx;
+  bool int4;
+  int cus;                        // compute units of the device
+  const void* h;
+  int p;
+  int probe_sample, token_sample;
+  float temperature, tprime;
+  uint64_t seed;
+  unsigned epoch;                 // this call's tag, never 0
+  unsigned long long* tscores;    // [c] tagged scores (zeroed at create)
+  unsigned long long* tsel;       // [c] tagged probe ids (zeroed at create)
+  unsigned long long* tparts;     // [5 x batch1_stage2_blocks(c, b, cus)] (zeroed at create)
+  int32_t* out_clusters;          // [p] or null
+  int32_t* out_ids;
+  float* out_logits;
+  int32_t* out_token;
+  float* out_logit;
+  float* out_lse;
+  unsigned* err;                  // sticky flag: a bounded poll gave up
+};
+hipError_t launch_batch1(const FusedLaunch& f);
+int batch1_stage1_blocks(int64_t c, int cus);
+int batch1_stage2_blocks(int64_t p, int64_t b, int cus);
+
 }  // namespace fh

@@ -95,6 +95,14 @@ def fh_get_int4(eng, packed, scales, stream=None) -> None:
     check(_abi.load().fh_get_int4(eng, _ptr(packed), _ptr(scales), _stream(stream)))
 
 
+def fh_set_path(eng, path: int) -> None:
+    check(_abi.load().fh_set_path(eng, path))
+
+
+def fh_sync_status(eng, stream=None) -> None:
+    check(_abi.load().fh_sync_status(eng, _stream(stream)))
+
+
 def fh_profile_begin(eng, max_launches: int) -> None:
     check(_abi.load().fh_profile_begin(eng, max_launches))
 
@@ -172,6 +180,13 @@ class FlashHead:
         fh_dense_forward(self.eng, h, mode, temperature, seed, out["token"], out["token_logit"],
                          out["lse"], out.get("logits"), stream)
         return out
+
+    def set_path(self, path: str) -> None:
+        """"auto" (single launch at B=1) or "multi" (one launch per stage)."""
+        fh_set_path(self.eng, {"auto": _abi.FH_PATH_AUTO, "multi": _abi.FH_PATH_MULTI}[path])
+
+    def sync_status(self, stream=None) -> None:
+        fh_sync_status(self.eng, stream)
 
     def int4(self, stream=None):
         packed = self._alloc((self.c, self.d // 2), torch.uint8)

@@ -277,3 +277,43 @@ def test_argument_errors_are_reported():
     with pytest.raises(FlashHeadError):
         FlashHead(E, C, bad)
     head.close()
+
+
+# ------------------------------------------- single-launch vs multi-launch ---
+
+@pytest.mark.parametrize("shape,quant,mode,T", [
+    ("tiny", "none", TOPK, 1.0),
+    ("tiny", "none", PSAMPLE | TSAMPLE, 0.8),
+    ("llama32_1b", "none", TOPK, 1.0),
+    ("llama32_1b", "int4", TOPK, 1.0),
+    ("llama32_1b", "none", TSAMPLE, 0.7),
+    ("gemma3_1b", "none", PSAMPLE | TSAMPLE, 1.0),
+])
+def test_fused_batch1_matches_multi_launch_and_oracle(shape, quant, mode, T):
+    """B=1 runs in one cooperative launch; it must agree with the per-stage
+    launches (ids and logits bit-identical, LSE to rounding) and the oracle."""
+    pb = make_problem(shape, nq=8)
+    head, H = _engine(pb, quant=quant)
+    ref = _oracle(pb, quant)
+    p = pb.shape.p
+    runs = {}
+    for path in ("auto", "multi"):
+        head.set_path(path)
+        outs = {k: [] for k in ("token", "token_logit", "lse", "clusters", "ids", "logits")}
+        for q in range(4):
+            say("paths", shape, quant, mode, path, "q", q)
+            o = host(head.forward(H[q:q + 1], p, mode=mode, temperature=T, seed=0x5EED + q,
+                                  want_clusters=True, want_retrieved=True))
+            for k in outs:
+                outs[k].append(o[k][0])
+        head.sync_status()
+        runs[path] = {k: np.stack(v) for k, v in outs.items()}
+    a, b = runs["auto"], runs["multi"]
+    for k in ("token", "token_logit", "clusters", "ids", "logits"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.allclose(a["lse"], b["lse"], rtol=1e-5, atol=1e-5)
+    for q in range(4):
+        one = {k: v[q:q + 1] for k, v in a.items()}
+        rep = parity.check_forward(ref, pb.H[q:q + 1], p, mode, T, 0x5EED + q, one)
+        assert_report(rep, f"fused {shape} q{q}")
+    head.close()
