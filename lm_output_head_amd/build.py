@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashhead.so")
 
-SOURCES = ["fh_kernels.hip", "fh_engine.cpp"]
+SOURCES = ["fh_kernels.hip", "fh_batch1_bf16.hip", "fh_batch1_bf16_int4.hip", "fh_batch1_f32.hip",
+           "fh_batch1_f32_int4.hip", "fh_engine.cpp"]
 
 # Packed FP32 instructions are disabled for all device code.
 COMMON = [
@@ -50,7 +51,8 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     """Compile every source and link libflashhead.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra or [])
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    workers = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -1,0 +1,449 @@
+// Device building blocks shared by the FlashHead kernels for gfx950: row
+// GEMVs over bf16 / fp32 / INT4 rows with a fused max / log-sum-exp / Gumbel
+// epilogue, the block-wide probe selection and the partial-result merge.
+//
+// Sources (page title and section): FlashHead technical explainer
+// (framerc.cn) §1.1, §1.2.1-§1.2.4, §2.2.2, §2.3; "FlashHead: Efficient
+// Drop-In Replacement for the Classification Head in Language Model
+// Inference" (arXiv 2603.14591), abstract.
+#pragma once
+
+#include <cfloat>
+#include <cstdint>
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "fh_device.hpp"
+#include "fh_internal.hpp"
+
+namespace fh {
+
+// Optional per-workgroup phase timestamps for performance probes (off in
+// the library build): slot s, workgroup w -> wall clock at phase s.
+#ifdef FH_PHASE_TRACE
+__device__ unsigned long long g_fh_trace[16][4096];
+#define FH_TRACE(slot) \
+  if (threadIdx.x == 0 && blockIdx.x < 4096) g_fh_trace[slot][blockIdx.x] = wall_clock64();
+__device__ __forceinline__ void g_fh_trace_cnt(int n) { g_fh_trace[15][blockIdx.x] = (unsigned long long)n; }
+#else
+#define FH_TRACE(slot)
+#define g_fh_trace_cnt(n)
+#endif
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+// ======================================================================
+// Wave-level row GEMV.
+//
+// A wavefront computes z = M[src(r)] . h_q for rows r = r_begin, r_begin +
+// stride, ... < r_end and NQ queries.  Lane l owns the 16-byte chunks l,
+// l+64, ... of a row (MAXM of them at most), so a row is read as fully
+// coalesced 16-byte loads and the lane's slice of each h stays in registers
+// (hv) for all rows.  Two rows' loads are issued before any math.  `sink` is
+// called by every lane with the wave-uniform result of each (row, query).
+// ======================================================================
+template <typename T, int MAXM>
+__device__ __forceinline__ void load_hslice(const T* h, int nch, int lane, uint4 (&hv)[MAXM]) {
+  const uint4* hq = reinterpret_cast<const uint4*>(h);
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) {
+    const int ch = lane + 64 * m;
+    hv[m] = ch < nch ? hq[ch] : uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <typename T, int MAXM, int NQ, typename SrcOf, typename Sink>
+__device__ __forceinline__ void wave_rows(const T* __restrict__ M, int d, int lane,
+                                          const uint4 (&hv)[NQ][MAXM], int nq, int64_t r_begin,
+                                          int64_t r_end, int64_t stride, SrcOf src_of,
+                                          Sink sink) {
+  const int nch = d / Chunk<T>::kElems;
+#pragma unroll 1
+  for (int64_t r = r_begin; r < r_end; r += 2 * stride) {
+    const int64_t rb = r + stride;
+    const bool okb = rb < r_end;
+    const int64_t sa = src_of(r);
+    const int64_t sb = okb ? src_of(rb) : sa;
+    const uint4* ra_p = reinterpret_cast<const uint4*>(M + sa * d);
+    const uint4* rb_p = reinterpret_cast<const uint4*>(M + sb * d);
+    uint4 ma[MAXM], mb[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+      const int ch = lane + 64 * m;
+      ma[m] = ch < nch ? ra_p[ch] : uint4{0u, 0u, 0u, 0u};
+      mb[m] = (okb && ch < nch) ? rb_p[ch] : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (q >= nq) break;
+      float acc_a = 0.f, acc_b = 0.f;
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) {
+        acc_a = Chunk<T>::dot(ma[m], hv[q][m], acc_a);
+        acc_b = Chunk<T>::dot(mb[m], hv[q][m], acc_b);
+      }
+      acc_a = wave_sum(acc_a);
+      acc_b = wave_sum(acc_b);
+      sink(q, r, sa, acc_a);
+      if (okb) sink(q, rb, sb, acc_b);
+    }
+  }
+}
+
+// ======================================================================
+// Wave-level INT4 stage-1 GEMV: s[k] = sum_g sigma[k, g] sum_{i in g} q h.
+// Lane l owns groups l, l+64, ...: one 16-byte load is one group's 32
+// nibbles.  Nibbles become unsigned bytes u = q + 8 (xor 0x88888888, two
+// masks), cvt_f32_ubyte converts them, and sum q h = sum u h - 8 sum_g h
+// removes the offset with the group sums of h.
+// ======================================================================
+template <int MAXG>
+struct HGroups {
+  float h[MAXG][32];
+  float hsum[MAXG];
+};
+
+template <typename T, int MAXG>
+__device__ __forceinline__ void load_hgroups(const T* h, int G, int lane, HGroups<MAXG>& hg) {
+#pragma unroll
+  for (int m = 0; m < MAXG; ++m) {
+    const int g = lane + 64 * m;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      hg.h[m][i] = g < G ? load_elem<T>(h, (int64_t)g * 32 + i) : 0.f;
+      s += hg.h[m][i];
+    }
+    hg.hsum[m] = s;
+  }
+}
+
+template <int MAXG>
+__device__ __forceinline__ float int4_group_dot(const uint4& qv, float sg,
+                                                const HGroups<MAXG>& hg, int m, float acc) {
+  const uint32_t w4[4] = {qv.x ^ 0x88888888u, qv.y ^ 0x88888888u, qv.z ^ 0x88888888u,
+                          qv.w ^ 0x88888888u};
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = w4[j] & 0x0F0F0F0Fu;         // elements 8j+0, +2, +4, +6
+    const uint32_t hi = (w4[j] >> 4) & 0x0F0F0F0Fu;  // elements 8j+1, +3, +5, +7
+    t = fmaf((float)(lo & 0xFFu), hg.h[m][8 * j + 0], t);
+    t = fmaf((float)(hi & 0xFFu), hg.h[m][8 * j + 1], t);
+    t = fmaf((float)((lo >> 8) & 0xFFu), hg.h[m][8 * j + 2], t);
+    t = fmaf((float)((hi >> 8) & 0xFFu), hg.h[m][8 * j + 3], t);
+    t = fmaf((float)((lo >> 16) & 0xFFu), hg.h[m][8 * j + 4], t);
+    t = fmaf((float)((hi >> 16) & 0xFFu), hg.h[m][8 * j + 5], t);
+    t = fmaf((float)(lo >> 24), hg.h[m][8 * j + 6], t);
+    t = fmaf((float)(hi >> 24), hg.h[m][8 * j + 7], t);
+  }
+  return fmaf(sg, fmaf(-8.f, hg.hsum[m], t), acc);
+}
+
+template <int MAXG, int NQ, typename Sink>
+__device__ __forceinline__ void wave_rows_int4(const uint8_t* __restrict__ Q,
+                                               const uint16_t* __restrict__ SG, int d, int lane,
+                                               const HGroups<MAXG> (&hg)[NQ], int nq,
+                                               int64_t r_begin, int64_t r_end, int64_t stride,
+                                               Sink sink) {
+  const int G = d / 32;
+#pragma unroll 1
+  for (int64_t r = r_begin; r < r_end; r += 2 * stride) {
+    const int64_t rb = r + stride;
+    const bool okb = rb < r_end;
+    const uint4* qa = reinterpret_cast<const uint4*>(Q + r * (d / 2));
+    const uint4* qb = reinterpret_cast<const uint4*>(Q + (okb ? rb : r) * (d / 2));
+    uint4 va[MAXG], vb[MAXG];
+    float sa[MAXG], sb[MAXG];
+#pragma unroll
+    for (int m = 0; m < MAXG; ++m) {
+      const int g = lane + 64 * m;
+      const bool ok = g < G;
+      va[m] = ok ? qa[g] : uint4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+      vb[m] = (ok && okb) ? qb[g] : uint4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+      sa[m] = ok ? __half2float(__ushort_as_half(SG[r * G + g])) : 0.f;
+      sb[m] = (ok && okb) ? __half2float(__ushort_as_half(SG[rb * G + g])) : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (q >= nq) break;
+      float acc_a = 0.f, acc_b = 0.f;
+#pragma unroll
+      for (int m = 0; m < MAXG; ++m) {
+        acc_a = int4_group_dot<MAXG>(va[m], sa[m], hg[q], m, acc_a);
+        acc_b = int4_group_dot<MAXG>(vb[m], sb[m], hg[q], m, acc_b);
+      }
+      acc_a = wave_sum(acc_a);
+      acc_b = wave_sum(acc_b);
+      sink(q, r, r, acc_a);
+      if (okb) sink(q, rb, rb, acc_b);
+    }
+  }
+}
+
+// ======================================================================
+// Epilogue helpers: fold one (row, z) into a running Part; merge Parts
+// across the waves of a workgroup.
+// ======================================================================
+__device__ __forceinline__ Part part_of(float z, int32_t t, int token_sample, float tprime,
+                                        uint64_t seed, uint32_t row) {
+  float key = z;
+  if (token_sample) key = z / tprime + gumbel_at(seed, row, (uint32_t)t, 1u);
+  return Part{key, z, z / tprime, 1.f, t};
+}
+
+// Merge the NWAVES per-wave Parts of each of nq queries held by lane 0s;
+// thread q (< nq) returns the workgroup Part of query q.
+template <int NWAVES, int NQ>
+__device__ __forceinline__ Part block_merge_parts(const Part (&part)[NQ], int nq, Part* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) sh[wave * NQ + q] = part[q];
+  }
+  __syncthreads();
+  Part acc = part_empty();
+  if ((int)threadIdx.x < nq) {
+    const int q = threadIdx.x;
+    acc = sh[q];
+    for (int w = 1; w < NWAVES; ++w) acc = part_merge(acc, sh[w * NQ + q]);
+  }
+  return acc;
+}
+
+// ======================================================================
+// Probe selection (explainer §1.2.2 top-p, §1.2.3 multinomial probes), one
+// 1024-thread workgroup per query.
+//
+// The p largest of c float keys (ties to the smaller id) are found by an
+// exact radix select on order-preserving 32-bit images of the keys: a
+// histogram of the top 11 bits and a suffix scan locate the digit holding
+// the p-th key; keys with a larger digit are taken, smaller ones dropped, and
+// the keys sharing the boundary digit go on to the next 11 bits, then the
+// last 10.  A round stops as soon as the whole boundary digit is taken.
+// After three rounds the remaining keys are bit-identical and the smallest
+// ids among them are taken.  Keys stay in registers (thread t holds clusters
+// k = t + 1024 i, so consecutive threads read consecutive scores); chosen
+// and tied clusters go through bitsets in LDS so that the ids come out in
+// ascending order.
+// ======================================================================
+constexpr int kSelThreads = 1024;  // workgroup size of a selection
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelBins = 2048;
+constexpr int kSelMaxC = 16384;
+
+struct SelShared {
+  int hist[kSelBins];
+  uint32_t selbits[kSelMaxC / 32];
+  uint32_t tiebits[kSelMaxC / 32];
+  int red_scan[kSelWaves];
+  int red_out[kSelWaves];
+  int beta, above, cnt;
+};
+
+// Keys per thread for c clusters over 1024 threads (1, 2, 8 or 16).
+inline int sel_keys_per_thread(int64_t c) {
+  const int64_t k = (c + kSelThreads - 1) / kSelThreads;
+  return k <= 1 ? 1 : k <= 2 ? 2 : k <= 8 ? 8 : k <= 16 ? 16 : -1;
+}
+
+// Order-preserving image of a selection key: a larger float gives a larger
+// integer.  NaN is taken as -FLT_MAX and +-inf as +-FLT_MAX (keys saturate),
+// and -0 as +0, so that equal floats give equal images.
+__device__ __forceinline__ uint32_t ordered_key(float x) {
+  x = isnan(x) ? -FLT_MAX : fminf(fmaxf(x, -FLT_MAX), FLT_MAX);
+  const uint32_t b = x == 0.f ? 0u : __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Exclusive prefix sum of x over the 1024 threads (index order) through one
+// LDS exchange in `red` (one barrier); *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int x, int* red, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(x, lane);
+  if (lane == 63) red[wave] = inc;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int v = red[w];
+    before += w < wave ? v : 0;
+    tot += v;
+  }
+  *total = tot;
+  return before + inc - x;
+}
+
+// OR the bits of key slot i (clusters k = tid + 1024 i) into a bitset with
+// one ballot per wave: a wave's 64 lanes own 64 consecutive clusters.
+template <int KP>
+__device__ __forceinline__ void ballot_bits(uint32_t mask, uint32_t* bits) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const unsigned long long b = __ballot((mask >> i) & 1u);
+    if (lane == 0 && b) {
+      const int word = (kSelThreads * i + 64 * wave) >> 5;
+      if ((uint32_t)b) atomicOr(&bits[word], (uint32_t)b);
+      if ((uint32_t)(b >> 32)) atomicOr(&bits[word + 1], (uint32_t)(b >> 32));
+    }
+  }
+}
+
+// Clear the selection's LDS state; a barrier must follow before
+// radix_select (the caller's, e.g. after its keys have arrived).
+__device__ __forceinline__ void select_clear(SelShared& sh) {
+  const int tid = threadIdx.x;
+  sh.hist[2 * tid] = 0;
+  sh.hist[2 * tid + 1] = 0;
+  if (tid < kSelMaxC / 32) {
+    sh.selbits[tid] = 0u;
+    sh.tiebits[tid] = 0u;
+  }
+}
+
+// One radix round over the keys flagged in `cand`: histogram of the digit
+// (u >> shift) & mask, suffix scan, and the digit beta holding the need-th
+// largest key, with the count above it and its own count.  Leaves the
+// histogram cleared.
+template <int KP>
+__device__ __forceinline__ void radix_round(const uint32_t (&u)[KP], uint32_t cand, int shift,
+                                            uint32_t mask, int need, SelShared& sh, int* beta,
+                                            int* above, int* cnt) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < KP; ++i)
+    if (cand & (1u << i)) atomicAdd(&sh.hist[(u[i] >> shift) & mask], 1);
+  __syncthreads();
+  // thread t owns digits 2047 - 2t and 2046 - 2t (suffix order)
+  const int j0 = kSelBins - 1 - 2 * tid;
+  const int h0 = sh.hist[j0], h1 = sh.hist[j0 - 1];
+  sh.hist[j0] = 0;
+  sh.hist[j0 - 1] = 0;
+  int tot;
+  const int before = block_exclusive_scan(h0 + h1, sh.red_scan, &tot);
+  if (before < need && before + h0 >= need) {
+    sh.beta = j0;
+    sh.above = before;
+    sh.cnt = h0;
+  } else if (before + h0 < need && before + h0 + h1 >= need) {
+    sh.beta = j0 - 1;
+    sh.above = before + h0;
+    sh.cnt = h1;
+  }
+  __syncthreads();
+  *beta = sh.beta;
+  *above = sh.above;
+  *cnt = sh.cnt;
+}
+
+// Select the p largest of the c keys whose images u[i] thread t holds for
+// clusters k = t + 1024 i (entries with k >= c are ignored) and emit them in
+// ascending id: emit(position, cluster).  Run by the whole 1024-thread
+// workgroup after select_clear and a barrier.
+template <int KP, typename Emit>
+__device__ __forceinline__ void radix_select(const uint32_t (&u)[KP], int c, int p, Emit emit,
+                                             SelShared& sh) {
+  static_assert(KP <= 32, "key slots are tracked in 32-bit masks");
+  const int tid = threadIdx.x;
+  uint32_t cand = 0u, sel = 0u;
+#pragma unroll
+  for (int i = 0; i < KP; ++i)
+    if (tid + kSelThreads * i < c) cand |= 1u << i;
+  int need = p;
+  if (need >= c) {
+    sel = cand;
+    cand = 0u;
+    need = 0;
+  }
+  FH_TRACE(9);
+  // rounds over bits 31..21, 20..10, 9..0
+  for (int round = 0; round < 3 && need > 0; ++round) {
+    const int shift = round == 0 ? 21 : round == 1 ? 10 : 0;
+    const uint32_t mask = round == 2 ? 0x3FFu : 0x7FFu;
+    int beta, above, cnt;
+    radix_round<KP>(u, cand, shift, mask, need, sh, &beta, &above, &cnt);
+    FH_TRACE(10 + round);
+    if (round == 0 && tid == 0 && blockIdx.x < 4096) g_fh_trace_cnt(cnt);
+    need -= above;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const uint32_t bit = cand & (1u << i);
+      const int dig = (int)((u[i] >> shift) & mask);
+      if (bit && dig > beta) sel |= bit;
+      if (bit && dig != beta) cand &= ~bit;
+    }
+    if (cnt == need) {  // the whole boundary digit is taken
+      sel |= cand;
+      cand = 0u;
+      need = 0;
+    }
+  }
+  // need > 0 now means the keys left in `cand` are all equal: take the
+  // `need` smallest ids among them
+  const bool ties = need > 0;
+  ballot_bits<KP>(sel, sh.selbits);
+  if (ties) ballot_bits<KP>(cand, sh.tiebits);
+  __syncthreads();
+  // ascending compaction: thread t reads the bits of clusters
+  // [t*KP, t*KP + KP)
+  const int b0 = tid * KP;
+  uint32_t mine = 0u, tie_mine = 0u;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int k = b0 + i;
+    if (k < c && (sh.selbits[k >> 5] & (1u << (k & 31)))) mine |= 1u << i;
+    if (ties && k < c && (sh.tiebits[k >> 5] & (1u << (k & 31)))) tie_mine |= 1u << i;
+  }
+  if (ties) {
+    int tie_tot;
+    int rank = block_exclusive_scan(__popc(tie_mine), sh.red_scan, &tie_tot);
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      if (tie_mine & (1u << i)) {
+        if (rank < need) mine |= 1u << i;
+        ++rank;
+      }
+    }
+  }
+  int tot;
+  int off = block_exclusive_scan(__popc(mine), sh.red_out, &tot);
+#pragma unroll
+  for (int i = 0; i < KP; ++i)
+    if (mine & (1u << i)) emit(off++, b0 + i);
+  FH_TRACE(13);
+}
+
+// ======================================================================
+// Finisher: merge n Parts in a fixed order (threads stride, then a tree).
+// ======================================================================
+// Merge n Parts: each thread folds a strided subset in index order, the
+// waves merge their lanes, and thread 0 merges the waves in order.
+template <int NT>
+__device__ __forceinline__ Part merge_parts_block(const Part* __restrict__ pq, int n, Part* sh) {
+  Part acc = part_empty();
+  for (int i = threadIdx.x; i < n; i += NT) acc = part_merge(acc, pq[i]);
+  acc = wave_merge_part(acc);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  Part r = sh[0];
+  for (int w = 1; w < NT / 64; ++w) r = part_merge(r, sh[w]);
+  return r;
+}
+
+__device__ __forceinline__ void write_outputs(const Part& r, int q, int32_t* out_token,
+                                              float* out_logit, float* out_lse) {
+  if (out_token) out_token[q] = r.id;
+  if (out_logit) out_logit[q] = r.z;
+  if (out_lse) out_lse[q] = r.m + logf(r.s);
+}
+
+}  // namespace fh

@@ -75,6 +75,18 @@ struct FusedLaunch {
   unsigned* err;                  // sticky flag: a bounded poll gave up
 };
 hipError_t launch_batch1(const FusedLaunch& f);
+// per storage variant, one translation unit each
+hipError_t launch_batch1_bf16(const FusedLaunch& f);
+hipError_t launch_batch1_bf16_int4(const FusedLaunch& f);
+hipError_t launch_batch1_f32(const FusedLaunch& f);
+hipError_t launch_batch1_f32_int4(const FusedLaunch& f);
+
+// Batch-1 sizing: rows per workgroup are a multiple of kBatch1RowsUnit
+// (16 waves x 2 rows), large enough that a stage needs at most `slots`
+// workgroups.
+constexpr int kBatch1RowsUnit = 32;
+int64_t batch1_rows(int64_t n, int64_t slots);
+int64_t batch1_slots1(int cus);  // stage-1 workgroup budget
 int batch1_stage1_blocks(int64_t c, int cus);
 int batch1_stage2_blocks(int64_t p, int64_t b, int cus);
 
