@@ -89,6 +89,10 @@ enum {
  *            where sigma = 0 ([X] §1.2.4).  A scale that overflows fp16 gives
  *            FH_EINVAL.
  *   max_batch largest B any later call will use (sizes the workspace).
+ *            Besides the workspace, the engine keeps a cluster-contiguous
+ *            copy of E (v x d of `dtype`, row f = E[C2T[f]]) so that each
+ *            probe's b rows are read as one block ([X] §1.2.1); FH_ENOMEM if
+ *            it does not fit.
  *   stream   stream for the set-up work; fh_create waits for it.
  *   out      receives the engine (set only on FH_OK).
  */

@@ -19,27 +19,30 @@ namespace fh {
 // The grid's workgroups (1024 threads) take roles by index, in the order
 // they are dispatched:
 //   [0, G1)        stage 1: rows1 centroid rows each (16 waves x 2 rows at a
-//                  time);
+//                  time), each score stored as soon as it is reduced;
 //   [G1, G1+G2)    stage 2: rows2 of the p*b retrieved tokens each, with the
 //                  fused epilogue.  The first of them (G1) is also the
-//                  selector: before its own rows it waits for the c scores
-//                  and selects the probes.  The last (G1+G2-1) is also the
-//                  finisher: after its own rows it waits for the G2 partials
-//                  and merges them.
+//                  selector: before its own rows it waits for the c scores,
+//                  selects the probes and publishes them as a bitset over
+//                  the clusters; each stage-2 workgroup finds the probes of
+//                  its rows by a prefix count over that bitset.  The last
+//                  stage-2 workgroup to finish (an arrival counter) also
+//                  merges the G2 partials.
 // Results pass between workgroups as 64-bit words tagged with the call's
 // epoch (epoch << 32 | payload), written and polled with agent-scope (sc1)
 // accesses.  A workgroup only ever waits for words written by workgroups
-// with smaller or equal indices.  Like a decoupled look-back scan, this
-// relies on workgroups being dispatched in index order, so every awaited
-// workgroup is already running and never waits for its waiter; the grid
-// need not be co-resident.  Sizes keep G1 < CUs and G2 <= CUs so that at
-// one workgroup per CU the selector starts at once and every stage-2
-// workgroup is resident when stage 1 retires.  Every wait is bounded: past
-// kSpinLimit polls the waiter sets *err and goes on with what it has, so the
-// grid always drains.
+// with smaller indices, or by workgroups that have already counted their
+// arrival.  Like a decoupled look-back scan, this relies on workgroups being
+// dispatched in index order, so every awaited workgroup is already running
+// and never waits for its waiter; the grid need not be co-resident.  Sizes
+// keep G1 < CUs and G2 <= CUs so that at one workgroup per CU the selector
+// starts at once and every stage-2 workgroup is resident when stage 1
+// retires.  Every wait is bounded: past kSpinLimit polls the waiter sets
+// *err and goes on with what it has, so the grid always drains.
 // ======================================================================
 struct FusedArgs {
   const void* E;
+  const void* Ec;  // cluster-contiguous copy of E, or null
   const void* C;
   const uint8_t* cq;
   const uint16_t* csig;
@@ -53,12 +56,13 @@ struct FusedArgs {
   int token_sample;
   float temperature;
   float tprime;
+  float zq;  // selection threshold quantile (select_quantile)
   uint64_t seed;
   int g1, g2;                   // stage-1 and stage-2 workgroup counts
   int rows1, rows2;             // rows per stage-1 / stage-2 workgroup
   unsigned epoch;               // never 0
   unsigned long long* tscores;  // [c] tagged scores
-  unsigned long long* tsel;     // [p] tagged probe ids (ascending)
+  unsigned long long* tsel;     // [ceil(c/32)] tagged bitset of the probes
   unsigned long long* tparts;   // [5 x g2] tagged Parts
   int32_t* out_clusters;        // [p] or null
   int32_t* out_ids;
@@ -66,7 +70,8 @@ struct FusedArgs {
   int32_t* out_token;
   float* out_logit;
   float* out_lse;
-  unsigned* err;  // sticky: a poll gave up
+  unsigned* err;    // sticky: a poll gave up
+  unsigned* count;  // stage-2 arrivals of this call (0 between calls)
 };
 
 constexpr unsigned kSpinLimit = 1u << 20;
@@ -119,6 +124,7 @@ union Batch1Shared {
 template <typename T, int MAXM, int KP, bool INT4, int MAXG>
 __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   __shared__ Batch1Shared sh;
+  __shared__ bool s_last;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int w = blockIdx.x;
@@ -129,11 +135,12 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     const int64_t r_lo = (int64_t)w * a.rows1;
     const int64_t r_hi = min((int64_t)a.c, r_lo + a.rows1);
     // probe sampling: the Gumbel-perturbed key s/T + G is formed here, one
-    // row per lane-0 store, so the selector only ranks
+    // row per lane-0 store, so the selector only ranks (keys saturate as in
+    // the selection)
     auto sink = [&](int, int64_t r, int64_t, float s) {
       if (lane == 0) {
         if (a.probe_sample) s = s / a.temperature + gumbel_at(a.seed, 0u, (uint32_t)r, 0u);
-        st_tagged(a.tscores + r, tag(a.epoch, __float_as_uint(s)));
+        st_tagged(a.tscores + r, tag(a.epoch, __float_as_uint(saturate_key(s))));
       }
     };
     if (INT4) {
@@ -143,8 +150,9 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     } else {
       uint4 hv[1][MAXM];
       load_hslice<T, MAXM>(hp, a.d / Chunk<T>::kElems, lane, hv[0]);
+      auto same = [](int64_t r) { return r; };
       wave_rows<T, MAXM, 1>(static_cast<const T*>(a.C), a.d, lane, hv, 1, r_lo + wave, r_hi, 16,
-                            [](int64_t r) { return r; }, sink);
+                            same, same, sink);
     }
     FH_TRACE(1);
 #ifdef FH_PHASE_TRACE
@@ -162,25 +170,22 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     select_clear(sh.sel);
     unsigned long long* ptr[KP];
     bool live[KP];
-    uint32_t u[KP];
+    uint32_t raw[KP];
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int k = (int)threadIdx.x + kSelThreads * i;
       live[i] = k < a.c;
       ptr[i] = a.tscores + (live[i] ? k : 0);
     }
-    poll_tagged<KP>(ptr, live, a.epoch, a.err, u);
+    poll_tagged<KP>(ptr, live, a.epoch, a.err, raw);
+    float x[KP];
 #pragma unroll
-    for (int i = 0; i < KP; ++i) u[i] = ordered_key(__uint_as_float(u[i]));
-    FH_TRACE(8);
+    for (int i = 0; i < KP; ++i) x[i] = __uint_as_float(raw[i]);
     __syncthreads();
-    radix_select<KP>(
-        u, a.c, a.p,
-        [&](int pos, int k) {
-          st_tagged(a.tsel + pos, tag(a.epoch, (uint32_t)k));
-          if (a.out_clusters) a.out_clusters[pos] = k;
-        },
-        sh.sel);
+    select_bits<KP>(x, a.c, a.p, a.zq, sh.sel);
+    // publish the chosen clusters as a bitset, one tagged word per 32
+    for (int t = threadIdx.x; t < (a.c + 31) / 32; t += kSelThreads)
+      st_tagged(a.tsel + t, tag(a.epoch, sh.sel.selbits[t]));
     FH_TRACE(3);
     __syncthreads();  // sh.sel is reused below
   }
@@ -192,22 +197,43 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   const int64_t r_hi = min(n2, r_lo + a.rows2);
   uint4 hv[1][MAXM];
   load_hslice<T, MAXM>(hp, a.d / Chunk<T>::kElems, lane, hv[0]);
-  // the probes this workgroup's rows come from, published by the selector
+  // the probes this workgroup's rows come from: positions [pos0, pos0+npos)
+  // of the ascending probe list, read off the selector's bitset
   const int pos0 = (int)(r_lo / a.bsz);
   const int npos = r_hi > r_lo ? (int)((r_hi - 1) / a.bsz) - pos0 + 1 : 0;
-  for (int t = threadIdx.x; t < npos; t += 1024) {
-    unsigned long long* const ptr[1] = {a.tsel + pos0 + t};
-    const bool live[1] = {true};
-    uint32_t k[1];
-    poll_tagged<1>(ptr, live, a.epoch, a.err, k);
-    sh.probes[t] = (int)k[0];
+  if (npos > 0) {
+    const int nw = (a.c + 31) / 32;
+    const int t = threadIdx.x;
+    uint32_t word = 0u;
+    if (t < nw) {
+      unsigned long long* const ptr[1] = {a.tsel + t};
+      const bool live[1] = {true};
+      uint32_t got[1];
+      poll_tagged<1>(ptr, live, a.epoch, a.err, got);
+      word = got[0];
+    }
+    int tot;
+    int pos = block_exclusive_scan(__popc(word), sh.sel.red_scan, &tot);
+    if (pos < pos0 + npos && pos + __popc(word) > pos0) {
+      for (uint32_t bitsleft = word; bitsleft; bitsleft &= bitsleft - 1, ++pos) {
+        if (pos < pos0 || pos >= pos0 + npos) continue;
+        const int k = 32 * t + __builtin_ctz(bitsleft);
+        sh.probes[pos - pos0] = k;
+        // the workgroup holding a probe's first row reports it
+        if (a.out_clusters && (int64_t)pos * a.bsz >= r_lo) a.out_clusters[pos] = k;
+      }
+    }
   }
   __syncthreads();
   FH_TRACE(5);
   Part part[1] = {part_empty()};
+  // slot f of the clustering; with the cluster-contiguous copy of E it is
+  // also the row, else the row is the token C2T[f]
   auto src_of = [&](int64_t r) -> int64_t {
-    return a.c2t[(int64_t)sh.probes[r / a.bsz - pos0] * a.bsz + r % a.bsz];
+    const int64_t f = (int64_t)sh.probes[r / a.bsz - pos0] * a.bsz + r % a.bsz;
+    return a.Ec ? f : (int64_t)a.c2t[f];
   };
+  auto tok_of = [&](int64_t src) -> int64_t { return a.Ec ? (int64_t)a.c2t[src] : src; };
   auto sink = [&](int, int64_t r, int64_t src, float z) {
     if (lane == 0) {
       if (a.out_logits) a.out_logits[r] = z;
@@ -215,8 +241,8 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     }
     part[0] = part_merge(part[0], part_of(z, (int32_t)src, a.token_sample, a.tprime, a.seed, 0u));
   };
-  wave_rows<T, MAXM, 1>(static_cast<const T*>(a.E), a.d, lane, hv, 1, r_lo + wave, r_hi, 16,
-                        src_of, sink);
+  wave_rows<T, MAXM, 1>(static_cast<const T*>(a.Ec ? a.Ec : a.E), a.d, lane, hv, 1, r_lo + wave,
+                        r_hi, 16, src_of, tok_of, sink);
   __syncthreads();  // sh.probes is read above; sh.parts aliases it
   const Part wg = block_merge_parts<16, 1>(part, 1, sh.parts);
   if (threadIdx.x == 0) {
@@ -226,12 +252,19 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     st_tagged(tp + 2, tag(a.epoch, __float_as_uint(wg.m)));
     st_tagged(tp + 3, tag(a.epoch, __float_as_uint(wg.s)));
     st_tagged(tp + 4, tag(a.epoch, (uint32_t)wg.id));
+    // the last stage-2 workgroup to get here merges
+    s_last = __hip_atomic_fetch_add(a.count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(a.g2 - 1);
   }
   FH_TRACE(6);
-  if (j != a.g2 - 1) return;
+  __syncthreads();
+  if (!s_last) return;
 
   // ---- finisher: every stage-2 partial, merged in a fixed order
-  __syncthreads();  // sh.parts is reused
+  if (threadIdx.x == 0)  // every increment of this call is in: ready for the next
+    __hip_atomic_store(a.count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // waves [0, nwv) hold partials: part i goes to thread i mod 1024
+  const int nwv = min(16, (a.g2 + 63) / 64);
   Part acc = part_empty();
   for (int i = threadIdx.x; i < a.g2; i += 1024) {
     unsigned long long* tp = a.tparts + 5 * (int64_t)i;
@@ -242,11 +275,13 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     acc = part_merge(acc, Part{__uint_as_float(wv[0]), __uint_as_float(wv[1]),
                                __uint_as_float(wv[2]), __uint_as_float(wv[3]), (int32_t)wv[4]});
   }
-  acc = wave_merge_part(acc);
-  if (lane == 0) sh.parts[wave] = acc;
+  if (wave < nwv) {
+    acc = wave_merge_part(acc);
+    if (lane == 0) sh.parts[wave] = acc;
+  }
   __syncthreads();
   Part r = sh.parts[0];
-  for (int w2 = 1; w2 < 16; ++w2) r = part_merge(r, sh.parts[w2]);
+  for (int w2 = 1; w2 < nwv; ++w2) r = part_merge(r, sh.parts[w2]);
   if (threadIdx.x == 0) write_outputs(r, 0, a.out_token, a.out_logit, a.out_lse);
   FH_TRACE(14);
 }
@@ -254,7 +289,7 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
 static FusedArgs fused_args(const FusedLaunch& f) {
   const KernelCtx& k = *f.ctx;
   FusedArgs a{};
-  a.E = k.E; a.C = k.C; a.cq = k.cq; a.csig = k.csig; a.c2t = k.c2t;
+  a.E = k.E; a.Ec = k.Ec; a.C = k.C; a.cq = k.cq; a.csig = k.csig; a.c2t = k.c2t;
   a.c = (int)k.c; a.bsz = (int)k.b; a.d = k.d; a.h = f.h; a.p = f.p;
   a.probe_sample = f.probe_sample; a.token_sample = f.token_sample;
   a.temperature = f.temperature; a.tprime = f.tprime; a.seed = f.seed;
@@ -266,6 +301,8 @@ static FusedArgs fused_args(const FusedLaunch& f) {
   a.out_clusters = f.out_clusters; a.out_ids = f.out_ids; a.out_logits = f.out_logits;
   a.out_token = f.out_token; a.out_logit = f.out_logit; a.out_lse = f.out_lse;
   a.err = f.err;
+  a.count = f.count;
+  a.zq = select_quantile(k.c, f.p);
   return a;
 }
 

@@ -48,7 +48,8 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t 
 // l+64, ... of a row (MAXM of them at most), so a row is read as fully
 // coalesced 16-byte loads and the lane's slice of each h stays in registers
 // (hv) for all rows.  Two rows' loads are issued before any math.  `sink` is
-// called by every lane with the wave-uniform result of each (row, query).
+// called by every lane with the wave-uniform result of each (row, query) and
+// the token id tok_of(src(r)).
 // ======================================================================
 template <typename T, int MAXM>
 __device__ __forceinline__ void load_hslice(const T* h, int nch, int lane, uint4 (&hv)[MAXM]) {
@@ -60,11 +61,11 @@ __device__ __forceinline__ void load_hslice(const T* h, int nch, int lane, uint4
   }
 }
 
-template <typename T, int MAXM, int NQ, typename SrcOf, typename Sink>
+template <typename T, int MAXM, int NQ, typename SrcOf, typename TokOf, typename Sink>
 __device__ __forceinline__ void wave_rows(const T* __restrict__ M, int d, int lane,
                                           const uint4 (&hv)[NQ][MAXM], int nq, int64_t r_begin,
                                           int64_t r_end, int64_t stride, SrcOf src_of,
-                                          Sink sink) {
+                                          TokOf tok_of, Sink sink) {
   const int nch = d / Chunk<T>::kElems;
 #pragma unroll 1
   for (int64_t r = r_begin; r < r_end; r += 2 * stride) {
@@ -72,6 +73,8 @@ __device__ __forceinline__ void wave_rows(const T* __restrict__ M, int d, int la
     const bool okb = rb < r_end;
     const int64_t sa = src_of(r);
     const int64_t sb = okb ? src_of(rb) : sa;
+    const int64_t ta = tok_of(sa);
+    const int64_t tb = okb ? tok_of(sb) : ta;
     const uint4* ra_p = reinterpret_cast<const uint4*>(M + sa * d);
     const uint4* rb_p = reinterpret_cast<const uint4*>(M + sb * d);
     uint4 ma[MAXM], mb[MAXM];
@@ -92,8 +95,8 @@ __device__ __forceinline__ void wave_rows(const T* __restrict__ M, int d, int la
       }
       acc_a = wave_sum(acc_a);
       acc_b = wave_sum(acc_b);
-      sink(q, r, sa, acc_a);
-      if (okb) sink(q, rb, sb, acc_b);
+      sink(q, r, ta, acc_a);
+      if (okb) sink(q, rb, tb, acc_b);
     }
   }
 }
@@ -221,29 +224,39 @@ __device__ __forceinline__ Part block_merge_parts(const Part (&part)[NQ], int nq
 
 // ======================================================================
 // Probe selection (explainer §1.2.2 top-p, §1.2.3 multinomial probes), one
-// 1024-thread workgroup per query.
+// 1024-thread workgroup per query.  Thread t holds the keys of clusters
+// k = t + 1024 i (i < KP), so consecutive threads read consecutive scores.
+// The result is a bitset of the p chosen clusters in LDS (the p largest keys,
+// ties to the smaller id).
 //
-// The p largest of c float keys (ties to the smaller id) are found by an
-// exact radix select on order-preserving 32-bit images of the keys: a
-// histogram of the top 11 bits and a suffix scan locate the digit holding
-// the p-th key; keys with a larger digit are taken, smaller ones dropped, and
-// the keys sharing the boundary digit go on to the next 11 bits, then the
-// last 10.  A round stops as soon as the whole boundary digit is taken.
-// After three rounds the remaining keys are bit-identical and the smallest
-// ids among them are taken.  Keys stay in registers (thread t holds clusters
-// k = t + 1024 i, so consecutive threads read consecutive scores); chosen
-// and tied clusters go through bitsets in LDS so that the ids come out in
-// ascending order.
+// Fast path: a threshold tau is placed from the keys' mean and standard
+// deviation (a normal-tail quantile for a little more than p keys) and the
+// keys above it are compacted into per-wave candidate lists.  If there are at
+// least p of them and no list overflowed, the exact selection runs over the
+// candidates only; otherwise over all keys.  Either way the selection is an
+// exact radix select on order-preserving 32-bit images of the keys, taken
+// relative to the smallest image in play: a histogram of the top 11 bits of
+// the range and a suffix scan locate the digit holding the p-th key, keys
+// with a larger digit are taken, smaller ones dropped, and the keys sharing
+// the boundary digit go on to the next 11 bits.  A round stops as soon as
+// the whole boundary digit is taken; keys still tied after the last bits are
+// bit-identical, and the smallest ids among them are taken.
 // ======================================================================
 constexpr int kSelThreads = 1024;  // workgroup size of a selection
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelBins = 2048;
 constexpr int kSelMaxC = 16384;
+constexpr int kCandPerWave = 128;
+constexpr int kCandMax = kCandPerWave * kSelWaves;
 
 struct SelShared {
   int hist[kSelBins];
   uint32_t selbits[kSelMaxC / 32];
   uint32_t tiebits[kSelMaxC / 32];
+  uint32_t cand_v[kCandMax];
+  int cand_id[kCandMax];
+  float red[3][kSelWaves];
+  int wcnt[kSelWaves];
   int red_scan[kSelWaves];
   int red_out[kSelWaves];
   int beta, above, cnt;
@@ -255,30 +268,39 @@ inline int sel_keys_per_thread(int64_t c) {
   return k <= 1 ? 1 : k <= 2 ? 2 : k <= 8 ? 8 : k <= 16 ? 16 : -1;
 }
 
-// Order-preserving image of a selection key: a larger float gives a larger
-// integer.  NaN is taken as -FLT_MAX and +-inf as +-FLT_MAX (keys saturate),
-// and -0 as +0, so that equal floats give equal images.
-__device__ __forceinline__ uint32_t ordered_key(float x) {
-  x = isnan(x) ? -FLT_MAX : fminf(fmaxf(x, -FLT_MAX), FLT_MAX);
+// Selection keys saturate: NaN is taken as -FLT_MAX and +-inf as +-FLT_MAX.
+__device__ __forceinline__ float saturate_key(float x) {
+  return isnan(x) ? -FLT_MAX : fminf(fmaxf(x, -FLT_MAX), FLT_MAX);
+}
+
+// Order-preserving image of a (saturated) key: a larger float gives a larger
+// integer, and -0 maps like +0 so that equal floats give equal images.
+__device__ __forceinline__ uint32_t ordered_bits(float x) {
   const uint32_t b = x == 0.f ? 0u : __float_as_uint(x);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Inclusive prefix sum over each row of 16 lanes (row_shr 1, 2, 4, 8 with
+// zero fill).
+__device__ __forceinline__ int row_inclusive_scan(int x) {
+  x += dpp_i<0x111>(x);
+  x += dpp_i<0x112>(x);
+  x += dpp_i<0x114>(x);
+  x += dpp_i<0x118>(x);
+  return x;
+}
+
 // Exclusive prefix sum of x over the 1024 threads (index order) through one
-// LDS exchange in `red` (one barrier); *total gets the sum.
+// LDS exchange in `red` (one barrier); *total gets the sum.  The 16 wave
+// totals are combined lane-parallel (lanes 0..15 of every wave).
 __device__ __forceinline__ int block_exclusive_scan(int x, int* red, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int inc = wave_inclusive_scan(x, lane);
   if (lane == 63) red[wave] = inc;
   __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int v = red[w];
-    before += w < wave ? v : 0;
-    tot += v;
-  }
-  *total = tot;
+  const int t = row_inclusive_scan(lane < kSelWaves ? red[lane] : 0);
+  *total = __builtin_amdgcn_readlane(t, kSelWaves - 1);
+  const int before = wave > 0 ? __builtin_amdgcn_readlane(t, wave - 1) : 0;
   return before + inc - x;
 }
 
@@ -298,8 +320,8 @@ __device__ __forceinline__ void ballot_bits(uint32_t mask, uint32_t* bits) {
   }
 }
 
-// Clear the selection's LDS state; a barrier must follow before
-// radix_select (the caller's, e.g. after its keys have arrived).
+// Clear the selection's LDS state; a barrier must follow before the
+// selection proper.
 __device__ __forceinline__ void select_clear(SelShared& sh) {
   const int tid = threadIdx.x;
   sh.hist[2 * tid] = 0;
@@ -310,18 +332,18 @@ __device__ __forceinline__ void select_clear(SelShared& sh) {
   }
 }
 
-// One radix round over the keys flagged in `cand`: histogram of the digit
-// (u >> shift) & mask, suffix scan, and the digit beta holding the need-th
-// largest key, with the count above it and its own count.  Leaves the
+// One radix round over the entries flagged in `cand`: histogram of the digit
+// (v >> shift) & 2047, suffix scan, and the digit beta holding the need-th
+// largest entry, with the count above it and its own count.  Leaves the
 // histogram cleared.
-template <int KP>
-__device__ __forceinline__ void radix_round(const uint32_t (&u)[KP], uint32_t cand, int shift,
-                                            uint32_t mask, int need, SelShared& sh, int* beta,
-                                            int* above, int* cnt) {
+template <int N>
+__device__ __forceinline__ void radix_round(const uint32_t (&v)[N], uint32_t cand, int shift,
+                                            int need, SelShared& sh, int* beta, int* above,
+                                            int* cnt) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < KP; ++i)
-    if (cand & (1u << i)) atomicAdd(&sh.hist[(u[i] >> shift) & mask], 1);
+  for (int i = 0; i < N; ++i)
+    if (cand & (1u << i)) atomicAdd(&sh.hist[(v[i] >> shift) & (kSelBins - 1)], 1);
   __syncthreads();
   // thread t owns digits 2047 - 2t and 2046 - 2t (suffix order)
   const int j0 = kSelBins - 1 - 2 * tid;
@@ -345,39 +367,25 @@ __device__ __forceinline__ void radix_round(const uint32_t (&u)[KP], uint32_t ca
   *cnt = sh.cnt;
 }
 
-// Select the p largest of the c keys whose images u[i] thread t holds for
-// clusters k = t + 1024 i (entries with k >= c are ignored) and emit them in
-// ascending id: emit(position, cluster).  Run by the whole 1024-thread
-// workgroup after select_clear and a barrier.
-template <int KP, typename Emit>
-__device__ __forceinline__ void radix_select(const uint32_t (&u)[KP], int c, int p, Emit emit,
-                                             SelShared& sh) {
-  static_assert(KP <= 32, "key slots are tracked in 32-bit masks");
-  const int tid = threadIdx.x;
-  uint32_t cand = 0u, sel = 0u;
-#pragma unroll
-  for (int i = 0; i < KP; ++i)
-    if (tid + kSelThreads * i < c) cand |= 1u << i;
-  int need = p;
-  if (need >= c) {
-    sel = cand;
-    cand = 0u;
-    need = 0;
-  }
-  FH_TRACE(9);
-  // rounds over bits 31..21, 20..10, 9..0
+// Radix rounds over entries v (images relative to the smallest in play,
+// span = the largest such value): narrows `cand` to the boundary entries and
+// sets bits in `sel` for entries taken.  Returns how many of the boundary
+// entries are still to be taken (> 0 only when they are all equal).
+template <int N>
+__device__ __forceinline__ int radix_rounds(const uint32_t (&v)[N], uint32_t span, int need,
+                                            uint32_t& cand, uint32_t& sel, SelShared& sh) {
+  const int bits = span ? 32 - __clz((int)span) : 0;
+  int shift = bits > 11 ? bits - 11 : 0;
   for (int round = 0; round < 3 && need > 0; ++round) {
-    const int shift = round == 0 ? 21 : round == 1 ? 10 : 0;
-    const uint32_t mask = round == 2 ? 0x3FFu : 0x7FFu;
     int beta, above, cnt;
-    radix_round<KP>(u, cand, shift, mask, need, sh, &beta, &above, &cnt);
+    radix_round<N>(v, cand, shift, need, sh, &beta, &above, &cnt);
     FH_TRACE(10 + round);
-    if (round == 0 && tid == 0 && blockIdx.x < 4096) g_fh_trace_cnt(cnt);
+    if (round == 0 && threadIdx.x == 0 && blockIdx.x < 4096) g_fh_trace_cnt(cnt);
     need -= above;
 #pragma unroll
-    for (int i = 0; i < KP; ++i) {
+    for (int i = 0; i < N; ++i) {
       const uint32_t bit = cand & (1u << i);
-      const int dig = (int)((u[i] >> shift) & mask);
+      const int dig = (int)((v[i] >> shift) & (kSelBins - 1));
       if (bit && dig > beta) sel |= bit;
       if (bit && dig != beta) cand &= ~bit;
     }
@@ -386,33 +394,191 @@ __device__ __forceinline__ void radix_select(const uint32_t (&u)[KP], int c, int
       cand = 0u;
       need = 0;
     }
+    if (shift == 0) break;
+    shift = shift > 11 ? shift - 11 : 0;
   }
-  // need > 0 now means the keys left in `cand` are all equal: take the
-  // `need` smallest ids among them
-  const bool ties = need > 0;
-  ballot_bits<KP>(sel, sh.selbits);
-  if (ties) ballot_bits<KP>(cand, sh.tiebits);
+  return need;
+}
+
+// Add the `need` smallest ids flagged in sh.tiebits to sh.selbits.  Thread t
+// scans clusters [t*KP, t*KP + KP).  Call after a barrier; ends with one.
+template <int KP>
+__device__ __forceinline__ void take_ties(int c, int need, SelShared& sh) {
+  const int b0 = threadIdx.x * KP;
+  uint32_t tie_mine = 0u;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int k = b0 + i;
+    if (k < c && (sh.tiebits[k >> 5] & (1u << (k & 31)))) tie_mine |= 1u << i;
+  }
+  int tot;
+  int rank = block_exclusive_scan(__popc(tie_mine), sh.red_scan, &tot);
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    if (tie_mine & (1u << i)) {
+      const int k = b0 + i;
+      if (rank < need) atomicOr(&sh.selbits[k >> 5], 1u << (k & 31));
+      ++rank;
+    }
+  }
   __syncthreads();
-  // ascending compaction: thread t reads the bits of clusters
-  // [t*KP, t*KP + KP)
-  const int b0 = tid * KP;
-  uint32_t mine = 0u, tie_mine = 0u;
+}
+
+// Exact selection over all keys (thread t holds clusters t + 1024 i).
+template <int KP>
+__device__ __forceinline__ void select_all(const float (&x)[KP], int c, int p, float xmin,
+                                           float xmax, SelShared& sh) {
+  const int tid = threadIdx.x;
+  uint32_t cand = 0u, sel = 0u;
+  uint32_t v[KP];
+  const uint32_t lo = ordered_bits(xmin);
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    if (tid + kSelThreads * i < c) cand |= 1u << i;
+    v[i] = ordered_bits(x[i]) - lo;
+  }
+  const int need = radix_rounds<KP>(v, ordered_bits(xmax) - lo, p, cand, sel, sh);
+  ballot_bits<KP>(sel, sh.selbits);
+  if (need > 0) ballot_bits<KP>(cand, sh.tiebits);
+  __syncthreads();
+  if (need > 0) take_ties<KP>(c, need, sh);
+}
+
+// Candidate target for the fast path: a few more than p keys above tau.
+__host__ __device__ inline int select_target(int p) { return p + p / 4 + 64; }
+__host__ __device__ inline bool select_fast_ok(int c, int p) {
+  return p < c && 2 * select_target(p) <= c && select_target(p) <= kCandMax * 3 / 4;
+}
+
+// The p largest of the c keys x (thread t holds clusters t + 1024 i; keys
+// saturated) into sh.selbits.  `zq` is the standard-normal quantile with
+// P(Z > zq) = select_target(p) / c (used when select_fast_ok(c, p)).  Run by
+// the whole workgroup after select_clear and a barrier; ends with a barrier.
+template <int KP>
+__device__ __forceinline__ void select_bits(const float (&x)[KP], int c, int p, float zq,
+                                            SelShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  FH_TRACE(9);
+  if (p >= c) {
+    uint32_t all = 0u;
+#pragma unroll
+    for (int i = 0; i < KP; ++i)
+      if (tid + kSelThreads * i < c) all |= 1u << i;
+    ballot_bits<KP>(all, sh.selbits);
+    __syncthreads();
+    return;
+  }
+  if (select_fast_ok(c, p)) {
+    // largest key over all; mean and spread from the first 1024 keys
+    float mx = -FLT_MAX;
+#pragma unroll
+    for (int i = 0; i < KP; ++i)
+      if (tid + kSelThreads * i < c) mx = fmaxf(mx, x[i]);
+    const bool s0 = tid < c;
+    float sum = s0 ? x[0] : 0.f, sq = s0 ? x[0] * x[0] : 0.f;
+    mx = wave_max(mx);
+    sum = wave_sum(sum);
+    sq = wave_sum(sq);
+    if (lane == 0) {
+      sh.red[0][wave] = mx;
+      sh.red[1][wave] = sum;
+      sh.red[2][wave] = sq;
+    }
+    __syncthreads();
+    const bool rl = lane < kSelWaves;
+    mx = readlane_f(row_allreduce(rl ? sh.red[0][lane] : -FLT_MAX,
+                                  [](float a, float b) { return fmaxf(a, b); }), 0);
+    sum = readlane_f(row_allreduce(rl ? sh.red[1][lane] : 0.f,
+                                   [](float a, float b) { return a + b; }), 0);
+    sq = readlane_f(row_allreduce(rl ? sh.red[2][lane] : 0.f,
+                                  [](float a, float b) { return a + b; }), 0);
+    const float inv = 1.f / (float)min(c, kSelThreads);
+    const float mean = sum * inv;
+    const float sd = sqrtf(fmaxf(sq * inv - mean * mean, 0.f));
+    const float tau = mean + sd * zq;
+    const uint32_t lo = ordered_bits(tau);
+    // compact the keys above tau into this wave's candidate list
+    int wcount = 0;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int k = tid + kSelThreads * i;
+      const bool take = k < c && x[i] > tau;
+      const unsigned long long b = __ballot(take);
+      if (b) {
+        const int off = wcount + __builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        if (take && off < kCandPerWave) {
+          sh.cand_v[wave * kCandPerWave + off] = ordered_bits(x[i]) - lo;
+          sh.cand_id[wave * kCandPerWave + off] = k;
+        }
+        wcount += __popcll(b);
+      }
+    }
+    if (lane == 0) sh.wcnt[wave] = wcount;
+    __syncthreads();
+    const int wc = rl ? sh.wcnt[lane] : 0;
+    const int total = __builtin_amdgcn_readlane(row_inclusive_scan(wc), kSelWaves - 1);
+    const bool overflow = __ballot(wc > kCandPerWave) != 0ull;
+    if (!overflow && total >= p) {
+      FH_TRACE(8);
+      // this wave's list: entries lane and lane + 64
+      const int n = __builtin_amdgcn_readlane(wc, wave);
+      uint32_t v[2];
+      int id[2];
+      uint32_t cand = 0u, sel = 0u;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int slot = lane + 64 * e;
+        v[e] = slot < n ? sh.cand_v[wave * kCandPerWave + slot] : 0u;
+        id[e] = slot < n ? sh.cand_id[wave * kCandPerWave + slot] : 0;
+        if (slot < n) cand |= 1u << e;
+      }
+      const int need = radix_rounds<2>(v, ordered_bits(mx) - lo, p, cand, sel, sh);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (sel & (1u << e)) atomicOr(&sh.selbits[id[e] >> 5], 1u << (id[e] & 31));
+        if (need > 0 && (cand & (1u << e))) atomicOr(&sh.tiebits[id[e] >> 5], 1u << (id[e] & 31));
+      }
+      __syncthreads();
+      if (need > 0) take_ties<KP>(c, need, sh);
+      return;
+    }
+  }
+  // exact selection over all keys, relative to the smallest
+  float mn = FLT_MAX, mx = -FLT_MAX;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    if (tid + kSelThreads * i < c) {
+      mn = fminf(mn, x[i]);
+      mx = fmaxf(mx, x[i]);
+    }
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  __syncthreads();  // sh.red may still be read above
+  if (lane == 0) {
+    sh.red[0][wave] = mn;
+    sh.red[1][wave] = mx;
+  }
+  __syncthreads();
+  const bool rl = lane < kSelWaves;
+  mn = readlane_f(row_allreduce(rl ? sh.red[0][lane] : FLT_MAX,
+                                [](float a, float b) { return fminf(a, b); }), 0);
+  mx = readlane_f(row_allreduce(rl ? sh.red[1][lane] : -FLT_MAX,
+                                [](float a, float b) { return fmaxf(a, b); }), 0);
+  select_all<KP>(x, c, p, mn, mx, sh);
+}
+
+// Write the clusters flagged in sh.selbits in ascending id:
+// emit(position, cluster).  Thread t reads clusters [t*KP, t*KP + KP).
+template <int KP, typename Emit>
+__device__ __forceinline__ void emit_selected(int c, Emit emit, SelShared& sh) {
+  const int b0 = threadIdx.x * KP;
+  uint32_t mine = 0u;
 #pragma unroll
   for (int i = 0; i < KP; ++i) {
     const int k = b0 + i;
     if (k < c && (sh.selbits[k >> 5] & (1u << (k & 31)))) mine |= 1u << i;
-    if (ties && k < c && (sh.tiebits[k >> 5] & (1u << (k & 31)))) tie_mine |= 1u << i;
-  }
-  if (ties) {
-    int tie_tot;
-    int rank = block_exclusive_scan(__popc(tie_mine), sh.red_scan, &tie_tot);
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      if (tie_mine & (1u << i)) {
-        if (rank < need) mine |= 1u << i;
-        ++rank;
-      }
-    }
   }
   int tot;
   int off = block_exclusive_scan(__popc(mine), sh.red_out, &tot);

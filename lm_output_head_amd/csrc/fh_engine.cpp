@@ -48,13 +48,14 @@ struct fh_engine {
   const void* E = nullptr;
   const void* C = nullptr;
   int32_t* c2t = nullptr;
+  void* Ec = nullptr;         // cluster-contiguous copy of E: Ec[f] = E[C2T[f]]
   uint8_t* cq = nullptr;
   uint16_t* csig = nullptr;
   float* scores = nullptr;   // [max_batch x c]
   int32_t* sel = nullptr;    // [max_batch x c]
   fh::Part* parts = nullptr;  // [max_batch x parts_per_q]
   int64_t parts_per_q = 0;
-  unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up
+  unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up; [1]: arrival counter
   unsigned long long* tagged = nullptr;  // batch-1 hand-over words: c scores + 5 per partial
   unsigned epoch = 0;
   int cus = 0;                // compute units of the device
@@ -69,6 +70,7 @@ struct fh_engine {
     fh::KernelCtx k;
     k.bf16 = dtype == FH_BF16;
     k.E = E;
+    k.Ec = Ec;
     k.C = C;
     k.c2t = c2t;
     k.cq = cq;
@@ -119,6 +121,7 @@ struct DeviceGuard {
 void free_engine(fh_engine* e) {
   if (!e) return;
   (void)hipFree(e->c2t);
+  (void)hipFree(e->Ec);
   (void)hipFree(e->cq);
   (void)hipFree(e->csig);
   (void)hipFree(e->scores);
@@ -209,6 +212,7 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   struct Alloc { void** p; size_t bytes; const char* what; };
   const Alloc allocs[] = {
       {(void**)&e->c2t, sizeof(int32_t) * (size_t)v, "C2T"},
+      {(void**)&e->Ec, (size_t)(v * d) * (dtype == FH_BF16 ? 2 : 4), "cluster-contiguous E"},
       {(void**)&e->scores, sizeof(float) * (size_t)(max_batch * c), "scores"},
       {(void**)&e->sel, sizeof(int32_t) * (size_t)(max_batch * c), "selection"},
       {(void**)&e->parts, sizeof(fh::Part) * (size_t)(max_batch * e->parts_per_q), "partials"},
@@ -224,6 +228,8 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   if (r == hipSuccess)
     r = hipMemsetAsync(e->tagged, 0, sizeof(unsigned long long) * (size_t)ntag, st);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "copy C2T"); }
+  r = fh::launch_permute_rows(e->ctx(st), e->Ec);
+  if (r != hipSuccess) { free_engine(e); return hip_fail(r, "cluster-contiguous E"); }
 
   if (quant == FH_QUANT_INT4_G32) {
     int* bad = nullptr;
@@ -289,7 +295,7 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
   const float tprime = token_sample ? temperature : 1.f;
   int32_t* S = out_clusters ? out_clusters : e->sel;
 
-  if (B == 1 && e->path == FH_PATH_AUTO) {
+  if (B == 1 && e->path == FH_PATH_AUTO && fh::batch1_fits(p, e->b, e->cus)) {
     fh::FusedLaunch f{};
     f.ctx = &k;
     f.int4 = e->quant == FH_QUANT_INT4_G32;
@@ -313,6 +319,7 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
     f.out_logit = out_token_logit;
     f.out_lse = out_lse;
     f.err = e->sync;
+    f.count = e->sync + 1;
     hipError_t r = timed(e, st, "batch1", [&] { return fh::launch_batch1(f); });
     return r == hipSuccess ? FH_OK : hip_fail(r, "batch-1 launch");
   }

@@ -27,6 +27,7 @@ constexpr int kInt4RPW = 2;
 struct KernelCtx {
   bool bf16;
   const void* E;
+  const void* Ec;  // cluster-contiguous copy of E (Ec[f] = E[C2T[f]]), or null
   const void* C;
   const int32_t* c2t;
   const uint8_t* cq;
@@ -39,8 +40,10 @@ struct KernelCtx {
 int64_t rows_blocks(int64_t nrows, int rpw);
 
 hipError_t launch_quant_int4(const KernelCtx& k, int* bad);
+hipError_t launch_permute_rows(const KernelCtx& k, void* out);
 hipError_t launch_score(const KernelCtx& k, const void* h, int B, float* out);
 hipError_t launch_score_int4(const KernelCtx& k, const void* h, int B, float* out);
+float select_quantile(int64_t c, int64_t p);
 hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, int sample,
                          float temperature, uint64_t seed, int32_t* S, int ldS);
 hipError_t launch_gather(const KernelCtx& k, const void* h, int B, const int32_t* S, int p,
@@ -64,7 +67,7 @@ struct FusedLaunch {
   uint64_t seed;
   unsigned epoch;                 // this call's tag, never 0
   unsigned long long* tscores;    // [c] tagged scores (zeroed at create)
-  unsigned long long* tsel;       // [c] tagged probe ids (zeroed at create)
+  unsigned long long* tsel;       // [ceil(c/32)] tagged probe bitset (zeroed at create)
   unsigned long long* tparts;     // [5 x batch1_stage2_blocks(c, b, cus)] (zeroed at create)
   int32_t* out_clusters;          // [p] or null
   int32_t* out_ids;
@@ -73,6 +76,7 @@ struct FusedLaunch {
   float* out_logit;
   float* out_lse;
   unsigned* err;                  // sticky flag: a bounded poll gave up
+  unsigned* count;                // arrival counter, 0 between calls (zeroed at create)
 };
 hipError_t launch_batch1(const FusedLaunch& f);
 // per storage variant, one translation unit each
@@ -89,5 +93,8 @@ int64_t batch1_rows(int64_t n, int64_t slots);
 int64_t batch1_slots1(int cus);  // stage-1 workgroup budget
 int batch1_stage1_blocks(int64_t c, int cus);
 int batch1_stage2_blocks(int64_t p, int64_t b, int cus);
+// Whether a batch-1 call with p probes fits the single launch (a stage-2
+// workgroup holds the probes of its rows in a 1024-entry LDS list).
+bool batch1_fits(int64_t p, int64_t b, int cus);
 
 }  // namespace fh

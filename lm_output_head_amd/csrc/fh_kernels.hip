@@ -10,6 +10,7 @@
 // Inference" (arXiv 2603.14591), abstract.
 
 #include <algorithm>
+#include <cmath>
 
 #include "fh_blocks.hpp"
 
@@ -57,10 +58,29 @@ __global__ __launch_bounds__(256) void k_quant_int4(const T* __restrict__ C, int
 }
 
 // ======================================================================
+// Cluster-contiguous copy of E (explainer §1.2.1: the C2T table addresses a
+// cluster's tokens by slot): Ec[f] = E[C2T[f]] for every slot f, so that a
+// probe's b rows are one contiguous block.  One wave per row.
+// ======================================================================
+__global__ __launch_bounds__(256) void k_permute_rows(const uint4* __restrict__ E,
+                                                      const int32_t* __restrict__ c2t,
+                                                      uint4* __restrict__ out, int64_t v,
+                                                      int nch) {
+  const int lane = threadIdx.x & 63;
+  const int64_t f = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (f >= v) return;
+  const uint4* src = E + (int64_t)c2t[f] * nch;
+  uint4* dst = out + f * nch;
+  for (int ch = lane; ch < nch; ch += 64) dst[ch] = src[ch];
+}
+
+// ======================================================================
 // Multi-launch path: row GEMV kernel (any B).
 //   GATHER = false: row r is M's row r (stage 1 over C; the dense head over E).
 //   GATHER = true : row r of query q is token t = C2T[S[q, r / b], r % b]
-//                   of E (stage 2, explainer §1.2.4); one query per grid row.
+//                   (stage 2, explainer §1.2.4), read from the cluster-
+//                   contiguous copy of E when there is one; one query per
+//                   grid row.
 //   EPI: fold each (z, t) into per-query Parts; one Part per workgroup and
 //        query goes to parts[q * gridDim.x + blockIdx.x].
 // ======================================================================
@@ -69,6 +89,7 @@ struct RowsArgs {
   int64_t nrows;  // rows per query (c, v, or p*b)
   int d;
   const int32_t* c2t;
+  bool contiguous;  // GATHER: M is the cluster-contiguous copy of E
   int bsz;
   const int32_t* S;
   int ldS;
@@ -103,9 +124,16 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
   const int64_t r1 = min(r0 + RPW, a.nrows);
   const int32_t* Sq = GATHER ? a.S + (int64_t)q0 * a.ldS : nullptr;
+  // slot f = S[q, r / b] * b + r % b of the clustering; with the
+  // cluster-contiguous copy of E that slot is also the row, else the row is
+  // the token C2T[f]
   auto src_of = [&](int64_t r) -> int64_t {
-    if (GATHER) return a.c2t[(int64_t)Sq[r / a.bsz] * a.bsz + r % a.bsz];
-    return r;
+    if (!GATHER) return r;
+    const int64_t f = (int64_t)Sq[r / a.bsz] * a.bsz + r % a.bsz;
+    return a.contiguous ? f : (int64_t)a.c2t[f];
+  };
+  auto tok_of = [&](int64_t src) -> int64_t {
+    return GATHER && a.contiguous ? (int64_t)a.c2t[src] : src;
   };
   auto sink = [&](int q, int64_t r, int64_t src, float z) {
     const int64_t oq = q0 + q;
@@ -117,7 +145,8 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
       part[q] = part_merge(part[q], part_of(z, (int32_t)src, a.token_sample, a.tprime, a.seed,
                                             (uint32_t)oq));
   };
-  wave_rows<T, MAXM, NQ>(static_cast<const T*>(a.M), a.d, lane, hv, nq, r0, r1, 1, src_of, sink);
+  wave_rows<T, MAXM, NQ>(static_cast<const T*>(a.M), a.d, lane, hv, nq, r0, r1, 1, src_of, tok_of,
+                        sink);
   if (EPI) {
     const Part wg = block_merge_parts<4, NQ>(part, nq, sh);
     if ((int)threadIdx.x < nq) a.parts[(int64_t)(q0 + threadIdx.x) * gridDim.x + blockIdx.x] = wg;
@@ -148,8 +177,8 @@ __global__ __launch_bounds__(256) void k_score_int4(const uint8_t* __restrict__ 
 template <int KP>
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ scores, int c,
                                                         int p, int sample, float temperature,
-                                                        uint64_t seed, int32_t* __restrict__ S,
-                                                        int ldS) {
+                                                        uint64_t seed, float zq,
+                                                        int32_t* __restrict__ S, int ldS) {
   __shared__ SelShared sh;
   FH_TRACE(14);
   const int q = blockIdx.x;
@@ -158,17 +187,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   select_clear(sh);
   // key = s (top-p), or s/T + G(seed, q, k, 0): the p largest Gumbel-perturbed
   // keys are p draws without replacement from softmax(s/T)
-  uint32_t u[KP];
+  float x[KP];
 #pragma unroll
   for (int i = 0; i < KP; ++i) {
     const int k = (int)threadIdx.x + kSelThreads * i;
-    float x = k < c ? sq[k] : 0.f;
-    if (sample && k < c) x = x / temperature + gumbel_at(seed, (uint32_t)q, (uint32_t)k, 0u);
-    u[i] = ordered_key(x);
+    float v = k < c ? sq[k] : 0.f;
+    if (sample && k < c) v = v / temperature + gumbel_at(seed, (uint32_t)q, (uint32_t)k, 0u);
+    x[i] = saturate_key(v);
   }
-  FH_TRACE(8);
   __syncthreads();
-  radix_select<KP>(u, c, p, [&](int pos, int k) { Sq[pos] = k; }, sh);
+  select_bits<KP>(x, c, p, zq, sh);
+  emit_selected<KP>(c, [&](int pos, int k) { Sq[pos] = k; }, sh);
 }
 
 __global__ __launch_bounds__(256) void k_finish(const Part* __restrict__ parts, int nparts,
@@ -257,13 +286,40 @@ hipError_t launch_quant_int4(const KernelCtx& k, int* bad) {
   return hipGetLastError();
 }
 
+// Standard-normal upper quantile z with P(Z > z) = select_target(p) / c: the
+// rational approximation of Abramowitz & Stegun 26.2.23 refined by two
+// Newton steps on 0.5 erfc(z / sqrt 2) = q.  It only places the fast-path
+// threshold of the selection, so it affects speed, not results.
+float select_quantile(int64_t c, int64_t p) {
+  if (!select_fast_ok((int)c, (int)p)) return 0.f;
+  const double q = (double)select_target((int)p) / (double)c;
+  const double t = std::sqrt(-2.0 * std::log(q));
+  double z = t - (2.515517 + t * (0.802853 + t * 0.010328)) /
+                     (1.0 + t * (1.432788 + t * (0.189269 + t * 0.001308)));
+  for (int it = 0; it < 2; ++it) {
+    const double tail = 0.5 * std::erfc(z / std::sqrt(2.0));
+    const double dens = std::exp(-0.5 * z * z) / std::sqrt(2.0 * 3.14159265358979323846);
+    z += (tail - q) / dens;
+  }
+  return (float)z;
+}
+
+hipError_t launch_permute_rows(const KernelCtx& k, void* out) {
+  const int nch = k.d * (k.bf16 ? 2 : 4) / 16;
+  const unsigned blocks = (unsigned)((k.v + 3) / 4);
+  hipLaunchKernelGGL(k_permute_rows, dim3(blocks), dim3(256), 0, k.stream,
+                     static_cast<const uint4*>(k.E), k.c2t, static_cast<uint4*>(out), k.v, nch);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, int sample,
                          float temperature, uint64_t seed, int32_t* S, int ldS) {
   const dim3 grid((unsigned)B), block(kSelThreads);
   const int c = (int)k.c;
+  const float zq = select_quantile(k.c, p);
   switch (sel_keys_per_thread(k.c)) {
 #define FH_CASE(KK) \
-  case KK: hipLaunchKernelGGL((k_select<KK>), grid, block, 0, k.stream, scores, c, p, sample, temperature, seed, S, ldS); break;
+  case KK: hipLaunchKernelGGL((k_select<KK>), grid, block, 0, k.stream, scores, c, p, sample, temperature, seed, zq, S, ldS); break;
     FH_CASE(1) FH_CASE(2) FH_CASE(8) FH_CASE(16)
 #undef FH_CASE
     default: return hipErrorInvalidValue;
@@ -276,7 +332,8 @@ static hipError_t gather_t(const KernelCtx& k, const void* h, int B, const int32
                            int token_sample, float tprime, uint64_t seed, int32_t* out_ids,
                            float* out_logits, Part* parts, int64_t* nparts) {
   RowsArgs a{};
-  a.M = k.E; a.nrows = (int64_t)p * k.b; a.d = k.d; a.c2t = k.c2t; a.bsz = (int)k.b;
+  a.M = k.Ec ? k.Ec : k.E; a.contiguous = k.Ec != nullptr;
+  a.nrows = (int64_t)p * k.b; a.d = k.d; a.c2t = k.c2t; a.bsz = (int)k.b;
   a.S = S; a.ldS = p; a.H = h; a.B = B; a.out_vals = out_logits; a.ld_vals = a.nrows;
   a.out_ids = out_ids; a.token_sample = token_sample; a.tprime = tprime; a.seed = seed;
   a.parts = parts;
@@ -332,6 +389,11 @@ int batch1_stage1_blocks(int64_t c, int cus) {
 int batch1_stage2_blocks(int64_t p, int64_t b, int cus) {
   const int64_t r = batch1_rows(p * b, cus);
   return (int)std::max<int64_t>(1, (p * b + r - 1) / r);
+}
+
+bool batch1_fits(int64_t p, int64_t b, int cus) {
+  const int64_t rows2 = batch1_rows(p * b, cus);
+  return rows2 / b + 2 <= 1024;
 }
 
 hipError_t launch_batch1(const FusedLaunch& f) {

@@ -157,6 +157,44 @@ def test_all_equal_scores_take_smallest_cluster_ids():
         assert np.array_equal(out["clusters"], np.tile(np.arange(p), (3, 1)))
 
 
+@pytest.mark.parametrize("layout", ["narrow_first_keys", "high_first_keys", "quantised_levels"])
+def test_selection_with_misleading_key_statistics(layout):
+    """Scores built exactly (h = a e0, so s[k] = a C[k, 0]) such that a
+    threshold placed from the statistics of the first keys is far too low,
+    far too high, or lands in heavy exact ties.  The selection must still be
+    the exact top p with ties to the smaller id, at B = 1 (single launch) and
+    B = 3 (per-stage launches)."""
+    from lm_output_head_amd import FlashHead
+    v, d, c = 16032, 8, 8016
+    rng = np.random.default_rng(11)
+    s = rng.standard_normal(c).astype(np.float32)
+    if layout == "narrow_first_keys":
+        s[:2048] *= np.float32(0.01)
+    elif layout == "high_first_keys":
+        s[:2048] += np.float32(6.0)
+    else:
+        s = (np.rint(s * np.float32(3.0)) / np.float32(3.0)).astype(np.float32)
+    C = rng.standard_normal((c, d)).astype(np.float32)
+    C[:, 0] = s
+    E = rng.standard_normal((v, d)).astype(np.float32)
+    c2t = rng.permutation(v).reshape(c, v // c).astype(np.int32)
+    H = np.zeros((3, d), np.float32)
+    H[:, 0] = [1.0, 0.5, 2.0]
+    head = FlashHead(torch.from_numpy(E).cuda(), torch.from_numpy(C).cuda(), c2t, max_batch=3)
+    ref = oracle.OracleHead(E, C, c2t, "none")
+    Hd = torch.from_numpy(H).cuda()
+    for p in (100, 512, 1500):
+        say("misleading stats", layout, "p", p)
+        out = host(head.forward(Hd, p, want_clusters=True, want_retrieved=True))
+        assert_report(parity.check_forward(ref, H, p, TOPK, 1.0, 0, out), f"{layout} B=3 p={p}")
+        for q in range(3):
+            one = host(head.forward(Hd[q:q + 1], p, want_clusters=True, want_retrieved=True))
+            assert np.array_equal(one["clusters"][0], out["clusters"][q]), (layout, p, q)
+            assert np.array_equal(one["ids"][0], out["ids"][q]), (layout, p, q)
+    head.sync_status()
+    head.close()
+
+
 # -------------------------------------------------------- Llama-3.2-1B shape --
 
 @pytest.fixture(scope="module")
