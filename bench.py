@@ -5,7 +5,7 @@ the dense head z = E h on the same inputs and the CPU oracle.
 One step is one fh_forward call (stage-1 scores, probe selection,
 gather-score of the p*b retrieved tokens, argmax epilogue) over one batch of
 B synthetic queries.  Inputs are resident in HBM before timing starts.  The
-engine is replicated R times (default 8) and consecutive steps rotate over
+engine is replicated R times (default 16) and consecutive steps rotate over
 the replicas and over 256 queries, so that the bytes a call touches are not
 still in the 256 MB Infinity Cache from the previous call: the working set
 between two uses of one replica is R * (|C| + |E rows read|), several times
@@ -42,14 +42,33 @@ def parse():
     ap.add_argument("--quant", default="none", choices=["none", "int4"])
     ap.add_argument("--mode", type=int, default=0)
     ap.add_argument("--temperature", type=float, default=1.0)
-    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--dense-steps", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "multi"],
-                    help="auto: one cooperative launch per batch-1 call; multi: one per stage")
+                    help="auto: one launch per batch-1 call; multi: one per stage")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain elementwise copy of known size (to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run) and exit")
     return ap.parse_args()
+
+
+COPY_BYTES = 512 << 20  # per launch of the calibration copy, read and written
+
+
+def copy_calibration():
+    """A plain device copy (torch's elementwise negation, read once, written
+    once) of COPY_BYTES, five launches."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel": "neg", "bytes_read_per_launch": COPY_BYTES,
+                      "bytes_written_per_launch": COPY_BYTES, "launches": 5}), flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -129,6 +148,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
