@@ -180,7 +180,7 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     poll_tagged<KP>(ptr, live, a.epoch, a.err, raw);
     float x[KP];
 #pragma unroll
-    for (int i = 0; i < KP; ++i) x[i] = __uint_as_float(raw[i]);
+    for (int i = 0; i < KP; ++i) x[i] = live[i] ? __uint_as_float(raw[i]) : -FLT_MAX;
     __syncthreads();
     select_bits<KP>(x, a.c, a.p, a.zq, sh.sel);
     // publish the chosen clusters as a bitset, one tagged word per 32

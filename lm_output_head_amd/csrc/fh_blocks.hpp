@@ -451,7 +451,7 @@ __host__ __device__ inline bool select_fast_ok(int c, int p) {
 }
 
 // The p largest of the c keys x (thread t holds clusters t + 1024 i; keys
-// saturated) into sh.selbits.  `zq` is the standard-normal quantile with
+// saturated; slots past c hold -FLT_MAX) into sh.selbits.  `zq` is the standard-normal quantile with
 // P(Z > zq) = select_target(p) / c (used when select_fast_ok(c, p)).  Run by
 // the whole workgroup after select_clear and a barrier; ends with a barrier.
 template <int KP>
@@ -469,11 +469,11 @@ __device__ __forceinline__ void select_bits(const float (&x)[KP], int c, int p, 
     return;
   }
   if (select_fast_ok(c, p)) {
-    // largest key over all; mean and spread from the first 1024 keys
-    float mx = -FLT_MAX;
+    // largest key over all (padding is -FLT_MAX); mean and spread from the
+    // first 1024 keys
+    float mx = x[0];
 #pragma unroll
-    for (int i = 0; i < KP; ++i)
-      if (tid + kSelThreads * i < c) mx = fmaxf(mx, x[i]);
+    for (int i = 1; i < KP; ++i) mx = x[i] > mx ? x[i] : mx;
     const bool s0 = tid < c;
     float sum = s0 ? x[0] : 0.f, sq = s0 ? x[0] * x[0] : 0.f;
     mx = wave_max(mx);
@@ -495,14 +495,16 @@ __device__ __forceinline__ void select_bits(const float (&x)[KP], int c, int p, 
     const float inv = 1.f / (float)min(c, kSelThreads);
     const float mean = sum * inv;
     const float sd = sqrtf(fmaxf(sq * inv - mean * mean, 0.f));
-    const float tau = mean + sd * zq;
+    // at least -FLT_MAX (also for a NaN or -inf estimate), so that padding
+    // slots are never above it
+    const float tau = fmaxf(mean + sd * zq, -FLT_MAX);
     const uint32_t lo = ordered_bits(tau);
     // compact the keys above tau into this wave's candidate list
     int wcount = 0;
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int k = tid + kSelThreads * i;
-      const bool take = k < c && x[i] > tau;
+      const bool take = x[i] > tau;
       const unsigned long long b = __ballot(take);
       if (b) {
         const int off = wcount + __builtin_amdgcn_mbcnt_hi(

@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     const int k = (int)threadIdx.x + kSelThreads * i;
     float v = k < c ? sq[k] : 0.f;
     if (sample && k < c) v = v / temperature + gumbel_at(seed, (uint32_t)q, (uint32_t)k, 0u);
-    x[i] = saturate_key(v);
+    x[i] = k < c ? saturate_key(v) : -FLT_MAX;
   }
   __syncthreads();
   select_bits<KP>(x, c, p, zq, sh);
