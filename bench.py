@@ -80,9 +80,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(shape, B, p, quant, elem):
+def algorithmic_bytes(shape, B, p, quant, elem, union=None):
     """Bytes each kernel must move per launch (the minimum the method reads
-    and writes), by kernel name."""
+    and writes), by kernel name.  `union` is the mean number of distinct
+    clusters probed by a batch (B > 1): the cluster-major stage 2 reads each
+    of them once."""
     v, d, c, b = shape.v, shape.d, shape.c, shape.b
     if quant == "int4":
         c_bytes = c * d // 2 + c * (d // 32) * 2
@@ -95,14 +97,20 @@ def algorithmic_bytes(shape, B, p, quant, elem):
     # counted), the retrieved ids/logits are optional outputs (off here)
     gather = B * p * b * d * elem + B * p * b * 4 + B * p * 4 + B * d * elem
     dense = v * d * elem + B * d * elem
-    return {"score": score, "score_int4": score, "select": select, "gather": gather,
-            "dense": dense, "batch1": score + select + gather,
-            "call": score + select + gather}
+    # cluster-major stage 2: the union's rows and C2T entries, h, the probe
+    # bitsets and their prefix counts
+    W = (c + 31) // 32
+    u = union if union is not None else B * p
+    gather_cm = int(round(u * b * (d * elem + 4))) + B * d * elem + 2 * W * B * 4
+    call = score + select + (gather_cm if (B > 1 and union is not None) else gather)
+    return {"score": score, "score_int4": score, "score_mfma": score, "score_int4_mfma": score,
+            "select": select, "gather": gather, "gather_cm": gather_cm, "dense": dense,
+            "dense_mfma": dense, "batch1": score + select + gather, "call": call}
 
 
-def traffic_from_profiles(kernel: str, src_hash: str):
+def traffic_from_profiles(kernel: str, src_hash: str, workload_key: str):
     """HBM bytes per launch measured by rocprofv3 PMC counters, if a summary
-    for the current kernel sources exists under profiles/."""
+    for the current kernel sources and this workload exists under profiles/."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(path):
         return None
@@ -111,7 +119,7 @@ def traffic_from_profiles(kernel: str, src_hash: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != src_hash:
+    if rec.get("source_hash") != src_hash or rec.get("workload_key") != workload_key:
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
@@ -240,16 +248,30 @@ def main():
             a[0] += n
             a[1] += tot
     kern = {k: {"launches": n, "avg_us": round(tot / n * 1e3, 3)} for k, (n, tot) in per.items()}
-    algo = algorithmic_bytes(shape, B, p, args.quant, elem)
+    union = None
+    if B > 1:
+        # distinct clusters per batch, from the engine's own probe lists
+        us = []
+        for hq in hb[:16]:
+            o = heads[0].forward(hq, p, mode=args.mode, temperature=args.temperature, seed=0x5EED,
+                                 want_clusters=True)
+            us.append(int(torch.unique(o["clusters"]).numel()))
+        union = sum(us) / len(us)
+    algo = algorithmic_bytes(shape, B, p, args.quant, elem, union)
     dominant = max((k for k in kern if k in algo),
                    key=lambda k: kern[k]["avg_us"] * kern[k]["launches"] * (algo[k] > 1e6))
     dom_bytes = algo[dominant]
     dom_us = kern[dominant]["avg_us"]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     src_hash = kernel_source_hash()
-    traffic = traffic_from_profiles(dominant, src_hash)
+    wkey = f"{shape.name}/B{B}/p{p}/{args.quant}/m{args.mode}"
+    traffic = traffic_from_profiles(dominant, src_hash, wkey)
     total_bytes = algo["call"]
 
+    if union is not None:
+        res_union = {"distinct_clusters_per_batch": round(union, 1)}
+    else:
+        res_union = {}
     res = {
         "metric": "FlashHead calls/s & achieved HBM GB/s (v=128256,d=2048,p=512) vs dense head",
         "value": round(1000.0 / ms, 2),
@@ -274,6 +296,7 @@ def main():
         "host_wall_ms_per_step": round(wall_ms, 5),
         "profiled_ms_per_step": round(ms_prof, 5),
         "kernels": kern,
+        **res_union,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

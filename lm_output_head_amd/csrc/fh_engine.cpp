@@ -51,8 +51,12 @@ struct fh_engine {
   void* Ec = nullptr;         // cluster-contiguous copy of E: Ec[f] = E[C2T[f]]
   uint8_t* cq = nullptr;
   uint16_t* csig = nullptr;
+  uint8_t* cq_mfma = nullptr;    // INT4 codes in the MFMA tile layout (bf16 engines)
+  uint16_t* sig_mfma = nullptr;  // INT4 scales, group-major
   float* scores = nullptr;   // [max_batch x c]
   int32_t* sel = nullptr;    // [max_batch x c]
+  uint32_t* mbits = nullptr;  // [ceil(c/32) x max_batch] probe bitsets, word-major
+  int32_t* mpre = nullptr;    // [ceil(c/32) x max_batch] probes in earlier words
   fh::Part* parts = nullptr;  // [max_batch x parts_per_q]
   int64_t parts_per_q = 0;
   unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up; [1]: arrival counter
@@ -75,6 +79,8 @@ struct fh_engine {
     k.c2t = c2t;
     k.cq = cq;
     k.csig = csig;
+    k.cq_mfma = cq_mfma;
+    k.sig_mfma = sig_mfma;
     k.v = v;
     k.c = c;
     k.b = b;
@@ -124,13 +130,33 @@ void free_engine(fh_engine* e) {
   (void)hipFree(e->Ec);
   (void)hipFree(e->cq);
   (void)hipFree(e->csig);
+  (void)hipFree(e->cq_mfma);
+  (void)hipFree(e->sig_mfma);
   (void)hipFree(e->scores);
   (void)hipFree(e->sel);
+  (void)hipFree(e->mbits);
+  (void)hipFree(e->mpre);
   (void)hipFree(e->parts);
   (void)hipFree(e->sync);
   (void)hipFree(e->tagged);
   for (hipEvent_t ev : e->prof_ev) (void)hipEventDestroy(ev);
   delete e;
+}
+
+// Stage-1 scores for B queries: matrix cores for batches of bf16 queries,
+// the row GEMV otherwise.
+hipError_t launch_stage1(fh_engine* e, hipStream_t st, const fh::KernelCtx& k, const void* h,
+                         int64_t B, float* out) {
+  const bool int4 = e->quant == FH_QUANT_INT4_G32;
+  const bool bf16 = e->dtype == FH_BF16;
+  if (bf16 && int4 && B >= fh::kMfmaMinBatchInt4)
+    return timed(e, st, "score_int4_mfma",
+                 [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out); });
+  if (bf16 && !int4 && B >= fh::kMfmaMinBatchBf16)
+    return timed(e, st, "score_mfma", [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out); });
+  return timed(e, st, int4 ? "score_int4" : "score", [&] {
+    return int4 ? fh::launch_score_int4(k, h, (int)B, out) : fh::launch_score(k, h, (int)B, out);
+  });
 }
 
 fh_status check_common(const fh_engine* e, const void* h, int64_t B) {
@@ -208,13 +234,16 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   const int64_t ntag = 2 * c + 5 * (int64_t)fh::batch1_stage2_blocks(c, b, e->cus);
 
   e->parts_per_q = std::max<int64_t>(
-      {fh::rows_blocks(v, fh::kGatherRPW), fh::rows_blocks(v, fh::kDenseRPW), 4096});
+      {fh::rows_blocks(v, fh::kGatherRPW), fh::rows_blocks(v, fh::kDenseRPW),
+       fh::gather_cm_blocks(c, e->cus), fh::mfma_blocks(v), 4096});
   struct Alloc { void** p; size_t bytes; const char* what; };
   const Alloc allocs[] = {
       {(void**)&e->c2t, sizeof(int32_t) * (size_t)v, "C2T"},
       {(void**)&e->Ec, (size_t)(v * d) * (dtype == FH_BF16 ? 2 : 4), "cluster-contiguous E"},
       {(void**)&e->scores, sizeof(float) * (size_t)(max_batch * c), "scores"},
       {(void**)&e->sel, sizeof(int32_t) * (size_t)(max_batch * c), "selection"},
+      {(void**)&e->mbits, sizeof(uint32_t) * (size_t)(max_batch * ((c + 31) / 32)), "probe bitsets"},
+      {(void**)&e->mpre, sizeof(int32_t) * (size_t)(max_batch * ((c + 31) / 32)), "probe prefix counts"},
       {(void**)&e->parts, sizeof(fh::Part) * (size_t)(max_batch * e->parts_per_q), "partials"},
       {(void**)&e->sync, 4 * sizeof(unsigned), "sync flags"},
       {(void**)&e->tagged, sizeof(unsigned long long) * (size_t)ntag, "tagged hand-over words"},
@@ -244,6 +273,15 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
     (void)hipFree(bad);
     if (r != hipSuccess) { free_engine(e); return hip_fail(r, "INT4 quantisation"); }
     if (hbad) { free_engine(e); return fail(FH_EINVAL, "a centroid group's INT4 scale overflows fp16"); }
+    if (dtype == FH_BF16) {  // the MFMA copy for batched stage 1
+      r = hipMalloc((void**)&e->cq_mfma, (size_t)(c * fh::mfma_int4_row_bytes((int)d)));
+      if (r == hipSuccess)
+        r = hipMalloc((void**)&e->sig_mfma,
+                      sizeof(uint16_t) * (size_t)((d / 32) * fh::mfma_sig_ld(c)));
+      if (r == hipSuccess) r = fh::launch_mfma_relayout(e->ctx(st), e->cq_mfma, e->sig_mfma);
+      if (r == hipSuccess) r = hipStreamSynchronize(st);
+      if (r != hipSuccess) { free_engine(e); return hip_fail(r, "INT4 MFMA layout"); }
+    }
     e->C = nullptr;  // not borrowed in INT4 mode
   } else {
     r = hipStreamSynchronize(st);
@@ -269,10 +307,7 @@ fh_status fh_score(fh_engine* e, const void* h, int64_t B, float* out_scores, vo
   if (!g.ok) return fail(FH_EHIP, "cannot select the engine's device");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const fh::KernelCtx k = e->ctx(st);
-  hipError_t r = timed(e, st, e->quant == FH_QUANT_INT4_G32 ? "score_int4" : "score", [&] {
-    return e->quant == FH_QUANT_INT4_G32 ? fh::launch_score_int4(k, h, (int)B, out_scores)
-                                         : fh::launch_score(k, h, (int)B, out_scores);
-  });
+  hipError_t r = launch_stage1(e, st, k, h, B, out_scores);
   return r == hipSuccess ? FH_OK : hip_fail(r, "score launch");
 }
 
@@ -324,20 +359,27 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
     return r == hipSuccess ? FH_OK : hip_fail(r, "batch-1 launch");
   }
 
-  hipError_t r = timed(e, st, e->quant == FH_QUANT_INT4_G32 ? "score_int4" : "score", [&] {
-    return e->quant == FH_QUANT_INT4_G32 ? fh::launch_score_int4(k, h, (int)B, e->scores)
-                                         : fh::launch_score(k, h, (int)B, e->scores);
-  });
+  // batches of bf16 queries that share probes: stage 2 cluster-major on the
+  // matrix cores, each probed cluster's rows read once for all its queries
+  const bool cm = e->dtype == FH_BF16 && fh::gather_cm_fits((int)B, p, e->c);
+  hipError_t r = launch_stage1(e, st, k, h, B, e->scores);
   if (r != hipSuccess) return hip_fail(r, "score launch");
   r = timed(e, st, "select", [&] {
-    return fh::launch_select(k, e->scores, (int)B, (int)p, probe_sample, temperature, seed, S, (int)p);
+    return fh::launch_select(k, e->scores, (int)B, (int)p, probe_sample, temperature, seed, S,
+                             (int)p, cm ? e->mbits : nullptr, cm ? e->mpre : nullptr);
   });
   if (r != hipSuccess) return hip_fail(r, "select launch");
   int64_t nparts = 0;
-  r = timed(e, st, "gather", [&] {
-    return fh::launch_gather(k, h, (int)B, S, (int)p, token_sample, tprime, seed, out_ids,
-                             out_logits, e->parts, &nparts);
-  });
+  if (cm)
+    r = timed(e, st, "gather_cm", [&] {
+      return fh::launch_gather_cm(k, e->cus, h, (int)B, (int)p, e->mbits, e->mpre, token_sample, tprime,
+                                  seed, out_ids, out_logits, e->parts, &nparts);
+    });
+  else
+    r = timed(e, st, "gather", [&] {
+      return fh::launch_gather(k, h, (int)B, S, (int)p, token_sample, tprime, seed, out_ids,
+                               out_logits, e->parts, &nparts);
+    });
   if (r != hipSuccess) return hip_fail(r, "gather launch");
   r = timed(e, st, "finish", [&] {
     return fh::launch_finish(k, e->parts, (int)B, nparts, out_token, out_token_logit, out_lse);
@@ -362,9 +404,17 @@ fh_status fh_dense_forward(fh_engine* e, const void* h, int64_t B, int mode, flo
   const int token_sample = (mode & FH_TOKEN_SAMPLE) ? 1 : 0;
   const float tprime = token_sample ? temperature : 1.f;
   int64_t nparts = 0;
-  hipError_t r = timed(e, st, "dense", [&] {
-    return fh::launch_dense(k, h, (int)B, token_sample, tprime, seed, out_logits, e->parts, &nparts);
-  });
+  hipError_t r;
+  if (e->dtype == FH_BF16 && B >= fh::kMfmaMinBatchBf16)
+    r = timed(e, st, "dense_mfma", [&] {
+      return fh::launch_dense_mfma(k, e->cus, h, (int)B, token_sample, tprime, seed, out_logits,
+                                   e->parts, &nparts);
+    });
+  else
+    r = timed(e, st, "dense", [&] {
+      return fh::launch_dense(k, h, (int)B, token_sample, tprime, seed, out_logits, e->parts,
+                              &nparts);
+    });
   if (r != hipSuccess) return hip_fail(r, "dense launch");
   r = timed(e, st, "finish", [&] {
     return fh::launch_finish(k, e->parts, (int)B, nparts, out_token, out_token_logit, out_lse);

@@ -32,6 +32,8 @@ struct KernelCtx {
   const int32_t* c2t;
   const uint8_t* cq;
   const uint16_t* csig;
+  const uint8_t* cq_mfma;    // INT4 codes re-laid for the MFMA tiles, or null
+  const uint16_t* sig_mfma;  // INT4 scales group-major [G x mfma_sig_ld(c)], or null
   int64_t v, c, b;
   int d;
   hipStream_t stream;
@@ -44,13 +46,37 @@ hipError_t launch_permute_rows(const KernelCtx& k, void* out);
 hipError_t launch_score(const KernelCtx& k, const void* h, int B, float* out);
 hipError_t launch_score_int4(const KernelCtx& k, const void* h, int B, float* out);
 float select_quantile(int64_t c, int64_t p);
+// S [B x ldS]: the p probes of each query, ascending.  With mbits/mpre non-
+// null also the probe bitsets word-major, mbits[w * B + q], and the probes of
+// q in words before w, mpre[w * B + q] (W = ceil(c/32) words).
 hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, int sample,
-                         float temperature, uint64_t seed, int32_t* S, int ldS);
+                         float temperature, uint64_t seed, int32_t* S, int ldS,
+                         uint32_t* mbits = nullptr, int32_t* mpre = nullptr);
 hipError_t launch_gather(const KernelCtx& k, const void* h, int B, const int32_t* S, int p,
                          int token_sample, float tprime, uint64_t seed, int32_t* out_ids,
                          float* out_logits, Part* parts, int64_t* nparts);
 hipError_t launch_dense(const KernelCtx& k, const void* h, int B, int token_sample, float tprime,
                         uint64_t seed, float* out_logits, Part* parts, int64_t* nparts);
+// Matrix-core (MFMA) paths for batches of bf16 queries.
+constexpr int kMfmaMinBatchBf16 = 8;  // bf16 stage 1 and the dense head
+constexpr int kMfmaMinBatchInt4 = 2;  // INT4 stage 1
+int64_t mfma_int4_row_bytes(int d);
+int64_t mfma_blocks(int64_t R);  // row blocks (partials per query) of the MFMA dense head
+int64_t mfma_sig_ld(int64_t c);
+hipError_t launch_mfma_relayout(const KernelCtx& k, uint8_t* cq_mfma, uint16_t* sigT);
+hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, float* out);
+// Cluster-major stage 2 on the matrix cores (bf16 engines, B >= 2): every
+// probed cluster's rows are read once for all queries that probe it.
+int64_t gather_cm_blocks(int64_t c, int cus);
+bool gather_cm_fits(int B, int64_t p, int64_t c);
+hipError_t launch_gather_cm(const KernelCtx& k, int cus, const void* h, int B, int p,
+                            const uint32_t* mbits,
+                            const int32_t* mpre, int token_sample, float tprime, uint64_t seed,
+                            int32_t* out_ids, float* out_logits, Part* parts, int64_t* nparts);
+hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, int token_sample,
+                             float tprime, uint64_t seed, float* out_logits, Part* parts,
+                             int64_t* nparts);
+
 hipError_t launch_finish(const KernelCtx& k, const Part* parts, int B, int64_t nparts,
                          int32_t* out_token, float* out_logit, float* out_lse);
 

@@ -178,7 +178,9 @@ template <int KP>
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ scores, int c,
                                                         int p, int sample, float temperature,
                                                         uint64_t seed, float zq,
-                                                        int32_t* __restrict__ S, int ldS) {
+                                                        int32_t* __restrict__ S, int ldS,
+                                                        uint32_t* __restrict__ mbits,
+                                                        int32_t* __restrict__ mpre) {
   __shared__ SelShared sh;
   FH_TRACE(14);
   const int q = blockIdx.x;
@@ -198,6 +200,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   __syncthreads();
   select_bits<KP>(x, c, p, zq, sh);
   emit_selected<KP>(c, [&](int pos, int k) { Sq[pos] = k; }, sh);
+  if (mbits) {
+    // membership word w of this query, and how many of its probes lie in
+    // words before w ([W x B], word-major, for the cluster-major stage 2)
+    const int W = (c + 31) / 32, t = threadIdx.x;
+    const uint32_t word = t < W ? sh.selbits[t] : 0u;
+    int tot;
+    const int before = block_exclusive_scan(__popc(word), sh.red_scan, &tot);
+    if (t < W) {
+      mbits[(int64_t)t * gridDim.x + q] = word;
+      mpre[(int64_t)t * gridDim.x + q] = before;
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void k_finish(const Part* __restrict__ parts, int nparts,
@@ -313,13 +327,14 @@ hipError_t launch_permute_rows(const KernelCtx& k, void* out) {
 }
 
 hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, int sample,
-                         float temperature, uint64_t seed, int32_t* S, int ldS) {
+                         float temperature, uint64_t seed, int32_t* S, int ldS, uint32_t* mbits,
+                         int32_t* mpre) {
   const dim3 grid((unsigned)B), block(kSelThreads);
   const int c = (int)k.c;
   const float zq = select_quantile(k.c, p);
   switch (sel_keys_per_thread(k.c)) {
 #define FH_CASE(KK) \
-  case KK: hipLaunchKernelGGL((k_select<KK>), grid, block, 0, k.stream, scores, c, p, sample, temperature, seed, zq, S, ldS); break;
+  case KK: hipLaunchKernelGGL((k_select<KK>), grid, block, 0, k.stream, scores, c, p, sample, temperature, seed, zq, S, ldS, mbits, mpre); break;
     FH_CASE(1) FH_CASE(2) FH_CASE(8) FH_CASE(16)
 #undef FH_CASE
     default: return hipErrorInvalidValue;

@@ -1,0 +1,521 @@
+// Batched row GEMMs on the gfx950 matrix cores: stage-1 centroid scores
+// (bf16 or INT4 centroids) and the dense head for B >= kMfmaMinBatch bf16
+// queries, with v_mfma_f32_16x16x32_bf16 tiles (16 rows x 16 queries x 32
+// elements of d per instruction, fp32 accumulation).
+//
+// Sources (page title and section): FlashHead technical explainer
+// (framerc.cn) §1.1 (dense head), §1.2.2 (stage-1 scores), §1.2.4 and §2.3
+// (INT4 g32 centroids, bf16 tokens); "FlashHead: Efficient Drop-In
+// Replacement for the Classification Head in Language Model Inference"
+// (arXiv 2603.14591), abstract.
+//
+// Operand layout of the instruction (checked on the device): lane l holds
+// A's row l % 16 and B's column l % 16 at k = 8 (l / 16) .. + 7, and the
+// result's column l % 16 at rows 4 (l / 16) .. + 3.
+//
+// A workgroup is 4 waves; wave w owns rows [64 x + 16 w, +16) of the grid's
+// row block x and NQT query tiles of 16 (grid row y).  Rows stream from HBM
+// once per grid row; the queries' h (a few hundred KB) stay in the caches.
+//
+// bf16 rows: for each 128-element block of d, lane l loads the 64 contiguous
+// bytes [128 blk + 32 g, +32) of its row and of each of its queries (g =
+// l / 16); MFMA step s uses elements 32 g + 8 s .. + 7 of that slice for both
+// operands, a fixed permutation of d that the sum does not see.
+//
+// INT4 rows (the defined value sum_g sigma[k, g] sum_{i in g} q h): one MFMA
+// step is exactly one 32-element group.  The packed nibbles are re-laid out
+// at create (fh_engine) so that lane group g's four-byte share of four
+// consecutive groups is one 16-byte load.  A nibble q becomes the bf16 value
+// 136 + q (bit pattern 0x4300 | (q + 8), exact), and a second MFMA with the
+// constant -136 removes the offset, so the tile holds sum q h exactly up to
+// fp32 rounding; the group's fp16 scales then scale it into the running
+// score with one FMA per element.
+#include <algorithm>
+#include <cmath>
+
+#include "fh_blocks.hpp"
+
+namespace fh {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Eight nibbles (two's complement q, element 8g + i in nibble i of w) as the
+// A fragment of bf16 values 136 + q.
+__device__ __forceinline__ uint4 int4_fragment(uint32_t w) {
+  const uint32_t u = w ^ 0x88888888u;         // nibble i = q_i + 8
+  const uint32_t lo = u & 0x0F0F0F0Fu;        // elements 0, 2, 4, 6 in bytes 0..3
+  const uint32_t hi = (u >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
+  // interleave: t0 = [e0 e1 e2 e3], t1 = [e4 e5 e6 e7] (bytes)
+  const uint32_t t0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  // each element byte under the bf16 high byte 0x43 (128 + byte)
+  const uint32_t c43 = 0x43434343u;
+  return uint4{__builtin_amdgcn_perm(c43, t0, 0x04010400u), __builtin_amdgcn_perm(c43, t0, 0x04030402u),
+               __builtin_amdgcn_perm(c43, t1, 0x04010400u), __builtin_amdgcn_perm(c43, t1, 0x04030402u)};
+}
+
+struct MfmaArgs {
+  const void* A;           // bf16 rows [R x d], or INT4 rows in the MFMA layout
+  const uint16_t* sigT;    // INT4: fp16 scales [G x ldsig], group-major
+  int64_t ldsig;           // INT4: rows per scale row (R rounded up to 16)
+  int64_t a_row_bytes;     // INT4: bytes per re-laid row (64 per 4 groups)
+  int64_t R;
+  int d;
+  const uint16_t* H;  // [B x d] bf16
+  int B;
+  float* out;  // [B x ld_out] scores / logits, or null
+  int64_t ld_out;
+  int token_sample;  // EPI
+  float tprime;
+  uint64_t seed;
+  Part* parts;  // EPI: [B x gridDim.x]
+};
+
+template <int NQT, bool INT4, bool EPI>
+__global__ __launch_bounds__(256) void k_mfma_rows(MfmaArgs a) {
+  __shared__ Part sh[4][16 * NQT];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t r0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  const int64_t ra = min(r0 + col, a.R - 1);  // the row this lane loads (clamped)
+  const int q0 = blockIdx.y * (16 * NQT);
+  int qrow[NQT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) qrow[t] = min(q0 + 16 * t + col, a.B - 1);
+
+  f32x4 acc[NQT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (r0 < a.R) {
+    if (!INT4) {
+      const uint16_t* Ar = static_cast<const uint16_t*>(a.A) + ra * a.d;
+      const int nblk = a.d / 128;
+      // ping-pong: the next 128-element block is in flight during the MFMAs
+      uint4 a0[4], b0[NQT][4], a1[4], b1[NQT][4];
+      auto ld = [&](int blk, uint4 (&av)[4], uint4 (&bv)[NQT][4]) {
+        const int k0 = 128 * blk + 32 * g;
+        const uint4* ap = reinterpret_cast<const uint4*>(Ar + k0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) av[s] = ap[s];
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          const uint4* bp = reinterpret_cast<const uint4*>(a.H + (int64_t)qrow[t] * a.d + k0);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) bv[t][s] = bp[s];
+        }
+      };
+      auto mm = [&](const uint4 (&av)[4], const uint4 (&bv)[NQT][4]) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int t = 0; t < NQT; ++t) acc[t] = mfma16(av[s], bv[t][s], acc[t]);
+      };
+      if (nblk > 0) ld(0, a0, b0);
+      for (int blk = 0; blk < nblk; blk += 2) {
+        if (blk + 1 < nblk) ld(blk + 1, a1, b1);
+        mm(a0, b0);
+        if (blk + 1 < nblk) {
+          if (blk + 2 < nblk) ld(blk + 2, a0, b0);
+          mm(a1, b1);
+        }
+      }
+      // the rest of d in steps of 32: lane group g takes elements 8g .. 8g+7
+      for (int kb = nblk * 128; kb < a.d; kb += 32) {
+        const int k = kb + 8 * g;
+        const bool ok = k < a.d;  // d is a multiple of 8
+        const uint4 av = ok ? *reinterpret_cast<const uint4*>(Ar + k) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          const uint4 bv =
+              ok ? *reinterpret_cast<const uint4*>(a.H + (int64_t)qrow[t] * a.d + k)
+                 : uint4{0u, 0u, 0u, 0u};
+          acc[t] = mfma16(av, bv, acc[t]);
+        }
+      }
+    } else {
+      const uint8_t* Ar = static_cast<const uint8_t*>(a.A) + ra * a.a_row_bytes;
+      const int G = a.d / 32;
+      const uint4 neg136 = uint4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
+      const int64_t srow = r0 + 4 * g;  // this lane's four result rows
+      // one block = 4 groups; ping-pong so the next block's codes, scales and
+      // h slices are in flight during the current block's MFMAs
+      struct Blk {
+        uint4 w;
+        uint2 sg[4];
+        uint4 bv[NQT][4];
+      };
+      const int nb = (G + 3) / 4;
+      auto ld = [&](int blk, Blk& x) {
+        x.w = *reinterpret_cast<const uint4*>(Ar + 64 * blk + 16 * g);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int grp = min(4 * blk + s, G - 1);
+          x.sg[s] = *reinterpret_cast<const uint2*>(a.sigT + (int64_t)grp * a.ldsig + srow);
+#pragma unroll
+          for (int t = 0; t < NQT; ++t)
+            x.bv[t][s] = *reinterpret_cast<const uint4*>(a.H + (int64_t)qrow[t] * a.d + 32 * grp + 8 * g);
+        }
+      };
+      auto mm = [&](int blk, const Blk& x) {
+        const uint32_t wv[4] = {x.w.x, x.w.y, x.w.z, x.w.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (4 * blk + s >= G) break;
+          const float sig[4] = {__half2float(__ushort_as_half((uint16_t)(x.sg[s].x & 0xFFFFu))),
+                                __half2float(__ushort_as_half((uint16_t)(x.sg[s].x >> 16))),
+                                __half2float(__ushort_as_half((uint16_t)(x.sg[s].y & 0xFFFFu))),
+                                __half2float(__ushort_as_half((uint16_t)(x.sg[s].y >> 16)))};
+          const uint4 af = int4_fragment(wv[s]);
+#pragma unroll
+          for (int t = 0; t < NQT; ++t) {
+            f32x4 part = mfma16(af, x.bv[t][s], f32x4{0.f, 0.f, 0.f, 0.f});
+            part = mfma16(neg136, x.bv[t][s], part);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(sig[i], part[i], acc[t][i]);
+          }
+        }
+      };
+      Blk x0, x1;
+      ld(0, x0);
+      for (int blk = 0; blk < nb; blk += 2) {
+        if (blk + 1 < nb) ld(blk + 1, x1);
+        mm(blk, x0);
+        if (blk + 1 < nb) {
+          if (blk + 2 < nb) ld(blk + 2, x0);
+          mm(blk + 1, x1);
+        }
+      }
+    }
+  }
+
+  // lane holds rows r0 + 4g + i (i < 4) of queries q0 + 16t + col
+  if (!EPI) {
+    if (a.out) {
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        const int q = q0 + 16 * t + col;
+        if (q >= a.B) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t r = r0 + 4 * g + i;
+          if (r < a.R) a.out[(int64_t)q * a.ld_out + r] = acc[t][i];
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    const int q = q0 + 16 * t + col;
+    Part p = part_empty();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 4 * g + i;
+      if (r < a.R && q < a.B) {
+        if (a.out) a.out[(int64_t)q * a.ld_out + r] = acc[t][i];
+        p = part_merge(p, part_of(acc[t][i], (int32_t)r, a.token_sample, a.tprime, a.seed,
+                                  (uint32_t)q));
+      }
+    }
+    // the four lane groups hold the same query: fold them (fixed order)
+#pragma unroll
+    for (int m = 16; m <= 32; m *= 2) {
+      const Part o{__shfl_xor(p.key, m), __shfl_xor(p.z, m), __shfl_xor(p.m, m),
+                   __shfl_xor(p.s, m), __shfl_xor(p.id, m)};
+      p = (lane & m) ? part_merge(o, p) : part_merge(p, o);
+    }
+    if (g == 0) sh[wave][16 * t + col] = p;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < 16 * NQT) {
+    const int q = q0 + threadIdx.x;
+    Part r = sh[0][threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) r = part_merge(r, sh[w][threadIdx.x]);
+    if (q < a.B) a.parts[(int64_t)q * gridDim.x + blockIdx.x] = r;
+  }
+}
+
+// ======================================================================
+// Cluster-major stage 2 (explainer §1.2.1, §1.2.4; batch semantics: each
+// query still takes only its own probes).  Workgroup x owns clusters
+// [8x, 8x + 8); wave w takes clusters 8x + w and 8x + w + 4.  For a cluster
+// k the wave lists the queries whose probe bitset holds k (ballots over the
+// bitset words, ascending query order), then for each 16-slot row tile of
+// the cluster (rows Ec[k b + j] of the cluster-contiguous E) and each tile of
+// 16 of those queries computes the 16 x 16 logits with MFMA over d (the next
+// 128-element block's loads in flight during the current block's products),
+// so the cluster's rows are read once for all its queries.  The epilogue
+// writes the optional outputs at the query's canonical position (probe rank
+// from the bitset and its word prefix counts, then slot) and folds
+// (z, token) into a per-wave, per-query partial in LDS; the workgroup's four
+// wave partials are merged in order into parts[q][x].
+// ======================================================================
+constexpr int kCmClusters = 8;  // clusters per workgroup
+constexpr int kCmMaxB = 256;    // queries the LDS lists hold
+
+struct GatherCmArgs {
+  const uint16_t* Ec;  // cluster-contiguous E [v x d]
+  const int32_t* c2t;
+  int c, b, d;
+  const uint16_t* H;  // [B x d]
+  int B, p;
+  const uint32_t* mbits;  // [W x B] probe bitset words
+  const int32_t* mpre;    // [W x B] probes in earlier words
+  int32_t* out_ids;       // [B x p b] or null
+  float* out_logits;      // [B x p b] or null
+  int token_sample;
+  float tprime;
+  uint64_t seed;
+  Part* parts;  // [B x gridDim.x]
+};
+
+__global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
+  __shared__ uint32_t s_word[kCmMaxB];
+  __shared__ int s_pre[kCmMaxB];
+  __shared__ short s_q[4][kCmMaxB];
+  __shared__ Part s_acc[4][kCmMaxB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int k0 = blockIdx.x * kCmClusters;
+  const int w = k0 >> 5;  // the workgroup's clusters share one bitset word
+  for (int q = threadIdx.x; q < a.B; q += 256) {
+    s_word[q] = a.mbits[(int64_t)w * a.B + q];
+    s_pre[q] = a.mpre[(int64_t)w * a.B + q];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s_acc[v][q] = part_empty();
+  }
+  __syncthreads();
+  const int64_t ldo = (int64_t)a.p * a.b;
+  for (int ci = wave; ci < kCmClusters; ci += 4) {
+    const int k = k0 + ci;
+    if (k >= a.c) break;
+    const int bit = k & 31;
+    // the queries probing k, ascending
+    int n = 0;
+    for (int qb = 0; qb < a.B; qb += 64) {
+      const int q = qb + lane;
+      const bool in = q < a.B && ((s_word[q] >> bit) & 1u);
+      const unsigned long long m = __ballot(in);
+      if (in)
+        s_q[wave][n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+            (short)q;
+      n += __popcll(m);
+    }
+    if (n == 0) continue;
+    for (int rt = 0; 16 * rt < a.b; ++rt) {
+      const int64_t f = (int64_t)k * a.b + min(16 * rt + col, a.b - 1);
+      const uint16_t* Ar = a.Ec + f * a.d;
+      // the tile's token ids, loaded ahead of the products
+      int32_t tok[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        tok[i] = a.c2t[(int64_t)k * a.b + min(16 * rt + 4 * g + i, a.b - 1)];
+      for (int qt = 0; 16 * qt < n; ++qt) {
+        const int qi = 16 * qt + col;
+        const int q = s_q[wave][min(qi, n - 1)];
+        const uint16_t* Hr = a.H + (int64_t)q * a.d;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int nblk = a.d / 128;
+        // ping-pong: the next 128-element block is in flight during the MFMAs
+        uint4 a0[4], b0[4], a1[4], b1[4];
+        auto ld = [&](int blk, uint4 (&av)[4], uint4 (&bv)[4]) {
+          const int kk = 128 * blk + 32 * g;
+          const uint4* ap = reinterpret_cast<const uint4*>(Ar + kk);
+          const uint4* bp = reinterpret_cast<const uint4*>(Hr + kk);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            av[s] = ap[s];
+            bv[s] = bp[s];
+          }
+        };
+        if (nblk > 0) ld(0, a0, b0);
+        for (int blk = 0; blk < nblk; blk += 2) {
+          if (blk + 1 < nblk) ld(blk + 1, a1, b1);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc = mfma16(a0[s], b0[s], acc);
+          if (blk + 1 < nblk) {
+            if (blk + 2 < nblk) ld(blk + 2, a0, b0);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = mfma16(a1[s], b1[s], acc);
+          }
+        }
+        for (int kb = nblk * 128; kb < a.d; kb += 32) {
+          const int kk = kb + 8 * g;
+          const bool ok = kk < a.d;
+          const uint4 av = ok ? *reinterpret_cast<const uint4*>(Ar + kk) : uint4{0u, 0u, 0u, 0u};
+          const uint4 bv = ok ? *reinterpret_cast<const uint4*>(Hr + kk) : uint4{0u, 0u, 0u, 0u};
+          acc = mfma16(av, bv, acc);
+        }
+        // lane: slots j = 16 rt + 4 g + i of cluster k for query q
+        const bool qok = qi < n;
+        const int pos = qok ? s_pre[q] + __popc(s_word[q] & ((1u << bit) - 1u)) : 0;
+        Part pt = part_empty();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 16 * rt + 4 * g + i;
+          if (qok && j < a.b) {
+            const int64_t o = (int64_t)q * ldo + (int64_t)pos * a.b + j;
+            if (a.out_logits) a.out_logits[o] = acc[i];
+            if (a.out_ids) a.out_ids[o] = tok[i];
+            pt = part_merge(pt, part_of(acc[i], tok[i], a.token_sample, a.tprime, a.seed, (uint32_t)q));
+          }
+        }
+#pragma unroll
+        for (int m = 16; m <= 32; m *= 2) {
+          const Part o{__shfl_xor(pt.key, m), __shfl_xor(pt.z, m), __shfl_xor(pt.m, m),
+                       __shfl_xor(pt.s, m), __shfl_xor(pt.id, m)};
+          pt = (lane & m) ? part_merge(o, pt) : part_merge(pt, o);
+        }
+        if (g == 0 && qok) s_acc[wave][q] = part_merge(s_acc[wave][q], pt);
+      }
+    }
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < a.B; q += 256) {
+    Part r = s_acc[0][q];
+#pragma unroll
+    for (int v = 1; v < 4; ++v) r = part_merge(r, s_acc[v][q]);
+    a.parts[(int64_t)q * gridDim.x + blockIdx.x] = r;
+  }
+}
+
+// Re-lay INT4 rows for the MFMA tiles: in every 64-byte block of four
+// groups, lane group g's four bytes of each group (elements 8g .. 8g+7)
+// become the 16 contiguous bytes [16 g, 16 g + 16).  Rows are padded to whole
+// blocks with zero codes.  One thread per 16-byte output chunk.
+__global__ __launch_bounds__(256) void k_relayout_int4(const uint8_t* __restrict__ q, int64_t c,
+                                                       int G, uint8_t* __restrict__ out,
+                                                       int64_t row_bytes) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // output chunk
+  const int64_t per_row = row_bytes / 16;
+  if (i >= c * per_row) return;
+  const int64_t r = i / per_row;
+  const int blk = (int)((i % per_row) / 4), g = (int)(i % 4);
+  uint32_t w[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int grp = 4 * blk + s;
+    w[s] = grp < G ? *reinterpret_cast<const uint32_t*>(q + r * (G * 16) + grp * 16 + 4 * g) : 0u;
+  }
+  *reinterpret_cast<uint4*>(out + r * row_bytes + 16 * i % row_bytes) = uint4{w[0], w[1], w[2], w[3]};
+}
+
+// Scales group-major: sigT[grp][r] = sig[r][grp] (rows past c are 0).
+__global__ __launch_bounds__(256) void k_transpose_sig(const uint16_t* __restrict__ sig, int64_t c,
+                                                       int G, int64_t ld, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)G * ld) return;
+  const int64_t grp = i / ld, r = i % ld;
+  out[i] = r < c ? sig[r * G + grp] : (uint16_t)0;
+}
+
+// ----------------------------------------------------------------- host ---
+
+int64_t mfma_int4_row_bytes(int d) { return (int64_t)((d / 32 + 3) / 4) * 64; }
+int64_t mfma_sig_ld(int64_t c) { return (c + 15) / 16 * 16; }
+
+hipError_t launch_mfma_relayout(const KernelCtx& k, uint8_t* cq_mfma, uint16_t* sigT) {
+  const int G = k.d / 32;
+  const int64_t rb = mfma_int4_row_bytes(k.d);
+  const int64_t chunks = k.c * (rb / 16);
+  hipLaunchKernelGGL(k_relayout_int4, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                     k.stream, k.cq, k.c, G, cq_mfma, rb);
+  hipError_t r = hipGetLastError();
+  if (r != hipSuccess) return r;
+  const int64_t ld = mfma_sig_ld(k.c);
+  hipLaunchKernelGGL(k_transpose_sig, dim3((unsigned)((G * ld + 255) / 256)), dim3(256), 0,
+                     k.stream, k.csig, k.c, G, ld, sigT);
+  return hipGetLastError();
+}
+
+// Query tiles per workgroup: as many as keep at least ~2 workgroups per CU
+// busy, up to 4.
+static int mfma_nqt(int64_t R, int B, int cus) {
+  const int64_t rblocks = (R + 63) / 64;
+  const int tiles = (B + 15) / 16;
+  int nqt = 4;
+  while (nqt > 1 && rblocks * ((tiles + nqt - 1) / nqt) < 2 * (int64_t)cus) nqt /= 2;
+  return std::min(nqt, std::max(1, tiles));
+}
+
+template <int NQT, bool INT4, bool EPI>
+static hipError_t mfma_go(const MfmaArgs& a, hipStream_t st, int64_t* nblocks) {
+  const dim3 grid((unsigned)((a.R + 63) / 64), (unsigned)((a.B + 16 * NQT - 1) / (16 * NQT)));
+  if (nblocks) *nblocks = grid.x;
+  hipLaunchKernelGGL((k_mfma_rows<NQT, INT4, EPI>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <bool INT4, bool EPI>
+static hipError_t mfma_dispatch(const MfmaArgs& a, int cus, hipStream_t st, int64_t* nblocks) {
+  switch (mfma_nqt(a.R, a.B, cus)) {
+    case 1: return mfma_go<1, INT4, EPI>(a, st, nblocks);
+    case 2: return mfma_go<2, INT4, EPI>(a, st, nblocks);
+    default: return mfma_go<4, INT4, EPI>(a, st, nblocks);
+  }
+}
+
+int64_t mfma_blocks(int64_t R) { return (R + 63) / 64; }
+
+hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, float* out) {
+  MfmaArgs a{};
+  a.R = k.c; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
+  a.out = out; a.ld_out = k.c;
+  if (k.cq_mfma) {
+    a.A = k.cq_mfma; a.sigT = k.sig_mfma; a.ldsig = mfma_sig_ld(k.c);
+    a.a_row_bytes = mfma_int4_row_bytes(k.d);
+    return mfma_dispatch<true, false>(a, cus, k.stream, nullptr);
+  }
+  a.A = k.C;
+  return mfma_dispatch<false, false>(a, cus, k.stream, nullptr);
+}
+
+int64_t gather_cm_blocks(int64_t c, int) { return (c + kCmClusters - 1) / kCmClusters; }
+// Cluster-major pays off when clusters are shared: the expected number of
+// queries per probed cluster, B p / (c (1 - (1 - p/c)^B)), is at least 3.
+bool gather_cm_fits(int B, int64_t p, int64_t c) {
+  if (B < 2 || B > kCmMaxB) return false;
+  const double f = (double)p / (double)c;
+  const double u = (double)c * (1.0 - std::pow(1.0 - f, (double)B));
+  return (double)B * (double)p >= 3.0 * u;
+}
+
+hipError_t launch_gather_cm(const KernelCtx& k, int cus, const void* h, int B, int p,
+                            const uint32_t* mbits,
+                            const int32_t* mpre, int token_sample, float tprime, uint64_t seed,
+                            int32_t* out_ids, float* out_logits, Part* parts, int64_t* nparts) {
+  GatherCmArgs a{};
+  a.Ec = static_cast<const uint16_t*>(k.Ec); a.c2t = k.c2t;
+  a.c = (int)k.c; a.b = (int)k.b; a.d = k.d;
+  a.H = static_cast<const uint16_t*>(h); a.B = B; a.p = p;
+  a.mbits = mbits; a.mpre = mpre; a.out_ids = out_ids; a.out_logits = out_logits;
+  a.token_sample = token_sample; a.tprime = tprime; a.seed = seed; a.parts = parts;
+  const int64_t blocks = gather_cm_blocks(k.c, cus);
+  *nparts = blocks;
+  hipLaunchKernelGGL(k_gather_cm, dim3((unsigned)blocks), dim3(256), 0, k.stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, int token_sample,
+                             float tprime, uint64_t seed, float* out_logits, Part* parts,
+                             int64_t* nparts) {
+  MfmaArgs a{};
+  a.A = k.E; a.R = k.v; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
+  a.out = out_logits; a.ld_out = k.v;
+  a.token_sample = token_sample; a.tprime = tprime; a.seed = seed; a.parts = parts;
+  return mfma_dispatch<false, true>(a, cus, k.stream, nparts);
+}
+
+}  // namespace fh

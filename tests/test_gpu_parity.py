@@ -259,6 +259,34 @@ def test_int4_batched_probe_sweep(llama, B, p):
     head.close()
 
 
+@pytest.mark.parametrize("v,d,c,quant", [
+    (2000, 160, 250, "int4"),   # 5 INT4 groups (a partial block of 4); c not a multiple of 16
+    (2560, 96, 160, "int4"),    # 3 groups: a single partial block
+    (3000, 1032, 1000, "none"),  # bf16 d with a 8-element tail after 128-element blocks
+    (1200, 40, 75, "none"),      # d below one 128-element block
+])
+def test_batched_matrix_core_paths(v, d, c, quant):
+    """Batched stage 1 and the dense head on the matrix cores (bf16 queries,
+    B above the thresholds), on ragged shapes, against the oracle; B = 1 and
+    small B take the GEMV paths on the same engine."""
+    pb = _custom_problem(v, d, c, "bf16", 40, seed=9)
+    head, H = _engine(pb, quant=quant, max_batch=40)
+    ref = _oracle(pb, quant)
+    for B in (1, 2, 7, 8, 17, 40):
+        say("mfma", v, d, c, quant, "B", B)
+        s = host({"s": head.score(H[:B])})["s"]
+        assert_report(parity.check_scores(ref.C_hat, pb.H[:B], s), f"scores B={B}")
+        for mode, T in ((TOPK, 1.0), (PSAMPLE | TSAMPLE, 0.8)):
+            out = host(head.forward(H[:B], max(1, c // 10), mode=mode, temperature=T, seed=5,
+                                    want_clusters=True, want_retrieved=True))
+            assert_report(parity.check_forward(ref, pb.H[:B], max(1, c // 10), mode, T, 5, out),
+                          f"forward B={B} mode={mode}")
+        for mode, T in ((TOPK, 1.0), (TSAMPLE, 0.7)):
+            dn = host(head.dense(H[:B], mode=mode, temperature=T, seed=3, want_logits=True))
+            assert_report(parity.check_dense(pb.E, pb.H[:B], mode, T, 3, dn), f"dense B={B} m={mode}")
+    head.close()
+
+
 # ------------------------------------------------ Gemma-3-1B shape (cfg4) ---
 
 def test_gemma_sampled_probes_and_tokens():
