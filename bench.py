@@ -309,6 +309,16 @@ def main():
         res["dense"] = {"calls_per_s": round(1000.0 / dms, 2), "ms_per_call": round(dms, 5),
                         "achieved_gbs": round(dense_bytes / (dms * 1e-3) / 1e9, 1),
                         "speedup_flashhead_vs_dense": round(dms / ms, 3)}
+        # sanity reference for the dense baseline: the vendor GEMM (torch ->
+        # hipBLASLt / rocBLAS) for the logits plus an argmax, same replicas
+        Es = [hd._E for hd in heads]
+
+        def torch_dense(i):
+            z = torch.matmul(hb[i % len(hb)], Es[i % R].t())
+            return z.argmax(dim=1)
+
+        tms, _ = timed(torch_dense, args.dense_steps, 10)
+        res["dense"]["torch_matmul_argmax_ms"] = round(tms, 5)
     for hd in heads:
         hd.sync_status()
         hd.close()

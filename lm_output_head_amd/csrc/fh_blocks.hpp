@@ -116,15 +116,28 @@ struct HGroups {
 
 template <typename T, int MAXG>
 __device__ __forceinline__ void load_hgroups(const T* h, int G, int lane, HGroups<MAXG>& hg) {
+  constexpr int kPer = 16 / (int)sizeof(T);  // elements per 16-byte load
 #pragma unroll
   for (int m = 0; m < MAXG; ++m) {
     const int g = lane + 64 * m;
+    const uint4* src = reinterpret_cast<const uint4*>(h + (int64_t)min(g, G - 1) * 32);
+#pragma unroll
+    for (int c = 0; c < 32 / kPer; ++c) {
+      const uint4 v = g < G ? src[c] : uint4{0u, 0u, 0u, 0u};
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        float x;
+        if (sizeof(T) == 2)
+          x = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+        else
+          x = __uint_as_float(w[e]);
+        hg.h[m][kPer * c + e] = x;
+      }
+    }
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      hg.h[m][i] = g < G ? load_elem<T>(h, (int64_t)g * 32 + i) : 0.f;
-      s += hg.h[m][i];
-    }
+    for (int i = 0; i < 32; ++i) s += hg.h[m][i];
     hg.hsum[m] = s;
   }
 }
@@ -214,6 +227,18 @@ __device__ __forceinline__ Part block_merge_parts(const Part (&part)[NQ], int nq
   }
   __syncthreads();
   Part acc = part_empty();
+  if constexpr (NQ == 1 && NWAVES <= 16) {
+    // one query: lanes 0..15 of wave 0 merge the wave partials as a DPP tree
+    // within their row (4 levels, fixed pattern); thread 0 returns it
+    if (wave == 0) {
+      acc = lane < NWAVES ? sh[lane] : part_empty();
+      acc = part_merge(acc, dpp_part<0xB1>(acc));   // quad_perm [1,0,3,2]
+      acc = part_merge(acc, dpp_part<0x4E>(acc));   // quad_perm [2,3,0,1]
+      acc = part_merge(acc, dpp_part<0x141>(acc));  // row_half_mirror
+      acc = part_merge(acc, dpp_part<0x140>(acc));  // row_mirror
+    }
+    return acc;
+  }
   if ((int)threadIdx.x < nq) {
     const int q = threadIdx.x;
     acc = sh[q];

@@ -13,14 +13,19 @@
 // A's row l % 16 and B's column l % 16 at k = 8 (l / 16) .. + 7, and the
 // result's column l % 16 at rows 4 (l / 16) .. + 3.
 //
-// A workgroup is 4 waves; wave w owns rows [64 x + 16 w, +16) of the grid's
-// row block x and NQT query tiles of 16 (grid row y).  Rows stream from HBM
-// once per grid row; the queries' h (a few hundred KB) stay in the caches.
+// Tiling: a workgroup is 4 waves; wave w owns MT row tiles of 16 (rows
+// [64 MT x + 16 MT w, +16 MT)) and all NT query tiles of 16 of the grid row
+// y, so one workgroup covers 64 MT rows x 16 NT queries.  d is walked in
+// blocks of 128 elements: the queries' block of h is staged in LDS (double
+// buffered, the next block's loads in flight during the current block's
+// products) and shared by the 4 waves; each wave's rows stream from HBM
+// straight into registers, also one block ahead.  With B <= 128 queries in
+// one grid row, every row of E or C is read from HBM once per call.
 //
-// bf16 rows: for each 128-element block of d, lane l loads the 64 contiguous
-// bytes [128 blk + 32 g, +32) of its row and of each of its queries (g =
-// l / 16); MFMA step s uses elements 32 g + 8 s .. + 7 of that slice for both
-// operands, a fixed permutation of d that the sum does not see.
+// bf16 rows: lane l loads the 64 contiguous bytes [128 blk + 32 g, +32) of
+// its row (g = l / 16); MFMA step s uses elements 32 g + 8 s .. + 7 of that
+// slice for both operands, a fixed permutation of d that the sum does not
+// see.
 //
 // INT4 rows (the defined value sum_g sigma[k, g] sum_{i in g} q h): one MFMA
 // step is exactly one 32-element group.  The packed nibbles are re-laid out
@@ -80,168 +85,218 @@ struct MfmaArgs {
   Part* parts;  // EPI: [B x gridDim.x]
 };
 
-template <int NQT, bool INT4, bool EPI>
-__global__ __launch_bounds__(256) void k_mfma_rows(MfmaArgs a) {
-  __shared__ Part sh[4][16 * NQT];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+constexpr int kHRow = 128 + 8;  // LDS row of a staged h block (bf16), padded
+
+template <int NT, int MT, bool INT4, bool EPI>
+__global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
+  constexpr int QW = 16 * NT;  // queries per workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t sH[2][QW * kHRow];
+  __shared__ Part sh[EPI ? 4 : 1][EPI ? QW : 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
-  const int64_t r0 = (int64_t)blockIdx.x * 64 + wave * 16;
-  const int64_t ra = min(r0 + col, a.R - 1);  // the row this lane loads (clamped)
-  const int q0 = blockIdx.y * (16 * NQT);
-  int qrow[NQT];
-#pragma unroll
-  for (int t = 0; t < NQT; ++t) qrow[t] = min(q0 + 16 * t + col, a.B - 1);
+  const int64_t rbase = (int64_t)blockIdx.x * (64 * MT) + wave * (16 * MT);
+  const int q0 = blockIdx.y * QW;
+  const int nkb = (a.d + 127) / 128;
 
-  f32x4 acc[NQT];
+  // the queries' block kb of h -> registers (NT 16-byte chunks per thread)
+  uint4 hreg[NT];
+  auto load_h = [&](int kb) {
 #pragma unroll
-  for (int t = 0; t < NQT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NT; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 4, c16 = idx & 15;
+      const int k = 128 * kb + 8 * c16;
+      const int q = min(q0 + row, a.B - 1);
+      hreg[i] = k < a.d ? *reinterpret_cast<const uint4*>(a.H + (int64_t)q * a.d + k)
+                        : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_h = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 4, c16 = idx & 15;
+      *reinterpret_cast<uint4*>(&sH[buf][row * kHRow + 8 * c16]) = hreg[i];
+    }
+  };
 
-  if (r0 < a.R) {
-    if (!INT4) {
-      const uint16_t* Ar = static_cast<const uint16_t*>(a.A) + ra * a.d;
-      const int nblk = a.d / 128;
-      // ping-pong: the next 128-element block is in flight during the MFMAs
-      uint4 a0[4], b0[NQT][4], a1[4], b1[NQT][4];
-      auto ld = [&](int blk, uint4 (&av)[4], uint4 (&bv)[NQT][4]) {
-        const int k0 = 128 * blk + 32 * g;
-        const uint4* ap = reinterpret_cast<const uint4*>(Ar + k0);
+  f32x4 acc[MT][NT];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) av[s] = ap[s];
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int t = 0; t < NQT; ++t) {
-          const uint4* bp = reinterpret_cast<const uint4*>(a.H + (int64_t)qrow[t] * a.d + k0);
+    for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this lane's rows (clamped for loads; results past R are dropped)
+  int64_t ra[MT];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) bv[t][s] = bp[s];
-        }
-      };
-      auto mm = [&](const uint4 (&av)[4], const uint4 (&bv)[NQT][4]) {
+  for (int m = 0; m < MT; ++m) ra[m] = min(rbase + 16 * m + col, a.R - 1);
+
+  if (!INT4) {
+    const uint16_t* A = static_cast<const uint16_t*>(a.A);
+    uint4 av[2][MT][4];
+    auto load_a = [&](int kb, uint4 (&dst)[MT][4]) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int t = 0; t < NQT; ++t) acc[t] = mfma16(av[s], bv[t][s], acc[t]);
-      };
-      if (nblk > 0) ld(0, a0, b0);
-      for (int blk = 0; blk < nblk; blk += 2) {
-        if (blk + 1 < nblk) ld(blk + 1, a1, b1);
-        mm(a0, b0);
-        if (blk + 1 < nblk) {
-          if (blk + 2 < nblk) ld(blk + 2, a0, b0);
-          mm(a1, b1);
-        }
-      }
-      // the rest of d in steps of 32: lane group g takes elements 8g .. 8g+7
-      for (int kb = nblk * 128; kb < a.d; kb += 32) {
-        const int k = kb + 8 * g;
-        const bool ok = k < a.d;  // d is a multiple of 8
-        const uint4 av = ok ? *reinterpret_cast<const uint4*>(Ar + k) : uint4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int t = 0; t < NQT; ++t) {
-          const uint4 bv =
-              ok ? *reinterpret_cast<const uint4*>(a.H + (int64_t)qrow[t] * a.d + k)
-                 : uint4{0u, 0u, 0u, 0u};
-          acc[t] = mfma16(av, bv, acc[t]);
-        }
-      }
-    } else {
-      const uint8_t* Ar = static_cast<const uint8_t*>(a.A) + ra * a.a_row_bytes;
-      const int G = a.d / 32;
-      const uint4 neg136 = uint4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
-      const int64_t srow = r0 + 4 * g;  // this lane's four result rows
-      // one block = 4 groups; ping-pong so the next block's codes, scales and
-      // h slices are in flight during the current block's MFMAs
-      struct Blk {
-        uint4 w;
-        uint2 sg[4];
-        uint4 bv[NQT][4];
-      };
-      const int nb = (G + 3) / 4;
-      auto ld = [&](int blk, Blk& x) {
-        x.w = *reinterpret_cast<const uint4*>(Ar + 64 * blk + 16 * g);
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int grp = min(4 * blk + s, G - 1);
-          x.sg[s] = *reinterpret_cast<const uint2*>(a.sigT + (int64_t)grp * a.ldsig + srow);
-#pragma unroll
-          for (int t = 0; t < NQT; ++t)
-            x.bv[t][s] = *reinterpret_cast<const uint4*>(a.H + (int64_t)qrow[t] * a.d + 32 * grp + 8 * g);
+          const int k = 128 * kb + 32 * g + 8 * s;
+          dst[m][s] = k < a.d ? *reinterpret_cast<const uint4*>(A + ra[m] * a.d + k)
+                              : uint4{0u, 0u, 0u, 0u};
         }
-      };
-      auto mm = [&](int blk, const Blk& x) {
-        const uint32_t wv[4] = {x.w.x, x.w.y, x.w.z, x.w.w};
+    };
+    auto compute = [&](int buf, const uint4 (&cur)[MT][4]) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint4 bfr[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          bfr[n] = *reinterpret_cast<const uint4*>(&sH[buf][(16 * n + col) * kHRow + 32 * g + 8 * s]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[m][n] = mfma16(cur[m][s], bfr[n], acc[m][n]);
+      }
+    };
+    load_h(0);
+    load_a(0, av[0]);
+    store_h(0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; kb += 2) {
+      if (kb + 1 < nkb) {
+        load_h(kb + 1);
+        load_a(kb + 1, av[1]);
+      }
+      compute(0, av[0]);
+      if (kb + 1 < nkb) store_h(1);
+      __syncthreads();
+      if (kb + 1 < nkb) {
+        if (kb + 2 < nkb) {
+          load_h(kb + 2);
+          load_a(kb + 2, av[0]);
+        }
+        compute(1, av[1]);
+        if (kb + 2 < nkb) store_h(0);
+        __syncthreads();
+      }
+    }
+  } else {
+    const uint8_t* A = static_cast<const uint8_t*>(a.A);
+    const int G = a.d / 32;
+    const uint4 neg136 = uint4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
+    struct Blk {
+      uint4 w[MT];
+      uint2 sg[MT][4];
+    };
+    auto load_a = [&](int kb, Blk& x) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        x.w[m] = *reinterpret_cast<const uint4*>(A + ra[m] * a.a_row_bytes + 64 * kb + 16 * g);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          if (4 * blk + s >= G) break;
-          const float sig[4] = {__half2float(__ushort_as_half((uint16_t)(x.sg[s].x & 0xFFFFu))),
-                                __half2float(__ushort_as_half((uint16_t)(x.sg[s].x >> 16))),
-                                __half2float(__ushort_as_half((uint16_t)(x.sg[s].y & 0xFFFFu))),
-                                __half2float(__ushort_as_half((uint16_t)(x.sg[s].y >> 16)))};
+          const int grp = min(4 * kb + s, G - 1);
+          x.sg[m][s] = *reinterpret_cast<const uint2*>(a.sigT + (int64_t)grp * a.ldsig + rbase +
+                                                       16 * m + 4 * g);
+        }
+      }
+    };
+    auto compute = [&](int kb, int buf, const Blk& x) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (4 * kb + s >= G) break;
+        uint4 bfr[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          bfr[n] = *reinterpret_cast<const uint4*>(&sH[buf][(16 * n + col) * kHRow + 32 * s + 8 * g]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const uint32_t wv[4] = {x.w[m].x, x.w[m].y, x.w[m].z, x.w[m].w};
           const uint4 af = int4_fragment(wv[s]);
+          const float sig[4] = {
+              __half2float(__ushort_as_half((uint16_t)(x.sg[m][s].x & 0xFFFFu))),
+              __half2float(__ushort_as_half((uint16_t)(x.sg[m][s].x >> 16))),
+              __half2float(__ushort_as_half((uint16_t)(x.sg[m][s].y & 0xFFFFu))),
+              __half2float(__ushort_as_half((uint16_t)(x.sg[m][s].y >> 16)))};
 #pragma unroll
-          for (int t = 0; t < NQT; ++t) {
-            f32x4 part = mfma16(af, x.bv[t][s], f32x4{0.f, 0.f, 0.f, 0.f});
-            part = mfma16(neg136, x.bv[t][s], part);
+          for (int n = 0; n < NT; ++n) {
+            f32x4 part = mfma16(af, bfr[n], f32x4{0.f, 0.f, 0.f, 0.f});
+            part = mfma16(neg136, bfr[n], part);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(sig[i], part[i], acc[t][i]);
+            for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(sig[i], part[i], acc[m][n][i]);
           }
         }
-      };
-      Blk x0, x1;
-      ld(0, x0);
-      for (int blk = 0; blk < nb; blk += 2) {
-        if (blk + 1 < nb) ld(blk + 1, x1);
-        mm(blk, x0);
-        if (blk + 1 < nb) {
-          if (blk + 2 < nb) ld(blk + 2, x0);
-          mm(blk + 1, x1);
+      }
+    };
+    Blk x0, x1;
+    load_h(0);
+    load_a(0, x0);
+    store_h(0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; kb += 2) {
+      if (kb + 1 < nkb) {
+        load_h(kb + 1);
+        load_a(kb + 1, x1);
+      }
+      compute(kb, 0, x0);
+      if (kb + 1 < nkb) store_h(1);
+      __syncthreads();
+      if (kb + 1 < nkb) {
+        if (kb + 2 < nkb) {
+          load_h(kb + 2);
+          load_a(kb + 2, x0);
         }
+        compute(kb + 1, 1, x1);
+        if (kb + 2 < nkb) store_h(0);
+        __syncthreads();
       }
     }
   }
 
-  // lane holds rows r0 + 4g + i (i < 4) of queries q0 + 16t + col
+  // lane holds rows rbase + 16 m + 4 g + i (i < 4) of queries q0 + 16 n + col
   if (!EPI) {
     if (a.out) {
 #pragma unroll
-      for (int t = 0; t < NQT; ++t) {
-        const int q = q0 + 16 * t + col;
+      for (int n = 0; n < NT; ++n) {
+        const int q = q0 + 16 * n + col;
         if (q >= a.B) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t r = r0 + 4 * g + i;
-          if (r < a.R) a.out[(int64_t)q * a.ld_out + r] = acc[t][i];
-        }
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t r = rbase + 16 * m + 4 * g + i;
+            if (r < a.R) a.out[(int64_t)q * a.ld_out + r] = acc[m][n][i];
+          }
       }
     }
     return;
   }
 #pragma unroll
-  for (int t = 0; t < NQT; ++t) {
-    const int q = q0 + 16 * t + col;
+  for (int n = 0; n < NT; ++n) {
+    const int q = q0 + 16 * n + col;
     Part p = part_empty();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = r0 + 4 * g + i;
-      if (r < a.R && q < a.B) {
-        if (a.out) a.out[(int64_t)q * a.ld_out + r] = acc[t][i];
-        p = part_merge(p, part_of(acc[t][i], (int32_t)r, a.token_sample, a.tprime, a.seed,
-                                  (uint32_t)q));
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = rbase + 16 * m + 4 * g + i;
+        if (r < a.R && q < a.B) {
+          if (a.out) a.out[(int64_t)q * a.ld_out + r] = acc[m][n][i];
+          p = part_merge(p, part_of(acc[m][n][i], (int32_t)r, a.token_sample, a.tprime, a.seed,
+                                    (uint32_t)q));
+        }
       }
-    }
     // the four lane groups hold the same query: fold them (fixed order)
 #pragma unroll
-    for (int m = 16; m <= 32; m *= 2) {
-      const Part o{__shfl_xor(p.key, m), __shfl_xor(p.z, m), __shfl_xor(p.m, m),
-                   __shfl_xor(p.s, m), __shfl_xor(p.id, m)};
-      p = (lane & m) ? part_merge(o, p) : part_merge(p, o);
+    for (int msk = 16; msk <= 32; msk *= 2) {
+      const Part o{__shfl_xor(p.key, msk), __shfl_xor(p.z, msk), __shfl_xor(p.m, msk),
+                   __shfl_xor(p.s, msk), __shfl_xor(p.id, msk)};
+      p = (lane & msk) ? part_merge(o, p) : part_merge(p, o);
     }
-    if (g == 0) sh[wave][16 * t + col] = p;
+    if (g == 0) sh[wave][16 * n + col] = p;
   }
   __syncthreads();
-  if ((int)threadIdx.x < 16 * NQT) {
-    const int q = q0 + threadIdx.x;
-    Part r = sh[0][threadIdx.x];
+  if (tid < QW) {
+    const int q = q0 + tid;
+    Part r = sh[0][tid];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) r = part_merge(r, sh[w][threadIdx.x]);
+    for (int w = 1; w < 4; ++w) r = part_merge(r, sh[w][tid]);
     if (q < a.B) a.parts[(int64_t)q * gridDim.x + blockIdx.x] = r;
   }
 }
@@ -440,31 +495,47 @@ hipError_t launch_mfma_relayout(const KernelCtx& k, uint8_t* cq_mfma, uint16_t* 
   return hipGetLastError();
 }
 
-// Query tiles per workgroup: as many as keep at least ~2 workgroups per CU
-// busy, up to 4.
-static int mfma_nqt(int64_t R, int B, int cus) {
-  const int64_t rblocks = (R + 63) / 64;
+// Tile shape: all query tiles in one workgroup (up to 8: the rows are read
+// once), two row tiles per wave; fewer while that leaves less than ~2
+// workgroups per CU.
+struct GemmShape {
+  int nt, mt;
+};
+static GemmShape gemm_shape(int64_t R, int B, int cus) {
   const int tiles = (B + 15) / 16;
-  int nqt = 4;
-  while (nqt > 1 && rblocks * ((tiles + nqt - 1) / nqt) < 2 * (int64_t)cus) nqt /= 2;
-  return std::min(nqt, std::max(1, tiles));
+  GemmShape s{std::min(8, tiles) <= 1 ? 1 : std::min(8, tiles) <= 2 ? 2 : std::min(8, tiles) <= 4 ? 4 : 8, 2};
+  auto wgs = [&](const GemmShape& x) {
+    return ((R + 64 * x.mt - 1) / (64 * x.mt)) * ((tiles + x.nt - 1) / x.nt);
+  };
+  if (wgs(s) < 2 * (int64_t)cus) s.mt = 1;
+  while (s.nt > 1 && wgs(s) < (int64_t)cus) s.nt /= 2;
+  return s;
 }
 
-template <int NQT, bool INT4, bool EPI>
-static hipError_t mfma_go(const MfmaArgs& a, hipStream_t st, int64_t* nblocks) {
-  const dim3 grid((unsigned)((a.R + 63) / 64), (unsigned)((a.B + 16 * NQT - 1) / (16 * NQT)));
+template <int NT, int MT, bool INT4, bool EPI>
+static hipError_t gemm_go(const MfmaArgs& a, hipStream_t st, int64_t* nblocks) {
+  const dim3 grid((unsigned)((a.R + 64 * MT - 1) / (64 * MT)),
+                  (unsigned)((a.B + 16 * NT - 1) / (16 * NT)));
   if (nblocks) *nblocks = grid.x;
-  hipLaunchKernelGGL((k_mfma_rows<NQT, INT4, EPI>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_mfma_gemm<NT, MT, INT4, EPI>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+template <int MT, bool INT4, bool EPI>
+static hipError_t gemm_nt(const MfmaArgs& a, int nt, hipStream_t st, int64_t* nblocks) {
+  switch (nt) {
+    case 1: return gemm_go<1, MT, INT4, EPI>(a, st, nblocks);
+    case 2: return gemm_go<2, MT, INT4, EPI>(a, st, nblocks);
+    case 4: return gemm_go<4, MT, INT4, EPI>(a, st, nblocks);
+    default: return gemm_go<8, MT, INT4, EPI>(a, st, nblocks);
+  }
 }
 
 template <bool INT4, bool EPI>
 static hipError_t mfma_dispatch(const MfmaArgs& a, int cus, hipStream_t st, int64_t* nblocks) {
-  switch (mfma_nqt(a.R, a.B, cus)) {
-    case 1: return mfma_go<1, INT4, EPI>(a, st, nblocks);
-    case 2: return mfma_go<2, INT4, EPI>(a, st, nblocks);
-    default: return mfma_go<4, INT4, EPI>(a, st, nblocks);
-  }
+  const GemmShape s = gemm_shape(a.R, a.B, cus);
+  return s.mt == 2 ? gemm_nt<2, INT4, EPI>(a, s.nt, st, nblocks)
+                   : gemm_nt<1, INT4, EPI>(a, s.nt, st, nblocks);
 }
 
 int64_t mfma_blocks(int64_t R) { return (R + 63) / 64; }
@@ -484,12 +555,12 @@ hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, 
 
 int64_t gather_cm_blocks(int64_t c, int) { return (c + kCmClusters - 1) / kCmClusters; }
 // Cluster-major pays off when clusters are shared: the expected number of
-// queries per probed cluster, B p / (c (1 - (1 - p/c)^B)), is at least 3.
+// queries per probed cluster, B p / (c (1 - (1 - p/c)^B)), is at least 2.
 bool gather_cm_fits(int B, int64_t p, int64_t c) {
   if (B < 2 || B > kCmMaxB) return false;
   const double f = (double)p / (double)c;
   const double u = (double)c * (1.0 - std::pow(1.0 - f, (double)B));
-  return (double)B * (double)p >= 3.0 * u;
+  return (double)B * (double)p >= 2.0 * u;
 }
 
 hipError_t launch_gather_cm(const KernelCtx& k, int cus, const void* h, int B, int p,
