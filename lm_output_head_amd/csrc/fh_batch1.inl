@@ -25,19 +25,19 @@ namespace fh {
 //                  selector: before its own rows it waits for the c scores,
 //                  selects the probes and publishes them as a bitset over
 //                  the clusters; each stage-2 workgroup finds the probes of
-//                  its rows by a prefix count over that bitset.  The last
-//                  stage-2 workgroup to finish (an arrival counter) also
-//                  merges the G2 partials.
+//                  its rows by a prefix count over that bitset.
+//   G1+G2          the finisher: polls the G2 stage-2 partials and merges
+//                  them in index order.  G2 <= CUs - 1, so it finds a CU as
+//                  soon as stage 1 retires and its polls overlap stage 2.
 // Results pass between workgroups as 64-bit words tagged with the call's
 // epoch (epoch << 32 | payload), written and polled with agent-scope (sc1)
 // accesses.  A workgroup only ever waits for words written by workgroups
-// with smaller indices, or by workgroups that have already counted their
-// arrival.  Like a decoupled look-back scan, this relies on workgroups being
-// dispatched in index order, so every awaited workgroup is already running
-// and never waits for its waiter; the grid need not be co-resident.  Sizes
-// keep G1 < CUs and G2 <= CUs so that at one workgroup per CU the selector
-// starts at once and every stage-2 workgroup is resident when stage 1
-// retires.  Every wait is bounded: past kSpinLimit polls the waiter sets
+// with smaller indices.  Like a decoupled look-back scan, this relies on
+// workgroups being dispatched in index order, so every awaited workgroup is
+// already running and never waits for its waiter; the grid need not be
+// co-resident.  Sizes keep G1 < CUs and G2 < CUs so that at one workgroup
+// per CU the selector starts at once and every stage-2 workgroup and the
+// finisher are resident when stage 1 retires.  Every wait is bounded: past kSpinLimit polls the waiter sets
 // *err and goes on with what it has, so the grid always drains.
 // ======================================================================
 struct FusedArgs {
@@ -70,8 +70,7 @@ struct FusedArgs {
   int32_t* out_token;
   float* out_logit;
   float* out_lse;
-  unsigned* err;    // sticky: a poll gave up
-  unsigned* count;  // stage-2 arrivals of this call (0 between calls)
+  unsigned* err;  // sticky: a poll gave up
 };
 
 constexpr unsigned kSpinLimit = 1u << 20;
@@ -124,7 +123,6 @@ union Batch1Shared {
 template <typename T, int MAXM, int KP, bool INT4, int MAXG>
 __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   __shared__ Batch1Shared sh;
-  __shared__ bool s_last;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int w = blockIdx.x;
@@ -159,6 +157,31 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     __syncthreads();
     FH_TRACE(7);  // every wave of this workgroup is done
 #endif
+    return;
+  }
+
+  if (w == a.g1 + a.g2) {  // ---- finisher: the stage-2 partials in a fixed order
+    // waves [0, nwv) hold partials: part i goes to thread i mod 1024
+    const int nwv = min(16, (a.g2 + 63) / 64);
+    Part acc = part_empty();
+    for (int i = threadIdx.x; i < a.g2; i += 1024) {
+      unsigned long long* tp = a.tparts + 5 * (int64_t)i;
+      unsigned long long* const ptr[5] = {tp, tp + 1, tp + 2, tp + 3, tp + 4};
+      const bool live[5] = {true, true, true, true, true};
+      uint32_t wv[5];
+      poll_tagged<5>(ptr, live, a.epoch, a.err, wv);
+      acc = part_merge(acc, Part{__uint_as_float(wv[0]), __uint_as_float(wv[1]),
+                                 __uint_as_float(wv[2]), __uint_as_float(wv[3]), (int32_t)wv[4]});
+    }
+    if (wave < nwv) {
+      acc = wave_merge_part(acc);
+      if (lane == 0) sh.parts[wave] = acc;
+    }
+    __syncthreads();
+    Part r = sh.parts[0];
+    for (int w2 = 1; w2 < nwv; ++w2) r = part_merge(r, sh.parts[w2]);
+    if (threadIdx.x == 0) write_outputs(r, 0, a.out_token, a.out_logit, a.out_lse);
+    FH_TRACE(14);
     return;
   }
 
@@ -252,38 +275,8 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     st_tagged(tp + 2, tag(a.epoch, __float_as_uint(wg.m)));
     st_tagged(tp + 3, tag(a.epoch, __float_as_uint(wg.s)));
     st_tagged(tp + 4, tag(a.epoch, (uint32_t)wg.id));
-    // the last stage-2 workgroup to get here merges
-    s_last = __hip_atomic_fetch_add(a.count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(a.g2 - 1);
   }
   FH_TRACE(6);
-  __syncthreads();
-  if (!s_last) return;
-
-  // ---- finisher: every stage-2 partial, merged in a fixed order
-  if (threadIdx.x == 0)  // every increment of this call is in: ready for the next
-    __hip_atomic_store(a.count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // waves [0, nwv) hold partials: part i goes to thread i mod 1024
-  const int nwv = min(16, (a.g2 + 63) / 64);
-  Part acc = part_empty();
-  for (int i = threadIdx.x; i < a.g2; i += 1024) {
-    unsigned long long* tp = a.tparts + 5 * (int64_t)i;
-    unsigned long long* const ptr[5] = {tp, tp + 1, tp + 2, tp + 3, tp + 4};
-    const bool live[5] = {true, true, true, true, true};
-    uint32_t wv[5];
-    poll_tagged<5>(ptr, live, a.epoch, a.err, wv);
-    acc = part_merge(acc, Part{__uint_as_float(wv[0]), __uint_as_float(wv[1]),
-                               __uint_as_float(wv[2]), __uint_as_float(wv[3]), (int32_t)wv[4]});
-  }
-  if (wave < nwv) {
-    acc = wave_merge_part(acc);
-    if (lane == 0) sh.parts[wave] = acc;
-  }
-  __syncthreads();
-  Part r = sh.parts[0];
-  for (int w2 = 1; w2 < nwv; ++w2) r = part_merge(r, sh.parts[w2]);
-  if (threadIdx.x == 0) write_outputs(r, 0, a.out_token, a.out_logit, a.out_lse);
-  FH_TRACE(14);
 }
 
 static FusedArgs fused_args(const FusedLaunch& f) {
@@ -294,21 +287,20 @@ static FusedArgs fused_args(const FusedLaunch& f) {
   a.probe_sample = f.probe_sample; a.token_sample = f.token_sample;
   a.temperature = f.temperature; a.tprime = f.tprime; a.seed = f.seed;
   a.rows1 = (int)batch1_rows(k.c, batch1_slots1(f.cus));
-  a.rows2 = (int)batch1_rows((int64_t)f.p * k.b, f.cus);
+  a.rows2 = (int)batch1_rows((int64_t)f.p * k.b, batch1_slots2(f.cus));
   a.g1 = batch1_stage1_blocks(k.c, f.cus);
   a.g2 = batch1_stage2_blocks(f.p, k.b, f.cus);
   a.epoch = f.epoch; a.tscores = f.tscores; a.tsel = f.tsel; a.tparts = f.tparts;
   a.out_clusters = f.out_clusters; a.out_ids = f.out_ids; a.out_logits = f.out_logits;
   a.out_token = f.out_token; a.out_logit = f.out_logit; a.out_lse = f.out_lse;
   a.err = f.err;
-  a.count = f.count;
   a.zq = select_quantile(k.c, f.p);
   return a;
 }
 
 template <typename T, int MAXM, int KP, bool INT4, int MAXG>
 static hipError_t b1_go(const FusedLaunch& f, const FusedArgs& a) {
-  const unsigned grid = (unsigned)(a.g1 + a.g2);
+  const unsigned grid = (unsigned)(a.g1 + a.g2 + 1);
   hipLaunchKernelGGL((k_batch1<T, MAXM, KP, INT4, MAXG>), dim3(grid), dim3(1024), 0,
                      f.ctx->stream, a);
   return hipGetLastError();

@@ -59,7 +59,7 @@ struct fh_engine {
   int32_t* mpre = nullptr;    // [ceil(c/32) x max_batch] probes in earlier words
   fh::Part* parts = nullptr;  // [max_batch x parts_per_q]
   int64_t parts_per_q = 0;
-  unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up; [1]: arrival counter
+  unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up
   unsigned long long* tagged = nullptr;  // batch-1 hand-over words: c scores + 5 per partial
   unsigned epoch = 0;
   int cus = 0;                // compute units of the device
@@ -354,7 +354,6 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
     f.out_logit = out_token_logit;
     f.out_lse = out_lse;
     f.err = e->sync;
-    f.count = e->sync + 1;
     hipError_t r = timed(e, st, "batch1", [&] { return fh::launch_batch1(f); });
     return r == hipSuccess ? FH_OK : hip_fail(r, "batch-1 launch");
   }

@@ -102,7 +102,6 @@ struct FusedLaunch {
   float* out_logit;
   float* out_lse;
   unsigned* err;                  // sticky flag: a bounded poll gave up
-  unsigned* count;                // arrival counter, 0 between calls (zeroed at create)
 };
 hipError_t launch_batch1(const FusedLaunch& f);
 // per storage variant, one translation unit each
@@ -117,6 +116,7 @@ hipError_t launch_batch1_f32_int4(const FusedLaunch& f);
 constexpr int kBatch1RowsUnit = 32;
 int64_t batch1_rows(int64_t n, int64_t slots);
 int64_t batch1_slots1(int cus);  // stage-1 workgroup budget
+int64_t batch1_slots2(int cus);  // stage-2 workgroup budget (one CU left for the finisher)
 int batch1_stage1_blocks(int64_t c, int cus);
 int batch1_stage2_blocks(int64_t p, int64_t b, int cus);
 // Whether a batch-1 call with p probes fits the single launch (a stage-2
