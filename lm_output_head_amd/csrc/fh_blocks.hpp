@@ -285,6 +285,7 @@ struct SelShared {
   int red_scan[kSelWaves];
   int red_out[kSelWaves];
   int beta, above, cnt;
+  float tau, kmax;
 };
 
 // Keys per thread for c clusters over 1024 threads (1, 2, 8 or 16).
@@ -511,18 +512,27 @@ __device__ __forceinline__ void select_bits(const float (&x)[KP], int c, int p, 
     }
     __syncthreads();
     const bool rl = lane < kSelWaves;
-    mx = readlane_f(row_allreduce(rl ? sh.red[0][lane] : -FLT_MAX,
-                                  [](float a, float b) { return fmaxf(a, b); }), 0);
-    sum = readlane_f(row_allreduce(rl ? sh.red[1][lane] : 0.f,
-                                   [](float a, float b) { return a + b; }), 0);
-    sq = readlane_f(row_allreduce(rl ? sh.red[2][lane] : 0.f,
-                                  [](float a, float b) { return a + b; }), 0);
-    const float inv = 1.f / (float)min(c, kSelThreads);
-    const float mean = sum * inv;
-    const float sd = sqrtf(fmaxf(sq * inv - mean * mean, 0.f));
-    // at least -FLT_MAX (also for a NaN or -inf estimate), so that padding
-    // slots are never above it
-    const float tau = fmaxf(mean + sd * zq, -FLT_MAX);
+    if (wave == 0) {
+      // one wave combines the wave partials and places tau
+      const float m0 = readlane_f(row_allreduce(rl ? sh.red[0][lane] : -FLT_MAX,
+                                                [](float a, float b) { return fmaxf(a, b); }), 0);
+      const float s0 = readlane_f(row_allreduce(rl ? sh.red[1][lane] : 0.f,
+                                                [](float a, float b) { return a + b; }), 0);
+      const float q0 = readlane_f(row_allreduce(rl ? sh.red[2][lane] : 0.f,
+                                                [](float a, float b) { return a + b; }), 0);
+      const float inv = 1.f / (float)min(c, kSelThreads);
+      const float mean = s0 * inv;
+      const float sd = sqrtf(fmaxf(q0 * inv - mean * mean, 0.f));
+      // at least -FLT_MAX (also for a NaN or -inf estimate), so that padding
+      // slots are never above it
+      if (lane == 0) {
+        sh.tau = fmaxf(mean + sd * zq, -FLT_MAX);
+        sh.kmax = m0;
+      }
+    }
+    __syncthreads();
+    const float tau = sh.tau;
+    mx = sh.kmax;
     const uint32_t lo = ordered_bits(tau);
     // compact the keys above tau into this wave's candidate list
     int wcount = 0;

@@ -401,7 +401,10 @@ int batch1_stage1_blocks(int64_t c, int cus) {
   const int64_t r = batch1_rows(c, batch1_slots1(cus));
   return (int)((c + r - 1) / r);
 }
-int64_t batch1_slots2(int cus) { return std::max(1, cus - 1); }
+#ifndef FH_STAGE2_SLOTS_DIV
+#define FH_STAGE2_SLOTS_DIV 1  // stage-2 workgroup budget = (CUs - 1) / this
+#endif
+int64_t batch1_slots2(int cus) { return std::max(1, (cus - 1) / FH_STAGE2_SLOTS_DIV); }
 int batch1_stage2_blocks(int64_t p, int64_t b, int cus) {
   const int64_t r = batch1_rows(p * b, batch1_slots2(cus));
   return (int)std::max<int64_t>(1, (p * b + r - 1) / r);
