@@ -264,8 +264,9 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     }
     part[0] = part_merge(part[0], part_of(z, (int32_t)src, a.token_sample, a.tprime, a.seed, 0u));
   };
-  wave_rows<T, MAXM, 1>(static_cast<const T*>(a.Ec ? a.Ec : a.E), a.d, lane, hv, 1, r_lo + wave,
-                        r_hi, 16, src_of, tok_of, sink);
+  // four rows in flight per wave when the register slice allows it
+  wave_rows<T, MAXM, 1, (MAXM <= 4 ? 4 : 2)>(static_cast<const T*>(a.Ec ? a.Ec : a.E), a.d, lane,
+                                             hv, 1, r_lo + wave, r_hi, 16, src_of, tok_of, sink);
   __syncthreads();  // sh.probes is read above; sh.parts aliases it
   const Part wg = block_merge_parts<16, 1>(part, 1, sh.parts);
   if (threadIdx.x == 0) {

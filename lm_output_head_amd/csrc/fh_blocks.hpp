@@ -61,42 +61,45 @@ __device__ __forceinline__ void load_hslice(const T* h, int nch, int lane, uint4
   }
 }
 
-template <typename T, int MAXM, int NQ, typename SrcOf, typename TokOf, typename Sink>
+template <typename T, int MAXM, int NQ, int RPI = 2, typename SrcOf, typename TokOf,
+          typename Sink>
 __device__ __forceinline__ void wave_rows(const T* __restrict__ M, int d, int lane,
                                           const uint4 (&hv)[NQ][MAXM], int nq, int64_t r_begin,
                                           int64_t r_end, int64_t stride, SrcOf src_of,
                                           TokOf tok_of, Sink sink) {
   const int nch = d / Chunk<T>::kElems;
 #pragma unroll 1
-  for (int64_t r = r_begin; r < r_end; r += 2 * stride) {
-    const int64_t rb = r + stride;
-    const bool okb = rb < r_end;
-    const int64_t sa = src_of(r);
-    const int64_t sb = okb ? src_of(rb) : sa;
-    const int64_t ta = tok_of(sa);
-    const int64_t tb = okb ? tok_of(sb) : ta;
-    const uint4* ra_p = reinterpret_cast<const uint4*>(M + sa * d);
-    const uint4* rb_p = reinterpret_cast<const uint4*>(M + sb * d);
-    uint4 ma[MAXM], mb[MAXM];
+  for (int64_t r = r_begin; r < r_end; r += RPI * stride) {
+    // RPI rows' loads are issued before any math
+    bool ok[RPI];
+    int64_t src[RPI], tk[RPI];
+    uint4 mr[RPI][MAXM];
 #pragma unroll
-    for (int m = 0; m < MAXM; ++m) {
-      const int ch = lane + 64 * m;
-      ma[m] = ch < nch ? ra_p[ch] : uint4{0u, 0u, 0u, 0u};
-      mb[m] = (okb && ch < nch) ? rb_p[ch] : uint4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < RPI; ++i) {
+      ok[i] = i == 0 || r + i * stride < r_end;
+      src[i] = ok[i] ? src_of(r + i * stride) : src[0];
+      tk[i] = ok[i] ? tok_of(src[i]) : tk[0];
+      const uint4* rp = reinterpret_cast<const uint4*>(M + src[i] * d);
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) {
+        const int ch = lane + 64 * m;
+        mr[i][m] = (ok[i] && ch < nch) ? rp[ch] : uint4{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       if (q >= nq) break;
-      float acc_a = 0.f, acc_b = 0.f;
+      float acc[RPI];
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m) {
-        acc_a = Chunk<T>::dot(ma[m], hv[q][m], acc_a);
-        acc_b = Chunk<T>::dot(mb[m], hv[q][m], acc_b);
+      for (int i = 0; i < RPI; ++i) {
+        acc[i] = 0.f;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) acc[i] = Chunk<T>::dot(mr[i][m], hv[q][m], acc[i]);
+        acc[i] = wave_sum(acc[i]);
       }
-      acc_a = wave_sum(acc_a);
-      acc_b = wave_sum(acc_b);
-      sink(q, r, ta, acc_a);
-      if (okb) sink(q, rb, tb, acc_b);
+#pragma unroll
+      for (int i = 0; i < RPI; ++i)
+        if (ok[i]) sink(q, r + i * stride, tk[i], acc[i]);
     }
   }
 }
