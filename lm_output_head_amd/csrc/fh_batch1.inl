@@ -18,8 +18,8 @@ namespace fh {
 //
 // The grid's workgroups (1024 threads) take roles by index, in the order
 // they are dispatched:
-//   [0, G1)        stage 1: rows1 centroid rows each (16 waves x 2 rows at a
-//                  time), each score stored as soon as it is reduced;
+//   [0, G1)        stage 1: rows1 centroid rows each (wave w takes rows w,
+//                  w + 16, ...), each score stored as soon as it is reduced;
 //   [G1, G1+G2)    stage 2: rows2 of the p*b retrieved tokens each, with the
 //                  fused epilogue.  The first of them (G1) is also the
 //                  selector: before its own rows it waits for the c scores,

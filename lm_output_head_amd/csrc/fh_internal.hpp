@@ -111,9 +111,12 @@ hipError_t launch_batch1_f32(const FusedLaunch& f);
 hipError_t launch_batch1_f32_int4(const FusedLaunch& f);
 
 // Batch-1 sizing: rows per workgroup are a multiple of kBatch1RowsUnit
-// (16 waves x 2 rows), large enough that a stage needs at most `slots`
-// workgroups.
-constexpr int kBatch1RowsUnit = 32;
+// (one row for each of the 16 waves), large enough that a stage needs at
+// most `slots` workgroups.
+#ifndef FH_BATCH1_ROWS_UNIT
+#define FH_BATCH1_ROWS_UNIT 16
+#endif
+constexpr int kBatch1RowsUnit = FH_BATCH1_ROWS_UNIT;
 int64_t batch1_rows(int64_t n, int64_t slots);
 int64_t batch1_slots1(int cus);  // stage-1 workgroup budget
 int64_t batch1_slots2(int cus);  // stage-2 workgroup budget (one CU left for the finisher)

@@ -388,9 +388,10 @@ hipError_t launch_finish(const KernelCtx& k, const Part* parts, int B, int64_t n
 
 // ---- batch-1 path: one launch
 
-// Rows per workgroup: a multiple of 32 (16 waves x 2 rows) large enough that
-// a stage needs at most `slots` workgroups: cus - 4 for stage 1 (so the
-// selector and a few stage-2 workgroups start at once), cus for stage 2.
+// Rows per workgroup: a multiple of kBatch1RowsUnit (a row per wave) large
+// enough that a stage needs at most `slots` workgroups: cus - 4 for stage 1
+// (so the selector and a few stage-2 workgroups start at once), cus - 1 for
+// stage 2 (one CU for the finisher).
 int64_t batch1_rows(int64_t n, int64_t slots) {
   slots = std::max<int64_t>(slots, 1);
   const int64_t units = (n + kBatch1RowsUnit - 1) / kBatch1RowsUnit;
