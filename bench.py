@@ -49,6 +49,11 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "multi"],
                     help="auto: one launch per batch-1 call; multi: one per stage")
+    ap.add_argument("--cluster", action="store_true",
+                    help="time the offline balanced spherical k-means (fh_cluster) at --shape "
+                         "instead of the head, one JSON line of its own")
+    ap.add_argument("--cluster-iters", type=int, default=5)
+    ap.add_argument("--cluster-runs", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of known size (to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run) and exit")
@@ -150,6 +155,111 @@ def cpu_baseline(pb, p, quant, mode, temperature, seconds):
                       f"(float64 numpy oracle, BLAS threads={cores})"}
 
 
+def cluster_cpu_baseline(E, c, seconds):
+    """The clustering oracle on host cores over bounded samples, scaled to
+    one whole clustering: k-means++ steps on the full table (each a pass over
+    every row) and one iteration's similarities on a block of rows.  The
+    balanced rounds and the update are left out, so this underestimates the
+    oracle's time."""
+    import numpy as np
+
+    from oracle import cluster_oracle as co
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    v = E.shape[0]
+    Xn = co.normalize_rows(E)
+    u = np.random.default_rng(7).random(c)
+    t0 = time.perf_counter()
+    m = 1
+    D = 1.0 - Xn @ Xn[min(int(u[0] * v), v - 1)]
+    while time.perf_counter() - t0 < seconds / 2 and m < c:
+        t = co.pp_pick(D * D, u[m])
+        D = np.minimum(D, 1.0 - Xn @ Xn[t])
+        m += 1
+    pp_s = (time.perf_counter() - t0) / m * c
+    rows = min(v, 4096)
+    C = Xn[:c]
+    t1 = time.perf_counter()
+    _ = Xn[:rows] @ C.T
+    sims_s = (time.perf_counter() - t1) * v / rows
+    return pp_s, sims_s, {
+        "unit": "s per clustering", "cores": int(cores), "kind": "oracle",
+        "sample": f"{m} k-means++ steps over all {v} rows and one {rows}-row similarity block "
+                  f"(float64 numpy oracle), scaled to {c} centres and {v} rows; the balanced "
+                  f"rounds and the update are not included"}
+
+
+def cluster_main(args):
+    """One JSON line: seconds per balanced spherical k-means of the head's
+    embedding table (planted clusters, bf16), with the k-means++ phase's
+    achieved HBM bandwidth (it reads the fp32 unit rows once per centre)."""
+    import numpy as np
+    import torch
+
+    from lm_output_head_amd import flashhead as fhb
+    from synth import SHAPES, make_problem
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    shape = SHAPES[args.shape]
+    v, d, c = shape.v, shape.d, shape.c
+    print(f"[bench] generating {shape.name} table", file=sys.stderr, flush=True)
+    pb = make_problem(shape, nq=1)
+    if shape.dtype == "bf16":
+        E = torch.from_numpy(pb.E_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        E = torch.from_numpy(np.ascontiguousarray(pb.E, dtype=np.float32)).cuda()
+    u = np.random.default_rng(7).random(c)
+    C = torch.empty((c, d), dtype=torch.float32, device="cuda")
+    c2t = torch.empty((c, v // c), dtype=torch.int32, device="cuda")
+    asg = torch.empty(v, dtype=torch.int32, device="cuda")
+    runs = []
+    for i in range(max(1, args.cluster_runs)):
+        print(f"[bench] clustering run {i}", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tm = fhb.fh_cluster(E, c, args.cluster_iters, u, C, c2t, None, asg)
+        torch.cuda.synchronize()
+        tm["wall_s"] = time.perf_counter() - t0
+        runs.append(tm)
+    best = min(runs, key=lambda r: r["total_ms"])
+    truth = np.empty(v, dtype=np.int64)
+    truth[pb.C2T.ravel()] = np.repeat(np.arange(c), v // c)
+    from oracle import cluster_oracle as co  # quality figures of the result
+    got = asg.cpu().numpy()
+    ari = co.adjusted_rand_index(got, truth)
+    pp_bytes = c * (v * d * 4 + v * 4 * 3)  # X rows, D read/write, D in the pick
+    init_gbs = pp_bytes / (best["init_ms"] * 1e-3) / 1e9
+    sims_tflops = 2.0 * v * c * d * args.cluster_iters / (best["sims_ms"] * 1e-3) / 1e12
+    res = {
+        "metric": "balanced k-means s per clustering", "value": round(best["total_ms"] / 1e3, 4),
+        "unit": "s", "n_gpus": 1, "steps": len(runs), "warmup": 0,
+        "ms_per_step": round(best["total_ms"], 2), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic planted clusters",
+        "config": {"workload": f"{shape.name} table v={v} d={d} c={c} b={v // c}, "
+                               f"{args.cluster_iters} iterations, {shape.dtype} input"},
+        "phases_ms": {"kmeanspp": round(best["init_ms"], 2), "sims": round(best["sims_ms"], 2),
+                      "rounds_and_update": round(best["total_ms"] - best["init_ms"]
+                                                 - best["sims_ms"], 2)},
+        "rounds": best["rounds"],
+        "roofline": {"bound": "hbm", "achieved": round(init_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(init_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "phase": "k-means++ (per centre: one pass over the fp32 unit rows)"},
+        "sims_tflops_f32": round(sims_tflops, 2),
+        "quality": {"ari_vs_planted": round(ari, 5)},
+    }
+    if not args.no_cpu:
+        print("[bench] timing the clustering oracle", file=sys.stderr, flush=True)
+        pp_s, sims_s, base = cluster_cpu_baseline(pb.E.astype(np.float64), c, args.cpu_seconds)
+        base["value"] = round(pp_s + sims_s * args.cluster_iters, 2)
+        res["cpu_baseline"] = base
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -158,6 +268,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.cluster:
+        cluster_main(args)
         return
 
     import numpy as np

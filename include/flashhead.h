@@ -182,10 +182,10 @@ fh_status fh_profile_end(fh_engine* e, fh_kernel_time* out, int max, int* count)
 
 /*
  * fh_set_path — choose how fh_forward runs a batch-1 call.
- *   FH_PATH_AUTO  (default) two launches: stage 1 with the probe selection
- *                 done by its first workgroup, then stage 2 with the
- *                 epilogue merged by its first workgroup.  Batches of B > 1
- *                 use one launch per stage.
+ *   FH_PATH_AUTO  (default) one launch for the whole call when p probes fit
+ *                 it: stage-1 workgroups, a selecting workgroup, stage-2
+ *                 workgroups and a finishing workgroup hand over through
+ *                 device memory.  Batches of B > 1 use one launch per stage.
  *   FH_PATH_MULTI always one launch per stage.
  * Both paths return the same ids and logits; the LSE may differ in the last
  * bits (a different merge order).
@@ -200,6 +200,66 @@ fh_status fh_set_path(fh_engine* e, int path);
  * above) are what can cause it.
  */
 fh_status fh_sync_status(fh_engine* e, void* stream);
+
+/*
+ * Offline clustering: the step that produces C and C2T for fh_create
+ * ([X] §1.2.1 balanced clustering, §2.1 offline clustering; [A] abstract,
+ * innovation (1)).  Balanced spherical k-means: rows are L2-normalised; c
+ * centres are seeded with k-means++; every iteration computes the cosine
+ * similarity of every token to every centre, assigns tokens so that every
+ * cluster holds exactly b = v / c of them, and moves every centre to the
+ * normalised mean of its tokens.  The pages leave these steps open; this
+ * library reads them as:
+ *   - k-means++ on the sphere: D(t) = 1 - max_j cos(t, C_j); centre 0 is
+ *     token floor(u[0] v); centre i is the first token, in id order, whose
+ *     running sum of D^2 exceeds u[i] * sum(D^2) (token floor(u[i] v) if
+ *     every D is 0).  The uniforms u are inputs, so a run is repeatable.
+ *   - balanced assignment by rounds: each unassigned token proposes to its
+ *     most similar cluster that is not yet full (ties: smaller cluster id);
+ *     each cluster accepts, up to its remaining room, the proposals with the
+ *     highest similarity (ties: smaller token id); accepted tokens are final
+ *     and the rest propose again.
+ *   - update: C_k = normalise(sum of its tokens' unit rows); C2T[k] lists
+ *     cluster k's tokens in ascending id.
+ * Both calls allocate their own device workspace, run on `stream`, and
+ * return after waiting for it (the rounds need the host).
+ */
+
+/*
+ * fh_balanced_assign — the balanced assignment alone.
+ *   sims        device [v x c] float: similarity of token t to cluster k at
+ *               sims[t * c + k]; compared as given (no NaN).
+ *   v, c        v a positive multiple of c; b = v / c tokens per cluster.
+ *   out_assign  device [v] int32: the cluster of every token.
+ *   out_rounds  host, may be NULL: the number of rounds taken.
+ */
+fh_status fh_balanced_assign(const float* sims, int64_t v, int64_t c, int32_t* out_assign,
+                             int* out_rounds, void* stream);
+
+typedef struct {
+  float init_ms;  /* normalisation and k-means++ seeding                    */
+  float sims_ms;  /* the similarity products, summed over iterations        */
+  float total_ms; /* the whole call                                         */
+  int rounds;     /* balanced-assignment rounds, summed over iterations     */
+} fh_cluster_times;
+
+/*
+ * fh_cluster — the whole offline clustering.
+ *   E           device [v x d] of `dtype` (rows need not be unit length).
+ *   v, d, c     v a positive multiple of c, c <= 65536, d >= 1.
+ *   iters       >= 1 iterations of (similarities, assignment, update).
+ *   u           host [c] double, each in [0, 1): the k-means++ uniforms.
+ *   out_C       device [c x d] float: unit centres after the last update.
+ *   out_c2t     device [c x b] int32: C2T from the last assignment.
+ *   out_init    device [c] int32, may be NULL: the k-means++ token ids.
+ *   out_assign  device [v] int32, may be NULL: the last assignment.
+ *   out_times   host, may be NULL.
+ * out_C and out_c2t are what fh_create takes (after a cast of C to `dtype`
+ * for bf16 engines).
+ */
+fh_status fh_cluster(const void* E, fh_dtype dtype, int64_t v, int64_t d, int64_t c, int iters,
+                     const double* u, float* out_C, int32_t* out_c2t, int32_t* out_init,
+                     int32_t* out_assign, fh_cluster_times* out_times, void* stream);
 
 /* Thread-local description of the last error on this thread ("" if none). */
 const char* fh_last_error(void);

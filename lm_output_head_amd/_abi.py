@@ -21,13 +21,18 @@ FH_PATH_AUTO, FH_PATH_MULTI = 0, 1
 EXPORTS = (
     "fh_create", "fh_destroy", "fh_forward", "fh_score", "fh_dense_forward",
     "fh_get_int4", "fh_profile_begin", "fh_profile_end", "fh_set_path", "fh_sync_status",
-    "fh_last_error", "fh_version",
+    "fh_balanced_assign", "fh_cluster", "fh_last_error", "fh_version",
 )
 
 
 class FhKernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int64),
                 ("total_ms", ctypes.c_double)]
+
+
+class FhClusterTimes(ctypes.Structure):
+    _fields_ = [("init_ms", ctypes.c_float), ("sims_ms", ctypes.c_float),
+                ("total_ms", ctypes.c_float), ("rounds", ctypes.c_int)]
 
 
 class FlashHeadError(RuntimeError):
@@ -55,6 +60,9 @@ _SIGS = {
     "fh_profile_end": ([_p, ctypes.POINTER(FhKernelTime), _int, ctypes.POINTER(_int)], _int),
     "fh_set_path": ([_p, _int], _int),
     "fh_sync_status": ([_p, _p], _int),
+    "fh_balanced_assign": ([_p, _i64, _i64, _p, ctypes.POINTER(_int), _p], _int),
+    "fh_cluster": ([_p, _int, _i64, _i64, _i64, _int, ctypes.POINTER(ctypes.c_double), _p, _p, _p,
+                    _p, ctypes.POINTER(FhClusterTimes), _p], _int),
     "fh_last_error": ([], ctypes.c_char_p),
     "fh_version": ([], ctypes.c_char_p),
 }

@@ -1,0 +1,490 @@
+// The offline step that produces C and C2T: balanced spherical k-means on
+// gfx950 (FlashHead explainer, framerc.cn, §1.2.1 balanced clustering and
+// §2.1 offline clustering; arXiv 2603.14591 abstract, innovation (1)).
+//
+// Steps, as the pages order them:
+//   normalise  every embedding row to unit length (spherical k-means);
+//   k-means++  centre 0 is token floor(u_0 v); centre i is drawn with
+//              probability proportional to D(t)^2, D(t) = 1 - max_j cos(t, C_j)
+//              (inverse CDF over token order, u_i given): per step one
+//              kernel refreshes D against the newest centre, one workgroup
+//              sums D^2 in fp64 in a fixed order and finds the token;
+//   iterate    cosine similarities S = X C^T (fp32 tiled GEMM); the balanced
+//              assignment by rounds (each unassigned token proposes to its
+//              most similar non-full cluster, ties to the smaller cluster id;
+//              each cluster takes the most similar proposals up to its room,
+//              ties to the smaller token id), where the proposals are ranked
+//              by one stable radix sort on (cluster, similarity) keys; then
+//              C2T (each cluster's tokens ascending, by a stable sort on the
+//              cluster) and C_k = normalise(sum of its rows in slot order).
+// Every step is deterministic: no floating-point atomics, fixed orders.
+
+#include <hipcub/hipcub.hpp>
+
+#include <algorithm>
+#include <cstdio>
+#include <vector>
+
+#include "fh_blocks.hpp"
+
+namespace fh {
+
+// ----------------------------------------------------------- normalise ---
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_normalize_rows(const T* __restrict__ E, int64_t v, int d,
+                                                        float* __restrict__ X) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= v) return;
+  float ss = 0.f;
+  for (int i = lane; i < d; i += 64) {
+    const float x = load_elem<T>(E, t * d + i);
+    ss = fmaf(x, x, ss);
+  }
+  ss = wave_sum(ss);
+  const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+  for (int i = lane; i < d; i += 64) X[t * d + i] = load_elem<T>(E, t * d + i) * inv;
+}
+
+// ------------------------------------------------------------ k-means++ ---
+
+// D[t] = min(D[t], 1 - X_t . X_center) (or = when first); one wave per row.
+__global__ __launch_bounds__(256) void k_pp_update(const float* __restrict__ X, int64_t v, int d,
+                                                   const int32_t* __restrict__ centers, int i,
+                                                   float* __restrict__ D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= v) return;
+  const float* xc = X + (int64_t)centers[i] * d;
+  const float* xt = X + t * d;
+  float s = 0.f;
+  for (int k = lane; k < d; k += 64) s = fmaf(xt[k], xc[k], s);
+  s = wave_sum(s);
+  if (lane == 0) {
+    const float dist = 1.f - s;
+    D[t] = i == 0 ? dist : fminf(D[t], dist);
+  }
+}
+
+// One workgroup: total = sum D^2 (fp64, thread t sums its contiguous chunk
+// in order, then a fixed-order scan over threads); centre i is the first
+// token whose running sum exceeds u_i * total.
+__global__ __launch_bounds__(1024) void k_pp_pick(const float* __restrict__ D, int64_t v, double u,
+                                                  int32_t* __restrict__ centers, int i) {
+  __shared__ double part[1024];
+  const int tid = threadIdx.x;
+  const int64_t chunk = (v + 1023) / 1024;
+  const int64_t lo = min(v, tid * chunk), hi = min(v, lo + chunk);
+  double s = 0.0;
+  for (int64_t t = lo; t < hi; ++t) s += (double)D[t] * (double)D[t];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    double total = 0.0;
+    for (int j = 0; j < 1024; ++j) total += part[j];
+    int64_t pick = min<int64_t>((int64_t)(u * (double)v), v - 1);
+    if (total > 0.0) {
+      const double target = u * total;
+      double run = 0.0;
+      int j = 0;
+      for (; j < 1024; ++j) {
+        if (run + part[j] > target) break;
+        run += part[j];
+      }
+      pick = v - 1;
+      if (j < 1024) {
+        const int64_t jl = min(v, j * chunk), jh = min(v, jl + chunk);
+        for (int64_t t = jl; t < jh; ++t) {
+          run += (double)D[t] * (double)D[t];
+          if (run > target) {
+            pick = t;
+            break;
+          }
+        }
+      }
+    }
+    centers[i] = (int32_t)pick;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_gather_rows(const float* __restrict__ X, int d,
+                                                     const int32_t* __restrict__ idx, int64_t n,
+                                                     float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n * d) return;
+  out[i] = X[(int64_t)idx[i / d] * d + i % d];
+}
+
+// ------------------------------------------------------ similarity GEMM ---
+
+// S[t][k] = X_t . C_k in fp32 (sequential FMA over d): 64 x 64 tiles, 256
+// threads with 4 x 4 outputs each, 32-element slices of d through LDS.
+__global__ __launch_bounds__(256) void k_sims(const float* __restrict__ X, int64_t v,
+                                              const float* __restrict__ C, int64_t c, int d,
+                                              float* __restrict__ S) {
+  __shared__ float As[32][65];
+  __shared__ float Bs[32][65];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * 64, n0 = (int64_t)blockIdx.y * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < d; k0 += 32) {
+    // 64 rows x 32 elements of each operand: 8 per thread
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e, r = idx >> 5, k = idx & 31;
+      const int64_t am = m0 + r, bn = n0 + r;
+      As[k][r] = (am < v && k0 + k < d) ? X[am * d + k0 + k] : 0.f;
+      Bs[k][r] = (bn < c && k0 + k < d) ? C[bn * d + k0 + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = As[k][ty * 4 + i];
+        b[i] = Bs[k][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + ty * 4 + i;
+    if (m >= v) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + tx * 4 + j;
+      if (n < c) S[m * c + n] = acc[i][j];
+    }
+  }
+}
+
+// ------------------------------------------------- balanced assignment ---
+
+// Every unassigned token proposes to its most similar non-full cluster
+// (ties to the smaller id); sort key = cluster << 32 | (~order(similarity))
+// so that an ascending stable sort ranks each cluster's proposals by
+// similarity descending, then token id ascending.  Assigned tokens get the
+// largest key.  One wave per token.
+__global__ __launch_bounds__(256) void k_propose(const float* __restrict__ S, int64_t v, int64_t c,
+                                                 const int32_t* __restrict__ asg,
+                                                 const int32_t* __restrict__ fill, int b,
+                                                 uint64_t* __restrict__ keys,
+                                                 int32_t* __restrict__ vals) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= v) return;
+  if (asg[t] >= 0) {
+    if (lane == 0) {
+      keys[t] = ~0ull;
+      vals[t] = (int32_t)t;
+    }
+    return;
+  }
+  const float* row = S + t * c;
+  float best = 0.f;
+  int64_t bk = -1;
+  for (int64_t k = lane; k < c; k += 64) {
+    if (fill[k] >= b) continue;
+    const float x = row[k];
+    if (bk < 0 || x > best) {  // ascending k per lane: keeps the smaller id on ties
+      best = x;
+      bk = k;
+    }
+  }
+  // wave arg-max, ties to the smaller cluster id
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ob = __shfl_xor(best, m);
+    const int64_t ok = __shfl_xor(bk, m);
+    const bool take = ok >= 0 && (bk < 0 || ob > best || (ob == best && ok < bk));
+    if (take) {
+      best = ob;
+      bk = ok;
+    }
+  }
+  if (lane == 0) {
+    // no open cluster cannot happen while the counts agree (v = b c); the
+    // largest key keeps such a token out of every segment regardless
+    const uint32_t ord = ordered_bits(best);
+    keys[t] = bk < 0 ? ~0ull : ((uint64_t)bk << 32) | (uint64_t)(0xFFFFFFFFu - ord);
+    vals[t] = (int32_t)t;
+  }
+}
+
+// start[k] = first sorted position of cluster k's proposals.
+__global__ __launch_bounds__(256) void k_segment_starts(const uint64_t* __restrict__ keys, int64_t n,
+                                                        int32_t* __restrict__ start) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const uint64_t k = keys[i] >> 32;
+  if (keys[i] == ~0ull) return;
+  if (i == 0 || (keys[i - 1] >> 32) != k) start[k] = (int32_t)i;
+}
+
+// The first (b - fill[k]) proposals of cluster k in sorted order are taken.
+__global__ __launch_bounds__(256) void k_accept(const uint64_t* __restrict__ keys,
+                                                const int32_t* __restrict__ vals, int64_t n,
+                                                const int32_t* __restrict__ start,
+                                                const int32_t* __restrict__ fill, int b,
+                                                int32_t* __restrict__ asg,
+                                                int32_t* __restrict__ taken) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n || keys[i] == ~0ull) return;
+  const int64_t k = (int64_t)(keys[i] >> 32);
+  if (i - start[k] < b - fill[k]) {
+    asg[vals[i]] = (int32_t)k;
+    atomicAdd(&taken[k], 1);  // integer counts: order does not matter
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_update(int32_t* __restrict__ fill,
+                                                     int32_t* __restrict__ taken, int64_t c,
+                                                     int32_t* __restrict__ total) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= c) return;
+  if (taken[k]) {
+    fill[k] += taken[k];
+    atomicAdd(total, taken[k]);
+    taken[k] = 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_iota(int32_t* __restrict__ x, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) x[i] = (int32_t)i;
+}
+
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t* __restrict__ x, int64_t n, int32_t val) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) x[i] = val;
+}
+
+// --------------------------------------------------------------- update ---
+
+// C_k = normalise(sum_j X[c2t[k][j]]) in slot order; one wave per cluster.
+__global__ __launch_bounds__(256) void k_centroids(const float* __restrict__ X, int d,
+                                                   const int32_t* __restrict__ c2t, int64_t c,
+                                                   int b, float* __restrict__ C) {
+  const int lane = threadIdx.x & 63;
+  const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (k >= c) return;
+  float ss = 0.f;
+  for (int i = lane; i < d; i += 64) {
+    float s = 0.f;
+    for (int j = 0; j < b; ++j) s += X[(int64_t)c2t[k * b + j] * d + i];
+    C[k * d + i] = s;
+    ss = fmaf(s, s, ss);
+  }
+  ss = wave_sum(ss);
+  const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+  for (int i = lane; i < d; i += 64) C[k * d + i] *= inv;
+}
+
+// ----------------------------------------------------------------- host ---
+
+static unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+struct ClusterWork {
+  int64_t v = 0, c = 0;
+  uint64_t* keys = nullptr;
+  uint64_t* keys2 = nullptr;
+  int32_t* vals = nullptr;
+  int32_t* vals2 = nullptr;
+  int32_t* fill = nullptr;
+  int32_t* taken = nullptr;
+  int32_t* start = nullptr;
+  int32_t* total = nullptr;  // tokens assigned so far
+  void* temp = nullptr;
+  size_t temp_bytes = 0;
+};
+
+// Bits that hold every cluster id in [0, c).
+static int cluster_bits(int64_t c) {
+  int bits = 1;
+  while ((int64_t(1) << bits) < c) ++bits;
+  return bits;
+}
+
+static hipError_t work_alloc(ClusterWork& w, int64_t v, int64_t c, hipStream_t st) {
+  w.v = v;
+  w.c = c;
+  hipError_t r = hipMalloc((void**)&w.keys, sizeof(uint64_t) * v);
+  if (r == hipSuccess) r = hipMalloc((void**)&w.keys2, sizeof(uint64_t) * v);
+  if (r == hipSuccess) r = hipMalloc((void**)&w.vals, sizeof(int32_t) * v);
+  if (r == hipSuccess) r = hipMalloc((void**)&w.vals2, sizeof(int32_t) * v);
+  if (r == hipSuccess) r = hipMalloc((void**)&w.fill, sizeof(int32_t) * c);
+  if (r == hipSuccess) r = hipMalloc((void**)&w.taken, sizeof(int32_t) * c);
+  if (r == hipSuccess) r = hipMalloc((void**)&w.start, sizeof(int32_t) * c);
+  if (r == hipSuccess) r = hipMalloc((void**)&w.total, sizeof(int32_t));
+  if (r != hipSuccess) return r;
+  size_t b1 = 0, b2 = 0;
+  r = hipcub::DeviceRadixSort::SortPairs(nullptr, b1, w.keys, w.keys2, w.vals, w.vals2, (int)v, 0,
+                                         64, st);
+  if (r == hipSuccess)
+    r = hipcub::DeviceRadixSort::SortPairs(nullptr, b2, reinterpret_cast<uint32_t*>(w.vals),
+                                           reinterpret_cast<uint32_t*>(w.vals2), w.vals, w.vals2,
+                                           (int)v, 0, cluster_bits(c), st);
+  if (r != hipSuccess) return r;
+  w.temp_bytes = std::max(b1, b2);
+  return hipMalloc(&w.temp, w.temp_bytes);
+}
+
+static void work_free(ClusterWork& w) {
+  for (void* p : {(void*)w.keys, (void*)w.keys2, (void*)w.vals, (void*)w.vals2, (void*)w.fill,
+                  (void*)w.taken, (void*)w.start, (void*)w.total, w.temp})
+    (void)hipFree(p);
+  w = ClusterWork{};
+}
+
+// The rounds; asg must hold -1 for every token on entry.  Returns the
+// number of rounds in *rounds.
+static hipError_t assign_rounds(const float* S, int64_t v, int64_t c, int32_t* asg, ClusterWork& w,
+                                hipStream_t st, int* rounds) {
+  const int b = (int)(v / c);
+  hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(c, 256)), dim3(256), 0, st, w.fill, c, 0);
+  hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(c, 256)), dim3(256), 0, st, w.taken, c, 0);
+  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, st, w.total, (int64_t)1, 0);
+  hipError_t r = hipGetLastError();
+  int done = 0, n = 0;
+  while (r == hipSuccess && done < v) {
+    if (++n > v + 1) return hipErrorUnknown;  // every round assigns at least one token
+    hipLaunchKernelGGL(k_propose, dim3(blocks_for(v, 4)), dim3(256), 0, st, S, v, c, asg, w.fill, b,
+                       w.keys, w.vals);
+    r = hipGetLastError();
+    if (r != hipSuccess) break;
+    size_t tb = w.temp_bytes;
+    r = hipcub::DeviceRadixSort::SortPairs(w.temp, tb, w.keys, w.keys2, w.vals, w.vals2, (int)v, 0,
+                                           64, st);
+    if (r != hipSuccess) break;
+    hipLaunchKernelGGL(k_segment_starts, dim3(blocks_for(v, 256)), dim3(256), 0, st, w.keys2, v,
+                       w.start);
+    hipLaunchKernelGGL(k_accept, dim3(blocks_for(v, 256)), dim3(256), 0, st, w.keys2, w.vals2, v,
+                       w.start, w.fill, b, asg, w.taken);
+    hipLaunchKernelGGL(k_fill_update, dim3(blocks_for(c, 256)), dim3(256), 0, st, w.fill, w.taken,
+                       c, w.total);
+    r = hipGetLastError();
+    if (r == hipSuccess) r = hipMemcpyAsync(&done, w.total, sizeof(int), hipMemcpyDeviceToHost, st);
+    if (r == hipSuccess) r = hipStreamSynchronize(st);
+  }
+  if (rounds) *rounds = n;
+  return r;
+}
+
+// C2T by a stable sort of token ids on their cluster, then the centroids.
+static hipError_t update_step(const float* X, int64_t v, int d, int64_t c, const int32_t* asg,
+                              int32_t* c2t, float* C, ClusterWork& w, hipStream_t st) {
+  hipLaunchKernelGGL(k_iota, dim3(blocks_for(v, 256)), dim3(256), 0, st, w.vals, v);
+  hipError_t r = hipGetLastError();
+  if (r != hipSuccess) return r;
+  size_t tb = w.temp_bytes;
+  const int end_bit = cluster_bits(c);
+  // cluster ids are non-negative: sort them as unsigned keys
+  r = hipcub::DeviceRadixSort::SortPairs(w.temp, tb, reinterpret_cast<const uint32_t*>(asg),
+                                         reinterpret_cast<uint32_t*>(w.vals2), w.vals, c2t, (int)v,
+                                         0, end_bit, st);
+  if (r != hipSuccess) return r;
+  hipLaunchKernelGGL(k_centroids, dim3(blocks_for(c, 4)), dim3(256), 0, st, X, d, c2t, c,
+                     (int)(v / c), C);
+  return hipGetLastError();
+}
+
+hipError_t balanced_assign_device(const float* S, int64_t v, int64_t c, int32_t* asg,
+                                  hipStream_t st, int* rounds) {
+  ClusterWork w;
+  hipError_t r = work_alloc(w, v, c, st);
+  if (r == hipSuccess) {
+    hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(v, 256)), dim3(256), 0, st, asg, v, -1);
+    r = hipGetLastError();
+  }
+  if (r == hipSuccess) r = assign_rounds(S, v, c, asg, w, st, rounds);
+  if (r == hipSuccess) r = hipStreamSynchronize(st);
+  work_free(w);
+  return r;
+}
+
+hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, int iters,
+                         const double* u, float* C, int32_t* c2t, int32_t* init, int32_t* asg_out,
+                         hipStream_t st, ClusterTimes* times) {
+  float* X = nullptr;
+  float* D = nullptr;
+  float* S = nullptr;
+  int32_t* centers = nullptr;
+  int32_t* asg = nullptr;
+  ClusterWork w;
+  hipEvent_t ev[5] = {};
+  for (auto& e : ev) (void)hipEventCreate(&e);
+  hipError_t r = hipMalloc((void**)&X, sizeof(float) * v * d);
+  if (r == hipSuccess) r = hipMalloc((void**)&D, sizeof(float) * v);
+  if (r == hipSuccess) r = hipMalloc((void**)&S, sizeof(float) * v * c);
+  if (r == hipSuccess) r = hipMalloc((void**)&centers, sizeof(int32_t) * c);
+  if (r == hipSuccess) r = hipMalloc((void**)&asg, sizeof(int32_t) * v);
+  if (r == hipSuccess) r = work_alloc(w, v, c, st);
+  int total_rounds = 0;
+  if (r == hipSuccess) {
+    (void)hipEventRecord(ev[0], st);
+    if (bf16)
+      hipLaunchKernelGGL((k_normalize_rows<uint16_t>), dim3(blocks_for(v, 4)), dim3(256), 0, st,
+                         static_cast<const uint16_t*>(E), v, d, X);
+    else
+      hipLaunchKernelGGL((k_normalize_rows<float>), dim3(blocks_for(v, 4)), dim3(256), 0, st,
+                         static_cast<const float*>(E), v, d, X);
+    const int32_t first = (int32_t)std::min<int64_t>((int64_t)(u[0] * (double)v), v - 1);
+    r = hipMemcpyAsync(centers, &first, sizeof(int32_t), hipMemcpyHostToDevice, st);
+    for (int64_t i = 0; r == hipSuccess && i < c; ++i) {
+      if (i > 0) hipLaunchKernelGGL(k_pp_pick, dim3(1), dim3(1024), 0, st, D, v, u[i], centers, (int)i);
+      hipLaunchKernelGGL(k_pp_update, dim3(blocks_for(v, 4)), dim3(256), 0, st, X, v, d, centers,
+                         (int)i, D);
+      r = hipGetLastError();
+    }
+    if (r == hipSuccess) {
+      hipLaunchKernelGGL(k_gather_rows, dim3(blocks_for(c * d, 256)), dim3(256), 0, st, X, d,
+                         centers, c, C);
+      r = hipGetLastError();
+    }
+    (void)hipEventRecord(ev[1], st);
+    if (r == hipSuccess && init)
+      r = hipMemcpyAsync(init, centers, sizeof(int32_t) * c, hipMemcpyDeviceToDevice, st);
+    float sims_ms = 0.f;
+    for (int it = 0; r == hipSuccess && it < iters; ++it) {
+      (void)hipEventRecord(ev[2], st);
+      hipLaunchKernelGGL(k_sims, dim3(blocks_for(v, 64), blocks_for(c, 64)), dim3(256), 0, st, X, v,
+                         C, c, d, S);
+      (void)hipEventRecord(ev[3], st);
+      hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(v, 256)), dim3(256), 0, st, asg, v, -1);
+      r = hipGetLastError();
+      int rounds = 0;
+      if (r == hipSuccess) r = assign_rounds(S, v, c, asg, w, st, &rounds);
+      total_rounds += rounds;
+      float ms = 0.f;
+      if (r == hipSuccess && hipEventElapsedTime(&ms, ev[2], ev[3]) == hipSuccess) sims_ms += ms;
+      if (r == hipSuccess) r = update_step(X, v, d, c, asg, c2t, C, w, st);
+    }
+    if (r == hipSuccess && asg_out)
+      r = hipMemcpyAsync(asg_out, asg, sizeof(int32_t) * v, hipMemcpyDeviceToDevice, st);
+    (void)hipEventRecord(ev[4], st);
+    if (r == hipSuccess) r = hipStreamSynchronize(st);
+    if (times && r == hipSuccess) {
+      float ms = 0.f;
+      (void)hipEventElapsedTime(&ms, ev[0], ev[1]);
+      times->init_ms = ms;
+      ms = 0.f;
+      (void)hipEventElapsedTime(&ms, ev[0], ev[4]);
+      times->total_ms = ms;
+      times->sims_ms = sims_ms;
+      times->rounds = total_rounds;
+    }
+  }
+  for (auto& e : ev) (void)hipEventDestroy(e);
+  work_free(w);
+  for (void* p : {(void*)X, (void*)D, (void*)S, (void*)centers, (void*)asg}) (void)hipFree(p);
+  return r;
+}
+
+}  // namespace fh

@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -179,6 +180,48 @@ fh_status check_mode(int mode, float temperature) {
 }  // namespace
 
 extern "C" {
+
+fh_status fh_balanced_assign(const float* sims, int64_t v, int64_t c, int32_t* out_assign,
+                             int* out_rounds, void* stream) {
+  g_err.clear();
+  if (!sims || !out_assign) return fail(FH_EINVAL, "sims and out_assign must not be NULL");
+  if (c < 1 || v < c || v % c != 0 || v > INT32_MAX)
+    return fail(FH_EINVAL, "need 1 <= c, v a multiple of c and v < 2^31 (v=" + std::to_string(v) +
+                               ", c=" + std::to_string(c) + ")");
+  int rounds = 0;
+  hipError_t r = fh::balanced_assign_device(sims, v, c, out_assign,
+                                            static_cast<hipStream_t>(stream), &rounds);
+  if (r != hipSuccess) return hip_fail(r, "balanced assignment");
+  if (out_rounds) *out_rounds = rounds;
+  return FH_OK;
+}
+
+fh_status fh_cluster(const void* E, fh_dtype dtype, int64_t v, int64_t d, int64_t c, int iters,
+                     const double* u, float* out_C, int32_t* out_c2t, int32_t* out_init,
+                     int32_t* out_assign, fh_cluster_times* out_times, void* stream) {
+  g_err.clear();
+  if (!E || !u || !out_C || !out_c2t) return fail(FH_EINVAL, "E, u, out_C and out_c2t must not be NULL");
+  if (dtype != FH_F32 && dtype != FH_BF16) return fail(FH_EINVAL, "unknown dtype");
+  if (c < 1 || c > 65536 || v < c || v % c != 0 || v > INT32_MAX)
+    return fail(FH_EINVAL, "need 1 <= c <= 65536, v a multiple of c and v < 2^31 (v=" +
+                               std::to_string(v) + ", c=" + std::to_string(c) + ")");
+  if (d < 1 || d > (int64_t)1 << 20) return fail(FH_EINVAL, "d=" + std::to_string(d) + " outside [1, 2^20]");
+  if (iters < 1) return fail(FH_EINVAL, "iters must be >= 1");
+  for (int64_t i = 0; i < c; ++i)
+    if (!(u[i] >= 0.0 && u[i] < 1.0))
+      return fail(FH_EINVAL, "u[" + std::to_string(i) + "] outside [0, 1)");
+  fh::ClusterTimes t{};
+  hipError_t r = fh::kmeans_device(E, dtype == FH_BF16, v, (int)d, c, iters, u, out_C, out_c2t,
+                                   out_init, out_assign, static_cast<hipStream_t>(stream), &t);
+  if (r != hipSuccess) return hip_fail(r, "clustering");
+  if (out_times) {
+    out_times->init_ms = t.init_ms;
+    out_times->sims_ms = t.sims_ms;
+    out_times->total_ms = t.total_ms;
+    out_times->rounds = t.rounds;
+  }
+  return FH_OK;
+}
 
 const char* fh_last_error(void) { return g_err.c_str(); }
 

@@ -103,6 +103,19 @@ struct FusedLaunch {
   float* out_lse;
   unsigned* err;                  // sticky flag: a bounded poll gave up
 };
+// The offline balanced spherical k-means (fh_cluster.hip).
+struct ClusterTimes {
+  float init_ms;  // normalisation and k-means++
+  float sims_ms;  // similarity GEMMs, all iterations
+  float total_ms;
+  int rounds;     // balanced-assignment rounds, all iterations
+};
+hipError_t balanced_assign_device(const float* S, int64_t v, int64_t c, int32_t* asg,
+                                  hipStream_t st, int* rounds);
+hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, int iters,
+                         const double* u, float* C, int32_t* c2t, int32_t* init, int32_t* asg_out,
+                         hipStream_t st, ClusterTimes* times);
+
 hipError_t launch_batch1(const FusedLaunch& f);
 // per storage variant, one translation unit each
 hipError_t launch_batch1_bf16(const FusedLaunch& f);

@@ -115,6 +115,46 @@ def fh_profile_end(eng) -> dict:
     return {recs[i].name.decode(): (recs[i].launches, recs[i].total_ms) for i in range(n.value)}
 
 
+def fh_balanced_assign(sims: torch.Tensor, out_assign: torch.Tensor, stream=None) -> int:
+    """Balanced assignment of v tokens to c clusters of v / c: sims [v x c]
+    float32 on the GPU, out_assign [v] int32 on the GPU.  Returns the number
+    of rounds."""
+    v, c = sims.shape
+    _require(sims, torch.float32, (v, c), "sims")
+    _require(out_assign, torch.int32, (v,), "out_assign")
+    rounds = ctypes.c_int(0)
+    check(_abi.load().fh_balanced_assign(_ptr(sims), v, c, _ptr(out_assign), ctypes.byref(rounds),
+                                         _stream(stream)))
+    return rounds.value
+
+
+def fh_cluster(E: torch.Tensor, c: int, iters: int, u, out_C: torch.Tensor, out_c2t: torch.Tensor,
+               out_init=None, out_assign=None, stream=None) -> dict:
+    """Balanced spherical k-means over E's rows (float32 or bfloat16 on the
+    GPU) into c clusters; u holds the c k-means++ uniforms (host).  Fills
+    out_C [c x d] float32 and out_c2t [c x v/c] int32 (and optionally
+    out_init [c], out_assign [v] int32) and returns the call's timings."""
+    if E.dtype not in _DTYPES:
+        raise ValueError("E must be float32 or bfloat16")
+    v, d = E.shape
+    if c < 1 or v % c:
+        raise ValueError("v must be a multiple of c")
+    _require(out_C, torch.float32, (c, d), "out_C")
+    _require(out_c2t, torch.int32, (c, v // c), "out_c2t")
+    _require(out_init, torch.int32, (c,), "out_init")
+    _require(out_assign, torch.int32, (v,), "out_assign")
+    uu = np.ascontiguousarray(np.asarray(u, dtype=np.float64))
+    if uu.shape != (c,):
+        raise ValueError("u must hold c uniforms")
+    t = _abi.FhClusterTimes()
+    check(_abi.load().fh_cluster(_ptr(E), _DTYPES[E.dtype], v, d, c, iters,
+                                 uu.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), _ptr(out_C),
+                                 _ptr(out_c2t), _ptr(out_init), _ptr(out_assign), ctypes.byref(t),
+                                 _stream(stream)))
+    return {"init_ms": t.init_ms, "sims_ms": t.sims_ms, "total_ms": t.total_ms,
+            "rounds": t.rounds}
+
+
 class FlashHead:
     """An engine over one head, with output allocation.
 

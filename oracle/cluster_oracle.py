@@ -78,30 +78,45 @@ def pp_weights(Xn: np.ndarray, centers) -> np.ndarray:
     return D * D
 
 
-def balanced_assign(sims, b: int) -> np.ndarray:
+def balanced_assign(sims, b: int, margins: list | None = None) -> np.ndarray:
     """Greedy balanced assignment by rounds (the reading above): returns the
     cluster of every token; every cluster gets exactly b tokens.  The
-    decisions compare the given similarity values as they are."""
+    decisions compare the given similarity values as they are.
+
+    If ``margins`` is a list, the smallest similarity gap that decided
+    anything is appended to it: per proposal, best minus second-best open
+    cluster; per cluster with more proposals than room, last accepted minus
+    first refused.  A caller that computes the similarities differently
+    (another precision) can expect the same assignment only when this gap
+    is well above the difference."""
     S = np.asarray(sims, dtype=np.float64)
     v, c = S.shape
     if v != b * c:
         raise ValueError("v must equal b * c")
     asg = np.full(v, -1, dtype=np.int64)
     fill = np.zeros(c, dtype=np.int64)
+    gap = np.inf
     while True:
         todo = np.flatnonzero(asg < 0)
         if todo.size == 0:
+            if margins is not None:
+                margins.append(gap)
             return asg
         open_k = np.flatnonzero(fill < b)
         sub = S[np.ix_(todo, open_k)]
         best = sub.argmax(axis=1)  # first maximum: the smaller cluster id
         prop = open_k[best]
         val = sub[np.arange(todo.size), best]
+        if margins is not None and open_k.size > 1:
+            top2 = -np.partition(-sub, 1, axis=1)[:, :2]
+            gap = min(gap, float((top2[:, 0] - top2[:, 1]).min()))
         for k in np.unique(prop):
             mine = prop == k
             toks, vals = todo[mine], val[mine]
             order = np.lexsort((toks, -vals))  # similarity desc, then token id asc
             room = b - fill[k]
+            if margins is not None and toks.size > room:
+                gap = min(gap, float(vals[order[room - 1]] - vals[order[room]]))
             take = toks[order[:room]]
             asg[take] = k
             fill[k] += take.size
