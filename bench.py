@@ -195,7 +195,7 @@ def cluster_cpu_baseline(E, c, seconds):
 def cluster_main(args):
     """One JSON line: seconds per balanced spherical k-means of the head's
     embedding table (planted clusters, bf16), with the k-means++ phase's
-    achieved HBM bandwidth (it reads the fp32 unit rows once per centre)."""
+    achieved HBM bandwidth (it reads the table's rows once per centre)."""
     import numpy as np
     import torch
 
@@ -232,7 +232,10 @@ def cluster_main(args):
     from oracle import cluster_oracle as co  # quality figures of the result
     got = asg.cpu().numpy()
     ari = co.adjusted_rand_index(got, truth)
-    pp_bytes = c * (v * d * 4 + v * 4 * 3)  # X rows, D read/write, D in the pick
+    elem = 2 if shape.dtype == "bf16" else 4
+    # per centre: the table's rows in their storage type, the inverse norms,
+    # D read and written, and the workgroup partials
+    pp_bytes = c * (v * d * elem + v * 4 * 3 + (v // 64) * 8)
     init_gbs = pp_bytes / (best["init_ms"] * 1e-3) / 1e9
     sims_tflops = 2.0 * v * c * d * args.cluster_iters / (best["sims_ms"] * 1e-3) / 1e12
     res = {
@@ -248,7 +251,7 @@ def cluster_main(args):
         "rounds": best["rounds"],
         "roofline": {"bound": "hbm", "achieved": round(init_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(init_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "phase": "k-means++ (per centre: one pass over the fp32 unit rows)"},
+                     "phase": "k-means++ (per centre: one pass over the table's rows)"},
         "sims_tflops_f32": round(sims_tflops, 2),
         "quality": {"ari_vs_planted": round(ari, 5)},
     }

@@ -246,7 +246,9 @@ typedef struct {
 /*
  * fh_cluster — the whole offline clustering.
  *   E           device [v x d] of `dtype` (rows need not be unit length).
- *   v, d, c     v a positive multiple of c, c <= 65536, d >= 1.
+ *   v, d, c     v a positive multiple of c, c <= 65536; d as for fh_create
+ *               (a multiple of 8 for bf16, of 4 for f32; at most 4096 bf16
+ *               or 2048 f32 elements).
  *   iters       >= 1 iterations of (similarities, assignment, update).
  *   u           host [c] double, each in [0, 1): the k-means++ uniforms.
  *   out_C       device [c x d] float: unit centres after the last update.

@@ -9,7 +9,9 @@
 //              (inverse CDF over token order, u_i given): per step one
 //              kernel refreshes D against the newest centre, one workgroup
 //              sums D^2 in fp64 in a fixed order and finds the token;
-//   iterate    cosine similarities S = X C^T (fp32 tiled GEMM); the balanced
+//   iterate    cosine similarities S = X C^T (bf16 tables: matrix cores with
+//              C split exactly into three bf16 pieces; fp32 tables: an fp32
+//              tiled GEMM on the vector units); the balanced
 //              assignment by rounds (each unassigned token proposes to its
 //              most similar non-full cluster, ties to the smaller cluster id;
 //              each cluster takes the most similar proposals up to its room,
@@ -31,9 +33,11 @@ namespace fh {
 
 // ----------------------------------------------------------- normalise ---
 
+// X[t] = E[t] / |E[t]| in fp32 and inv[t] = 1 / |E[t]| (0 for a zero row).
 template <typename T>
 __global__ __launch_bounds__(256) void k_normalize_rows(const T* __restrict__ E, int64_t v, int d,
-                                                        float* __restrict__ X) {
+                                                        float* __restrict__ X,
+                                                        float* __restrict__ inv) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= v) return;
@@ -43,68 +47,118 @@ __global__ __launch_bounds__(256) void k_normalize_rows(const T* __restrict__ E,
     ss = fmaf(x, x, ss);
   }
   ss = wave_sum(ss);
-  const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
-  for (int i = lane; i < d; i += 64) X[t * d + i] = load_elem<T>(E, t * d + i) * inv;
+  const float r = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+  for (int i = lane; i < d; i += 64) X[t * d + i] = load_elem<T>(E, t * d + i) * r;
+  if (lane == 0) inv[t] = r;
 }
 
 // ------------------------------------------------------------ k-means++ ---
 
-// D[t] = min(D[t], 1 - X_t . X_center) (or = when first); one wave per row.
-__global__ __launch_bounds__(256) void k_pp_update(const float* __restrict__ X, int64_t v, int d,
-                                                   const int32_t* __restrict__ centers, int i,
-                                                   float* __restrict__ D) {
+// Rows per workgroup of the k-means++ step (16 per wave); also the rows one
+// wave of the draw scans.
+constexpr int kPpRows = 64;
+
+// One k-means++ step's distance refresh against centre i:
+//   D[t] = min(D[t], 1 - inv[t] inv[ct] (E_t . E_ct))   (= when i == 0)
+// with the table read in its own storage type (coalesced 16-byte row loads,
+// the centre's row in registers), and part[w] = sum of D^2 over workgroup
+// w's 64 rows in fp64, in row order within each wave, then wave 0..3.
+template <typename T, int MAXM>
+__global__ __launch_bounds__(256) void k_pp_step(const T* __restrict__ E,
+                                                 const float* __restrict__ inv, int64_t v, int d,
+                                                 const int32_t* __restrict__ centers, int i,
+                                                 float* __restrict__ D, double* __restrict__ part) {
+  __shared__ double wsum[4];
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= v) return;
-  const float* xc = X + (int64_t)centers[i] * d;
-  const float* xt = X + t * d;
-  float s = 0.f;
-  for (int k = lane; k < d; k += 64) s = fmaf(xt[k], xc[k], s);
-  s = wave_sum(s);
-  if (lane == 0) {
-    const float dist = 1.f - s;
-    D[t] = i == 0 ? dist : fminf(D[t], dist);
-  }
+  const int wave = threadIdx.x >> 6;
+  const int64_t ct = centers[i];
+  const int nch = d / Chunk<T>::kElems;
+  uint4 hv[1][MAXM];
+  load_hslice<T, MAXM>(E + ct * d, nch, lane, hv[0]);
+  const float ic = inv[ct];
+  const int64_t r0 = (int64_t)blockIdx.x * kPpRows + wave * (kPpRows / 4);
+  const int64_t r1 = min(r0 + kPpRows / 4, v);
+  double s = 0.0;
+  auto row = [](int64_t r) -> int64_t { return r; };
+  auto sink = [&](int, int64_t r, int64_t, float z) {
+    float dist = 1.f - z * inv[r] * ic;
+    if (i > 0) dist = fminf(D[r], dist);
+    if (lane == 0) D[r] = dist;
+    s += (double)dist * (double)dist;
+  };
+  wave_rows<T, MAXM, 1>(E, d, lane, hv, 1, r0, r1, 1, row, row, sink);
+  if (lane == 0) wsum[wave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
 }
 
-// One workgroup: total = sum D^2 (fp64, thread t sums its contiguous chunk
-// in order, then a fixed-order scan over threads); centre i is the first
-// token whose running sum exceeds u_i * total.
-__global__ __launch_bounds__(1024) void k_pp_pick(const float* __restrict__ D, int64_t v, double u,
-                                                  int32_t* __restrict__ centers, int i) {
-  __shared__ double part[1024];
+// The draw of centre i (one workgroup of 1024): the running sums of the nb
+// workgroup partials (each thread sums its contiguous share in order, then a
+// fixed-order scan over threads) locate the 64-row block where the running
+// sum of D^2 first exceeds u * total; one wave then scans that block's rows
+// (fp64 prefix over lanes) for the first row that exceeds it.  With a zero
+// total the draw is token floor(u v); if rounding leaves no crossing, the
+// last row of the last block is taken.
+__global__ __launch_bounds__(1024) void k_pp_pick(const float* __restrict__ D,
+                                                  const double* __restrict__ part, int64_t nb,
+                                                  int64_t v, double u, int32_t* __restrict__ centers,
+                                                  int i) {
+  __shared__ double ps[1024];
+  __shared__ int found;
+  __shared__ int64_t blk;
+  __shared__ double base;
   const int tid = threadIdx.x;
-  const int64_t chunk = (v + 1023) / 1024;
-  const int64_t lo = min(v, tid * chunk), hi = min(v, lo + chunk);
+  const int64_t chunk = (nb + 1023) / 1024;
+  const int64_t lo = min(nb, tid * chunk), hi = min(nb, lo + chunk);
   double s = 0.0;
-  for (int64_t t = lo; t < hi; ++t) s += (double)D[t] * (double)D[t];
-  part[tid] = s;
+  for (int64_t j = lo; j < hi; ++j) s += part[j];
+  ps[tid] = s;
+  if (tid == 0) found = 1024;
   __syncthreads();
-  if (tid == 0) {
-    double total = 0.0;
-    for (int j = 0; j < 1024; ++j) total += part[j];
-    int64_t pick = min<int64_t>((int64_t)(u * (double)v), v - 1);
-    if (total > 0.0) {
-      const double target = u * total;
-      double run = 0.0;
-      int j = 0;
-      for (; j < 1024; ++j) {
-        if (run + part[j] > target) break;
-        run += part[j];
-      }
-      pick = v - 1;
-      if (j < 1024) {
-        const int64_t jl = min(v, j * chunk), jh = min(v, jl + chunk);
-        for (int64_t t = jl; t < jh; ++t) {
-          run += (double)D[t] * (double)D[t];
-          if (run > target) {
-            pick = t;
-            break;
-          }
-        }
-      }
+  for (int off = 1; off < 1024; off <<= 1) {
+    const double x = tid >= off ? ps[tid - off] : 0.0;
+    __syncthreads();
+    ps[tid] += x;
+    __syncthreads();
+  }
+  const double total = ps[1023];
+  if (!(total > 0.0)) {
+    if (tid == 0) centers[i] = (int32_t)min<int64_t>((int64_t)(u * (double)v), v - 1);
+    return;
+  }
+  const double target = u * total;
+  const double excl = tid ? ps[tid - 1] : 0.0;
+  if (ps[tid] > target && excl <= target) found = tid;  // the first crossing
+  __syncthreads();
+  if (tid == 0 && found == 1024) {  // no crossing: the last block, last row
+    blk = nb - 1;
+    base = total;
+  }
+  if (tid == found) {
+    double run = excl;
+    int64_t j = lo;
+    for (; j < hi - 1; ++j) {
+      if (run + part[j] > target) break;
+      run += part[j];
     }
-    centers[i] = (int32_t)pick;
+    blk = j;
+    base = run;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int64_t r = blk * kPpRows + tid;
+    const double w = r < v ? (double)D[r] * (double)D[r] : 0.0;
+    double x = w;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(x, off);
+      if (tid >= off) x += y;
+    }
+    const unsigned long long hit = __ballot(r < v && base + x > target);
+    if (tid == 0) {
+      const int64_t last = min<int64_t>(v, (blk + 1) * kPpRows) - 1;
+      centers[i] = (int32_t)(hit ? blk * kPpRows + __builtin_ctzll(hit) : last);
+    }
   }
 }
 
@@ -163,6 +217,133 @@ __global__ __launch_bounds__(256) void k_sims(const float* __restrict__ X, int64
       if (n < c) S[m * c + n] = acc[i][j];
     }
   }
+}
+
+// S on the matrix cores for bf16 tables.  The centres are fp32; each is
+// split exactly into three bf16 pieces, C = hi + mid + lo up to 2^-27
+// relative (hi = bf16(C), mid = bf16(C - hi), lo = bf16(C - hi - mid); each
+// difference is exact in fp32), so E_t . C_k = E_t . hi + E_t . mid +
+// E_t . lo with exact bf16 products and fp32 accumulation in
+// v_mfma_f32_16x16x32_bf16, and S[t][k] = inv[t] (E_t . C_k).
+typedef __bf16 sim_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float sim_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ sim_f32x4 sim_mfma(const uint4& a, const uint4& b, sim_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sim_bf16x8, a),
+                                                 __builtin_bit_cast(sim_bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// P[piece][k][i] for the three pieces of C[k][i].
+__global__ __launch_bounds__(256) void k_split_pieces(const float* __restrict__ C, int64_t n,
+                                                      uint16_t* __restrict__ P) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float x = C[i];
+  const uint16_t hi = bf16_rne(x);
+  const float r1 = x - __uint_as_float((uint32_t)hi << 16);
+  const uint16_t mid = bf16_rne(r1);
+  const float r2 = r1 - __uint_as_float((uint32_t)mid << 16);
+  P[i] = hi;
+  P[n + i] = mid;
+  P[2 * n + i] = bf16_rne(r2);
+}
+
+constexpr int kSimTile = 128;   // tokens and clusters per workgroup
+constexpr int kSimLds = 40;     // LDS row of one 32-element step (bf16), padded
+
+// One workgroup: tokens [128 x, +128) x clusters [128 y, +128); wave w owns
+// the 64 x 64 quadrant (w & 1, w >> 1): 4 x 4 tiles of 16 x 16, three
+// pieces each.  d is walked in steps of 32 elements through double-buffered
+// LDS (one barrier per step: the buffer written during step s was last read
+// in step s - 1).  Operand fragments as the instruction takes them: lane l
+// holds row (token) or column (cluster) l % 16 at elements 8 (l / 16) .. + 7
+// of the step; the result holds cluster l % 16 at tokens 4 (l / 16) .. + 3.
+__global__ __launch_bounds__(256) void k_sims_mfma(const uint16_t* __restrict__ E,
+                                                   const float* __restrict__ inv, int64_t v, int d,
+                                                   const uint16_t* __restrict__ P, int64_t c,
+                                                   float* __restrict__ S) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kSimTile * kSimLds];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][3 * kSimTile * kSimLds];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t t0 = (int64_t)blockIdx.x * kSimTile, k0 = (int64_t)blockIdx.y * kSimTile;
+  const int nks = (d + 31) / 32;
+  // per step: A is 128 rows x 4 chunks (2 per thread), B 384 rows x 4 (6 per thread)
+  uint4 ra[2], rb[6];
+  auto gload = [&](int ks) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int idx = tid + 256 * j, row = idx >> 2, kk = 32 * ks + 8 * (idx & 3);
+      const int64_t t = min(t0 + row, v - 1);
+      ra[j] = kk < d ? *reinterpret_cast<const uint4*>(E + t * d + kk) : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int idx = tid + 256 * j, pr = idx >> 2, kk = 32 * ks + 8 * (idx & 3);
+      const int piece = pr >> 7;
+      const int64_t k = min(k0 + (pr & 127), c - 1);
+      rb[j] = kk < d ? *reinterpret_cast<const uint4*>(P + ((int64_t)piece * c + k) * d + kk)
+                     : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int idx = tid + 256 * j;
+      *reinterpret_cast<uint4*>(&sA[buf][(idx >> 2) * kSimLds + 8 * (idx & 3)]) = ra[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int idx = tid + 256 * j;
+      *reinterpret_cast<uint4*>(&sB[buf][(idx >> 2) * kSimLds + 8 * (idx & 3)]) = rb[j];
+    }
+  };
+  sim_f32x4 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = sim_f32x4{0.f, 0.f, 0.f, 0.f};
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nks) gload(ks + 1);
+    uint4 af[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      af[m] = *reinterpret_cast<const uint4*>(&sA[buf][(64 * wm + 16 * m + col) * kSimLds + 8 * g]);
+#pragma unroll
+    for (int piece = 0; piece < 3; ++piece)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const uint4 bf = *reinterpret_cast<const uint4*>(
+            &sB[buf][(kSimTile * piece + 64 * wn + 16 * n + col) * kSimLds + 8 * g]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m][n] = sim_mfma(af[m], bf, acc[m][n]);
+      }
+    if (ks + 1 < nks) sstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + 64 * wm + 16 * m + 4 * g + i;
+      if (t >= v) continue;
+      const float sc = inv[t];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int64_t k = k0 + 64 * wn + 16 * n + col;
+        if (k < c) S[t * c + k] = acc[m][n][i] * sc;
+      }
+    }
 }
 
 // ------------------------------------------------- balanced assignment ---
@@ -395,6 +576,34 @@ static hipError_t update_step(const float* X, int64_t v, int d, int64_t c, const
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t pp_step_dispatch(const T* E, const float* inv, int64_t v, int d,
+                                   const int32_t* centers, int i, float* D, double* part,
+                                   int64_t nb, hipStream_t st) {
+  const int maxm = (d / Chunk<T>::kElems + 63) / 64;
+  const dim3 grid((unsigned)nb), block(256);
+  if (maxm <= 1)
+    hipLaunchKernelGGL((k_pp_step<T, 1>), grid, block, 0, st, E, inv, v, d, centers, i, D, part);
+  else if (maxm <= 2)
+    hipLaunchKernelGGL((k_pp_step<T, 2>), grid, block, 0, st, E, inv, v, d, centers, i, D, part);
+  else if (maxm <= 4)
+    hipLaunchKernelGGL((k_pp_step<T, 4>), grid, block, 0, st, E, inv, v, d, centers, i, D, part);
+  else if (maxm <= 8)
+    hipLaunchKernelGGL((k_pp_step<T, 8>), grid, block, 0, st, E, inv, v, d, centers, i, D, part);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+static hipError_t launch_pp_step(const void* E, bool bf16, const float* inv, int64_t v, int d,
+                                 const int32_t* centers, int i, float* D, double* part, int64_t nb,
+                                 hipStream_t st) {
+  return bf16 ? pp_step_dispatch(static_cast<const uint16_t*>(E), inv, v, d, centers, i, D, part,
+                                 nb, st)
+              : pp_step_dispatch(static_cast<const float*>(E), inv, v, d, centers, i, D, part, nb,
+                                 st);
+}
+
 hipError_t balanced_assign_device(const float* S, int64_t v, int64_t c, int32_t* asg,
                                   hipStream_t st, int* rounds) {
   ClusterWork w;
@@ -413,35 +622,42 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
                          const double* u, float* C, int32_t* c2t, int32_t* init, int32_t* asg_out,
                          hipStream_t st, ClusterTimes* times) {
   float* X = nullptr;
+  float* inv = nullptr;
   float* D = nullptr;
+  double* part = nullptr;
   float* S = nullptr;
   int32_t* centers = nullptr;
   int32_t* asg = nullptr;
+  uint16_t* pieces = nullptr;  // bf16 tables: the three bf16 pieces of C
   ClusterWork w;
   hipEvent_t ev[5] = {};
   for (auto& e : ev) (void)hipEventCreate(&e);
   hipError_t r = hipMalloc((void**)&X, sizeof(float) * v * d);
+  const int64_t nb = (v + kPpRows - 1) / kPpRows;
+  if (r == hipSuccess) r = hipMalloc((void**)&inv, sizeof(float) * v);
   if (r == hipSuccess) r = hipMalloc((void**)&D, sizeof(float) * v);
+  if (r == hipSuccess) r = hipMalloc((void**)&part, sizeof(double) * nb);
   if (r == hipSuccess) r = hipMalloc((void**)&S, sizeof(float) * v * c);
   if (r == hipSuccess) r = hipMalloc((void**)&centers, sizeof(int32_t) * c);
   if (r == hipSuccess) r = hipMalloc((void**)&asg, sizeof(int32_t) * v);
+  if (r == hipSuccess && bf16) r = hipMalloc((void**)&pieces, sizeof(uint16_t) * 3 * c * d);
   if (r == hipSuccess) r = work_alloc(w, v, c, st);
   int total_rounds = 0;
   if (r == hipSuccess) {
     (void)hipEventRecord(ev[0], st);
     if (bf16)
       hipLaunchKernelGGL((k_normalize_rows<uint16_t>), dim3(blocks_for(v, 4)), dim3(256), 0, st,
-                         static_cast<const uint16_t*>(E), v, d, X);
+                         static_cast<const uint16_t*>(E), v, d, X, inv);
     else
       hipLaunchKernelGGL((k_normalize_rows<float>), dim3(blocks_for(v, 4)), dim3(256), 0, st,
-                         static_cast<const float*>(E), v, d, X);
+                         static_cast<const float*>(E), v, d, X, inv);
     const int32_t first = (int32_t)std::min<int64_t>((int64_t)(u[0] * (double)v), v - 1);
     r = hipMemcpyAsync(centers, &first, sizeof(int32_t), hipMemcpyHostToDevice, st);
     for (int64_t i = 0; r == hipSuccess && i < c; ++i) {
-      if (i > 0) hipLaunchKernelGGL(k_pp_pick, dim3(1), dim3(1024), 0, st, D, v, u[i], centers, (int)i);
-      hipLaunchKernelGGL(k_pp_update, dim3(blocks_for(v, 4)), dim3(256), 0, st, X, v, d, centers,
-                         (int)i, D);
-      r = hipGetLastError();
+      if (i > 0)
+        hipLaunchKernelGGL(k_pp_pick, dim3(1), dim3(1024), 0, st, D, part, nb, v, u[i], centers,
+                           (int)i);
+      r = launch_pp_step(E, bf16, inv, v, d, centers, (int)i, D, part, nb, st);
     }
     if (r == hipSuccess) {
       hipLaunchKernelGGL(k_gather_rows, dim3(blocks_for(c * d, 256)), dim3(256), 0, st, X, d,
@@ -454,8 +670,16 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
     float sims_ms = 0.f;
     for (int it = 0; r == hipSuccess && it < iters; ++it) {
       (void)hipEventRecord(ev[2], st);
-      hipLaunchKernelGGL(k_sims, dim3(blocks_for(v, 64), blocks_for(c, 64)), dim3(256), 0, st, X, v,
-                         C, c, d, S);
+      if (bf16) {
+        hipLaunchKernelGGL(k_split_pieces, dim3(blocks_for(c * d, 256)), dim3(256), 0, st, C, c * d,
+                           pieces);
+        hipLaunchKernelGGL(k_sims_mfma, dim3(blocks_for(v, kSimTile), blocks_for(c, kSimTile)),
+                           dim3(256), 0, st, static_cast<const uint16_t*>(E), inv, v, d, pieces, c,
+                           S);
+      } else {
+        hipLaunchKernelGGL(k_sims, dim3(blocks_for(v, 64), blocks_for(c, 64)), dim3(256), 0, st, X,
+                           v, C, c, d, S);
+      }
       (void)hipEventRecord(ev[3], st);
       hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(v, 256)), dim3(256), 0, st, asg, v, -1);
       r = hipGetLastError();
@@ -483,7 +707,9 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
   }
   for (auto& e : ev) (void)hipEventDestroy(e);
   work_free(w);
-  for (void* p : {(void*)X, (void*)D, (void*)S, (void*)centers, (void*)asg}) (void)hipFree(p);
+  for (void* p : {(void*)X, (void*)inv, (void*)D, (void*)part, (void*)S, (void*)centers, (void*)asg,
+                  (void*)pieces})
+    (void)hipFree(p);
   return r;
 }
 

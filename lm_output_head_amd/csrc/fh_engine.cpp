@@ -205,7 +205,10 @@ fh_status fh_cluster(const void* E, fh_dtype dtype, int64_t v, int64_t d, int64_
   if (c < 1 || c > 65536 || v < c || v % c != 0 || v > INT32_MAX)
     return fail(FH_EINVAL, "need 1 <= c <= 65536, v a multiple of c and v < 2^31 (v=" +
                                std::to_string(v) + ", c=" + std::to_string(c) + ")");
-  if (d < 1 || d > (int64_t)1 << 20) return fail(FH_EINVAL, "d=" + std::to_string(d) + " outside [1, 2^20]");
+  const int64_t epc = dtype == FH_BF16 ? 8 : 4;  // elements per 16-byte chunk
+  if (d < 1 || d % epc != 0)
+    return fail(FH_EINVAL, dtype == FH_BF16 ? "bf16 needs d % 8 == 0" : "f32 needs d % 4 == 0");
+  if (d > 64 * 8 * epc) return fail(FH_EUNSUPPORTED, "d too large for this build");
   if (iters < 1) return fail(FH_EINVAL, "iters must be >= 1");
   for (int64_t i = 0; i < c; ++i)
     if (!(u[i] >= 0.0 && u[i] < 1.0))
