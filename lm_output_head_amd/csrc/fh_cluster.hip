@@ -54,16 +54,18 @@ __global__ __launch_bounds__(256) void k_normalize_rows(const T* __restrict__ E,
 
 // ------------------------------------------------------------ k-means++ ---
 
-// Rows per workgroup of the k-means++ step (16 per wave); also the rows one
-// wave of the draw scans.
-constexpr int kPpRows = 64;
+// Rows per workgroup of the k-means++ step, one per wave: many small
+// workgroups keep the most row reads in flight (measured on the 128256 x
+// 2048 bf16 table: 4 rows per workgroup stream 5.9 TB/s, 64 rows 4.8 TB/s).
+// Also the block of rows the draw scans last.
+constexpr int kPpRows = 4;
 
 // One k-means++ step's distance refresh against centre i:
 //   D[t] = min(D[t], 1 - inv[t] inv[ct] (E_t . E_ct))   (= when i == 0)
 // with the table read in its own storage type (coalesced 16-byte row loads,
 // the centre's row in registers), and part[w] = sum of D^2 over workgroup
-// w's 64 rows in fp64, in row order within each wave, then wave 0..3.
-template <typename T, int MAXM>
+// w's rows in fp64, in row order within each wave, then wave 0..3.
+template <typename T, int MAXM, int RPI = 1, int ROWS = kPpRows>
 __global__ __launch_bounds__(256) void k_pp_step(const T* __restrict__ E,
                                                  const float* __restrict__ inv, int64_t v, int d,
                                                  const int32_t* __restrict__ centers, int i,
@@ -76,8 +78,8 @@ __global__ __launch_bounds__(256) void k_pp_step(const T* __restrict__ E,
   uint4 hv[1][MAXM];
   load_hslice<T, MAXM>(E + ct * d, nch, lane, hv[0]);
   const float ic = inv[ct];
-  const int64_t r0 = (int64_t)blockIdx.x * kPpRows + wave * (kPpRows / 4);
-  const int64_t r1 = min(r0 + kPpRows / 4, v);
+  const int64_t r0 = (int64_t)blockIdx.x * ROWS + wave * (ROWS / 4);
+  const int64_t r1 = min(r0 + ROWS / 4, v);
   double s = 0.0;
   auto row = [](int64_t r) -> int64_t { return r; };
   auto sink = [&](int, int64_t r, int64_t, float z) {
@@ -86,80 +88,118 @@ __global__ __launch_bounds__(256) void k_pp_step(const T* __restrict__ E,
     if (lane == 0) D[r] = dist;
     s += (double)dist * (double)dist;
   };
-  wave_rows<T, MAXM, 1>(E, d, lane, hv, 1, r0, r1, 1, row, row, sink);
+  wave_rows<T, MAXM, 1, RPI>(E, d, lane, hv, 1, r0, r1, 1, row, row, sink);
   if (lane == 0) wsum[wave] = s;
   __syncthreads();
   if (threadIdx.x == 0) part[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
 }
 
-// The draw of centre i (one workgroup of 1024): the running sums of the nb
-// workgroup partials (each thread sums its contiguous share in order, then a
-// fixed-order scan over threads) locate the 64-row block where the running
-// sum of D^2 first exceeds u * total; one wave then scans that block's rows
-// (fp64 prefix over lanes) for the first row that exceeds it.  With a zero
-// total the draw is token floor(u v); if rounding leaves no crossing, the
-// last row of the last block is taken.
+// Inclusive prefix sum over the 64 lanes of a wave, in fp64 (fixed order).
+__device__ __forceinline__ double wave_prefix(double x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Partials of partials: part2[g] = sum of part[256 g .. 256 g + 255] (lane
+// prefix per wave, then the four wave sums in order).  Coalesced, and spread
+// over many workgroups, so the draw below reads only a few of them.
+constexpr int kPpGroup = 256;
+
+__global__ __launch_bounds__(256) void k_pp_reduce(const double* __restrict__ part, int64_t nb,
+                                                   double* __restrict__ part2) {
+  __shared__ double ws[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t j = (int64_t)blockIdx.x * kPpGroup + threadIdx.x;
+  const double x = wave_prefix(j < nb ? part[j] : 0.0, lane);
+  if (lane == 63) ws[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) part2[blockIdx.x] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+}
+
+// One wave walks vals[lo, hi) 64 at a time from the running sum *base and
+// returns the first index whose running sum exceeds target (hi - 1 if
+// rounding between the levels leaves none), with *base set to the running
+// sum before it.  Wave-uniform.
+template <typename Load>
+__device__ __forceinline__ int64_t wave_walk(Load load, int64_t lo, int64_t hi, double target,
+                                             double* base, int lane) {
+  double b = *base;
+  for (int64_t j0 = lo; j0 < hi; j0 += 64) {
+    const int64_t j = j0 + lane;
+    const double x = wave_prefix(j < hi ? load(j) : 0.0, lane);
+    const unsigned long long hit = __ballot(j < hi && b + x > target);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      const double before = __shfl(x, l > 0 ? l - 1 : 0);
+      *base = l > 0 ? b + before : b;
+      return j0 + l;
+    }
+    b += __shfl(x, 63);
+  }
+  *base = b;
+  return hi - 1;
+}
+
+// The draw of centre i (one workgroup of 1024).  Thread t sums its
+// contiguous share of the n2 group sums in order; the running sums over the
+// threads (lane prefix per wave, then the earlier waves' totals in order)
+// give the total and the first share where the running sum of D^2 exceeds
+// u * total; wave 0 then walks that share to the group, the group's 256
+// workgroup partials to the block, and the block's kPpRows rows to the
+// token.  With a zero total the draw is token floor(u v).
 __global__ __launch_bounds__(1024) void k_pp_pick(const float* __restrict__ D,
                                                   const double* __restrict__ part, int64_t nb,
+                                                  const double* __restrict__ part2, int64_t n2,
                                                   int64_t v, double u, int32_t* __restrict__ centers,
                                                   int i) {
-  __shared__ double ps[1024];
+  __shared__ double wtot[16];
+  __shared__ double ps_found;
   __shared__ int found;
-  __shared__ int64_t blk;
-  __shared__ double base;
-  const int tid = threadIdx.x;
-  const int64_t chunk = (nb + 1023) / 1024;
-  const int64_t lo = min(nb, tid * chunk), hi = min(nb, lo + chunk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t chunk = (n2 + 1023) / 1024;
+  const int64_t lo = min(n2, tid * chunk), hi = min(n2, lo + chunk);
   double s = 0.0;
-  for (int64_t j = lo; j < hi; ++j) s += part[j];
-  ps[tid] = s;
+  for (int64_t j = lo; j < hi; ++j) s += part2[j];
+  const double incl_w = wave_prefix(s, lane);
+  const double prev_w = __shfl_up(incl_w, 1);
+  if (lane == 63) wtot[wave] = incl_w;
   if (tid == 0) found = 1024;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const double x = tid >= off ? ps[tid - off] : 0.0;
-    __syncthreads();
-    ps[tid] += x;
-    __syncthreads();
+  double off = 0.0, total = 0.0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) off += wtot[w];
+    total += wtot[w];
   }
-  const double total = ps[1023];
   if (!(total > 0.0)) {
     if (tid == 0) centers[i] = (int32_t)min<int64_t>((int64_t)(u * (double)v), v - 1);
     return;
   }
   const double target = u * total;
-  const double excl = tid ? ps[tid - 1] : 0.0;
-  if (ps[tid] > target && excl <= target) found = tid;  // the first crossing
+  // a thread's exclusive sum is its predecessor's inclusive sum, formed by
+  // the same operations, so the crossings are exact; the lowest one counts
+  const double incl = off + incl_w, excl = lane ? off + prev_w : off;
+  if (incl > target && excl <= target) atomicMin(&found, tid);
   __syncthreads();
-  if (tid == 0 && found == 1024) {  // no crossing: the last block, last row
-    blk = nb - 1;
-    base = total;
-  }
-  if (tid == found) {
-    double run = excl;
-    int64_t j = lo;
-    for (; j < hi - 1; ++j) {
-      if (run + part[j] > target) break;
-      run += part[j];
-    }
-    blk = j;
-    base = run;
-  }
+  const int f = found < 1024 ? found : 1023;  // no crossing: the last share
+  if (tid == f) ps_found = excl;
   __syncthreads();
-  if (tid < 64) {
-    const int64_t r = blk * kPpRows + tid;
-    const double w = r < v ? (double)D[r] * (double)D[r] : 0.0;
-    double x = w;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double y = __shfl_up(x, off);
-      if (tid >= off) x += y;
-    }
-    const unsigned long long hit = __ballot(r < v && base + x > target);
-    if (tid == 0) {
-      const int64_t last = min<int64_t>(v, (blk + 1) * kPpRows) - 1;
-      centers[i] = (int32_t)(hit ? blk * kPpRows + __builtin_ctzll(hit) : last);
-    }
-  }
+  if (tid >= 64) return;
+  double base = ps_found;
+  const int64_t flo = min(n2, f * chunk), fhi = min(n2, flo + chunk);
+  const int64_t g = flo < fhi ? wave_walk([&](int64_t j) { return part2[j]; }, flo, fhi, target,
+                                          &base, lane)
+                              : n2 - 1;
+  const int64_t blk = wave_walk([&](int64_t j) { return part[j]; }, g * kPpGroup,
+                                min(nb, (g + 1) * kPpGroup), target, &base, lane);
+  const int64_t rlo = blk * kPpRows, rhi = min(v, rlo + kPpRows);
+  const int64_t r = wave_walk([&](int64_t t) { return (double)D[t] * (double)D[t]; }, rlo, rhi,
+                              target, &base, lane);
+  if (lane == 0) centers[i] = (int32_t)r;
 }
 
 __global__ __launch_bounds__(256) void k_gather_rows(const float* __restrict__ X, int d,
@@ -625,6 +665,7 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
   float* inv = nullptr;
   float* D = nullptr;
   double* part = nullptr;
+  double* part2 = nullptr;
   float* S = nullptr;
   int32_t* centers = nullptr;
   int32_t* asg = nullptr;
@@ -636,7 +677,9 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
   const int64_t nb = (v + kPpRows - 1) / kPpRows;
   if (r == hipSuccess) r = hipMalloc((void**)&inv, sizeof(float) * v);
   if (r == hipSuccess) r = hipMalloc((void**)&D, sizeof(float) * v);
+  const int64_t n2 = (nb + kPpGroup - 1) / kPpGroup;
   if (r == hipSuccess) r = hipMalloc((void**)&part, sizeof(double) * nb);
+  if (r == hipSuccess) r = hipMalloc((void**)&part2, sizeof(double) * n2);
   if (r == hipSuccess) r = hipMalloc((void**)&S, sizeof(float) * v * c);
   if (r == hipSuccess) r = hipMalloc((void**)&centers, sizeof(int32_t) * c);
   if (r == hipSuccess) r = hipMalloc((void**)&asg, sizeof(int32_t) * v);
@@ -654,9 +697,11 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
     const int32_t first = (int32_t)std::min<int64_t>((int64_t)(u[0] * (double)v), v - 1);
     r = hipMemcpyAsync(centers, &first, sizeof(int32_t), hipMemcpyHostToDevice, st);
     for (int64_t i = 0; r == hipSuccess && i < c; ++i) {
-      if (i > 0)
-        hipLaunchKernelGGL(k_pp_pick, dim3(1), dim3(1024), 0, st, D, part, nb, v, u[i], centers,
-                           (int)i);
+      if (i > 0) {
+        hipLaunchKernelGGL(k_pp_reduce, dim3((unsigned)n2), dim3(kPpGroup), 0, st, part, nb, part2);
+        hipLaunchKernelGGL(k_pp_pick, dim3(1), dim3(1024), 0, st, D, part, nb, part2, n2, v, u[i],
+                           centers, (int)i);
+      }
       r = launch_pp_step(E, bf16, inv, v, d, centers, (int)i, D, part, nb, st);
     }
     if (r == hipSuccess) {
@@ -707,8 +752,8 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
   }
   for (auto& e : ev) (void)hipEventDestroy(e);
   work_free(w);
-  for (void* p : {(void*)X, (void*)inv, (void*)D, (void*)part, (void*)S, (void*)centers, (void*)asg,
-                  (void*)pieces})
+  for (void* p : {(void*)X, (void*)inv, (void*)D, (void*)part, (void*)part2, (void*)S,
+                  (void*)centers, (void*)asg, (void*)pieces})
     (void)hipFree(p);
   return r;
 }
