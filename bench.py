@@ -76,10 +76,17 @@ def copy_calibration():
                       "bytes_written_per_launch": COPY_BYTES, "launches": 5}), flush=True)
 
 
-def kernel_source_hash() -> str:
+CLUSTER_SOURCES = ("fh_cluster.hip",)  # the offline clustering, its own translation unit
+
+
+def kernel_source_hash(cluster: bool = False) -> str:
+    """Hash of the kernel sources a measurement depends on: the head's (every
+    file under csrc/ but the clustering's), or the clustering's."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lm_output_head_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if (name in CLUSTER_SOURCES) != cluster:
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -113,10 +120,11 @@ def algorithmic_bytes(shape, B, p, quant, elem, union=None):
             "dense_mfma": dense, "batch1": score + select + gather, "call": call}
 
 
-def traffic_from_profiles(kernel: str, src_hash: str, workload_key: str):
+def traffic_from_profiles(kernel: str, src_hash: str, workload_key: str,
+                          name: str = "pmc_traffic.json"):
     """HBM bytes per launch measured by rocprofv3 PMC counters, if a summary
     for the current kernel sources and this workload exists under profiles/."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     try:
@@ -233,10 +241,15 @@ def cluster_main(args):
     got = asg.cpu().numpy()
     ari = co.adjusted_rand_index(got, truth)
     elem = 2 if shape.dtype == "bf16" else 4
-    # per centre: the table's rows in their storage type, the inverse norms,
-    # D read and written, and the workgroup partials
-    pp_bytes = c * (v * d * elem + v * 4 * 3 + (v // 64) * 8)
-    init_gbs = pp_bytes / (best["init_ms"] * 1e-3) / 1e9
+    # one k-means++ distance refresh (k_pp_step): the table's rows in their
+    # storage type, the inverse norms, D read and written, one fp64 partial
+    # per 4-row workgroup
+    step_bytes = v * d * elem + v * 4 * 3 + ((v + 3) // 4) * 8
+    step_gbs = step_bytes / (best["pp_step_us"] * 1e-6) / 1e9
+    init_gbs = c * step_bytes / (best["init_ms"] * 1e-3) / 1e9
+    workload_key = f"cluster/{shape.name}"
+    traffic = traffic_from_profiles("k_pp_step", kernel_source_hash(cluster=True), workload_key,
+                                    name="cluster_pmc_traffic.json")
     sims_tflops = 2.0 * v * c * d * args.cluster_iters / (best["sims_ms"] * 1e-3) / 1e12
     res = {
         "metric": "balanced k-means s per clustering", "value": round(best["total_ms"] / 1e3, 4),
@@ -249,9 +262,12 @@ def cluster_main(args):
                       "rounds_and_update": round(best["total_ms"] - best["init_ms"]
                                                  - best["sims_ms"], 2)},
         "rounds": best["rounds"],
-        "roofline": {"bound": "hbm", "achieved": round(init_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(init_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "phase": "k-means++ (per centre: one pass over the table's rows)"},
+        "roofline": {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "k_pp_step",
+                     "algorithmic_bytes": step_bytes,
+                     "avg_launch_us": round(best["pp_step_us"], 2)},
+        "kmeanspp_phase_gbs": round(init_gbs, 1),
         "sims_tflops_f32": round(sims_tflops, 2),
         "quality": {"ari_vs_planted": round(ari, 5)},
     }

@@ -240,6 +240,9 @@ typedef struct {
   float init_ms;  /* normalisation and k-means++ seeding                    */
   float sims_ms;  /* the similarity products, summed over iterations        */
   float total_ms; /* the whole call                                         */
+  float pp_step_us; /* average duration of the k-means++ distance refresh
+                       (one pass over the table), from HIP events around
+                       every 16th launch                                    */
   int rounds;     /* balanced-assignment rounds, summed over iterations     */
 } fh_cluster_times;
 

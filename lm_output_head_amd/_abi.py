@@ -32,7 +32,8 @@ class FhKernelTime(ctypes.Structure):
 
 class FhClusterTimes(ctypes.Structure):
     _fields_ = [("init_ms", ctypes.c_float), ("sims_ms", ctypes.c_float),
-                ("total_ms", ctypes.c_float), ("rounds", ctypes.c_int)]
+                ("total_ms", ctypes.c_float), ("pp_step_us", ctypes.c_float),
+                ("rounds", ctypes.c_int)]
 
 
 class FlashHeadError(RuntimeError):

@@ -696,14 +696,29 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
                          static_cast<const float*>(E), v, d, X, inv);
     const int32_t first = (int32_t)std::min<int64_t>((int64_t)(u[0] * (double)v), v - 1);
     r = hipMemcpyAsync(centers, &first, sizeof(int32_t), hipMemcpyHostToDevice, st);
+    // every 16th distance refresh is bracketed by an event pair
+    constexpr int64_t kSample = 16;
+    std::vector<hipEvent_t> sev(2 * ((c + kSample - 1) / kSample), nullptr);
+    for (auto& e : sev) (void)hipEventCreate(&e);
     for (int64_t i = 0; r == hipSuccess && i < c; ++i) {
       if (i > 0) {
         hipLaunchKernelGGL(k_pp_reduce, dim3((unsigned)n2), dim3(kPpGroup), 0, st, part, nb, part2);
         hipLaunchKernelGGL(k_pp_pick, dim3(1), dim3(1024), 0, st, D, part, nb, part2, n2, v, u[i],
                            centers, (int)i);
       }
+      const bool sample = i % kSample == 0;
+      if (sample) (void)hipEventRecord(sev[2 * (i / kSample)], st);
       r = launch_pp_step(E, bf16, inv, v, d, centers, (int)i, D, part, nb, st);
+      if (sample) (void)hipEventRecord(sev[2 * (i / kSample) + 1], st);
     }
+    if (r == hipSuccess) r = hipStreamSynchronize(st);
+    double step_ms = 0.0;
+    for (size_t j = 0; r == hipSuccess && j < sev.size(); j += 2) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, sev[j], sev[j + 1]) == hipSuccess) step_ms += ms;
+    }
+    if (times) times->pp_step_us = (float)(1e3 * step_ms / (double)(sev.size() / 2));
+    for (auto& e : sev) (void)hipEventDestroy(e);
     if (r == hipSuccess) {
       hipLaunchKernelGGL(k_gather_rows, dim3(blocks_for(c * d, 256)), dim3(256), 0, st, X, d,
                          centers, c, C);

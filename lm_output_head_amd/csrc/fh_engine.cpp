@@ -221,6 +221,7 @@ fh_status fh_cluster(const void* E, fh_dtype dtype, int64_t v, int64_t d, int64_
     out_times->init_ms = t.init_ms;
     out_times->sims_ms = t.sims_ms;
     out_times->total_ms = t.total_ms;
+    out_times->pp_step_us = t.pp_step_us;
     out_times->rounds = t.rounds;
   }
   return FH_OK;

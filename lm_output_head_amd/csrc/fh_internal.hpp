@@ -108,6 +108,7 @@ struct ClusterTimes {
   float init_ms;  // normalisation and k-means++
   float sims_ms;  // similarity GEMMs, all iterations
   float total_ms;
+  float pp_step_us;  // average k-means++ distance-refresh kernel, sampled launches
   int rounds;     // balanced-assignment rounds, all iterations
 };
 hipError_t balanced_assign_device(const float* S, int64_t v, int64_t c, int32_t* asg,

@@ -152,7 +152,7 @@ def fh_cluster(E: torch.Tensor, c: int, iters: int, u, out_C: torch.Tensor, out_
                                  _ptr(out_c2t), _ptr(out_init), _ptr(out_assign), ctypes.byref(t),
                                  _stream(stream)))
     return {"init_ms": t.init_ms, "sims_ms": t.sims_ms, "total_ms": t.total_ms,
-            "rounds": t.rounds}
+            "pp_step_us": t.pp_step_us, "rounds": t.rounds}
 
 
 class FlashHead:
