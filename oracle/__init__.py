@@ -19,12 +19,15 @@ from .flashhead_oracle import (  # noqa: F401
     MODE_TOKEN_SAMPLE,
     OracleHead,
     dense,
+    dequantize_g32,
     dequantize_int4,
+    dequantize_int8,
     finish,
     forward,
     gather,
     pack_int4,
     quantize_int4_g32,
+    quantize_int8_g32,
     score,
     select,
     unpack_int4,

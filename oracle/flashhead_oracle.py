@@ -7,7 +7,8 @@ What the method computes (FlashHead explainer, framerc.cn, §1.1, §1.2 and
 z = E h.  FlashHead replaces this with a two-stage retrieval over a balanced
 clustering of E's rows:
 
-1. score h against the c centroids (optionally INT4-quantised, §1.2.4);
+1. score h against the c centroids (optionally INT4-quantised, §1.2.4, or
+   INT8-quantised, the W8A16 row of the tuning table, §5.2);
 2. choose p probe clusters, by top-p score (§1.2.2) or by multinomial
    sampling with temperature (§1.2.3);
 3. score only the b = v/c tokens of each chosen cluster, found through the
@@ -17,14 +18,14 @@ clustering of E's rows:
 
 Inside a stage nothing is approximated, so each stage is its plain
 definition: float64 dot products over the exact stored values (bfloat16
-widened exactly, or dequantised INT4), a full lexicographic sort for
+widened exactly, or dequantised INT4 / INT8), a full lexicographic sort for
 selection, and Gumbel-max for every draw.  Readings where the pages are
-silent (the INT4 scheme, tie-breaks, output order, sampling without
+silent (the INT4 and INT8 schemes, tie-breaks, output order, sampling without
 replacement, one temperature for both stages) are the ones listed under
 "Readings" in the design notes and restated at each function.
 
 Where a floating-point value decides an integer (a top-p cut, an argmax, an
-INT4 code), the decision is taken in float32, the precision the kernels
+INT4 or INT8 code), the decision is taken in float32, the precision the kernels
 decide in; all other arithmetic is float64.
 """
 
@@ -70,38 +71,54 @@ def validate_c2t(c2t, v: int, c: int, b: int) -> np.ndarray:
 # Stage-1 quantisation (§1.2.4 selective quantisation; §2.3 quant config)
 # ---------------------------------------------------------------------------
 
-def quantize_int4_g32(C: np.ndarray):
-    """Symmetric INT4 with one fp16 scale per 32 consecutive row elements.
-
-    For each centroid row k and group g (elements 32g..32g+31):
-    sigma = fp16(amax / 7) with the division in float32 and round-to-nearest-
-    even to fp16; q = clamp(rint(x / sigma), -7, 7) with float32 division and
-    ties to even; q = 0 where sigma = 0.  Returns (q int8 [c x d],
-    sigma float16 [c x d/32]).  Raises OverflowError if a scale is not a
-    finite fp16 number and ValueError if d is not a multiple of 32.
-    """
+def _quantize_sym_g32(C: np.ndarray, qmax: int, name: str):
+    """Symmetric integer codes with one fp16 scale per 32 consecutive row
+    elements: for each centroid row k and group g (elements 32g..32g+31),
+    sigma = fp16(amax / qmax) with the division in float32 and round-to-
+    nearest-even to fp16; q = clamp(rint(x / sigma), -qmax, qmax) with
+    float32 division and ties to even; q = 0 where sigma = 0.  Returns
+    (q int8 [c x d], sigma float16 [c x d/32]).  Raises OverflowError if a
+    scale is not a finite fp16 number and ValueError if d is not a multiple
+    of 32."""
     C = np.asarray(C, dtype=np.float32)
     c, d = C.shape
     if d % 32 != 0:
-        raise ValueError("INT4 g32 needs d % 32 == 0")
+        raise ValueError(f"{name} g32 needs d % 32 == 0")
     g = C.reshape(c, d // 32, 32)
     amax = np.abs(g).max(axis=2)
     with np.errstate(over="ignore"):
-        sigma = (amax / np.float32(7.0)).astype(np.float16)
+        sigma = (amax / np.float32(qmax)).astype(np.float16)
     if not np.all(np.isfinite(sigma)):
-        raise OverflowError("a centroid group's scale overflows fp16")
+        raise OverflowError(f"a centroid group's {name} scale overflows fp16")
     s = sigma.astype(np.float32)[..., None]
     nz = s > 0
     q = np.rint(g / np.where(nz, s, np.float32(1.0)))
-    q = np.where(nz, np.clip(q, -7, 7), 0).astype(np.int8)
+    q = np.where(nz, np.clip(q, -qmax, qmax), 0).astype(np.int8)
     return q.reshape(c, d), sigma
 
 
-def dequantize_int4(q: np.ndarray, sigma: np.ndarray) -> np.ndarray:
+def quantize_int4_g32(C: np.ndarray):
+    """INT4 stage-1 centroids (§1.2.4, §2.3 "centroid: int4"): the symmetric
+    g32 scheme with qmax = 7."""
+    return _quantize_sym_g32(C, 7, "INT4")
+
+
+def quantize_int8_g32(C: np.ndarray):
+    """INT8 stage-1 centroids, the W8A16 configuration of the tuning table
+    (§5.2): the same symmetric g32 scheme with qmax = 127; queries stay in
+    their 16-bit type."""
+    return _quantize_sym_g32(C, 127, "INT8")
+
+
+def dequantize_g32(q: np.ndarray, sigma: np.ndarray) -> np.ndarray:
     """C_hat = sigma * q in float64 (exact)."""
     c, d = q.shape
     return (sigma.astype(np.float64)[:, :, None]
             * q.reshape(c, d // 32, 32).astype(np.float64)).reshape(c, d)
+
+
+dequantize_int4 = dequantize_g32
+dequantize_int8 = dequantize_g32
 
 
 def pack_int4(q: np.ndarray) -> np.ndarray:
@@ -279,7 +296,7 @@ class ForwardResult:
 
 
 class OracleHead:
-    """The engine's state: E, C (or its INT4 form) and C2T, validated once."""
+    """The engine's state: E, C (or its INT4 / INT8 form) and C2T, validated once."""
 
     def __init__(self, E, C, c2t, quant: str = "none"):
         E = np.asarray(E)
@@ -297,7 +314,10 @@ class OracleHead:
             self.C_hat = C.astype(np.float64)
         elif quant == "int4":
             self.q, self.sigma = quantize_int4_g32(C)
-            self.C_hat = dequantize_int4(self.q, self.sigma)
+            self.C_hat = dequantize_g32(self.q, self.sigma)
+        elif quant == "int8":
+            self.q, self.sigma = quantize_int8_g32(C)
+            self.C_hat = dequantize_g32(self.q, self.sigma)
         else:
             raise ValueError(f"unknown quant {quant}")
 

@@ -145,6 +145,77 @@ def test_int4_rejects_bad_shapes_and_overflow():
         oracle.quantize_int4_g32(np.full((1, 32), 1e6, dtype=np.float32))
 
 
+def test_int8_fixture_codes():
+    """Hand-worked INT8 codes and scales (W8A16, §5.2; scheme as INT4 with 127)."""
+    g = _load("int8_groups.json")
+    C = np.array([grp["x"] for grp in g["groups"]], dtype=np.float32)
+    q, sigma = oracle.quantize_int8_g32(C)
+    for r, grp in enumerate(g["groups"]):
+        assert float(sigma[r, 0]) == grp["sigma"]
+        assert q[r].tolist() == grp["q"]
+
+
+def test_int8_exact_round_trip_on_representable_rows():
+    """Rows of q*sigma with a power-of-two sigma and max|q| = 127 quantise
+    back exactly (amax/127 = sigma exactly, and every quotient is an
+    integer)."""
+    rng = np.random.default_rng(15)
+    c, d = 8, 128
+    sig = (2.0 ** rng.integers(-12, 2, size=(c, d // 32))).astype(np.float16)
+    qs = rng.integers(-127, 128, size=(c, d // 32, 32))
+    qs[:, :, 3] = rng.choice([-127, 127], size=(c, d // 32))
+    C = (sig.astype(np.float32)[..., None] * qs.astype(np.float32)).reshape(c, d)
+    q, sigma = oracle.quantize_int8_g32(C)
+    assert np.array_equal(sigma, sig)
+    assert np.array_equal(q.reshape(c, d // 32, 32), qs)
+    assert np.array_equal(oracle.dequantize_int8(q, sigma), C.astype(np.float64))
+
+
+def test_int8_error_bound_and_amax():
+    """|C - C_hat| <= sigma/2 (plus fp16 scale rounding); amax maps to +-127;
+    and INT8 is closer to C than INT4 on the same rows."""
+    rng = np.random.default_rng(16)
+    C = rng.standard_normal((32, 256)).astype(np.float32)
+    q, sigma = oracle.quantize_int8_g32(C)
+    Ch = oracle.dequantize_int8(q, sigma)
+    s = sigma.astype(np.float64).repeat(32, axis=1)
+    err = np.abs(C.astype(np.float64) - Ch)
+    assert np.all(err <= s / 2 + 127 * s * 2.0 ** -10)
+    g = np.abs(C).reshape(32, 8, 32)
+    arg = g.argmax(axis=2)
+    top = np.take_along_axis(q.reshape(32, 8, 32), arg[..., None], axis=2)[..., 0]
+    assert np.all(np.abs(top) == 127)
+    assert q.min() >= -127 and q.max() <= 127
+    q4, s4 = oracle.quantize_int4_g32(C)
+    assert err.max() < np.abs(C - oracle.dequantize_int4(q4, s4)).max() / 8
+
+
+def test_int8_rejects_bad_shapes_and_overflow():
+    with pytest.raises(ValueError):
+        oracle.quantize_int8_g32(np.ones((2, 48), dtype=np.float32))
+    with pytest.raises(OverflowError):  # 1e7 / 127 exceeds the largest fp16
+        oracle.quantize_int8_g32(np.full((1, 32), 1e7, dtype=np.float32))
+
+
+def test_int8_head_scores_are_the_group_sums():
+    """Stage-1 scores of an INT8 head: sum_g sigma_g sum_{i in g} q_i h_i,
+    written out with math.fsum."""
+    rng = np.random.default_rng(17)
+    c, d, v = 4, 64, 8
+    C = rng.standard_normal((c, d)).astype(np.float32)
+    E = rng.standard_normal((v, d)).astype(np.float32)
+    H = rng.standard_normal((2, d)).astype(np.float32)
+    head = oracle.OracleHead(E, C, np.arange(v).reshape(c, 2), "int8")
+    q, sigma = oracle.quantize_int8_g32(C)
+    s = oracle.score(head.C_hat, H)
+    for b in range(2):
+        for k in range(c):
+            want = math.fsum(float(sigma[k, g]) * math.fsum(int(q[k, 32 * g + i]) * float(H[b, 32 * g + i])
+                                                            for i in range(32))
+                             for g in range(d // 32))
+            assert abs(s[b, k] - want) <= 1e-12 * (1 + abs(want))
+
+
 # ---------------------------------------------------------------- stage 1 --
 
 def test_score_matches_fsum_on_tiny_inputs():
