@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--shape", default="llama32_1b")
     ap.add_argument("--B", type=int, default=1)
     ap.add_argument("--p", type=int, default=512)
-    ap.add_argument("--quant", default="none", choices=["none", "int4"])
+    ap.add_argument("--quant", default="none", choices=["none", "int4", "int8"])
     ap.add_argument("--mode", type=int, default=0)
     ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--replicas", type=int, default=16)
@@ -100,6 +100,8 @@ def algorithmic_bytes(shape, B, p, quant, elem, union=None):
     v, d, c, b = shape.v, shape.d, shape.c, shape.b
     if quant == "int4":
         c_bytes = c * d // 2 + c * (d // 32) * 2
+    elif quant == "int8":
+        c_bytes = c * d + c * (d // 32) * 2
     else:
         c_bytes = c * d * elem
     score = c_bytes + B * d * elem + B * c * 4
@@ -115,7 +117,7 @@ def algorithmic_bytes(shape, B, p, quant, elem, union=None):
     u = union if union is not None else B * p
     gather_cm = int(round(u * b * (d * elem + 4))) + B * d * elem + 2 * W * B * 4
     call = score + select + (gather_cm if (B > 1 and union is not None) else gather)
-    return {"score": score, "score_int4": score, "score_mfma": score, "score_int4_mfma": score,
+    return {"score": score, "score_int4": score, "score_int8": score, "score_mfma": score, "score_int4_mfma": score,
             "select": select, "gather": gather, "gather_cm": gather_cm, "dense": dense,
             "dense_mfma": dense, "batch1": score + select + gather, "call": call}
 

@@ -53,10 +53,17 @@ typedef enum {
 /* Storage type shared by E, C and h. */
 typedef enum { FH_F32 = 0, FH_BF16 = 1 } fh_dtype;
 
-/* Stage-1 centroid storage ([X] §1.2.4, §2.3). */
+/* Stage-1 centroid storage ([X] §1.2.4, §2.3; the W4A16 and W8A16 rows of
+ * the tuning table, [X] §5.2).  Both integer forms are symmetric with one
+ * fp16 scale per 32 consecutive elements of a centroid row:
+ * sigma = fp16_rne(amax / qmax) (fp32 division), q = clamp(rint(x / sigma),
+ * -qmax, qmax) with ties to even, q = 0 where sigma = 0; the score is
+ * sum_g sigma_g sum_{i in g} q_i h_i.  Queries and token embeddings stay in
+ * the engine's dtype. */
 typedef enum {
-  FH_QUANT_NONE = 0,     /* centroids used as given                          */
-  FH_QUANT_INT4_G32 = 1  /* symmetric INT4, one fp16 scale per 32 elements   */
+  FH_QUANT_NONE = 0,      /* centroids used as given                         */
+  FH_QUANT_INT4_G32 = 1,  /* qmax 7, two's-complement nibbles                */
+  FH_QUANT_INT8_G32 = 2   /* qmax 127, int8                                  */
 } fh_quant;
 
 /* `mode` is the OR of one probe flag and one token flag. */
@@ -75,19 +82,19 @@ enum {
  *            ([X] §1.1).  BORROWED: not copied; keep it alive and unchanged
  *            until fh_destroy.
  *   C        device, [c x d] of `dtype`: cluster centroids ([X] §1.2.1).
- *            Borrowed for FH_QUANT_NONE.  For FH_QUANT_INT4_G32 it is read
- *            once here and may be freed after the call returns.
+ *            Borrowed for FH_QUANT_NONE.  For FH_QUANT_INT4_G32 and
+ *            FH_QUANT_INT8_G32 it is read once here and may be freed after
+ *            the call returns.
  *   C2T      HOST, [c x b] int32 with b = v / c: C2T[k*b + j] is the token in
  *            slot j of cluster k ([X] §1.2.1, [A] (1)).  Copied.  Must hold
  *            every token of [0, v) exactly once (balanced clustering).
  *   v, d, c  vocabulary size, hidden size, cluster count; v % c == 0.
  *            d % 4 == 0 for FH_F32, d % 8 == 0 for FH_BF16, and
- *            d % 32 == 0 with FH_QUANT_INT4_G32.  c <= 16384, d <= 8192.
- *   quant    FH_QUANT_INT4_G32 quantises C here: per row k and group g of 32
- *            consecutive elements, sigma = fp16(amax / 7) (float32 division,
- *            round to nearest even), q = clamp(rint(x / sigma), -7, 7), q = 0
- *            where sigma = 0 ([X] §1.2.4).  A scale that overflows fp16 gives
- *            FH_EINVAL.
+ *            d % 32 == 0 with a quantised stage 1.  c <= 16384; d <= 4096
+ *            for FH_BF16, d <= 2048 for FH_F32 (else FH_EUNSUPPORTED).
+ *   quant    FH_QUANT_INT4_G32 / FH_QUANT_INT8_G32 quantise C here (the
+ *            scheme above, qmax 7 or 127).  A scale that overflows fp16
+ *            gives FH_EINVAL.
  *   max_batch largest B any later call will use (sizes the workspace).
  *            Besides the workspace, the engine keeps a cluster-contiguous
  *            copy of E (v x d of `dtype`, row f = E[C2T[f]]) so that each
@@ -163,6 +170,14 @@ fh_status fh_dense_forward(fh_engine* e, const void* h, int64_t B, int mode,
  *   scales  device [c x d/32] uint16: fp16 bit patterns of sigma.
  */
 fh_status fh_get_int4(fh_engine* e, uint8_t* packed, uint16_t* scales, void* stream);
+
+/*
+ * fh_get_int8 — copy the engine's INT8 centroids out (FH_QUANT_INT8_G32
+ * only, else FH_EINVAL).
+ *   codes   device [c x d] int8, row-major.
+ *   scales  device [c x d/32] uint16: fp16 bit patterns of sigma.
+ */
+fh_status fh_get_int8(fh_engine* e, int8_t* codes, uint16_t* scales, void* stream);
 
 /*
  * Per-kernel timing.  fh_profile_begin(e, n) makes the engine record a HIP

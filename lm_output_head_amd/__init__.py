@@ -2,7 +2,8 @@
 C ABI (include/flashhead.h), with this thin torch/ctypes binding on top."""
 
 from ._abi import (FH_BF16, FH_F32, FH_PROBE_SAMPLE, FH_PROBE_TOPK,  # noqa: F401
-                   FH_QUANT_INT4_G32, FH_QUANT_NONE, FH_TOKEN_ARGMAX, FH_TOKEN_SAMPLE,
+                   FH_QUANT_INT4_G32, FH_QUANT_INT8_G32, FH_QUANT_NONE, FH_TOKEN_ARGMAX,
+                   FH_TOKEN_SAMPLE,
                    FlashHeadError)
 from ._abi import load as load_library  # noqa: F401
 
@@ -11,7 +12,7 @@ def __getattr__(name):
     # the torch-facing binding is imported lazily so that the ABI module and
     # the build script stay usable without initialising torch
     if name in ("FlashHead", "fh_create", "fh_destroy", "fh_forward", "fh_score",
-                "fh_dense_forward", "fh_get_int4", "fh_profile_begin", "fh_profile_end",
+                "fh_dense_forward", "fh_get_int4", "fh_get_int8", "fh_profile_begin", "fh_profile_end",
                 "fh_set_path", "fh_sync_status", "fh_balanced_assign", "fh_cluster",
                 "fh_last_error", "fh_version"):
         from . import flashhead

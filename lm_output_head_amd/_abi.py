@@ -13,14 +13,14 @@ LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashhead.so"
 
 FH_OK, FH_EINVAL, FH_ENOMEM, FH_EHIP, FH_EUNSUPPORTED = 0, -1, -2, -3, -4
 FH_F32, FH_BF16 = 0, 1
-FH_QUANT_NONE, FH_QUANT_INT4_G32 = 0, 1
+FH_QUANT_NONE, FH_QUANT_INT4_G32, FH_QUANT_INT8_G32 = 0, 1, 2
 FH_PROBE_TOPK, FH_PROBE_SAMPLE, FH_TOKEN_ARGMAX, FH_TOKEN_SAMPLE = 0, 1, 0, 2
 FH_PATH_AUTO, FH_PATH_MULTI = 0, 1
 
 # Every symbol the header declares.
 EXPORTS = (
     "fh_create", "fh_destroy", "fh_forward", "fh_score", "fh_dense_forward",
-    "fh_get_int4", "fh_profile_begin", "fh_profile_end", "fh_set_path", "fh_sync_status",
+    "fh_get_int4", "fh_get_int8", "fh_profile_begin", "fh_profile_end", "fh_set_path", "fh_sync_status",
     "fh_balanced_assign", "fh_cluster", "fh_last_error", "fh_version",
 )
 
@@ -57,6 +57,7 @@ _SIGS = {
     "fh_score": ([_p, _p, _i64, _p, _p], _int),
     "fh_dense_forward": ([_p, _p, _i64, _int, _f, _u64, _p, _p, _p, _p, _p], _int),
     "fh_get_int4": ([_p, _p, _p, _p], _int),
+    "fh_get_int8": ([_p, _p, _p, _p], _int),
     "fh_profile_begin": ([_p, _i64], _int),
     "fh_profile_end": ([_p, ctypes.POINTER(FhKernelTime), _int, ctypes.POINTER(_int)], _int),
     "fh_set_path": ([_p, _int], _int),

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashhead.so")
 
-SOURCES = ["fh_kernels.hip", "fh_mfma.hip", "fh_cluster.hip", "fh_batch1_bf16.hip", "fh_batch1_bf16_int4.hip", "fh_batch1_f32.hip",
+SOURCES = ["fh_kernels.hip", "fh_mfma.hip", "fh_cluster.hip", "fh_batch1_bf16.hip", "fh_batch1_bf16_int4.hip",
+           "fh_batch1_bf16_int8.hip", "fh_batch1_f32.hip", "fh_batch1_f32_int8.hip",
            "fh_batch1_f32_int4.hip", "fh_engine.cpp"]
 
 # Packed FP32 instructions are disabled for all device code.

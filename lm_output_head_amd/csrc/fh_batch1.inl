@@ -1,7 +1,7 @@
 // The single-launch batch-1 kernel, instantiated per storage type and
 // stage-1 storage by the fh_batch1_*.hip translation units, which define
 //   FH_BATCH1_T      element type of E, C and h (uint16_t = bf16, float)
-//   FH_BATCH1_INT4   true for INT4 stage-1 centroids
+//   FH_BATCH1_QB     stage-1 centroid codes: 0 (as stored), 4 (INT4 g32), 8 (INT8 g32)
 //   FH_BATCH1_ENTRY  name of the exported launcher
 //
 // Sources (page title and section): FlashHead technical explainer
@@ -120,7 +120,7 @@ union Batch1Shared {
   int probes[1024];
 };
 
-template <typename T, int MAXM, int KP, bool INT4, int MAXG>
+template <typename T, int MAXM, int KP, int QB, int MAXG>
 __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   __shared__ Batch1Shared sh;
   const int lane = threadIdx.x & 63;
@@ -141,10 +141,10 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
         st_tagged(a.tscores + r, tag(a.epoch, __float_as_uint(saturate_key(s))));
       }
     };
-    if (INT4) {
+    if constexpr (QB != 0) {
       HGroups<MAXG> hg[1];
       load_hgroups<T, MAXG>(hp, a.d / 32, lane, hg[0]);
-      wave_rows_int4<MAXG, 1>(a.cq, a.csig, a.d, lane, hg, 1, r_lo + wave, r_hi, 16, sink);
+      wave_rows_q<QB, MAXG, 1>(a.cq, a.csig, a.d, lane, hg, 1, r_lo + wave, r_hi, 16, sink);
     } else {
       uint4 hv[1][MAXM];
       load_hslice<T, MAXM>(hp, a.d / Chunk<T>::kElems, lane, hv[0]);
@@ -299,48 +299,48 @@ static FusedArgs fused_args(const FusedLaunch& f) {
   return a;
 }
 
-template <typename T, int MAXM, int KP, bool INT4, int MAXG>
+template <typename T, int MAXM, int KP, int QB, int MAXG>
 static hipError_t b1_go(const FusedLaunch& f, const FusedArgs& a) {
   const unsigned grid = (unsigned)(a.g1 + a.g2 + 1);
-  hipLaunchKernelGGL((k_batch1<T, MAXM, KP, INT4, MAXG>), dim3(grid), dim3(1024), 0,
+  hipLaunchKernelGGL((k_batch1<T, MAXM, KP, QB, MAXG>), dim3(grid), dim3(1024), 0,
                      f.ctx->stream, a);
   return hipGetLastError();
 }
 
-template <typename T, int KP, bool INT4, int MAXG>
+template <typename T, int KP, int QB, int MAXG>
 static hipError_t b1_m(const FusedLaunch& f, const FusedArgs& a) {
   const int nch = f.ctx->d / Chunk<T>::kElems;
   // register slices rounded up to 1, 2, 4, 6 or 8 chunks per lane (the
   // extra ones stay zero and load nothing)
   switch ((nch + 63) / 64) {
-    case 1: return b1_go<T, 1, KP, INT4, MAXG>(f, a);
-    case 2: return b1_go<T, 2, KP, INT4, MAXG>(f, a);
-    case 3: case 4: return b1_go<T, 4, KP, INT4, MAXG>(f, a);
-    case 5: case 6: return b1_go<T, 6, KP, INT4, MAXG>(f, a);
-    case 7: case 8: return b1_go<T, 8, KP, INT4, MAXG>(f, a);
+    case 1: return b1_go<T, 1, KP, QB, MAXG>(f, a);
+    case 2: return b1_go<T, 2, KP, QB, MAXG>(f, a);
+    case 3: case 4: return b1_go<T, 4, KP, QB, MAXG>(f, a);
+    case 5: case 6: return b1_go<T, 6, KP, QB, MAXG>(f, a);
+    case 7: case 8: return b1_go<T, 8, KP, QB, MAXG>(f, a);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, bool INT4, int MAXG>
+template <typename T, int QB, int MAXG>
 static hipError_t b1_k(const FusedLaunch& f, const FusedArgs& a) {
   switch (sel_keys_per_thread(f.ctx->c)) {
-    case 1: return b1_m<T, 1, INT4, MAXG>(f, a);
-    case 2: return b1_m<T, 2, INT4, MAXG>(f, a);
-    case 8: return b1_m<T, 8, INT4, MAXG>(f, a);
-    case 16: return b1_m<T, 16, INT4, MAXG>(f, a);
+    case 1: return b1_m<T, 1, QB, MAXG>(f, a);
+    case 2: return b1_m<T, 2, QB, MAXG>(f, a);
+    case 8: return b1_m<T, 8, QB, MAXG>(f, a);
+    case 16: return b1_m<T, 16, QB, MAXG>(f, a);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t FH_BATCH1_ENTRY(const FusedLaunch& f) {
   const FusedArgs a = fused_args(f);
-  if constexpr (!FH_BATCH1_INT4) {
-    return b1_k<FH_BATCH1_T, false, 1>(f, a);
+  if constexpr (FH_BATCH1_QB == 0) {
+    return b1_k<FH_BATCH1_T, 0, 1>(f, a);
   } else {
     switch ((f.ctx->d / 32 + 63) / 64) {
-      case 1: return b1_k<FH_BATCH1_T, true, 1>(f, a);
-      case 2: return b1_k<FH_BATCH1_T, true, 2>(f, a);
+      case 1: return b1_k<FH_BATCH1_T, FH_BATCH1_QB, 1>(f, a);
+      case 2: return b1_k<FH_BATCH1_T, FH_BATCH1_QB, 2>(f, a);
       default: return hipErrorInvalidValue;
     }
   }

@@ -1,5 +1,5 @@
 // Batch-1 single-launch kernel for fp32 heads.
 #define FH_BATCH1_T float
-#define FH_BATCH1_INT4 false
+#define FH_BATCH1_QB 0
 #define FH_BATCH1_ENTRY launch_batch1_f32
 #include "fh_batch1.inl"

@@ -167,27 +167,58 @@ __device__ __forceinline__ float int4_group_dot(const uint4& qv, float sg,
   return fmaf(sg, fmaf(-8.f, hg.hsum[m], t), acc);
 }
 
-template <int MAXG, int NQ, typename Sink>
-__device__ __forceinline__ void wave_rows_int4(const uint8_t* __restrict__ Q,
-                                               const uint16_t* __restrict__ SG, int d, int lane,
-                                               const HGroups<MAXG> (&hg)[NQ], int nq,
-                                               int64_t r_begin, int64_t r_end, int64_t stride,
-                                               Sink sink) {
+// INT8 (the W8A16 configuration): one group is 32 bytes, two 16-byte loads;
+// bytes become u = q + 128 (xor 0x80 each), converted as unsigned bytes, and
+// sum q h = sum u h - 128 sum_g h.
+template <int MAXG>
+__device__ __forceinline__ float int8_group_dot(const uint4& q0, const uint4& q1, float sg,
+                                                const HGroups<MAXG>& hg, int m, float acc) {
+  const uint32_t w8[8] = {q0.x ^ 0x80808080u, q0.y ^ 0x80808080u, q0.z ^ 0x80808080u,
+                          q0.w ^ 0x80808080u, q1.x ^ 0x80808080u, q1.y ^ 0x80808080u,
+                          q1.z ^ 0x80808080u, q1.w ^ 0x80808080u};
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // dword j holds elements 4j .. 4j + 3
+    t = fmaf((float)(w8[j] & 0xFFu), hg.h[m][4 * j + 0], t);
+    t = fmaf((float)((w8[j] >> 8) & 0xFFu), hg.h[m][4 * j + 1], t);
+    t = fmaf((float)((w8[j] >> 16) & 0xFFu), hg.h[m][4 * j + 2], t);
+    t = fmaf((float)(w8[j] >> 24), hg.h[m][4 * j + 3], t);
+  }
+  return fmaf(sg, fmaf(-128.f, hg.hsum[m], t), acc);
+}
+
+// Stage-1 scores of g32-quantised centroid rows (BITS = 4: packed nibbles,
+// d/2 bytes per row; BITS = 8: int8, d bytes per row) against NQ queries'
+// register-resident groups.  Lane l owns groups l, l + 64, ...; two rows'
+// loads are issued before any math.
+template <int BITS, int MAXG, int NQ, typename Sink>
+__device__ __forceinline__ void wave_rows_q(const uint8_t* __restrict__ Q,
+                                            const uint16_t* __restrict__ SG, int d, int lane,
+                                            const HGroups<MAXG> (&hg)[NQ], int nq,
+                                            int64_t r_begin, int64_t r_end, int64_t stride,
+                                            Sink sink) {
+  static_assert(BITS == 4 || BITS == 8, "INT4 or INT8 codes");
+  constexpr int L = BITS / 4;  // 16-byte loads per group
+  constexpr uint32_t kZero = BITS == 4 ? 0x88888888u : 0x80808080u;  // q = 0 after the offset
   const int G = d / 32;
+  const int64_t row_bytes = (int64_t)d * BITS / 8;
 #pragma unroll 1
   for (int64_t r = r_begin; r < r_end; r += 2 * stride) {
     const int64_t rb = r + stride;
     const bool okb = rb < r_end;
-    const uint4* qa = reinterpret_cast<const uint4*>(Q + r * (d / 2));
-    const uint4* qb = reinterpret_cast<const uint4*>(Q + (okb ? rb : r) * (d / 2));
-    uint4 va[MAXG], vb[MAXG];
+    const uint4* qa = reinterpret_cast<const uint4*>(Q + r * row_bytes);
+    const uint4* qb = reinterpret_cast<const uint4*>(Q + (okb ? rb : r) * row_bytes);
+    uint4 va[MAXG][L], vb[MAXG][L];
     float sa[MAXG], sb[MAXG];
 #pragma unroll
     for (int m = 0; m < MAXG; ++m) {
       const int g = lane + 64 * m;
       const bool ok = g < G;
-      va[m] = ok ? qa[g] : uint4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-      vb[m] = (ok && okb) ? qb[g] : uint4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+#pragma unroll
+      for (int j = 0; j < L; ++j) {
+        va[m][j] = ok ? qa[g * L + j] : uint4{kZero, kZero, kZero, kZero};
+        vb[m][j] = (ok && okb) ? qb[g * L + j] : uint4{kZero, kZero, kZero, kZero};
+      }
       sa[m] = ok ? __half2float(__ushort_as_half(SG[r * G + g])) : 0.f;
       sb[m] = (ok && okb) ? __half2float(__ushort_as_half(SG[rb * G + g])) : 0.f;
     }
@@ -197,8 +228,13 @@ __device__ __forceinline__ void wave_rows_int4(const uint8_t* __restrict__ Q,
       float acc_a = 0.f, acc_b = 0.f;
 #pragma unroll
       for (int m = 0; m < MAXG; ++m) {
-        acc_a = int4_group_dot<MAXG>(va[m], sa[m], hg[q], m, acc_a);
-        acc_b = int4_group_dot<MAXG>(vb[m], sb[m], hg[q], m, acc_b);
+        if constexpr (BITS == 4) {
+          acc_a = int4_group_dot<MAXG>(va[m][0], sa[m], hg[q], m, acc_a);
+          acc_b = int4_group_dot<MAXG>(vb[m][0], sb[m], hg[q], m, acc_b);
+        } else {
+          acc_a = int8_group_dot<MAXG>(va[m][0], va[m][L - 1], sa[m], hg[q], m, acc_a);
+          acc_b = int8_group_dot<MAXG>(vb[m][0], vb[m][L - 1], sb[m], hg[q], m, acc_b);
+        }
       }
       acc_a = wave_sum(acc_a);
       acc_b = wave_sum(acc_b);

@@ -87,6 +87,7 @@ struct fh_engine {
     k.b = b;
     k.d = (int)d;
     k.stream = st;
+    k.qbits = quant == FH_QUANT_INT4_G32 ? 4 : quant == FH_QUANT_INT8_G32 ? 8 : 0;
     return k;
   }
 };
@@ -149,15 +150,20 @@ void free_engine(fh_engine* e) {
 hipError_t launch_stage1(fh_engine* e, hipStream_t st, const fh::KernelCtx& k, const void* h,
                          int64_t B, float* out) {
   const bool int4 = e->quant == FH_QUANT_INT4_G32;
+  const bool int8 = e->quant == FH_QUANT_INT8_G32;
   const bool bf16 = e->dtype == FH_BF16;
   if (bf16 && int4 && B >= fh::kMfmaMinBatchInt4)
     return timed(e, st, "score_int4_mfma",
                  [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out); });
-  if (bf16 && !int4 && B >= fh::kMfmaMinBatchBf16)
+  if (bf16 && int8 && B >= fh::kMfmaMinBatchInt8)
+    return timed(e, st, "score_int8_mfma",
+                 [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out); });
+  if (bf16 && e->quant == FH_QUANT_NONE && B >= fh::kMfmaMinBatchBf16)
     return timed(e, st, "score_mfma", [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out); });
-  return timed(e, st, int4 ? "score_int4" : "score", [&] {
-    return int4 ? fh::launch_score_int4(k, h, (int)B, out) : fh::launch_score(k, h, (int)B, out);
-  });
+  if (int4 || int8)
+    return timed(e, st, int4 ? "score_int4" : "score_int8",
+                 [&] { return fh::launch_score_quant(k, h, (int)B, out); });
+  return timed(e, st, "score", [&] { return fh::launch_score(k, h, (int)B, out); });
 }
 
 fh_status check_common(const fh_engine* e, const void* h, int64_t B) {
@@ -238,7 +244,8 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   if (!out) return fail(FH_EINVAL, "out is NULL");
   if (!E || !C || !C2T) return fail(FH_EINVAL, "E, C and C2T must be non-NULL");
   if (dtype != FH_F32 && dtype != FH_BF16) return fail(FH_EINVAL, "unknown dtype");
-  if (quant != FH_QUANT_NONE && quant != FH_QUANT_INT4_G32) return fail(FH_EINVAL, "unknown quant");
+  if (quant != FH_QUANT_NONE && quant != FH_QUANT_INT4_G32 && quant != FH_QUANT_INT8_G32)
+    return fail(FH_EINVAL, "unknown quant");
   if (v <= 0 || d <= 0 || c <= 0) return fail(FH_EINVAL, "v, d and c must be positive");
   if (v % c != 0) return fail(FH_EINVAL, "v must be a multiple of c (balanced clusters)");
   if (v >= (int64_t(1) << 31)) return fail(FH_EUNSUPPORTED, "v must be below 2^31");
@@ -247,8 +254,8 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   if (d % epc != 0)
     return fail(FH_EINVAL, dtype == FH_BF16 ? "bf16 needs d % 8 == 0" : "f32 needs d % 4 == 0");
   if (d > 64 * 8 * epc) return fail(FH_EUNSUPPORTED, "d too large for this build");
-  if (quant == FH_QUANT_INT4_G32 && d % 32 != 0)
-    return fail(FH_EUNSUPPORTED, "INT4 g32 needs d % 32 == 0");
+  if (quant != FH_QUANT_NONE && d % 32 != 0)
+    return fail(FH_EUNSUPPORTED, "g32 quantisation needs d % 32 == 0");
   if (max_batch < 1 || max_batch > 65535) return fail(FH_EINVAL, "max_batch outside [1, 65535]");
   if (!aligned16(E) || !aligned16(C)) return fail(FH_EINVAL, "E and C must be 16-byte aligned");
   const int64_t b = v / c;
@@ -307,29 +314,30 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   r = fh::launch_permute_rows(e->ctx(st), e->Ec);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "cluster-contiguous E"); }
 
-  if (quant == FH_QUANT_INT4_G32) {
+  if (quant != FH_QUANT_NONE) {
+    const int bits = quant == FH_QUANT_INT4_G32 ? 4 : 8;
     int* bad = nullptr;
-    r = hipMalloc((void**)&e->cq, (size_t)(c * d / 2));
+    r = hipMalloc((void**)&e->cq, (size_t)(c * d * bits / 8));
     if (r == hipSuccess) r = hipMalloc((void**)&e->csig, sizeof(uint16_t) * (size_t)(c * d / 32));
     if (r == hipSuccess) r = hipMalloc((void**)&bad, sizeof(int));
     if (r == hipSuccess) r = hipMemsetAsync(bad, 0, sizeof(int), st);
-    if (r == hipSuccess) r = fh::launch_quant_int4(e->ctx(st), bad);
+    if (r == hipSuccess) r = fh::launch_quant(e->ctx(st), bad);
     int hbad = 0;
     if (r == hipSuccess) r = hipMemcpyAsync(&hbad, bad, sizeof(int), hipMemcpyDeviceToHost, st);
     if (r == hipSuccess) r = hipStreamSynchronize(st);
     (void)hipFree(bad);
-    if (r != hipSuccess) { free_engine(e); return hip_fail(r, "INT4 quantisation"); }
-    if (hbad) { free_engine(e); return fail(FH_EINVAL, "a centroid group's INT4 scale overflows fp16"); }
-    if (dtype == FH_BF16) {  // the MFMA copy for batched stage 1
-      r = hipMalloc((void**)&e->cq_mfma, (size_t)(c * fh::mfma_int4_row_bytes((int)d)));
+    if (r != hipSuccess) { free_engine(e); return hip_fail(r, "centroid quantisation"); }
+    if (hbad) { free_engine(e); return fail(FH_EINVAL, "a centroid group's scale overflows fp16"); }
+    if (dtype == FH_BF16) {  // the MFMA layouts for batched stage 1 (INT8 rows are read as stored)
+      if (bits == 4) r = hipMalloc((void**)&e->cq_mfma, (size_t)(c * fh::mfma_int4_row_bytes((int)d)));
       if (r == hipSuccess)
         r = hipMalloc((void**)&e->sig_mfma,
                       sizeof(uint16_t) * (size_t)((d / 32) * fh::mfma_sig_ld(c)));
       if (r == hipSuccess) r = fh::launch_mfma_relayout(e->ctx(st), e->cq_mfma, e->sig_mfma);
       if (r == hipSuccess) r = hipStreamSynchronize(st);
-      if (r != hipSuccess) { free_engine(e); return hip_fail(r, "INT4 MFMA layout"); }
+      if (r != hipSuccess) { free_engine(e); return hip_fail(r, "MFMA layout"); }
     }
-    e->C = nullptr;  // not borrowed in INT4 mode
+    e->C = nullptr;  // not borrowed in quantised modes
   } else {
     r = hipStreamSynchronize(st);
     if (r != hipSuccess) { free_engine(e); return hip_fail(r, "create"); }
@@ -380,7 +388,6 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
   if (B == 1 && e->path == FH_PATH_AUTO && fh::batch1_fits(p, e->b, e->cus)) {
     fh::FusedLaunch f{};
     f.ctx = &k;
-    f.int4 = e->quant == FH_QUANT_INT4_G32;
     f.cus = e->cus;
     f.h = h;
     f.p = (int)p;
@@ -502,6 +509,20 @@ fh_status fh_get_int4(fh_engine* e, uint8_t* packed, uint16_t* scales, void* str
     r = hipMemcpyAsync(scales, e->csig, sizeof(uint16_t) * (size_t)(e->c * e->d / 32),
                        hipMemcpyDeviceToDevice, st);
   return r == hipSuccess ? FH_OK : hip_fail(r, "copy INT4 centroids");
+}
+
+fh_status fh_get_int8(fh_engine* e, int8_t* codes, uint16_t* scales, void* stream) {
+  g_err.clear();
+  if (!e) return fail(FH_EINVAL, "engine is NULL");
+  if (e->quant != FH_QUANT_INT8_G32) return fail(FH_EINVAL, "engine is not INT8");
+  if (!codes || !scales) return fail(FH_EINVAL, "NULL output");
+  DeviceGuard g(e->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t r = hipMemcpyAsync(codes, e->cq, (size_t)(e->c * e->d), hipMemcpyDeviceToDevice, st);
+  if (r == hipSuccess)
+    r = hipMemcpyAsync(scales, e->csig, sizeof(uint16_t) * (size_t)(e->c * e->d / 32),
+                       hipMemcpyDeviceToDevice, st);
+  return r == hipSuccess ? FH_OK : hip_fail(r, "copy INT8 centroids");
 }
 
 fh_status fh_profile_begin(fh_engine* e, int64_t max_launches) {

@@ -33,18 +33,21 @@ struct KernelCtx {
   const uint8_t* cq;
   const uint16_t* csig;
   const uint8_t* cq_mfma;    // INT4 codes re-laid for the MFMA tiles, or null
-  const uint16_t* sig_mfma;  // INT4 scales group-major [G x mfma_sig_ld(c)], or null
+  const uint16_t* sig_mfma;  // INT4 / INT8 scales group-major [G x mfma_sig_ld(c)], or null
   int64_t v, c, b;
   int d;
   hipStream_t stream;
+  int qbits = 0;  // stage-1 codes: 0 (C as stored), 4 (INT4 g32) or 8 (INT8 g32)
 };
 
 int64_t rows_blocks(int64_t nrows, int rpw);
 
-hipError_t launch_quant_int4(const KernelCtx& k, int* bad);
+// g32 quantisation of C into cq / csig (k.qbits = 4 or 8)
+hipError_t launch_quant(const KernelCtx& k, int* bad);
 hipError_t launch_permute_rows(const KernelCtx& k, void* out);
 hipError_t launch_score(const KernelCtx& k, const void* h, int B, float* out);
-hipError_t launch_score_int4(const KernelCtx& k, const void* h, int B, float* out);
+// stage-1 scores from the g32 codes (k.qbits = 4 or 8), on the vector units
+hipError_t launch_score_quant(const KernelCtx& k, const void* h, int B, float* out);
 float select_quantile(int64_t c, int64_t p);
 // S [B x ldS]: the p probes of each query, ascending.  With mbits/mpre non-
 // null also the probe bitsets word-major, mbits[w * B + q], and the probes of
@@ -60,6 +63,7 @@ hipError_t launch_dense(const KernelCtx& k, const void* h, int B, int token_samp
 // Matrix-core (MFMA) paths for batches of bf16 queries.
 constexpr int kMfmaMinBatchBf16 = 8;  // bf16 stage 1 and the dense head
 constexpr int kMfmaMinBatchInt4 = 2;  // INT4 stage 1
+constexpr int kMfmaMinBatchInt8 = 16;  // INT8 stage 1 (measured: vector units 21 us at B = 8, MFMA 27 us)
 int64_t mfma_int4_row_bytes(int d);
 int64_t mfma_blocks(int64_t R);  // row blocks (partials per query) of the MFMA dense head
 int64_t mfma_sig_ld(int64_t c);
@@ -84,7 +88,6 @@ hipError_t launch_finish(const KernelCtx& k, const Part* parts, int B, int64_t n
 // finish by workgroups in dispatch order, handed over through tagged words).
 struct FusedLaunch {
   const KernelCtx* ctx;
-  bool int4;
   int cus;                        // compute units of the device
   const void* h;
   int p;
@@ -123,6 +126,8 @@ hipError_t launch_batch1_bf16(const FusedLaunch& f);
 hipError_t launch_batch1_bf16_int4(const FusedLaunch& f);
 hipError_t launch_batch1_f32(const FusedLaunch& f);
 hipError_t launch_batch1_f32_int4(const FusedLaunch& f);
+hipError_t launch_batch1_bf16_int8(const FusedLaunch& f);
+hipError_t launch_batch1_f32_int8(const FusedLaunch& f);
 
 // Batch-1 sizing: rows per workgroup are a multiple of kBatch1RowsUnit
 // (one row for each of the 16 waves), large enough that a stage needs at

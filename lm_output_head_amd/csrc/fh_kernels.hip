@@ -24,11 +24,12 @@ namespace fh {
 // to even); q = 0 where sigma = 0.  Nibbles are packed two's-complement,
 // element 2m in the low nibble of byte m.  *bad is set if a scale overflows.
 // ======================================================================
-template <typename T>
-__global__ __launch_bounds__(256) void k_quant_int4(const T* __restrict__ C, int64_t c, int d,
-                                                    uint8_t* __restrict__ qout,
-                                                    uint16_t* __restrict__ sout,
-                                                    int* __restrict__ bad) {
+template <typename T, int BITS>
+__global__ __launch_bounds__(256) void k_quant_g32(const T* __restrict__ C, int64_t c, int d,
+                                                   uint8_t* __restrict__ qout,
+                                                   uint16_t* __restrict__ sout,
+                                                   int* __restrict__ bad) {
+  constexpr int kQmax = BITS == 4 ? 7 : 127;
   const int G = d / 32;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= c * G) return;
@@ -42,18 +43,26 @@ __global__ __launch_bounds__(256) void k_quant_int4(const T* __restrict__ C, int
     x[i] = load_elem<T>(C, base + i);
     amax = fmaxf(amax, fabsf(x[i]));
   }
-  const __half hs = __float2half_rn(amax / 7.0f);
+  const __half hs = __float2half_rn(amax / (float)kQmax);
   const float s = __half2float(hs);
   if (!isfinite(s)) atomicOr(bad, 1);
-  uint32_t words[4] = {0u, 0u, 0u, 0u};
+  constexpr int kWords = BITS;  // 32 codes of BITS bits in 32-bit words
+  uint32_t words[kWords];
+#pragma unroll
+  for (int j = 0; j < kWords; ++j) words[j] = 0u;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     int qi = 0;
-    if (s > 0.f) qi = (int)fminf(fmaxf(rintf(x[i] / s), -7.f), 7.f);
-    words[i >> 3] |= ((uint32_t)qi & 0xFu) << (4 * (i & 7));
+    if (s > 0.f) qi = (int)fminf(fmaxf(rintf(x[i] / s), (float)-kQmax), (float)kQmax);
+    if (BITS == 4)
+      words[i >> 3] |= ((uint32_t)qi & 0xFu) << (4 * (i & 7));
+    else
+      words[i >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (i & 3));
   }
-  uint4* dst = reinterpret_cast<uint4*>(qout + row * (d / 2) + (int64_t)g * 16);
-  *dst = uint4{words[0], words[1], words[2], words[3]};
+  uint4* dst = reinterpret_cast<uint4*>(qout + row * ((int64_t)d * BITS / 8) + (int64_t)g * 4 * BITS);
+#pragma unroll
+  for (int j = 0; j < kWords / 4; ++j)
+    dst[j] = uint4{words[4 * j], words[4 * j + 1], words[4 * j + 2], words[4 * j + 3]};
   sout[row * G + g] = __half_as_ushort(hs);
 }
 
@@ -153,8 +162,8 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   }
 }
 
-template <typename T, int MAXG, int NQ, int RPW>
-__global__ __launch_bounds__(256) void k_score_int4(const uint8_t* __restrict__ Q,
+template <typename T, int BITS, int MAXG, int NQ, int RPW>
+__global__ __launch_bounds__(256) void k_score_q(const uint8_t* __restrict__ Q,
                                                     const uint16_t* __restrict__ SG, int64_t c,
                                                     int d, const T* __restrict__ H, int B,
                                                     float* __restrict__ out) {
@@ -171,7 +180,7 @@ __global__ __launch_bounds__(256) void k_score_int4(const uint8_t* __restrict__ 
   auto sink = [&](int q, int64_t r, int64_t, float s) {
     if (lane == 0) out[(int64_t)(q0 + q) * c + r] = s;
   };
-  wave_rows_int4<MAXG, NQ>(Q, SG, d, lane, hg, nq, r0, r1, 1, sink);
+  wave_rows_q<BITS, MAXG, NQ>(Q, SG, d, lane, hg, nq, r0, r1, 1, sink);
 }
 
 template <int KP>
@@ -264,8 +273,8 @@ hipError_t launch_score(const KernelCtx& k, const void* h, int B, float* out) {
   return k.bf16 ? score_dispatch<uint16_t>(k, h, B, out) : score_dispatch<float>(k, h, B, out);
 }
 
-template <typename T, int NQ>
-static hipError_t int4_launch(const KernelCtx& k, const void* h, int B, float* out) {
+template <typename T, int BITS, int NQ>
+static hipError_t quant_score_launch(const KernelCtx& k, const void* h, int B, float* out) {
   const int G = k.d / 32;
   const int maxg = (G + 63) / 64;
   const int64_t gx = (k.c + 4 * kInt4RPW - 1) / (4 * kInt4RPW);
@@ -273,7 +282,7 @@ static hipError_t int4_launch(const KernelCtx& k, const void* h, int B, float* o
   const T* hp = static_cast<const T*>(h);
   switch (maxg) {
 #define FH_CASE(MG) \
-  case MG: hipLaunchKernelGGL((k_score_int4<T, MG, NQ, kInt4RPW>), grid, dim3(256), 0, k.stream, k.cq, k.csig, k.c, k.d, hp, B, out); break;
+  case MG: hipLaunchKernelGGL((k_score_q<T, BITS, MG, NQ, kInt4RPW>), grid, dim3(256), 0, k.stream, k.cq, k.csig, k.c, k.d, hp, B, out); break;
     FH_CASE(1) FH_CASE(2) FH_CASE(3) FH_CASE(4)
 #undef FH_CASE
     default: return hipErrorInvalidValue;
@@ -281,23 +290,40 @@ static hipError_t int4_launch(const KernelCtx& k, const void* h, int B, float* o
   return hipGetLastError();
 }
 
-hipError_t launch_score_int4(const KernelCtx& k, const void* h, int B, float* out) {
-  if (k.bf16) return B == 1 ? int4_launch<uint16_t, 1>(k, h, B, out) : int4_launch<uint16_t, 2>(k, h, B, out);
-  return B == 1 ? int4_launch<float, 1>(k, h, B, out) : int4_launch<float, 2>(k, h, B, out);
+template <int BITS>
+static hipError_t quant_score(const KernelCtx& k, const void* h, int B, float* out) {
+  if (k.bf16)
+    return B == 1 ? quant_score_launch<uint16_t, BITS, 1>(k, h, B, out)
+                  : quant_score_launch<uint16_t, BITS, 2>(k, h, B, out);
+  return B == 1 ? quant_score_launch<float, BITS, 1>(k, h, B, out)
+                : quant_score_launch<float, BITS, 2>(k, h, B, out);
 }
 
-hipError_t launch_quant_int4(const KernelCtx& k, int* bad) {
+hipError_t launch_score_quant(const KernelCtx& k, const void* h, int B, float* out) {
+  if (k.qbits == 4) return quant_score<4>(k, h, B, out);
+  if (k.qbits == 8) return quant_score<8>(k, h, B, out);
+  return hipErrorInvalidValue;
+}
+
+template <int BITS>
+static hipError_t quant_launch(const KernelCtx& k, int* bad) {
   const int64_t n = k.c * (k.d / 32);
   const dim3 grid((unsigned)((n + 255) / 256));
   if (k.bf16)
-    hipLaunchKernelGGL((k_quant_int4<uint16_t>), grid, dim3(256), 0, k.stream,
+    hipLaunchKernelGGL((k_quant_g32<uint16_t, BITS>), grid, dim3(256), 0, k.stream,
                        static_cast<const uint16_t*>(k.C), k.c, k.d, const_cast<uint8_t*>(k.cq),
                        const_cast<uint16_t*>(k.csig), bad);
   else
-    hipLaunchKernelGGL((k_quant_int4<float>), grid, dim3(256), 0, k.stream,
+    hipLaunchKernelGGL((k_quant_g32<float, BITS>), grid, dim3(256), 0, k.stream,
                        static_cast<const float*>(k.C), k.c, k.d, const_cast<uint8_t*>(k.cq),
                        const_cast<uint16_t*>(k.csig), bad);
   return hipGetLastError();
+}
+
+hipError_t launch_quant(const KernelCtx& k, int* bad) {
+  if (k.qbits == 4) return quant_launch<4>(k, bad);
+  if (k.qbits == 8) return quant_launch<8>(k, bad);
+  return hipErrorInvalidValue;
 }
 
 // Standard-normal upper quantile z with P(Z > z) = select_target(p) / c: the
@@ -417,8 +443,12 @@ bool batch1_fits(int64_t p, int64_t b, int cus) {
 }
 
 hipError_t launch_batch1(const FusedLaunch& f) {
-  if (f.ctx->bf16) return f.int4 ? launch_batch1_bf16_int4(f) : launch_batch1_bf16(f);
-  return f.int4 ? launch_batch1_f32_int4(f) : launch_batch1_f32(f);
+  switch (f.ctx->qbits) {
+    case 0: return f.ctx->bf16 ? launch_batch1_bf16(f) : launch_batch1_f32(f);
+    case 4: return f.ctx->bf16 ? launch_batch1_bf16_int4(f) : launch_batch1_f32_int4(f);
+    case 8: return f.ctx->bf16 ? launch_batch1_bf16_int8(f) : launch_batch1_f32_int8(f);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fh

@@ -68,10 +68,26 @@ __device__ __forceinline__ uint4 int4_fragment(uint32_t w) {
                __builtin_amdgcn_perm(c43, t1, 0x04010400u), __builtin_amdgcn_perm(c43, t1, 0x04030402u)};
 }
 
+// Eight int8 codes (element i in byte i of w) as the A fragment of bf16
+// values q (|q| <= 127 is exact in bf16): sign-extend, convert, keep the
+// high half.
+__device__ __forceinline__ uint4 int8_fragment(const uint2& w) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t word = j < 2 ? w.x : w.y;
+    const int sh = 16 * (j & 1);
+    const float lo = (float)(int8_t)((word >> sh) & 0xFFu);
+    const float hi = (float)(int8_t)((word >> (sh + 8)) & 0xFFu);
+    o[j] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
+}
+
 struct MfmaArgs {
-  const void* A;           // bf16 rows [R x d], or INT4 rows in the MFMA layout
-  const uint16_t* sigT;    // INT4: fp16 scales [G x ldsig], group-major
-  int64_t ldsig;           // INT4: rows per scale row (R rounded up to 16)
+  const void* A;           // bf16 rows [R x d], INT4 rows in the MFMA layout, or int8 rows [R x d]
+  const uint16_t* sigT;    // INT4 / INT8: fp16 scales [G x ldsig], group-major
+  int64_t ldsig;           // INT4 / INT8: rows per scale row (R rounded up to 128)
   int64_t a_row_bytes;     // INT4: bytes per re-laid row (64 per 4 groups)
   int64_t R;
   int d;
@@ -87,7 +103,7 @@ struct MfmaArgs {
 
 constexpr int kHRow = 128 + 8;  // LDS row of a staged h block (bf16), padded
 
-template <int NT, int MT, bool INT4, bool EPI>
+template <int NT, int MT, int QB, bool EPI>
 __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
   constexpr int QW = 16 * NT;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t sH[2][QW * kHRow];
@@ -129,7 +145,7 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
 #pragma unroll
   for (int m = 0; m < MT; ++m) ra[m] = min(rbase + 16 * m + col, a.R - 1);
 
-  if (!INT4) {
+  if constexpr (QB == 0) {
     const uint16_t* A = static_cast<const uint16_t*>(a.A);
     uint4 av[2][MT][4];
     auto load_a = [&](int kb, uint4 (&dst)[MT][4]) {
@@ -177,7 +193,7 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
         __syncthreads();
       }
     }
-  } else {
+  } else if constexpr (QB == 4) {
     const uint8_t* A = static_cast<const uint8_t*>(a.A);
     const int G = a.d / 32;
     const uint4 neg136 = uint4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
@@ -218,6 +234,77 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
           for (int n = 0; n < NT; ++n) {
             f32x4 part = mfma16(af, bfr[n], f32x4{0.f, 0.f, 0.f, 0.f});
             part = mfma16(neg136, bfr[n], part);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(sig[i], part[i], acc[m][n][i]);
+          }
+        }
+      }
+    };
+    Blk x0, x1;
+    load_h(0);
+    load_a(0, x0);
+    store_h(0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; kb += 2) {
+      if (kb + 1 < nkb) {
+        load_h(kb + 1);
+        load_a(kb + 1, x1);
+      }
+      compute(kb, 0, x0);
+      if (kb + 1 < nkb) store_h(1);
+      __syncthreads();
+      if (kb + 1 < nkb) {
+        if (kb + 2 < nkb) {
+          load_h(kb + 2);
+          load_a(kb + 2, x0);
+        }
+        compute(kb + 1, 1, x1);
+        if (kb + 2 < nkb) store_h(0);
+        __syncthreads();
+      }
+    }
+  } else {
+    // INT8 rows, row-major (d bytes per row): MFMA step s of block kb is
+    // group 4 kb + s; lane group g takes its elements 8 g .. + 7 (8 bytes),
+    // widened exactly to bf16; the group's fp16 scales then scale the tile
+    // into the running score with one FMA per element
+    static_assert(QB == 8, "QB is 0, 4 or 8");
+    const uint8_t* A = static_cast<const uint8_t*>(a.A);
+    const int G = a.d / 32;
+    struct Blk {
+      uint2 w[MT][4];
+      uint2 sg[MT][4];
+    };
+    auto load_a = [&](int kb, Blk& x) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int grp = min(4 * kb + s, G - 1);
+          x.w[m][s] = *reinterpret_cast<const uint2*>(A + ra[m] * a.d + 32 * grp + 8 * g);
+          x.sg[m][s] = *reinterpret_cast<const uint2*>(a.sigT + (int64_t)grp * a.ldsig + rbase +
+                                                       16 * m + 4 * g);
+        }
+    };
+    auto compute = [&](int kb, int buf, const Blk& x) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (4 * kb + s >= G) break;
+        uint4 bfr[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          bfr[n] = *reinterpret_cast<const uint4*>(&sH[buf][(16 * n + col) * kHRow + 32 * s + 8 * g]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const uint4 af = int8_fragment(x.w[m][s]);
+          const float sig[4] = {
+              __half2float(__ushort_as_half((uint16_t)(x.sg[m][s].x & 0xFFFFu))),
+              __half2float(__ushort_as_half((uint16_t)(x.sg[m][s].x >> 16))),
+              __half2float(__ushort_as_half((uint16_t)(x.sg[m][s].y & 0xFFFFu))),
+              __half2float(__ushort_as_half((uint16_t)(x.sg[m][s].y >> 16)))};
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const f32x4 part = mfma16(af, bfr[n], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(sig[i], part[i], acc[m][n][i]);
           }
@@ -479,16 +566,21 @@ __global__ __launch_bounds__(256) void k_transpose_sig(const uint16_t* __restric
 // ----------------------------------------------------------------- host ---
 
 int64_t mfma_int4_row_bytes(int d) { return (int64_t)((d / 32 + 3) / 4) * 64; }
-int64_t mfma_sig_ld(int64_t c) { return (c + 15) / 16 * 16; }
+// Rows per group of the group-major scales: every row a workgroup of the
+// GEMM covers (64 MT <= 128 rows per workgroup), zero past c, so the scale
+// loads of the last workgroup stay inside the table.
+int64_t mfma_sig_ld(int64_t c) { return (c + 127) / 128 * 128; }
 
 hipError_t launch_mfma_relayout(const KernelCtx& k, uint8_t* cq_mfma, uint16_t* sigT) {
   const int G = k.d / 32;
-  const int64_t rb = mfma_int4_row_bytes(k.d);
-  const int64_t chunks = k.c * (rb / 16);
-  hipLaunchKernelGGL(k_relayout_int4, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
-                     k.stream, k.cq, k.c, G, cq_mfma, rb);
-  hipError_t r = hipGetLastError();
-  if (r != hipSuccess) return r;
+  if (k.qbits == 4) {  // INT8 rows are read as stored
+    const int64_t rb = mfma_int4_row_bytes(k.d);
+    const int64_t chunks = k.c * (rb / 16);
+    hipLaunchKernelGGL(k_relayout_int4, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                       k.stream, k.cq, k.c, G, cq_mfma, rb);
+    const hipError_t r = hipGetLastError();
+    if (r != hipSuccess) return r;
+  }
   const int64_t ld = mfma_sig_ld(k.c);
   hipLaunchKernelGGL(k_transpose_sig, dim3((unsigned)((G * ld + 255) / 256)), dim3(256), 0,
                      k.stream, k.csig, k.c, G, ld, sigT);
@@ -512,30 +604,30 @@ static GemmShape gemm_shape(int64_t R, int B, int cus) {
   return s;
 }
 
-template <int NT, int MT, bool INT4, bool EPI>
+template <int NT, int MT, int QB, bool EPI>
 static hipError_t gemm_go(const MfmaArgs& a, hipStream_t st, int64_t* nblocks) {
   const dim3 grid((unsigned)((a.R + 64 * MT - 1) / (64 * MT)),
                   (unsigned)((a.B + 16 * NT - 1) / (16 * NT)));
   if (nblocks) *nblocks = grid.x;
-  hipLaunchKernelGGL((k_mfma_gemm<NT, MT, INT4, EPI>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_mfma_gemm<NT, MT, QB, EPI>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int MT, bool INT4, bool EPI>
+template <int MT, int QB, bool EPI>
 static hipError_t gemm_nt(const MfmaArgs& a, int nt, hipStream_t st, int64_t* nblocks) {
   switch (nt) {
-    case 1: return gemm_go<1, MT, INT4, EPI>(a, st, nblocks);
-    case 2: return gemm_go<2, MT, INT4, EPI>(a, st, nblocks);
-    case 4: return gemm_go<4, MT, INT4, EPI>(a, st, nblocks);
-    default: return gemm_go<8, MT, INT4, EPI>(a, st, nblocks);
+    case 1: return gemm_go<1, MT, QB, EPI>(a, st, nblocks);
+    case 2: return gemm_go<2, MT, QB, EPI>(a, st, nblocks);
+    case 4: return gemm_go<4, MT, QB, EPI>(a, st, nblocks);
+    default: return gemm_go<8, MT, QB, EPI>(a, st, nblocks);
   }
 }
 
-template <bool INT4, bool EPI>
+template <int QB, bool EPI>
 static hipError_t mfma_dispatch(const MfmaArgs& a, int cus, hipStream_t st, int64_t* nblocks) {
   const GemmShape s = gemm_shape(a.R, a.B, cus);
-  return s.mt == 2 ? gemm_nt<2, INT4, EPI>(a, s.nt, st, nblocks)
-                   : gemm_nt<1, INT4, EPI>(a, s.nt, st, nblocks);
+  return s.mt == 2 ? gemm_nt<2, QB, EPI>(a, s.nt, st, nblocks)
+                   : gemm_nt<1, QB, EPI>(a, s.nt, st, nblocks);
 }
 
 int64_t mfma_blocks(int64_t R) { return (R + 63) / 64; }
@@ -544,13 +636,17 @@ hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, 
   MfmaArgs a{};
   a.R = k.c; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
   a.out = out; a.ld_out = k.c;
-  if (k.cq_mfma) {
+  if (k.qbits == 4) {
     a.A = k.cq_mfma; a.sigT = k.sig_mfma; a.ldsig = mfma_sig_ld(k.c);
     a.a_row_bytes = mfma_int4_row_bytes(k.d);
-    return mfma_dispatch<true, false>(a, cus, k.stream, nullptr);
+    return mfma_dispatch<4, false>(a, cus, k.stream, nullptr);
+  }
+  if (k.qbits == 8) {
+    a.A = k.cq; a.sigT = k.sig_mfma; a.ldsig = mfma_sig_ld(k.c);
+    return mfma_dispatch<8, false>(a, cus, k.stream, nullptr);
   }
   a.A = k.C;
-  return mfma_dispatch<false, false>(a, cus, k.stream, nullptr);
+  return mfma_dispatch<0, false>(a, cus, k.stream, nullptr);
 }
 
 int64_t gather_cm_blocks(int64_t c, int) { return (c + kCmClusters - 1) / kCmClusters; }
@@ -586,7 +682,7 @@ hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, 
   a.A = k.E; a.R = k.v; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
   a.out = out_logits; a.ld_out = k.v;
   a.token_sample = token_sample; a.tprime = tprime; a.seed = seed; a.parts = parts;
-  return mfma_dispatch<false, true>(a, cus, k.stream, nparts);
+  return mfma_dispatch<0, true>(a, cus, k.stream, nparts);
 }
 
 }  // namespace fh

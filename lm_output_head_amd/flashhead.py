@@ -16,10 +16,10 @@ import torch
 
 from . import _abi
 from ._abi import (FH_BF16, FH_F32, FH_PROBE_SAMPLE, FH_PROBE_TOPK, FH_QUANT_INT4_G32,  # noqa: F401
-                   FH_QUANT_NONE, FH_TOKEN_ARGMAX, FH_TOKEN_SAMPLE, FlashHeadError, check)
+                   FH_QUANT_INT8_G32, FH_QUANT_NONE, FH_TOKEN_ARGMAX, FH_TOKEN_SAMPLE, FlashHeadError, check)
 
 _DTYPES = {torch.float32: FH_F32, torch.bfloat16: FH_BF16}
-_QUANTS = {"none": FH_QUANT_NONE, "int4": FH_QUANT_INT4_G32}
+_QUANTS = {"none": FH_QUANT_NONE, "int4": FH_QUANT_INT4_G32, "int8": FH_QUANT_INT8_G32}
 
 
 def _ptr(t):
@@ -93,6 +93,10 @@ def fh_dense_forward(eng, h, mode, temperature, seed, out_token, out_token_logit
 
 def fh_get_int4(eng, packed, scales, stream=None) -> None:
     check(_abi.load().fh_get_int4(eng, _ptr(packed), _ptr(scales), _stream(stream)))
+
+
+def fh_get_int8(eng, codes, scales, stream=None) -> None:
+    check(_abi.load().fh_get_int8(eng, _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def fh_set_path(eng, path: int) -> None:
@@ -233,3 +237,9 @@ class FlashHead:
         scales = self._alloc((self.c, self.d // 32), torch.int16)
         fh_get_int4(self.eng, packed, scales, stream)
         return packed, scales
+
+    def int8(self, stream=None):
+        codes = self._alloc((self.c, self.d), torch.int8)
+        scales = self._alloc((self.c, self.d // 32), torch.int16)
+        fh_get_int8(self.eng, codes, scales, stream)
+        return codes, scales

@@ -259,8 +259,36 @@ def test_int4_batched_probe_sweep(llama, B, p):
     head.close()
 
 
+# --------------------------------------------------------- INT8 (W8A16) ---
+
+def test_int8_codes_bit_exact(llama):
+    pb = llama
+    head, _ = _engine(pb, quant="int8")
+    say("int8 codes")
+    codes, scales = head.int8()
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
+    q, sigma = oracle.quantize_int8_g32(pb.C)
+    assert np.array_equal(scales, sigma.view(np.uint16))
+    assert np.array_equal(codes, q)
+    head.close()
+
+
+@pytest.mark.parametrize("B,p", [(1, 512), (3, 64), (8, 512)])
+def test_int8_batched_probe_sweep(llama, B, p):
+    pb = llama
+    head, H = _engine(pb, quant="int8", max_batch=8)
+    ref = _oracle(pb, "int8")
+    say("int8 B", B, "p", p)
+    out = host(head.forward(H[:B], p, want_clusters=True, want_retrieved=True))
+    assert_report(parity.check_forward(ref, pb.H[:B], p, TOPK, 1.0, 0, out), f"int8 B={B} p={p}")
+    s = host({"s": head.score(H[:B])})["s"]
+    assert_report(parity.check_scores(ref.C_hat, pb.H[:B], s), "int8 scores")
+    head.close()
+
+
 @pytest.mark.parametrize("v,d,c,quant", [
     (2000, 160, 250, "int4"),   # 5 INT4 groups (a partial block of 4); c not a multiple of 16
+    (2000, 160, 250, "int8"),   # 5 INT8 groups of two 16-byte loads each (vector units at every B)
     (2560, 96, 160, "int4"),    # 3 groups: a single partial block
     (3000, 1032, 1000, "none"),  # bf16 d with a 8-element tail after 128-element blocks
     (1200, 40, 75, "none"),      # d below one 128-element block
@@ -352,6 +380,8 @@ def test_argument_errors_are_reported():
     ("tiny", "none", PSAMPLE | TSAMPLE, 0.8),
     ("llama32_1b", "none", TOPK, 1.0),
     ("llama32_1b", "int4", TOPK, 1.0),
+    ("llama32_1b", "int8", TOPK, 1.0),
+    ("tiny", "int8", PSAMPLE | TSAMPLE, 0.8),
     ("llama32_1b", "none", TSAMPLE, 0.7),
     ("gemma3_1b", "none", PSAMPLE | TSAMPLE, 1.0),
 ])
