@@ -35,3 +35,4 @@ from .flashhead_oracle import (  # noqa: F401
 )
 from .philox import gumbel, philox4x32_10, uniform_from_word  # noqa: F401
 from . import cluster_oracle  # noqa: F401,E402  (balanced k-means, the offline step)
+from . import spec_oracle  # noqa: F401,E402  (speculative sampling: FlashHead draft, dense target)

@@ -22,7 +22,9 @@ of (seed, row, index, stage) to a counter is fixed here:
     u       = ((word >> 9) + 0.5) * 2^-23      in (0, 1), exact in float32
     G       = -ln(-ln u)                       a standard Gumbel variate
 
-Stage 0 keys probe (cluster) sampling, stage 1 keys token sampling.
+Stage 0 keys probe (cluster) sampling, stage 1 keys token sampling; the
+speculative verification (spec_oracle) keys its acceptance uniform with
+stage 2 and its residual draw with stage 3.
 """
 
 from __future__ import annotations
