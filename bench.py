@@ -54,6 +54,9 @@ def parse():
                          "instead of the head, one JSON line of its own")
     ap.add_argument("--cluster-iters", type=int, default=5)
     ap.add_argument("--cluster-runs", type=int, default=2)
+    ap.add_argument("--spec", type=int, default=0, metavar="K",
+                    help="time the speculative verification of K draft positions (fh_spec_verify) "
+                         "beside K single-position drafts and the dense head at B=K; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of known size (to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run) and exit")
@@ -281,6 +284,82 @@ def cluster_main(args):
     print(json.dumps(res), flush=True)
 
 
+def spec_main(args):
+    """Speculative decoding with FlashHead drafts: K draft calls at B = 1
+    (sampled tokens, their probes kept) and one verification of the K
+    positions against the dense head, timed with HIP events on the launch
+    stream; beside it, the dense head sampling the same K positions."""
+    import numpy as np
+    import torch
+
+    from lm_output_head_amd import flashhead as fhb
+    from synth import SHAPES, make_problem
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    shape = SHAPES[args.shape]
+    K, p, T = args.spec, args.p, args.temperature
+    pb = make_problem(shape, nq=max(K, 16))
+    bf16 = shape.dtype == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+
+    def dev(x):
+        if bf16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+    E, C, H = dev(pb.E_bits if bf16 else pb.E), dev(pb.C_bits if bf16 else pb.C), \
+        dev(pb.H_bits if bf16 else pb.H)
+    head = fhb.FlashHead(E, C, pb.C2T, quant=args.quant, max_batch=K)
+    Hk = H[:K].contiguous()
+    st = torch.cuda.current_stream()
+    drafts = [head.forward(Hk[i:i + 1], p, mode=2, temperature=T, seed=100 + i, want_clusters=True)
+              for i in range(K)]
+    draft = {k: torch.cat([d[k] for d in drafts]) for k in ("clusters", "token", "lse")}
+
+    def timed(fn, n):
+        for _ in range(5):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(st)
+        for _ in range(n):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    steps = max(20, min(args.steps, 400))
+    draft_us = timed(lambda: head.forward(Hk[:1], p, mode=2, temperature=T, seed=1,
+                                          want_clusters=True), steps)
+    verify_us = timed(lambda: head.spec_verify(Hk, draft, p, T, 7), steps)
+    dense_us = timed(lambda: head.dense(Hk, mode=2, temperature=T, seed=7), steps)
+    dense1_us = timed(lambda: head.dense(Hk[:1], mode=2, temperature=T, seed=7), steps)
+    acc = torch.cat([head.spec_verify(Hk, draft, p, T, s)["accepted"] for s in range(64)])
+    rate = float(acc.float().mean())
+    elem = 2 if bf16 else 4
+    verify_bytes = shape.v * shape.d * elem + K * shape.d * elem + shape.v * 4
+    res = {
+        "metric": "speculative verification of K FlashHead drafts against the dense head",
+        "value": round(verify_us, 2), "unit": "us per verification", "n_gpus": 1, "steps": steps,
+        "higher_is_better": False, "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic seeded clustered embeddings (no trained weights)",
+        "config": {"workload": f"{shape.name} K={K} p={p} T={T}", "K": K, "p": p,
+                   "temperature": T, "quant": args.quant},
+        "draft_us_per_position": round(draft_us, 2),
+        "dense_sample_us": {"B=1": round(dense1_us, 2), f"B={K}": round(dense_us, 2)},
+        "acceptance_rate": round(rate, 4),
+        "verify_achieved_gbs": round(verify_bytes / (verify_us * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(verify_bytes / (verify_us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(verify_bytes / (verify_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "spec verification (probe bits, row pass, finish)"},
+    }
+    print(json.dumps(res), flush=True)
+    head.close()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -292,6 +371,9 @@ def main():
         return
     if args.cluster:
         cluster_main(args)
+        return
+    if args.spec:
+        spec_main(args)
         return
 
     import numpy as np

@@ -180,6 +180,45 @@ fh_status fh_get_int4(fh_engine* e, uint8_t* packed, uint16_t* scales, void* str
 fh_status fh_get_int8(fh_engine* e, int8_t* codes, uint16_t* scales, void* stream);
 
 /*
+ * fh_spec_verify — verify B FlashHead draft tokens against the dense head
+ * with the standard speculative-sampling rule ([X] §4.2 speculative
+ * decoding: a FlashHead draft, the original head's probabilities, accept or
+ * reject; the rule is Leviathan et al. 2023 / Chen et al. 2023).  Query q
+ * is one position with hidden state h[q]:
+ *   p(t) = softmax(E h / T) over all v tokens;
+ *   q(t) = softmax(E_t h / T) over the retrieved tokens of the draft's
+ *          probes, 0 elsewhere (what the draft sampled from);
+ *   the draft token x is kept when u < min(1, p(x) / q(x)) with
+ *   u = Philox uniform (seed, q, 0, stage 2); otherwise the output is a draw
+ *   from max(0, p - q), i.e. from p over the tokens outside the probes
+ *   (Gumbel-max with Philox (seed, q, t, stage 3)).
+ * The output token is distributed exactly as p.  As both heads score a
+ * retrieved token with the same E_t . h, p(x) / q(x) = exp(draft_lse -
+ * LSE_full) for x inside the probes.
+ *   h               device [B x d] of the engine's dtype, 16-byte aligned.
+ *   p               probes per draft, 1 <= p <= c.
+ *   draft_clusters  device [B x p] int32: the draft's probes (out_clusters
+ *                   of fh_forward); ids outside [0, c) are ignored.
+ *   draft_token     device [B] int32: the draft's tokens (out_token of
+ *                   fh_forward with FH_TOKEN_SAMPLE at this temperature); a
+ *                   token outside [0, v) is rejected, one outside its own
+ *                   probes (q = 0) is kept.
+ *   draft_lse       device [B] float: the draft's out_lse (log sum exp(z/T)
+ *                   over its retrieved tokens).
+ *   temperature     T > 0, the draft's temperature.
+ *   out_token       device [B] int32: the verified token.
+ *   out_accepted    device [B] int32, may be NULL: 1 where the draft was kept.
+ *   out_lse         device [B] float, may be NULL: log sum exp(z/T) over all v.
+ * Uses the engine's workspace like the other calls (B <= max_batch).
+ */
+fh_status fh_spec_verify(fh_engine* e, const void* h, int64_t B, int64_t p,
+                         const int32_t* draft_clusters, const int32_t* draft_token,
+                         const float* draft_lse, float temperature, uint64_t seed,
+                         int32_t* out_token, int32_t* out_accepted, float* out_lse,
+                         void* stream);
+
+/*
+ * Per-kernel timing./*
  * Per-kernel timing.  fh_profile_begin(e, n) makes the engine record a HIP
  * event pair on the launch stream around each of its next n kernel launches.
  * fh_profile_end waits for those events and fills up to `max` records

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libflashhead.so")
 
 SOURCES = ["fh_kernels.hip", "fh_mfma.hip", "fh_cluster.hip", "fh_batch1_bf16.hip", "fh_batch1_bf16_int4.hip",
            "fh_batch1_bf16_int8.hip", "fh_batch1_f32.hip", "fh_batch1_f32_int8.hip",
-           "fh_batch1_f32_int4.hip", "fh_engine.cpp"]
+           "fh_batch1_f32_int4.hip", "fh_spec.hip", "fh_engine.cpp"]
 
 # Packed FP32 instructions are disabled for all device code.
 COMMON = [

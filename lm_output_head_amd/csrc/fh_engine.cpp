@@ -49,6 +49,7 @@ struct fh_engine {
   const void* E = nullptr;
   const void* C = nullptr;
   int32_t* c2t = nullptr;
+  int32_t* t2c = nullptr;     // cluster of every token (speculative verification)
   void* Ec = nullptr;         // cluster-contiguous copy of E: Ec[f] = E[C2T[f]]
   uint8_t* cq = nullptr;
   uint16_t* csig = nullptr;
@@ -130,6 +131,7 @@ void free_engine(fh_engine* e) {
   if (!e) return;
   (void)hipFree(e->c2t);
   (void)hipFree(e->Ec);
+  (void)hipFree(e->t2c);
   (void)hipFree(e->cq);
   (void)hipFree(e->csig);
   (void)hipFree(e->cq_mfma);
@@ -293,6 +295,7 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   struct Alloc { void** p; size_t bytes; const char* what; };
   const Alloc allocs[] = {
       {(void**)&e->c2t, sizeof(int32_t) * (size_t)v, "C2T"},
+      {(void**)&e->t2c, sizeof(int32_t) * (size_t)v, "token clusters"},
       {(void**)&e->Ec, (size_t)(v * d) * (dtype == FH_BF16 ? 2 : 4), "cluster-contiguous E"},
       {(void**)&e->scores, sizeof(float) * (size_t)(max_batch * c), "scores"},
       {(void**)&e->sel, sizeof(int32_t) * (size_t)(max_batch * c), "selection"},
@@ -313,6 +316,8 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "copy C2T"); }
   r = fh::launch_permute_rows(e->ctx(st), e->Ec);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "cluster-contiguous E"); }
+  r = fh::launch_t2c(e->ctx(st), e->t2c);
+  if (r != hipSuccess) { free_engine(e); return hip_fail(r, "token clusters"); }
 
   if (quant != FH_QUANT_NONE) {
     const int bits = quant == FH_QUANT_INT4_G32 ? 4 : 8;
@@ -458,7 +463,7 @@ fh_status fh_dense_forward(fh_engine* e, const void* h, int64_t B, int mode, flo
   const float tprime = token_sample ? temperature : 1.f;
   int64_t nparts = 0;
   hipError_t r;
-  if (e->dtype == FH_BF16 && B >= fh::kMfmaMinBatchBf16)
+  if (e->dtype == FH_BF16 && B >= fh::kMfmaMinBatchDense)
     r = timed(e, st, "dense_mfma", [&] {
       return fh::launch_dense_mfma(k, e->cus, h, (int)B, token_sample, tprime, seed, out_logits,
                                    e->parts, &nparts);
@@ -474,6 +479,32 @@ fh_status fh_dense_forward(fh_engine* e, const void* h, int64_t B, int mode, flo
   });
   if (r != hipSuccess) return hip_fail(r, "finish launch");
   return FH_OK;
+}
+
+fh_status fh_spec_verify(fh_engine* e, const void* h, int64_t B, int64_t p,
+                         const int32_t* draft_clusters, const int32_t* draft_token,
+                         const float* draft_lse, float temperature, uint64_t seed,
+                         int32_t* out_token, int32_t* out_accepted, float* out_lse,
+                         void* stream) {
+  g_err.clear();
+  fh_status s = check_common(e, h, B);
+  if (s != FH_OK) return s;
+  if (p < 1 || p > e->c)
+    return fail(FH_EINVAL, "p=" + std::to_string(p) + " outside [1, c=" + std::to_string(e->c) + "]");
+  if (!draft_clusters || !draft_token || !draft_lse || !out_token)
+    return fail(FH_EINVAL, "draft_clusters, draft_token, draft_lse and out_token must not be NULL");
+  if (!(temperature > 0.f && std::isfinite(temperature)))
+    return fail(FH_EINVAL, "speculative sampling needs a finite temperature > 0");
+  DeviceGuard g(e->device);
+  if (!g.ok) return fail(FH_EHIP, "cannot select the engine's device");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const fh::KernelCtx k = e->ctx(st);
+  const hipError_t r = timed(e, st, "spec_verify", [&] {
+    return fh::launch_spec_verify(k, e->cus, e->t2c, e->mbits, e->parts, h, (int)B, (int)p, draft_clusters,
+                                  draft_token, draft_lse, temperature, seed, out_token,
+                                  out_accepted, out_lse);
+  });
+  return r == hipSuccess ? FH_OK : hip_fail(r, "speculative verification");
 }
 
 fh_status fh_set_path(fh_engine* e, int path) {

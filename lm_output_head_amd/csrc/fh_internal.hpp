@@ -61,7 +61,8 @@ hipError_t launch_gather(const KernelCtx& k, const void* h, int B, const int32_t
 hipError_t launch_dense(const KernelCtx& k, const void* h, int B, int token_sample, float tprime,
                         uint64_t seed, float* out_logits, Part* parts, int64_t* nparts);
 // Matrix-core (MFMA) paths for batches of bf16 queries.
-constexpr int kMfmaMinBatchBf16 = 8;  // bf16 stage 1 and the dense head
+constexpr int kMfmaMinBatchBf16 = 8;  // bf16 stage 1
+constexpr int kMfmaMinBatchDense = 2;  // the dense head and the speculative verification (bf16)
 constexpr int kMfmaMinBatchInt4 = 2;  // INT4 stage 1
 constexpr int kMfmaMinBatchInt8 = 16;  // INT8 stage 1 (measured: vector units 21 us at B = 8, MFMA 27 us)
 int64_t mfma_int4_row_bytes(int d);
@@ -119,6 +120,19 @@ hipError_t balanced_assign_device(const float* S, int64_t v, int64_t c, int32_t*
 hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, int iters,
                          const double* u, float* C, int32_t* c2t, int32_t* init, int32_t* asg_out,
                          hipStream_t st, ClusterTimes* times);
+
+// Speculative verification (fh_spec.hip): the token -> cluster map, and the
+// verification of B draft tokens against the dense head.
+hipError_t launch_t2c(const KernelCtx& k, int32_t* t2c);
+// the dense pass of the verification on the matrix cores (bf16, B >= kMfmaMinBatchDense)
+hipError_t launch_spec_mfma(const KernelCtx& k, int cus, const void* h, int B, float T,
+                            uint64_t seed, const int32_t* t2c, const uint32_t* bits, int W,
+                            Part* parts, int64_t* nparts);
+hipError_t launch_spec_verify(const KernelCtx& k, int cus, const int32_t* t2c, uint32_t* bits, Part* parts,
+                              const void* h, int B, int p, const int32_t* draft_clusters,
+                              const int32_t* draft_token, const float* draft_lse, float T,
+                              uint64_t seed, int32_t* out_token, int32_t* out_accepted,
+                              float* out_lse);
 
 hipError_t launch_batch1(const FusedLaunch& f);
 // per storage variant, one translation unit each

@@ -99,6 +99,12 @@ struct MfmaArgs {
   float tprime;
   uint64_t seed;
   Part* parts;  // EPI: [B x gridDim.x]
+  // EPI, speculative verification: with bits set, a token whose cluster
+  // t2c[t] is among query q's probes (bit of bits[q W + k / 32]) gets key
+  // -inf, any other z / T' + G(seed, q, t, stage 3); the LSE is unchanged
+  const int32_t* t2c;
+  const uint32_t* bits;
+  int W;
 };
 
 constexpr int kHRow = 128 + 8;  // LDS row of a staged h block (bf16), padded
@@ -365,8 +371,14 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
         const int64_t r = rbase + 16 * m + 4 * g + i;
         if (r < a.R && q < a.B) {
           if (a.out) a.out[(int64_t)q * a.ld_out + r] = acc[m][n][i];
-          p = part_merge(p, part_of(acc[m][n][i], (int32_t)r, a.token_sample, a.tprime, a.seed,
-                                    (uint32_t)q));
+          Part pt = part_of(acc[m][n][i], (int32_t)r, a.token_sample, a.tprime, a.seed, (uint32_t)q);
+          if (a.bits) {
+            const int k = a.t2c[r];
+            const bool probed = (a.bits[(int64_t)q * a.W + (k >> 5)] >> (k & 31)) & 1u;
+            pt.key = probed ? -INFINITY
+                            : acc[m][n][i] / a.tprime + gumbel_at(a.seed, (uint32_t)q, (uint32_t)r, 3u);
+          }
+          p = part_merge(p, pt);
         }
       }
     // the four lane groups hold the same query: fold them (fixed order)
@@ -682,6 +694,16 @@ hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, 
   a.A = k.E; a.R = k.v; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
   a.out = out_logits; a.ld_out = k.v;
   a.token_sample = token_sample; a.tprime = tprime; a.seed = seed; a.parts = parts;
+  return mfma_dispatch<0, true>(a, cus, k.stream, nparts);
+}
+
+hipError_t launch_spec_mfma(const KernelCtx& k, int cus, const void* h, int B, float T,
+                            uint64_t seed, const int32_t* t2c, const uint32_t* bits, int W,
+                            Part* parts, int64_t* nparts) {
+  MfmaArgs a{};
+  a.A = k.E; a.R = k.v; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
+  a.token_sample = 0; a.tprime = T; a.seed = seed; a.parts = parts;
+  a.t2c = t2c; a.bits = bits; a.W = W;
   return mfma_dispatch<0, true>(a, cus, k.stream, nparts);
 }
 

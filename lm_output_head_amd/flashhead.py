@@ -99,6 +99,14 @@ def fh_get_int8(eng, codes, scales, stream=None) -> None:
     check(_abi.load().fh_get_int8(eng, _ptr(codes), _ptr(scales), _stream(stream)))
 
 
+def fh_spec_verify(eng, h, p, draft_clusters, draft_token, draft_lse, temperature, seed,
+                   out_token, out_accepted=None, out_lse=None, stream=None) -> None:
+    check(_abi.load().fh_spec_verify(eng, _ptr(h), h.shape[0], p, _ptr(draft_clusters),
+                                     _ptr(draft_token), _ptr(draft_lse), temperature, seed,
+                                     _ptr(out_token), _ptr(out_accepted), _ptr(out_lse),
+                                     _stream(stream)))
+
+
 def fh_set_path(eng, path: int) -> None:
     check(_abi.load().fh_set_path(eng, path))
 
@@ -223,6 +231,19 @@ class FlashHead:
             out["logits"] = self._alloc((B, self.v), torch.float32)
         fh_dense_forward(self.eng, h, mode, temperature, seed, out["token"], out["token_logit"],
                          out["lse"], out.get("logits"), stream)
+        return out
+
+    def spec_verify(self, h: torch.Tensor, draft: dict, p: int, temperature: float,
+                    seed: int = 0, stream=None) -> dict:
+        """Verify the draft of ``forward(h, p, mode=...|FH_TOKEN_SAMPLE,
+        temperature, want_clusters=True)`` against the dense head."""
+        B = h.shape[0]
+        _require(draft["clusters"], torch.int32, (B, p), "draft clusters")
+        out = {"token": self._alloc((B,), torch.int32),
+               "accepted": self._alloc((B,), torch.int32),
+               "lse": self._alloc((B,), torch.float32)}
+        fh_spec_verify(self.eng, h, p, draft["clusters"], draft["token"], draft["lse"],
+                       temperature, seed, out["token"], out["accepted"], out["lse"], stream)
         return out
 
     def set_path(self, path: str) -> None:
