@@ -54,6 +54,15 @@ def parse():
                          "instead of the head, one JSON line of its own")
     ap.add_argument("--cluster-iters", type=int, default=5)
     ap.add_argument("--cluster-runs", type=int, default=2)
+    ap.add_argument("--sweep", action="store_true",
+                    help="latency and agreement with the dense head over B in {1,8,32,64} x p in "
+                         "{128,256,512,1024} at --shape / --quant; one JSON line")
+    ap.add_argument("--alpha", type=float, default=None,
+                    help="--sweep: query scale on its source token's embedding (default: the "
+                         "shape's); smaller is harder for the probes")
+    ap.add_argument("--spread", type=float, default=None,
+                    help="--sweep: within-cluster noise scale of the embeddings (default 0.3; "
+                         "1.3 puts tokens at cosine ~0.6 to their cluster, the pages' quality bound)")
     ap.add_argument("--spec", type=int, default=0, metavar="K",
                     help="time the speculative verification of K draft positions (fh_spec_verify) "
                          "beside K single-position drafts and the dense head at B=K; one JSON line")
@@ -284,6 +293,113 @@ def cluster_main(args):
     print(json.dumps(res), flush=True)
 
 
+def sweep_main(args):
+    """The accuracy/latency curve against the dense head: for every (B, p),
+    the per-call latency (HIP events over rotated engine replicas, as in the
+    default run) and, over all generated queries, the top-1 agreement of
+    FlashHead's argmax with the dense head's and the recall of the dense
+    argmax's cluster among the probes (greedy calls)."""
+    import numpy as np
+    import torch
+
+    from lm_output_head_amd import flashhead as fhb
+    from synth import SHAPES, make_problem
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    shape = SHAPES[args.shape]
+    import dataclasses
+    if args.alpha is not None:
+        shape = dataclasses.replace(shape, alpha=float(args.alpha))
+    if args.spread is not None:
+        shape = dataclasses.replace(shape, spread=float(args.spread))
+    Bs, ps = (1, 8, 32, 64), (128, 256, 512, 1024)
+    pb = make_problem(shape)
+    bf16 = shape.dtype == "bf16"
+
+    def dev(x):
+        a = np.ascontiguousarray(x)
+        if bf16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a.astype(np.float32)).cuda()
+
+    E0, C0 = dev(pb.E_bits if bf16 else pb.E), dev(pb.C_bits if bf16 else pb.C)
+    Hall = dev(pb.H_bits if bf16 else pb.H)
+    nq = Hall.shape[0]
+    R = max(1, min(args.replicas, 8))
+    heads = [fhb.FlashHead(E0 if r == 0 else E0.clone(), C0 if r == 0 else C0.clone(), pb.C2T,
+                           quant=args.quant, max_batch=max(Bs)) for r in range(R)]
+    stream = torch.cuda.current_stream()
+    lib = fhb._abi.load()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    otok = torch.empty(max(Bs), dtype=torch.int32, device="cuda")
+    olog = torch.empty(max(Bs), dtype=torch.float32, device="cuda")
+    olse = torch.empty(max(Bs), dtype=torch.float32, device="cuda")
+
+    def timed_us(B, call, steps):
+        hts = [Hall[(i * B) % nq:(i * B) % nq + B].contiguous() for i in range(max(1, nq // B))]
+        hp = [ptr(h) for h in hts]
+
+        def fn(i):
+            st = call(heads[i % R].eng, hp[i % len(hp)], B, i)
+            if st != 0:
+                raise RuntimeError(lib.fh_last_error().decode())
+        for i in range(10):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            fn(10 + i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    # dense tokens of every query, and the cluster of every token
+    t2c = np.empty(shape.v, dtype=np.int64)
+    t2c[pb.C2T.ravel()] = np.arange(shape.v) // shape.b
+    dense_tok = np.concatenate([heads[0].dense(Hall[i:i + 64])["token"].cpu().numpy()
+                                for i in range(0, nq, 64)])
+    rows = []
+    for p in ps:
+        toks, hits = [], []
+        for i in range(0, nq, 64):
+            o = heads[0].forward(Hall[i:i + 64], p, want_clusters=True)
+            toks.append(o["token"].cpu().numpy())
+            cl = o["clusters"].cpu().numpy()
+            dt = dense_tok[i:i + 64]
+            hits.append(np.array([t2c[t] in set(cl[j].tolist()) for j, t in enumerate(dt)]))
+        agree = float((np.concatenate(toks) == dense_tok).mean())
+        recall = float(np.concatenate(hits).mean())
+        for B in Bs:
+            steps = max(50, 800 // B)
+            us = timed_us(B, lambda e, h, b, i: lib.fh_forward(e, h, b, p, 0, 1.0, 0x5EED + i,
+                                                                ptr(otok), ptr(olog), ptr(olse),
+                                                                None, None, None, sp), steps)
+            rows.append({"B": B, "p": p, "us_per_call": round(us, 2),
+                         "tokens_per_s": round(B / (us * 1e-6), 1),
+                         "top1_agreement": round(agree, 4), "cluster_recall": round(recall, 4)})
+            print(f"[bench] B={B} p={p} {us:.1f} us agree {agree:.3f}", file=sys.stderr, flush=True)
+    dense = []
+    for B in Bs:
+        us = timed_us(B, lambda e, h, b, i: lib.fh_dense_forward(e, h, b, 0, 1.0, 0x5EED + i,
+                                                                  ptr(otok), ptr(olog), ptr(olse),
+                                                                  None, sp), max(50, 400 // B))
+        dense.append({"B": B, "us_per_call": round(us, 2), "tokens_per_s": round(B / (us * 1e-6), 1)})
+    res = {"metric": "FlashHead latency and top-1 agreement with the dense head, B x p sweep",
+           "unit": "us per call", "n_gpus": 1, "dtype": "bf16" if bf16 else "f32",
+           "data": f"synthetic seeded clustered embeddings (no trained weights), {nq} queries",
+           "config": {"workload": f"{shape.name} sweep", "quant": args.quant, "replicas": R,
+                      "alpha": shape.alpha, "spread": shape.spread,
+                      "mode": "greedy (top-p probes, argmax)"},
+           "rows": rows, "dense": dense}
+    print(json.dumps(res), flush=True)
+    for h in heads:
+        h.close()
+
+
 def spec_main(args):
     """Speculative decoding with FlashHead drafts: K draft calls at B = 1
     (sampled tokens, their probes kept) and one verification of the K
@@ -374,6 +490,9 @@ def main():
         return
     if args.spec:
         spec_main(args)
+        return
+    if args.sweep:
+        sweep_main(args)
         return
 
     import numpy as np

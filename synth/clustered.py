@@ -12,7 +12,9 @@ such a structure directly:
 3. ``perm = rng.permutation(v)``; ``C2T = perm.reshape(c, b)``: token
    ``perm[k*b + j]`` sits in cluster k, slot j.
 4. ``noise``: v x d standard-normal float32; ``E[t] = normalize(mu[k(t)] +
-   0.3 * noise[t] / sqrt(d))`` where k(t) is t's cluster.
+   spread * noise[t] / sqrt(d))`` where k(t) is t's cluster; spread = 0.3
+   unless the shape sets another (a token's cosine to its cluster's
+   direction is about 1 / sqrt(1 + spread^2)).
 5. ``C[k] = normalize(mean_j E[C2T[k, j]])`` in float32.
 6. E and C are rounded to bfloat16 (round to nearest, ties to even) unless the
    shape is float32.
@@ -43,6 +45,7 @@ class Shape:
     dtype: str  # "f32" or "bf16": the storage type of E, C and h
     alpha: float  # query scale on its source token's embedding
     nq: int  # number of generated queries
+    spread: float = 0.3  # within-cluster noise scale of the embeddings
 
     @property
     def b(self) -> int:
@@ -140,7 +143,7 @@ def _make_problem_cached(shape: Shape, seed_data: int, seed_query: int, nq: int)
     cluster_of = np.empty(v, dtype=np.int64)
     cluster_of[perm] = np.arange(v, dtype=np.int64) // b
     noise = rng.standard_normal((v, d), dtype=np.float32)
-    noise *= np.float32(0.3) / np.float32(np.sqrt(np.float32(d)))
+    noise *= np.float32(shape.spread) / np.float32(np.sqrt(np.float32(d)))
     noise += mu[cluster_of]
     E32 = _normalize_rows(noise)
     del noise
