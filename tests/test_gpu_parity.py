@@ -141,6 +141,54 @@ def test_ragged_shapes(v, d, c, dtype):
     assert_report(parity.check_dense(pb.E, pb.H, TOPK, 1.0, 0, dn), "ragged dense")
 
 
+@pytest.mark.parametrize("v,d,c,dtype,quant", [
+    (4096, 4096, 256, "bf16", "none"),  # the largest bf16 d: 8 chunks per lane
+    (4096, 4096, 256, "bf16", "int4"),  # 128 INT4 groups: two per lane
+    (4096, 4096, 256, "bf16", "int8"),
+    (2048, 2048, 128, "f32", "none"),   # the largest fp32 d
+])
+def test_maximum_hidden_size(v, d, c, dtype, quant):
+    """d at the build's limit, through every path: the single launch (B = 1),
+    per-stage launches, the matrix cores for stage 1 (INT4 from B = 2, bf16
+    from 8) and the dense head (from 2)."""
+    pb = _custom_problem(v, d, c, dtype, 8, seed=13)
+    head, H = _engine(pb, quant=quant, max_batch=8)
+    ref = _oracle(pb, quant)
+    for B in (1, 3, 8):
+        say("max d", v, d, c, dtype, quant, "B", B)
+        out = host(head.forward(H[:B], 32, want_clusters=True, want_retrieved=True))
+        assert_report(parity.check_forward(ref, pb.H[:B], 32, TOPK, 1.0, 0, out), f"max d B={B}")
+        s = host({"s": head.score(H[:B])})["s"]
+        assert_report(parity.check_scores(ref.C_hat, pb.H[:B], s), f"max d scores B={B}")
+        dn = host(head.dense(H[:B], mode=TSAMPLE, temperature=0.9, seed=2, want_logits=True))
+        assert_report(parity.check_dense(pb.E, pb.H[:B], TSAMPLE, 0.9, 2, dn), f"max d dense B={B}")
+    head.close()
+
+
+def test_hidden_size_beyond_the_limit_is_unsupported():
+    from lm_output_head_amd import FlashHead, FlashHeadError
+    for d, dt in ((4104, torch.bfloat16), (2052, torch.float32)):
+        E = torch.zeros((64, d), dtype=dt, device="cuda")
+        C = torch.zeros((4, d), dtype=dt, device="cuda")
+        with pytest.raises(FlashHeadError):
+            FlashHead(E, C, np.arange(64, dtype=np.int32).reshape(4, 16))
+
+
+@pytest.mark.parametrize("B", [256, 257])
+def test_batches_at_the_cluster_major_limit(B):
+    """256 queries: the cluster-major stage 2 (its LDS lists hold 256); 257:
+    the query-major one.  Both against the oracle on a sample of rows."""
+    pb = _custom_problem(8192, 128, 512, "bf16", 257, seed=17)
+    head, H = _engine(pb, max_batch=257)
+    ref = _oracle(pb)
+    say("cm limit B", B)
+    out = host(head.forward(H[:B], 96, want_clusters=True, want_retrieved=True))
+    rows = sorted({0, 1, 100, 255, B - 1})
+    assert_report(parity.check_forward(ref, pb.H[:B], 96, TOPK, 1.0, 0, out, queries=rows),
+                  f"cm limit B={B}")
+    head.close()
+
+
 def test_all_equal_scores_take_smallest_cluster_ids():
     """Degenerate: identical centroids give equal scores; ties go to small ids."""
     from lm_output_head_amd import FlashHead
