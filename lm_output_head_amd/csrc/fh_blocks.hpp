@@ -105,11 +105,12 @@ __device__ __forceinline__ void wave_rows(const T* __restrict__ M, int d, int la
 }
 
 // ======================================================================
-// Wave-level INT4 stage-1 GEMV: s[k] = sum_g sigma[k, g] sum_{i in g} q h.
-// Lane l owns groups l, l+64, ...: one 16-byte load is one group's 32
-// nibbles.  Nibbles become unsigned bytes u = q + 8 (xor 0x88888888, two
-// masks), cvt_f32_ubyte converts them, and sum q h = sum u h - 8 sum_g h
-// removes the offset with the group sums of h.
+// Wave-level stage-1 GEMV on g32 codes: s[k] = sum_g sigma[k, g] sum_{i in g}
+// q h (INT4 or INT8).  Lane l owns groups l, l+64, ...; the query's groups
+// and their sums stay in registers (HGroups).  INT4: one 16-byte load is one
+// group's 32 nibbles; nibbles become unsigned bytes u = q + 8 (xor
+// 0x88888888, two masks), cvt_f32_ubyte converts them, and sum q h =
+// sum u h - 8 sum_g h removes the offset with the group sums of h.
 // ======================================================================
 template <int MAXG>
 struct HGroups {

@@ -3,8 +3,9 @@
 // The path per call follows the FlashHead computation graph (explainer,
 // framerc.cn, §2.2.2): centroid scores -> top-p (or sampled) clusters ->
 // retrieved-token scores -> argmax / sample.  Every step runs in the HIP
-// kernels of fh_kernels.hip; this file only checks arguments, owns device
-// buffers and enqueues work on the caller's stream.
+// kernels (fh_kernels.hip, fh_batch1_*.hip, fh_mfma.hip, fh_spec.hip,
+// fh_cluster.hip); this file only checks arguments, owns device buffers and
+// enqueues work on the caller's stream.
 
 #include <hip/hip_runtime.h>
 

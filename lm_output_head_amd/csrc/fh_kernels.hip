@@ -1,8 +1,8 @@
-// FlashHead kernels for gfx950 (MI355X) of the multi-launch path: INT4
-// centroid quantisation, row GEMV (stage-1 scores, stage-2 gather-score,
-// dense head) with the fused epilogue, probe selection and the finisher;
-// plus the host-side launchers.  The single-launch batch-1 kernel lives in
-// fh_batch1.inl.
+// FlashHead kernels for gfx950 (MI355X) of the multi-launch path: g32
+// centroid quantisation (INT4, INT8), row GEMV (stage-1 scores, stage-2
+// gather-score, dense head) with the fused epilogue, probe selection and the
+// finisher; plus the host-side launchers.  The single-launch batch-1 kernel
+// lives in fh_batch1.inl, the matrix-core paths in fh_mfma.hip.
 //
 // Sources (page title and section): FlashHead technical explainer
 // (framerc.cn) §1.1, §1.2.1-§1.2.4, §2.2.2, §2.3; "FlashHead: Efficient
@@ -17,12 +17,14 @@
 namespace fh {
 
 // ======================================================================
-// INT4 g32 quantisation of the centroids (explainer §1.2.4, §2.3).
-// One thread per (row, group of 32 consecutive elements).  sigma is
-// fp16(amax / 7) with an IEEE float32 division and round-to-nearest-even to
-// fp16; q = clamp(rint(x / sigma), -7, 7) with float32 division (rint ties
-// to even); q = 0 where sigma = 0.  Nibbles are packed two's-complement,
-// element 2m in the low nibble of byte m.  *bad is set if a scale overflows.
+// g32 quantisation of the centroids (explainer §1.2.4, §2.3; INT8 is the
+// W8A16 row of §5.2).  One thread per (row, group of 32 consecutive
+// elements).  sigma is fp16(amax / qmax) (qmax 7 or 127) with an IEEE float32
+// division and round-to-nearest-even to fp16; q = clamp(rint(x / sigma),
+// -qmax, qmax) with float32 division (rint ties to even); q = 0 where
+// sigma = 0.  INT4 nibbles are packed two's-complement, element 2m in the
+// low nibble of byte m; INT8 codes are stored as bytes.  *bad is set if a
+// scale overflows.
 // ======================================================================
 template <typename T, int BITS>
 __global__ __launch_bounds__(256) void k_quant_g32(const T* __restrict__ C, int64_t c, int d,
