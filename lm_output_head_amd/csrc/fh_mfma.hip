@@ -23,10 +23,12 @@
 // straight into registers, also one block ahead.  With B <= 128 queries in
 // one grid row, every row of E or C is read from HBM once per call.
 //
-// bf16 rows: lane l loads the 64 contiguous bytes [128 blk + 32 g, +32) of
-// its row (g = l / 16); MFMA step s uses elements 32 g + 8 s .. + 7 of that
-// slice for both operands, a fixed permutation of d that the sum does not
-// see.
+// bf16 rows: MFMA step s of block blk takes elements 128 blk + 32 s .. + 31,
+// lane group g (g = l / 16) holding 8 g .. + 7 of them, for both operands:
+// one load instruction then reads one contiguous 64-byte run per row.  (With
+// lane group g owning 64 contiguous bytes across the steps, an instruction
+// touched four sectors per row; that order was 5-7% slower on the dense head
+// and the cluster-major stage 2.)
 //
 // INT4 rows (the defined value sum_g sigma[k, g] sum_{i in g} q h): one MFMA
 // step is exactly one 32-element group.  The packed nibbles are re-laid out
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int k = 128 * kb + 32 * g + 8 * s;
+          const int k = 128 * kb + 32 * s + 8 * g;
           dst[m][s] = k < a.d ? *reinterpret_cast<const uint4*>(A + ra[m] * a.d + k)
                               : uint4{0u, 0u, 0u, 0u};
         }
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
         uint4 bfr[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n)
-          bfr[n] = *reinterpret_cast<const uint4*>(&sH[buf][(16 * n + col) * kHRow + 32 * g + 8 * s]);
+          bfr[n] = *reinterpret_cast<const uint4*>(&sH[buf][(16 * n + col) * kHRow + 32 * s + 8 * g]);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -490,13 +492,11 @@ __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
         // ping-pong: the next 128-element block is in flight during the MFMAs
         uint4 a0[4], b0[4], a1[4], b1[4];
         auto ld = [&](int blk, uint4 (&av)[4], uint4 (&bv)[4]) {
-          const int kk = 128 * blk + 32 * g;
-          const uint4* ap = reinterpret_cast<const uint4*>(Ar + kk);
-          const uint4* bp = reinterpret_cast<const uint4*>(Hr + kk);
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            av[s] = ap[s];
-            bv[s] = bp[s];
+          for (int s = 0; s < 4; ++s) {  // step s: elements 32 s + 8 g .. + 7 of the block
+            const int kk = 128 * blk + 32 * s + 8 * g;
+            av[s] = *reinterpret_cast<const uint4*>(Ar + kk);
+            bv[s] = *reinterpret_cast<const uint4*>(Hr + kk);
           }
         };
         if (nblk > 0) ld(0, a0, b0);
