@@ -16,6 +16,7 @@ see ``tests/test_oracle_*.py``.
 
 from .flashhead_oracle import (  # noqa: F401
     MODE_PROBE_SAMPLE,
+    MODE_PROBE_SHARED,
     MODE_TOKEN_SAMPLE,
     OracleHead,
     dense,
@@ -30,6 +31,7 @@ from .flashhead_oracle import (  # noqa: F401
     quantize_int8_g32,
     score,
     select,
+    select_shared,
     unpack_int4,
     validate_c2t,
 )

@@ -41,6 +41,7 @@ from .philox import gumbel
 # (0 = argmax, 2 = sampled)
 MODE_PROBE_SAMPLE = 1
 MODE_TOKEN_SAMPLE = 2
+MODE_PROBE_SHARED = 4
 
 
 # ---------------------------------------------------------------------------
@@ -192,13 +193,36 @@ def _top_ids(key32_row: np.ndarray, ids_row: np.ndarray, n: int) -> np.ndarray:
     return order[:n]
 
 
+def select_shared(s: np.ndarray, p: int) -> Selection:
+    """One probe set for the whole batch (explainer §4.2, server-side
+    batching: share the cluster selection across the samples).  The pages
+    give no rule; the reading here: the p clusters with the largest summed
+    score sum_b s[b, k] (the top p for the batch's mean query), compared in
+    float32, ties to the smaller id.  Every row gets the same set."""
+    s = np.atleast_2d(np.asarray(s, dtype=np.float64))
+    B, c = s.shape
+    if not 1 <= p <= c:
+        raise ValueError(f"p={p} outside [1, c={c}]")
+    key = s.sum(axis=0)
+    key32 = key.astype(np.float32)
+    top = _top_ids(key32, np.arange(c), p)
+    S = np.tile(np.sort(top), (B, 1))
+    return Selection(S, np.tile(key, (B, 1)), np.tile(key32, (B, 1)),
+                     np.full(B, key32[top[-1]], dtype=np.float32))
+
+
 def select(s: np.ndarray, p: int, mode: int = 0, temperature: float = 1.0,
            seed: int = 0, rows=None) -> Selection:
     """Pick p clusters per row: the p largest keys, returned in ascending id.
 
     Top-p here counts clusters (the pages' p probes), not nucleus mass.  Keys
-    are compared in float32; equal keys go to the smaller cluster id.
+    are compared in float32; equal keys go to the smaller cluster id.  With
+    MODE_PROBE_SHARED the batch shares one set (select_shared).
     """
+    if mode & MODE_PROBE_SHARED:
+        if mode & MODE_PROBE_SAMPLE:
+            raise ValueError("shared probes are chosen by score, not sampled")
+        return select_shared(s, p)
     key = probe_keys(s, mode, temperature, seed, rows)
     B, c = key.shape
     if not 1 <= p <= c:

@@ -65,14 +65,16 @@ def check_forward(head: OracleHead, H, p, mode, temperature, seed, gpu: dict, qu
     rows = range(B) if queries is None else queries
     rep = Report()
     rows = list(rows)
-    s = H[rows] @ head.C_hat.T  # float64 scores of the checked rows
-    sel = select(s, p, mode, temperature, seed, rows=rows)
+    shared = bool(mode & 4)  # a shared probe set depends on every row of the batch
+    s = (H if shared else H[rows]) @ head.C_hat.T  # float64 scores
+    sel = select(s, p, mode, temperature, seed, rows=None if shared else rows)
     for pos, r in enumerate(rows):
         rep.queries += 1
         h = H[r]
-        keys_all = sel.key[pos]
-        S_ref = sel.S[pos]
-        theta = float(sel.theta[pos])
+        i = r if shared else pos
+        keys_all = sel.key[i]
+        S_ref = sel.S[i]
+        theta = float(sel.theta[i])
         S_gpu = np.asarray(gpu["clusters"][r]) if "clusters" in gpu else S_ref
         if not np.array_equal(S_gpu, S_ref):
             if (len(S_gpu) != p or np.any(np.diff(S_gpu) <= 0) or S_gpu.min() < 0

@@ -387,3 +387,46 @@ def _pl_set_prob(w, S):
             used += w[k]
         total += pr
     return total
+
+
+# ------------------------------------------------------ batch-shared probes --
+
+def test_shared_selection_hand_worked():
+    """Summed scores (explainer §4.2, read as the top p of sum_b s[b, k]):
+    rows (1, 0, 3, 2, 0), (0, 4, 0, 1, 1), (2, 0, 0, 0, 1) sum to
+    (3, 4, 3, 3, 2); p = 3 takes cluster 1 and then two of the three tied at 3,
+    by the smaller id: {0, 1, 2}."""
+    s = np.array([[1, 0, 3, 2, 0], [0, 4, 0, 1, 1], [2, 0, 0, 0, 1]], dtype=np.float64)
+    sel = oracle.select(s, 3, oracle.MODE_PROBE_SHARED)
+    assert sel.S.tolist() == [[0, 1, 2]] * 3
+    assert float(sel.theta[0]) == 3.0
+
+
+def test_shared_selection_reductions_and_invariances():
+    rng = np.random.default_rng(21)
+    s = rng.standard_normal((6, 40))
+    one = oracle.select(s[2:3], 7, oracle.MODE_PROBE_SHARED)
+    assert np.array_equal(one.S, oracle.select(s[2:3], 7).S)  # B = 1: per-query top-p
+    sh = oracle.select(s, 7, oracle.MODE_PROBE_SHARED).S
+    assert np.all(sh == sh[0])                                 # one set for every row
+    perm = rng.permutation(6)
+    assert np.array_equal(oracle.select(s[perm], 7, oracle.MODE_PROBE_SHARED).S, sh)
+    top = np.argsort(-s.sum(axis=0), kind="stable")[:7]
+    assert sorted(top.tolist()) == sh[0].tolist()
+    with pytest.raises(ValueError):
+        oracle.select(s, 7, oracle.MODE_PROBE_SHARED | oracle.MODE_PROBE_SAMPLE, 1.0)
+
+
+def test_shared_probes_with_all_clusters_reproduce_the_dense_head():
+    """p = c: every row retrieves every token, as the dense head does."""
+    rng = np.random.default_rng(22)
+    v, c, d = 48, 6, 8
+    E = rng.standard_normal((v, d))
+    C = rng.standard_normal((c, d))
+    c2t = rng.permutation(v).reshape(c, v // c)
+    H = rng.standard_normal((3, d))
+    head = oracle.OracleHead(E, C, c2t)
+    r = head.forward(H, c, oracle.MODE_PROBE_SHARED)
+    dn = oracle.dense(E, H)
+    assert np.array_equal(r.fin.token, dn.token)
+    assert np.allclose(r.fin.lse, dn.lse, rtol=1e-12)
