@@ -362,20 +362,27 @@ def sweep_main(args):
     t2c[pb.C2T.ravel()] = np.arange(shape.v) // shape.b
     dense_tok = np.concatenate([heads[0].dense(Hall[i:i + 64])["token"].cpu().numpy()
                                 for i in range(0, nq, 64)])
-    rows = []
-    for p in ps:
+    shared = bool(args.mode & 4)  # one probe set per batch: agreement depends on B
+
+    def agreement(p, chunk):
         toks, hits = [], []
-        for i in range(0, nq, 64):
-            o = heads[0].forward(Hall[i:i + 64], p, want_clusters=True)
+        for i in range(0, nq, chunk):
+            o = heads[0].forward(Hall[i:i + chunk], p, mode=args.mode & 4, want_clusters=True)
             toks.append(o["token"].cpu().numpy())
             cl = o["clusters"].cpu().numpy()
-            dt = dense_tok[i:i + 64]
+            dt = dense_tok[i:i + chunk]
             hits.append(np.array([t2c[t] in set(cl[j].tolist()) for j, t in enumerate(dt)]))
-        agree = float((np.concatenate(toks) == dense_tok).mean())
-        recall = float(np.concatenate(hits).mean())
+        return float((np.concatenate(toks) == dense_tok).mean()), float(np.concatenate(hits).mean())
+
+    rows = []
+    for p in ps:
+        if not shared:
+            agree, recall = agreement(p, 64)
         for B in Bs:
+            if shared:
+                agree, recall = agreement(p, B)
             steps = max(50, 800 // B)
-            us = timed_us(B, lambda e, h, b, i: lib.fh_forward(e, h, b, p, 0, 1.0, 0x5EED + i,
+            us = timed_us(B, lambda e, h, b, i: lib.fh_forward(e, h, b, p, args.mode & 4, 1.0, 0x5EED + i,
                                                                 ptr(otok), ptr(olog), ptr(olse),
                                                                 None, None, None, sp), steps)
             rows.append({"B": B, "p": p, "us_per_call": round(us, 2),
@@ -393,7 +400,8 @@ def sweep_main(args):
            "data": f"synthetic seeded clustered embeddings (no trained weights), {nq} queries",
            "config": {"workload": f"{shape.name} sweep", "quant": args.quant, "replicas": R,
                       "alpha": shape.alpha, "spread": shape.spread,
-                      "mode": "greedy (top-p probes, argmax)"},
+                      "mode": "greedy, probes shared by the batch (top p of the summed scores)"
+                      if shared else "greedy (top-p probes, argmax)"},
            "rows": rows, "dense": dense}
     print(json.dumps(res), flush=True)
     for h in heads:

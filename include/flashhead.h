@@ -72,7 +72,13 @@ enum {
   FH_PROBE_SAMPLE = 1, /* p distinct clusters drawn from softmax(s/T)
                           without replacement ([X] §1.2.3)                  */
   FH_TOKEN_ARGMAX = 0, /* highest logit among retrieved tokens              */
-  FH_TOKEN_SAMPLE = 2  /* one draw from softmax(z/T) over retrieved tokens  */
+  FH_TOKEN_SAMPLE = 2, /* one draw from softmax(z/T) over retrieved tokens  */
+  FH_PROBE_SHARED = 4  /* one probe set for the whole batch: the p clusters
+                          with the largest summed score sum_b s[b, k]
+                          (ties to the smaller id) -- [X] §4.2's shared
+                          selection across samples, read this way; changes
+                          results for B > 1, equals FH_PROBE_TOPK at B = 1;
+                          not combinable with FH_PROBE_SAMPLE               */
 };
 
 /*

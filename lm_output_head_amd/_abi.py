@@ -15,6 +15,7 @@ FH_OK, FH_EINVAL, FH_ENOMEM, FH_EHIP, FH_EUNSUPPORTED = 0, -1, -2, -3, -4
 FH_F32, FH_BF16 = 0, 1
 FH_QUANT_NONE, FH_QUANT_INT4_G32, FH_QUANT_INT8_G32 = 0, 1, 2
 FH_PROBE_TOPK, FH_PROBE_SAMPLE, FH_TOKEN_ARGMAX, FH_TOKEN_SAMPLE = 0, 1, 0, 2
+FH_PROBE_SHARED = 4
 FH_PATH_AUTO, FH_PATH_MULTI = 0, 1
 
 # Every symbol the header declares.

@@ -60,6 +60,7 @@ struct fh_engine {
   int32_t* sel = nullptr;    // [max_batch x c]
   uint32_t* mbits = nullptr;  // [ceil(c/32) x max_batch] probe bitsets, word-major
   int32_t* mpre = nullptr;    // [ceil(c/32) x max_batch] probes in earlier words
+  float* sumscores = nullptr;  // [c] summed scores of a batch (shared probes)
   fh::Part* parts = nullptr;  // [max_batch x parts_per_q]
   int64_t parts_per_q = 0;
   unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up
@@ -133,6 +134,7 @@ void free_engine(fh_engine* e) {
   (void)hipFree(e->c2t);
   (void)hipFree(e->Ec);
   (void)hipFree(e->t2c);
+  (void)hipFree(e->sumscores);
   (void)hipFree(e->cq);
   (void)hipFree(e->csig);
   (void)hipFree(e->cq_mfma);
@@ -180,10 +182,53 @@ fh_status check_common(const fh_engine* e, const void* h, int64_t B) {
 }
 
 fh_status check_mode(int mode, float temperature) {
-  if (mode < 0 || mode > 3) return fail(FH_EINVAL, "mode must be FH_PROBE_* | FH_TOKEN_*");
+  if (mode < 0 || mode > 7) return fail(FH_EINVAL, "mode must be FH_PROBE_* | FH_TOKEN_*");
+  if ((mode & FH_PROBE_SHARED) && (mode & FH_PROBE_SAMPLE))
+    return fail(FH_EINVAL, "FH_PROBE_SHARED chooses probes by score; it cannot be sampled");
   if (mode != 0 && !(temperature > 0.f && std::isfinite(temperature)))
     return fail(FH_EINVAL, "sampling needs a finite temperature > 0");
   return FH_OK;
+}
+
+
+// One probe set for the whole batch: the top p of the summed stage-1 scores
+// (FH_PROBE_SHARED, B > 1), then stage 2 for every query over those probes:
+// for bf16 one matrix-core GEMM [B x d] . [d x p b] over the probes' rows of
+// the cluster-contiguous E, else the row GEMV reading one shared probe row.
+fh_status shared_forward(fh_engine* e, hipStream_t st, const fh::KernelCtx& k, const void* h,
+                         int64_t B, int64_t p, int token_sample, float tprime, uint64_t seed,
+                         int32_t* out_token, float* out_token_logit, float* out_lse,
+                         int32_t* out_clusters, int32_t* out_ids, float* out_logits) {
+  hipError_t r = launch_stage1(e, st, k, h, B, e->scores);
+  if (r != hipSuccess) return hip_fail(r, "score launch");
+  r = timed(e, st, "sum_scores", [&] { return fh::launch_sum_rows(k, e->scores, (int)B, e->sumscores); });
+  if (r != hipSuccess) return hip_fail(r, "summed scores");
+  r = timed(e, st, "select", [&] {
+    return fh::launch_select(k, e->sumscores, 1, (int)p, 0, 1.f, seed, e->sel, (int)p, nullptr,
+                             nullptr);
+  });
+  if (r != hipSuccess) return hip_fail(r, "select launch");
+  if (out_clusters) {
+    r = fh::launch_broadcast_row(k, e->sel, (int)p, (int)B, out_clusters);
+    if (r != hipSuccess) return hip_fail(r, "probe broadcast");
+  }
+  int64_t nparts = 0;
+  if (e->dtype == FH_BF16) {
+    r = timed(e, st, "gather_shared_mfma", [&] {
+      return fh::launch_gather_shared_mfma(k, e->cus, h, (int)B, e->sel, (int)p, token_sample,
+                                           tprime, seed, out_ids, out_logits, e->parts, &nparts);
+    });
+  } else {
+    r = timed(e, st, "gather", [&] {
+      return fh::launch_gather(k, h, (int)B, e->sel, (int)p, token_sample, tprime, seed, out_ids,
+                               out_logits, e->parts, &nparts, 0);
+    });
+  }
+  if (r != hipSuccess) return hip_fail(r, "gather launch");
+  r = timed(e, st, "finish", [&] {
+    return fh::launch_finish(k, e->parts, (int)B, nparts, out_token, out_token_logit, out_lse);
+  });
+  return r == hipSuccess ? FH_OK : hip_fail(r, "finish launch");
 }
 
 }  // namespace
@@ -297,6 +342,7 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   const Alloc allocs[] = {
       {(void**)&e->c2t, sizeof(int32_t) * (size_t)v, "C2T"},
       {(void**)&e->t2c, sizeof(int32_t) * (size_t)v, "token clusters"},
+      {(void**)&e->sumscores, sizeof(float) * (size_t)c, "summed scores"},
       {(void**)&e->Ec, (size_t)(v * d) * (dtype == FH_BF16 ? 2 : 4), "cluster-contiguous E"},
       {(void**)&e->scores, sizeof(float) * (size_t)(max_batch * c), "scores"},
       {(void**)&e->sel, sizeof(int32_t) * (size_t)(max_batch * c), "selection"},
@@ -417,6 +463,10 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
     hipError_t r = timed(e, st, "batch1", [&] { return fh::launch_batch1(f); });
     return r == hipSuccess ? FH_OK : hip_fail(r, "batch-1 launch");
   }
+
+  if (mode & FH_PROBE_SHARED)
+    return shared_forward(e, st, k, h, B, p, token_sample, tprime, seed, out_token, out_token_logit,
+                          out_lse, out_clusters, out_ids, out_logits);
 
   // batches of bf16 queries that share probes: stage 2 cluster-major on the
   // matrix cores, each probed cluster's rows read once for all its queries

@@ -57,7 +57,12 @@ hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, 
                          uint32_t* mbits = nullptr, int32_t* mpre = nullptr);
 hipError_t launch_gather(const KernelCtx& k, const void* h, int B, const int32_t* S, int p,
                          int token_sample, float tprime, uint64_t seed, int32_t* out_ids,
-                         float* out_logits, Part* parts, int64_t* nparts);
+                         float* out_logits, Part* parts, int64_t* nparts,
+                         int ldS = -1);
+// batch-shared probes: summed scores, and one probe list broadcast to every row
+hipError_t launch_sum_rows(const KernelCtx& k, const float* scores, int B, float* out);
+hipError_t launch_broadcast_row(const KernelCtx& k, const int32_t* src, int n, int B,
+                                int32_t* dst);
 hipError_t launch_dense(const KernelCtx& k, const void* h, int B, int token_sample, float tprime,
                         uint64_t seed, float* out_logits, Part* parts, int64_t* nparts);
 // Matrix-core (MFMA) paths for batches of bf16 queries.
@@ -74,6 +79,13 @@ hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, 
 // probed cluster's rows are read once for all queries that probe it.
 int64_t gather_cm_blocks(int64_t c, int cus);
 bool gather_cm_fits(int B, int64_t p, int64_t c);
+int gather_cm_max_batch();  // queries the cluster-major stage 2 can take
+// stage 2 over one probe list shared by the batch, as the matrix-core GEMM
+// with a row map (bf16 engines with the cluster-contiguous E)
+hipError_t launch_gather_shared_mfma(const KernelCtx& k, int cus, const void* h, int B,
+                                     const int32_t* S, int p, int token_sample, float tprime,
+                                     uint64_t seed, int32_t* out_ids, float* out_logits,
+                                     Part* parts, int64_t* nparts);
 hipError_t launch_gather_cm(const KernelCtx& k, int cus, const void* h, int B, int p,
                             const uint32_t* mbits,
                             const int32_t* mpre, int token_sample, float tprime, uint64_t seed,

@@ -373,11 +373,11 @@ hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, 
 template <typename T>
 static hipError_t gather_t(const KernelCtx& k, const void* h, int B, const int32_t* S, int p,
                            int token_sample, float tprime, uint64_t seed, int32_t* out_ids,
-                           float* out_logits, Part* parts, int64_t* nparts) {
+                           float* out_logits, Part* parts, int64_t* nparts, int ldS) {
   RowsArgs a{};
   a.M = k.Ec ? k.Ec : k.E; a.contiguous = k.Ec != nullptr;
   a.nrows = (int64_t)p * k.b; a.d = k.d; a.c2t = k.c2t; a.bsz = (int)k.b;
-  a.S = S; a.ldS = p; a.H = h; a.B = B; a.out_vals = out_logits; a.ld_vals = a.nrows;
+  a.S = S; a.ldS = ldS < 0 ? p : ldS; a.H = h; a.B = B; a.out_vals = out_logits; a.ld_vals = a.nrows;
   a.out_ids = out_ids; a.token_sample = token_sample; a.tprime = tprime; a.seed = seed;
   a.parts = parts;
   return launch_rows<T, 1, kGatherRPW, true, true>(a, k.stream, nparts);
@@ -385,9 +385,44 @@ static hipError_t gather_t(const KernelCtx& k, const void* h, int B, const int32
 
 hipError_t launch_gather(const KernelCtx& k, const void* h, int B, const int32_t* S, int p,
                          int token_sample, float tprime, uint64_t seed, int32_t* out_ids,
-                         float* out_logits, Part* parts, int64_t* nparts) {
-  return k.bf16 ? gather_t<uint16_t>(k, h, B, S, p, token_sample, tprime, seed, out_ids, out_logits, parts, nparts)
-                : gather_t<float>(k, h, B, S, p, token_sample, tprime, seed, out_ids, out_logits, parts, nparts);
+                         float* out_logits, Part* parts, int64_t* nparts, int ldS) {
+  return k.bf16 ? gather_t<uint16_t>(k, h, B, S, p, token_sample, tprime, seed, out_ids, out_logits, parts, nparts, ldS)
+                : gather_t<float>(k, h, B, S, p, token_sample, tprime, seed, out_ids, out_logits, parts, nparts, ldS);
+}
+
+// ---- batch-shared probes (explainer §4.2: share the cluster selection
+// across the batch; read as the top p of the summed scores)
+
+// out[k] = sum_b s[b, k], b ascending.
+__global__ __launch_bounds__(256) void k_sum_rows(const float* __restrict__ s, int B, int c,
+                                                  float* __restrict__ out) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= c) return;
+  float acc = 0.f;
+#pragma unroll 16
+  for (int b = 0; b < B; ++b) acc += s[(int64_t)b * c + k];
+  out[k] = acc;
+}
+
+// dst[q * n + i] = src[i]: one probe list as every row of [B x n].
+__global__ __launch_bounds__(256) void k_broadcast_row(const int32_t* __restrict__ src, int n,
+                                                       int B, int32_t* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < (int64_t)n * B) dst[i] = src[i % n];
+}
+
+hipError_t launch_sum_rows(const KernelCtx& k, const float* scores, int B, float* out) {
+  hipLaunchKernelGGL(k_sum_rows, dim3((unsigned)((k.c + 255) / 256)), dim3(256), 0, k.stream,
+                     scores, B, (int)k.c, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_broadcast_row(const KernelCtx& k, const int32_t* src, int n, int B,
+                                int32_t* dst) {
+  const int64_t m = (int64_t)n * B;
+  hipLaunchKernelGGL(k_broadcast_row, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, k.stream,
+                     src, n, B, dst);
+  return hipGetLastError();
 }
 
 template <typename T>

@@ -108,6 +108,13 @@ struct MfmaArgs {
   const int32_t* t2c;
   const uint32_t* bits;
   int W;
+  // optional row map (stage 2 over a probe list shared by the batch): logical
+  // row r is row S[r / bsz] * bsz + r % bsz of A (the cluster-contiguous E),
+  // its token C2T of that row; out_ids[q * ld_out + r] receives the token
+  const int32_t* rows_map;
+  int bsz;
+  const int32_t* c2t;
+  int32_t* out_ids;
 };
 
 constexpr int kHRow = 128 + 8;  // LDS row of a staged h block (bf16), padded
@@ -149,10 +156,14 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this lane's rows (clamped for loads; results past R are dropped)
+  // this lane's rows (clamped for loads; results past R are dropped), as
+  // rows of A (through the row map when there is one)
+  auto phys = [&](int64_t r) -> int64_t {
+    return a.rows_map ? (int64_t)a.rows_map[r / a.bsz] * a.bsz + r % a.bsz : r;
+  };
   int64_t ra[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) ra[m] = min(rbase + 16 * m + col, a.R - 1);
+  for (int m = 0; m < MT; ++m) ra[m] = phys(min(rbase + 16 * m + col, a.R - 1));
 
   if constexpr (QB == 0) {
     const uint16_t* A = static_cast<const uint16_t*>(a.A);
@@ -374,7 +385,9 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
         const int64_t r = rbase + 16 * m + 4 * g + i;
         if (r < a.R && q < a.B) {
           if (a.out) a.out[(int64_t)q * a.ld_out + r] = acc[m][n][i];
-          Part pt = part_of(acc[m][n][i], (int32_t)r, a.token_sample, a.tprime, a.seed, (uint32_t)q);
+          const int32_t tok = a.rows_map ? a.c2t[phys(r)] : (int32_t)r;
+          if (a.out_ids) a.out_ids[(int64_t)q * a.ld_out + r] = tok;
+          Part pt = part_of(acc[m][n][i], tok, a.token_sample, a.tprime, a.seed, (uint32_t)q);
           if (a.bits) {
             const int k = a.t2c[r];
             const bool probed = (a.bits[(int64_t)q * a.W + (k >> 5)] >> (k & 31)) & 1u;
@@ -406,13 +419,14 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
 // ======================================================================
 // Cluster-major stage 2 (explainer §1.2.1, §1.2.4; batch semantics: each
 // query still takes only its own probes).  Workgroup x owns clusters
-// [8x, 8x + 8); wave w takes clusters 8x + w and 8x + w + 4.  For a cluster
-// k the wave lists the queries whose probe bitset holds k (ballots over the
-// bitset words, ascending query order), then for each 16-slot row tile of
-// the cluster (rows Ec[k b + j] of the cluster-contiguous E) and each tile of
-// 16 of those queries computes the 16 x 16 logits with MFMA over d (the next
-// 128-element block's loads in flight during the current block's products),
-// so the cluster's rows are read once for all its queries.  The epilogue
+// [8x, 8x + 8).  For each of them the workgroup lists the queries whose
+// probe bitset holds it (ballots over the bitset words, ascending query
+// order).  The work items -- (cluster, 16-slot row tile of the cluster's rows
+// Ec[k b + j] in the cluster-contiguous E, tile of 16 of its queries) -- are
+// taken round-robin by the four waves; each computes its 16 x 16 logits with
+// MFMA over d (the next 128-element block's loads in flight during the
+// current block's products), so a cluster's rows are read once for all its
+// queries and a much-probed cluster's query tiles run in parallel.  The epilogue
 // writes the optional outputs at the query's canonical position (probe rank
 // from the bitset and its word prefix counts, then slot) and folds
 // (z, token) into a per-wave, per-query partial in LDS; the workgroup's four
@@ -444,7 +458,8 @@ struct GatherCmArgs {
 __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
   __shared__ uint32_t s_word[kCmMaxB];
   __shared__ int s_pre[kCmMaxB];
-  __shared__ short s_q[4][kCmMaxB];
+  __shared__ short s_q[kCmClusters][kCmMaxB];
+  __shared__ int s_n[kCmClusters];
   __shared__ Part s_acc[4][kCmMaxB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -457,89 +472,106 @@ __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
     for (int v = 0; v < 4; ++v) s_acc[v][q] = part_empty();
   }
   __syncthreads();
-  const int64_t ldo = (int64_t)a.p * a.b;
+  // the queries probing each of the workgroup's clusters, ascending
   for (int ci = wave; ci < kCmClusters; ci += 4) {
     const int k = k0 + ci;
-    if (k >= a.c) break;
-    const int bit = k & 31;
-    // the queries probing k, ascending
     int n = 0;
-    for (int qb = 0; qb < a.B; qb += 64) {
-      const int q = qb + lane;
-      const bool in = q < a.B && ((s_word[q] >> bit) & 1u);
-      const unsigned long long m = __ballot(in);
-      if (in)
-        s_q[wave][n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
-            (short)q;
-      n += __popcll(m);
-    }
-    if (n == 0) continue;
-    for (int rt = 0; 16 * rt < a.b; ++rt) {
-      const int64_t f = (int64_t)k * a.b + min(16 * rt + col, a.b - 1);
-      const uint16_t* Ar = a.Ec + f * a.d;
-      // the tile's token ids, loaded ahead of the products
-      int32_t tok[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        tok[i] = a.c2t[(int64_t)k * a.b + min(16 * rt + 4 * g + i, a.b - 1)];
-      for (int qt = 0; 16 * qt < n; ++qt) {
-        const int qi = 16 * qt + col;
-        const int q = s_q[wave][min(qi, n - 1)];
-        const uint16_t* Hr = a.H + (int64_t)q * a.d;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int nblk = a.d / 128;
-        // ping-pong: the next 128-element block is in flight during the MFMAs
-        uint4 a0[4], b0[4], a1[4], b1[4];
-        auto ld = [&](int blk, uint4 (&av)[4], uint4 (&bv)[4]) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {  // step s: elements 32 s + 8 g .. + 7 of the block
-            const int kk = 128 * blk + 32 * s + 8 * g;
-            av[s] = *reinterpret_cast<const uint4*>(Ar + kk);
-            bv[s] = *reinterpret_cast<const uint4*>(Hr + kk);
-          }
-        };
-        if (nblk > 0) ld(0, a0, b0);
-        for (int blk = 0; blk < nblk; blk += 2) {
-          if (blk + 1 < nblk) ld(blk + 1, a1, b1);
-#pragma unroll
-          for (int s = 0; s < 4; ++s) acc = mfma16(a0[s], b0[s], acc);
-          if (blk + 1 < nblk) {
-            if (blk + 2 < nblk) ld(blk + 2, a0, b0);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma16(a1[s], b1[s], acc);
-          }
-        }
-        for (int kb = nblk * 128; kb < a.d; kb += 32) {
-          const int kk = kb + 8 * g;
-          const bool ok = kk < a.d;
-          const uint4 av = ok ? *reinterpret_cast<const uint4*>(Ar + kk) : uint4{0u, 0u, 0u, 0u};
-          const uint4 bv = ok ? *reinterpret_cast<const uint4*>(Hr + kk) : uint4{0u, 0u, 0u, 0u};
-          acc = mfma16(av, bv, acc);
-        }
-        // lane: slots j = 16 rt + 4 g + i of cluster k for query q
-        const bool qok = qi < n;
-        const int pos = qok ? s_pre[q] + __popc(s_word[q] & ((1u << bit) - 1u)) : 0;
-        Part pt = part_empty();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = 16 * rt + 4 * g + i;
-          if (qok && j < a.b) {
-            const int64_t o = (int64_t)q * ldo + (int64_t)pos * a.b + j;
-            if (a.out_logits) a.out_logits[o] = acc[i];
-            if (a.out_ids) a.out_ids[o] = tok[i];
-            pt = part_merge(pt, part_of(acc[i], tok[i], a.token_sample, a.tprime, a.seed, (uint32_t)q));
-          }
-        }
-#pragma unroll
-        for (int m = 16; m <= 32; m *= 2) {
-          const Part o{__shfl_xor(pt.key, m), __shfl_xor(pt.z, m), __shfl_xor(pt.m, m),
-                       __shfl_xor(pt.s, m), __shfl_xor(pt.id, m)};
-          pt = (lane & m) ? part_merge(o, pt) : part_merge(pt, o);
-        }
-        if (g == 0 && qok) s_acc[wave][q] = part_merge(s_acc[wave][q], pt);
+    if (k < a.c) {
+      const int bit = k & 31;
+      for (int qb = 0; qb < a.B; qb += 64) {
+        const int q = qb + lane;
+        const bool in = q < a.B && ((s_word[q] >> bit) & 1u);
+        const unsigned long long m = __ballot(in);
+        if (in)
+          s_q[ci][n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = (short)q;
+        n += __popcll(m);
       }
     }
+    if (lane == 0) s_n[ci] = n;
+  }
+  __syncthreads();
+  // work items (cluster, row tile, query tile), in that order, taken round-
+  // robin by the four waves: a cluster probed by many queries spreads its
+  // query tiles over the waves
+  const int nrt = (a.b + 15) / 16;
+  int total = 0;
+#pragma unroll
+  for (int ci = 0; ci < kCmClusters; ++ci) total += nrt * ((s_n[ci] + 15) / 16);
+  const int64_t ldo = (int64_t)a.p * a.b;
+  for (int it = wave; it < total; it += 4) {
+    int ci = 0, rem = it;
+    for (; ci < kCmClusters; ++ci) {
+      const int cnt = nrt * ((s_n[ci] + 15) / 16);
+      if (rem < cnt) break;
+      rem -= cnt;
+    }
+    const int n = s_n[ci];
+    const int nqt = (n + 15) / 16;
+    const int rt = rem / nqt, qt = rem % nqt;
+    const int k = k0 + ci;
+    const int bit = k & 31;
+    const int64_t f = (int64_t)k * a.b + min(16 * rt + col, a.b - 1);
+    const uint16_t* Ar = a.Ec + f * a.d;
+    // the tile's token ids, loaded ahead of the products
+    int32_t tok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tok[i] = a.c2t[(int64_t)k * a.b + min(16 * rt + 4 * g + i, a.b - 1)];
+    const int qi = 16 * qt + col;
+    const int q = s_q[ci][min(qi, n - 1)];
+    const uint16_t* Hr = a.H + (int64_t)q * a.d;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nblk = a.d / 128;
+    // ping-pong: the next 128-element block is in flight during the MFMAs
+    // (measured: rings of 3, 4 or 6 blocks are no faster)
+    uint4 a0[4], b0[4], a1[4], b1[4];
+    auto ld = [&](int blk, uint4 (&av)[4], uint4 (&bv)[4]) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {  // step s: elements 32 s + 8 g .. + 7 of the block
+        const int kk = 128 * blk + 32 * s + 8 * g;
+        av[s] = *reinterpret_cast<const uint4*>(Ar + kk);
+        bv[s] = *reinterpret_cast<const uint4*>(Hr + kk);
+      }
+    };
+    if (nblk > 0) ld(0, a0, b0);
+    for (int blk = 0; blk < nblk; blk += 2) {
+      if (blk + 1 < nblk) ld(blk + 1, a1, b1);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = mfma16(a0[s], b0[s], acc);
+      if (blk + 1 < nblk) {
+        if (blk + 2 < nblk) ld(blk + 2, a0, b0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma16(a1[s], b1[s], acc);
+      }
+    }
+    for (int kb = nblk * 128; kb < a.d; kb += 32) {
+      const int kk = kb + 8 * g;
+      const bool ok = kk < a.d;
+      const uint4 av = ok ? *reinterpret_cast<const uint4*>(Ar + kk) : uint4{0u, 0u, 0u, 0u};
+      const uint4 bv = ok ? *reinterpret_cast<const uint4*>(Hr + kk) : uint4{0u, 0u, 0u, 0u};
+      acc = mfma16(av, bv, acc);
+    }
+    // lane: slots j = 16 rt + 4 g + i of cluster k for query q
+    const bool qok = qi < n;
+    const int pos = qok ? s_pre[q] + __popc(s_word[q] & ((1u << bit) - 1u)) : 0;
+    Part pt = part_empty();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 16 * rt + 4 * g + i;
+      if (qok && j < a.b) {
+        const int64_t o = (int64_t)q * ldo + (int64_t)pos * a.b + j;
+        if (a.out_logits) a.out_logits[o] = acc[i];
+        if (a.out_ids) a.out_ids[o] = tok[i];
+        pt = part_merge(pt, part_of(acc[i], tok[i], a.token_sample, a.tprime, a.seed, (uint32_t)q));
+      }
+    }
+#pragma unroll
+    for (int m = 16; m <= 32; m *= 2) {
+      const Part o{__shfl_xor(pt.key, m), __shfl_xor(pt.z, m), __shfl_xor(pt.m, m),
+                   __shfl_xor(pt.s, m), __shfl_xor(pt.id, m)};
+      pt = (lane & m) ? part_merge(o, pt) : part_merge(pt, o);
+    }
+    if (g == 0 && qok) s_acc[wave][q] = part_merge(s_acc[wave][q], pt);
   }
   __syncthreads();
   for (int q = threadIdx.x; q < a.B; q += 256) {
@@ -669,6 +701,7 @@ hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, 
 int64_t gather_cm_blocks(int64_t c, int) { return (c + kCmClusters - 1) / kCmClusters; }
 // Cluster-major pays off when clusters are shared: the expected number of
 // queries per probed cluster, B p / (c (1 - (1 - p/c)^B)), is at least 2.
+int gather_cm_max_batch() { return kCmMaxB; }
 bool gather_cm_fits(int B, int64_t p, int64_t c) {
   if (B < 2 || B > kCmMaxB) return false;
   const double f = (double)p / (double)c;
@@ -699,6 +732,18 @@ hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, 
   a.A = k.E; a.R = k.v; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
   a.out = out_logits; a.ld_out = k.v;
   a.token_sample = token_sample; a.tprime = tprime; a.seed = seed; a.parts = parts;
+  return mfma_dispatch<0, true>(a, cus, k.stream, nparts);
+}
+
+hipError_t launch_gather_shared_mfma(const KernelCtx& k, int cus, const void* h, int B,
+                                     const int32_t* S, int p, int token_sample, float tprime,
+                                     uint64_t seed, int32_t* out_ids, float* out_logits,
+                                     Part* parts, int64_t* nparts) {
+  MfmaArgs a{};
+  a.A = k.Ec; a.R = (int64_t)p * k.b; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
+  a.out = out_logits; a.ld_out = a.R; a.out_ids = out_ids;
+  a.token_sample = token_sample; a.tprime = tprime; a.seed = seed; a.parts = parts;
+  a.rows_map = S; a.bsz = (int)k.b; a.c2t = k.c2t;
   return mfma_dispatch<0, true>(a, cus, k.stream, nparts);
 }
 

@@ -21,7 +21,7 @@ from _gpu import assert_report, host, need_gpu, problem_tensors, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TOPK, PSAMPLE, TSAMPLE = 0, 1, 2
+TOPK, PSAMPLE, TSAMPLE, SHARED = 0, 1, 2, 4
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -186,6 +186,49 @@ def test_batches_at_the_cluster_major_limit(B):
     rows = sorted({0, 1, 100, 255, B - 1})
     assert_report(parity.check_forward(ref, pb.H[:B], 96, TOPK, 1.0, 0, out, queries=rows),
                   f"cm limit B={B}")
+    head.close()
+
+
+@pytest.mark.parametrize("shape,quant,B,p,mode,T", [
+    ("tiny", "none", 8, 16, SHARED, 1.0),               # fp32: query-major, one probe row
+    ("tiny", "none", 64, 16, SHARED | TSAMPLE, 0.8),
+    ("llama32_1b", "none", 8, 512, SHARED, 1.0),        # bf16: one GEMM over the probes' rows
+    ("llama32_1b", "int4", 64, 512, SHARED | TSAMPLE, 0.7),
+    ("llama32_1b", "none", 1, 512, SHARED, 1.0),        # B = 1: the single launch, top-p
+])
+def test_shared_probes(shape, quant, B, p, mode, T):
+    """One probe set for the batch (the top p of the summed scores): the same
+    set in every row, and every query's stage 2 and finish over it."""
+    pb = make_problem(shape, nq=max(B, 8))
+    head, H = _engine(pb, quant=quant, max_batch=B)
+    ref = _oracle(pb, quant)
+    say("shared", shape, quant, B, p, mode)
+    out = host(head.forward(H[:B], p, mode=mode, temperature=T, seed=9, want_clusters=True,
+                            want_retrieved=True))
+    assert np.all(out["clusters"] == out["clusters"][0])
+    assert_report(parity.check_forward(ref, pb.H[:B], p, mode, T, 9, out), f"shared {shape} B={B}")
+    if B == 1:
+        plain = host(head.forward(H[:1], p, mode=mode & TSAMPLE, temperature=T, seed=9,
+                                  want_clusters=True))
+        assert np.array_equal(plain["clusters"], out["clusters"])
+        assert np.array_equal(plain["token"], out["token"])
+    head.close()
+
+
+def test_shared_probes_large_batch():
+    """257 bf16 queries sharing one probe set (one GEMM over the probes' rows,
+    no batch limit), checked on sampled rows; sampled shared probes are refused."""
+    from lm_output_head_amd import FlashHeadError
+    pb = _custom_problem(8192, 128, 512, "bf16", 257, seed=17)
+    head, H = _engine(pb, max_batch=257)
+    ref = _oracle(pb)
+    say("shared B=257")
+    out = host(head.forward(H, 96, mode=SHARED, want_clusters=True, want_retrieved=True))
+    assert np.all(out["clusters"] == out["clusters"][0])
+    assert_report(parity.check_forward(ref, pb.H, 96, SHARED, 1.0, 0, out,
+                                       queries=[0, 1, 128, 256]), "shared B=257")
+    with pytest.raises(FlashHeadError):
+        head.forward(H[:4], 96, mode=SHARED | PSAMPLE, temperature=1.0)
     head.close()
 
 
