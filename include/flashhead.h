@@ -248,7 +248,10 @@ fh_status fh_profile_end(fh_engine* e, fh_kernel_time* out, int max, int* count)
  *                 device memory.  Batches of B > 1 use one launch per stage.
  *   FH_PATH_MULTI always one launch per stage.
  * Both paths return the same ids and logits; the LSE may differ in the last
- * bits (a different merge order).
+ * bits (a different merge order).  While `stream` is being captured into a
+ * graph, fh_forward uses the per-stage launches whatever the path: they keep
+ * no state between calls, so the graph can be replayed (the single launch
+ * tells calls apart by a counter kept on the host).
  */
 enum { FH_PATH_AUTO = 0, FH_PATH_MULTI = 1 };
 fh_status fh_set_path(fh_engine* e, int path);

@@ -437,7 +437,13 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
   const float tprime = token_sample ? temperature : 1.f;
   int32_t* S = out_clusters ? out_clusters : e->sel;
 
-  if (B == 1 && e->path == FH_PATH_AUTO && fh::batch1_fits(p, e->b, e->cus)) {
+  // The single launch identifies a call by a host-side epoch baked into its
+  // arguments, which a captured graph would replay unchanged; under stream
+  // capture the per-stage launches (no state between calls) are used.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &capture) != hipSuccess) capture = hipStreamCaptureStatusNone;
+  if (B == 1 && e->path == FH_PATH_AUTO && capture == hipStreamCaptureStatusNone &&
+      fh::batch1_fits(p, e->b, e->cus)) {
     fh::FusedLaunch f{};
     f.ctx = &k;
     f.cus = e->cus;

@@ -1,0 +1,63 @@
+"""Graph capture: FlashHead calls captured into a HIP graph (torch.cuda.CUDAGraph
+over the caller's stream) and replayed with new inputs give exactly the
+results of eager calls (explainer §2.2.2 suggests capturing the whole flow).
+Replays run with eager work and synchronisations between them."""
+
+import numpy as np
+import pytest
+import torch
+
+from synth import make_problem
+
+from _gpu import need_gpu, problem_tensors, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    from lm_output_head_amd import load_library
+    load_library()
+
+
+@pytest.mark.parametrize("shape,quant,B,p,mode", [
+    ("llama32_1b", "none", 1, 512, 0),   # batch 1: per-stage launches under capture
+    ("llama32_1b", "int4", 8, 512, 2),   # matrix-core stage 1, sampled tokens
+    ("tiny", "none", 4, 16, 3),          # fp32, sampled probes and tokens
+    ("llama32_1b", "none", 8, 256, 4),   # shared probes
+])
+def test_captured_calls_replay_exactly(shape, quant, B, p, mode):
+    from lm_output_head_amd import FlashHead
+    pb = make_problem(shape, nq=4 * B)
+    E, C, H = problem_tensors(pb)
+    head = FlashHead(E, C, pb.C2T, quant=quant, max_batch=B)
+    h_static = H[:B].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the graph
+        head.forward(h_static, p, mode=mode, temperature=0.9, seed=3)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("graph capture", shape, quant, B, p, mode)
+    with torch.cuda.graph(g):
+        out = head.forward(h_static, p, mode=mode, temperature=0.9, seed=3, want_clusters=True,
+                           want_retrieved=True)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        batch = H[rep * B:(rep + 1) * B]
+        h_static.copy_(batch)
+        g.replay()
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy().copy() for k, v in out.items()}
+        ref = head.forward(batch.contiguous(), p, mode=mode, temperature=0.9, seed=3,
+                           want_clusters=True, want_retrieved=True)
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            if k == "lse":  # at B = 1 eager calls take the single launch: LSE to rounding
+                assert np.allclose(got[k], v.cpu().numpy(), rtol=1e-5, atol=1e-6), rep
+            else:
+                assert np.array_equal(got[k], v.cpu().numpy()), (rep, k)
+    head.sync_status()
+    head.close()
