@@ -638,7 +638,11 @@ hipError_t launch_mfma_relayout(const KernelCtx& k, uint8_t* cq_mfma, uint16_t* 
 
 // Tile shape: all query tiles in one workgroup (up to 8: the rows are read
 // once), two row tiles per wave; fewer while that leaves less than ~2
-// workgroups per CU.
+// workgroups per CU.  With 8 query tiles, two row tiles' accumulators and
+// loads take more than half the register file (one wave per SIMD), so a wave
+// keeps one row tile: on the dense head at 128 queries of the Qwen-3-4B shape
+// that is 384 us per call against 511 us, although every workgroup then
+// stages h for half as many rows.
 struct GemmShape {
   int nt, mt;
 };
@@ -648,7 +652,7 @@ static GemmShape gemm_shape(int64_t R, int B, int cus) {
   auto wgs = [&](const GemmShape& x) {
     return ((R + 64 * x.mt - 1) / (64 * x.mt)) * ((tiles + x.nt - 1) / x.nt);
   };
-  if (wgs(s) < 2 * (int64_t)cus) s.mt = 1;
+  if (s.nt == 8 || wgs(s) < 2 * (int64_t)cus) s.mt = 1;
   while (s.nt > 1 && wgs(s) < (int64_t)cus) s.nt /= 2;
   return s;
 }

@@ -186,6 +186,13 @@ def test_batches_at_the_cluster_major_limit(B):
     rows = sorted({0, 1, 100, 255, B - 1})
     assert_report(parity.check_forward(ref, pb.H[:B], 96, TOPK, 1.0, 0, out, queries=rows),
                   f"cm limit B={B}")
+    # the matrix-core GEMMs at 128 queries per workgroup: dense head (sampled
+    # tokens) and stage-1 scores, on the same rows
+    dn = host(head.dense(H[:B], TSAMPLE, 0.9, 4))
+    assert_report(parity.check_dense(pb.E, pb.H[:B], TSAMPLE, 0.9, 4, dn, queries=rows),
+                  f"cm limit dense B={B}")
+    s = host({"s": head.score(H[:B])})["s"]
+    assert_report(parity.check_scores(ref.C_hat, pb.H[rows], s[rows]), f"cm limit scores B={B}")
     head.close()
 
 
