@@ -637,12 +637,17 @@ hipError_t launch_mfma_relayout(const KernelCtx& k, uint8_t* cq_mfma, uint16_t* 
 }
 
 // Tile shape: all query tiles in one workgroup (up to 8: the rows are read
-// once), two row tiles per wave; fewer while that leaves less than ~2
-// workgroups per CU.  With 8 query tiles, two row tiles' accumulators and
-// loads take more than half the register file (one wave per SIMD), so a wave
-// keeps one row tile: on the dense head at 128 queries of the Qwen-3-4B shape
-// that is 384 us per call against 511 us, although every workgroup then
-// stages h for half as many rows.
+// once), two row tiles per wave.  One row tile when that leaves fewer than 4
+// workgroups per CU, then fewer query tiles per workgroup while there are
+// fewer than 2 per CU.  Against thresholds of 2 and 1 this gives 37 us
+// instead of 43 us for the INT4 stage 1 at 128 queries of the Qwen-3-4B
+// shape and 149 us instead of 163 us for the dense head at 64 queries of the
+// Llama-3.2-1B shape; 4 and 8 workgroups per CU gain no more.  With 8 query
+// tiles a wave always keeps one row tile: two row tiles' accumulators and
+// loads take more than half the register file (one wave per SIMD), and the
+// dense head at 128 queries of the Qwen-3-4B shape took 511 us per call
+// against 384 us, although every workgroup now stages h for half as many
+// rows.
 struct GemmShape {
   int nt, mt;
 };
@@ -652,8 +657,8 @@ static GemmShape gemm_shape(int64_t R, int B, int cus) {
   auto wgs = [&](const GemmShape& x) {
     return ((R + 64 * x.mt - 1) / (64 * x.mt)) * ((tiles + x.nt - 1) / x.nt);
   };
-  if (s.nt == 8 || wgs(s) < 2 * (int64_t)cus) s.mt = 1;
-  while (s.nt > 1 && wgs(s) < (int64_t)cus) s.nt /= 2;
+  if (s.nt == 8 || wgs(s) < 4 * (int64_t)cus) s.mt = 1;
+  while (s.nt > 1 && wgs(s) < 2 * (int64_t)cus) s.nt /= 2;
   return s;
 }
 
