@@ -63,8 +63,11 @@ constexpr int kPpRows = 4;
 // One k-means++ step's distance refresh against centre i:
 //   D[t] = min(D[t], 1 - inv[t] inv[ct] (E_t . E_ct))   (= when i == 0)
 // with the table read in its own storage type (coalesced 16-byte row loads,
-// the centre's row in registers), and part[w] = sum of D^2 over workgroup
-// w's rows in fp64, in row order within each wave, then wave 0..3.
+// the centre's row in registers), and the sum of D^2 over workgroup w's rows
+// in fp64 (row order within each wave, then wave 0..3) stored at
+// part[(w % n) * 1024 + w / n], n = ceil(gridDim.x / 1024): the draw's
+// thread t, which owns partials t n .. t n + n - 1, reads them 1024 apart,
+// coalesced with its neighbours.
 template <typename T, int MAXM, int RPI = 1, int ROWS = kPpRows>
 __global__ __launch_bounds__(256) void k_pp_step(const T* __restrict__ E,
                                                  const float* __restrict__ inv, int64_t v, int d,
@@ -91,7 +94,11 @@ __global__ __launch_bounds__(256) void k_pp_step(const T* __restrict__ E,
   wave_rows<T, MAXM, 1, RPI>(E, d, lane, hv, 1, r0, r1, 1, row, row, sink);
   if (lane == 0) wsum[wave] = s;
   __syncthreads();
-  if (threadIdx.x == 0) part[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  if (threadIdx.x == 0) {
+    const int64_t n = ((int64_t)gridDim.x + 1023) / 1024;
+    part[((int64_t)blockIdx.x % n) * 1024 + (int64_t)blockIdx.x / n] =
+        ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  }
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave, in fp64 (fixed order).
@@ -102,22 +109,6 @@ __device__ __forceinline__ double wave_prefix(double x, int lane) {
     if (lane >= off) x += y;
   }
   return x;
-}
-
-// Partials of partials: part2[g] = sum of part[256 g .. 256 g + 255] (lane
-// prefix per wave, then the four wave sums in order).  Coalesced, and spread
-// over many workgroups, so the draw below reads only a few of them.
-constexpr int kPpGroup = 256;
-
-__global__ __launch_bounds__(256) void k_pp_reduce(const double* __restrict__ part, int64_t nb,
-                                                   double* __restrict__ part2) {
-  __shared__ double ws[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t j = (int64_t)blockIdx.x * kPpGroup + threadIdx.x;
-  const double x = wave_prefix(j < nb ? part[j] : 0.0, lane);
-  if (lane == 63) ws[wave] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) part2[blockIdx.x] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
 }
 
 // One wave walks vals[lo, hi) 64 at a time from the running sum *base and
@@ -144,26 +135,33 @@ __device__ __forceinline__ int64_t wave_walk(Load load, int64_t lo, int64_t hi, 
   return hi - 1;
 }
 
-// The draw of centre i (one workgroup of 1024).  Thread t sums its
-// contiguous share of the n2 group sums in order; the running sums over the
+// The draw of centre i (one workgroup of 1024) from the nb workgroup
+// partials of k_pp_step.  Thread t sums its n = ceil(nb / 1024) partials
+// t n .. t n + n - 1 in order (stored 1024 apart); the running sums over the
 // threads (lane prefix per wave, then the earlier waves' totals in order)
 // give the total and the first share where the running sum of D^2 exceeds
-// u * total; wave 0 then walks that share to the group, the group's 256
-// workgroup partials to the block, and the block's kPpRows rows to the
-// token.  With a zero total the draw is token floor(u v).
+// u * total; wave 0 then walks that share to the block and the block's
+// kPpRows rows to the token.  With a zero total the draw is token floor(u v).
 __global__ __launch_bounds__(1024) void k_pp_pick(const float* __restrict__ D,
                                                   const double* __restrict__ part, int64_t nb,
-                                                  const double* __restrict__ part2, int64_t n2,
                                                   int64_t v, double u, int32_t* __restrict__ centers,
                                                   int i) {
   __shared__ double wtot[16];
   __shared__ double ps_found;
   __shared__ int found;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t chunk = (n2 + 1023) / 1024;
-  const int64_t lo = min(n2, tid * chunk), hi = min(n2, lo + chunk);
+  const int64_t n = (nb + 1023) / 1024;
+  const int64_t lo = min(nb, tid * n), hi = min(nb, lo + n);
+  // 16 loads in flight, then added in order (a zero past the share changes
+  // nothing: the sums are non-negative)
   double s = 0.0;
-  for (int64_t j = lo; j < hi; ++j) s += part2[j];
+  for (int64_t j0 = lo; j0 < hi; j0 += 16) {
+    double x[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = j0 + k < hi ? part[(j0 + k - lo) * 1024 + tid] : 0.0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s += x[k];
+  }
   const double incl_w = wave_prefix(s, lane);
   const double prev_w = __shfl_up(incl_w, 1);
   if (lane == 63) wtot[wave] = incl_w;
@@ -190,12 +188,10 @@ __global__ __launch_bounds__(1024) void k_pp_pick(const float* __restrict__ D,
   __syncthreads();
   if (tid >= 64) return;
   double base = ps_found;
-  const int64_t flo = min(n2, f * chunk), fhi = min(n2, flo + chunk);
-  const int64_t g = flo < fhi ? wave_walk([&](int64_t j) { return part2[j]; }, flo, fhi, target,
-                                          &base, lane)
-                              : n2 - 1;
-  const int64_t blk = wave_walk([&](int64_t j) { return part[j]; }, g * kPpGroup,
-                                min(nb, (g + 1) * kPpGroup), target, &base, lane);
+  const int64_t flo = min(nb, f * n), fhi = min(nb, flo + n);
+  const int64_t blk = flo < fhi ? wave_walk([&](int64_t j) { return part[(j - flo) * 1024 + f]; },
+                                            flo, fhi, target, &base, lane)
+                                : nb - 1;
   const int64_t rlo = blk * kPpRows, rhi = min(v, rlo + kPpRows);
   const int64_t r = wave_walk([&](int64_t t) { return (double)D[t] * (double)D[t]; }, rlo, rhi,
                               target, &base, lane);
@@ -665,7 +661,6 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
   float* inv = nullptr;
   float* D = nullptr;
   double* part = nullptr;
-  double* part2 = nullptr;
   float* S = nullptr;
   int32_t* centers = nullptr;
   int32_t* asg = nullptr;
@@ -677,9 +672,8 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
   const int64_t nb = (v + kPpRows - 1) / kPpRows;
   if (r == hipSuccess) r = hipMalloc((void**)&inv, sizeof(float) * v);
   if (r == hipSuccess) r = hipMalloc((void**)&D, sizeof(float) * v);
-  const int64_t n2 = (nb + kPpGroup - 1) / kPpGroup;
-  if (r == hipSuccess) r = hipMalloc((void**)&part, sizeof(double) * nb);
-  if (r == hipSuccess) r = hipMalloc((void**)&part2, sizeof(double) * n2);
+  // k_pp_step's partials, 1024 x ceil(nb / 1024) slots (see k_pp_pick)
+  if (r == hipSuccess) r = hipMalloc((void**)&part, sizeof(double) * 1024 * ((nb + 1023) / 1024));
   if (r == hipSuccess) r = hipMalloc((void**)&S, sizeof(float) * v * c);
   if (r == hipSuccess) r = hipMalloc((void**)&centers, sizeof(int32_t) * c);
   if (r == hipSuccess) r = hipMalloc((void**)&asg, sizeof(int32_t) * v);
@@ -702,8 +696,7 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
     for (auto& e : sev) (void)hipEventCreate(&e);
     for (int64_t i = 0; r == hipSuccess && i < c; ++i) {
       if (i > 0) {
-        hipLaunchKernelGGL(k_pp_reduce, dim3((unsigned)n2), dim3(kPpGroup), 0, st, part, nb, part2);
-        hipLaunchKernelGGL(k_pp_pick, dim3(1), dim3(1024), 0, st, D, part, nb, part2, n2, v, u[i],
+        hipLaunchKernelGGL(k_pp_pick, dim3(1), dim3(1024), 0, st, D, part, nb, v, u[i],
                            centers, (int)i);
       }
       const bool sample = i % kSample == 0;
@@ -767,7 +760,7 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
   }
   for (auto& e : ev) (void)hipEventDestroy(e);
   work_free(w);
-  for (void* p : {(void*)X, (void*)inv, (void*)D, (void*)part, (void*)part2, (void*)S,
+  for (void* p : {(void*)X, (void*)inv, (void*)D, (void*)part, (void*)S,
                   (void*)centers, (void*)asg, (void*)pieces})
     (void)hipFree(p);
   return r;
