@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--spec", type=int, default=0, metavar="K",
                     help="time the speculative verification of K draft positions (fh_spec_verify) "
                          "beside K single-position drafts and the dense head at B=K; one JSON line")
+    ap.add_argument("--burst", action="store_true",
+                    help="time the plain one-shot read probe (fh_read_probe) at the sizes of a "
+                         "batch-1 call's phases, the whole call and the dense head; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of known size (to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run) and exit")
@@ -86,6 +89,64 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_kernel": "neg", "bytes_read_per_launch": COPY_BYTES,
                       "bytes_written_per_launch": COPY_BYTES, "launches": 5}), flush=True)
+
+
+# One-shot read sizes (bytes) of the Llama-3.2-1B-shape head, as the roofline
+# table counts them: a batch-1 call's stage 1 and stage 2, the call, the dense head.
+BURST_SIZES = (("stage 1", 32_869_696), ("stage 2", 33_593_344), ("batch-1 call", 66_497_152),
+               ("dense head", 525_340_672))
+
+
+def burst_main(args):
+    """How fast the part streams a buffer of each size in one launch: the
+    library's plain read probe over 16 rotating buffers (their 8.4 GB exceed the
+    256 MB Infinity Cache, so every launch reads from HBM), timed back to back
+    and with a HIP event pair around each launch on its stream.  The timed
+    loops call the C ABI with the pointers marshalled beforehand, so that the
+    host keeps ahead of launches of a few microseconds."""
+    import ctypes
+
+    import torch
+
+    from lm_output_head_amd import _abi
+    lib = _abi.load()
+    nbuf, steps = 16, max(50, min(args.steps, 400))
+    big = max(n for _, n in BURST_SIZES)
+    bufs = [torch.full((big // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(nbuf)]
+    found = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ptrs = [ctypes.c_void_p(b.data_ptr()) for b in bufs]
+    fptr, sptr = ctypes.c_void_p(found.data_ptr()), ctypes.c_void_p(stream.cuda_stream)
+    probe = lib.fh_read_probe
+    rows = []
+    for what, n in BURST_SIZES:
+        for i in range(20):
+            assert probe(ptrs[i % nbuf], n, 0, fptr, sptr) == 0, lib.fh_last_error()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(steps):
+            probe(ptrs[i % nbuf], n, 0, fptr, sptr)
+        t1.record(stream)
+        t1.synchronize()
+        b2b = t0.elapsed_time(t1) * 1e3 / steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i, (a0, a1) in enumerate(ev):
+            a0.record(stream)
+            probe(ptrs[i % nbuf], n, 0, fptr, sptr)
+            a1.record(stream)
+        torch.cuda.synchronize()
+        evu = sum(a0.elapsed_time(a1) for a0, a1 in ev) * 1e3 / steps
+        rows.append({"what": what, "bytes": n, "us_back_to_back": round(b2b, 2),
+                     "gbs_back_to_back": round(n / b2b / 1e3, 1), "us_per_launch_events": round(evu, 2),
+                     "gbs_events": round(n / evu / 1e3, 1), "frac_of_8tbs_back_to_back": round(n / b2b / 8e6, 3)})
+    assert int(found.item()) == 0  # the key is absent: every launch read its whole buffer
+    print(json.dumps({"metric": "one-shot HBM read probe", "unit": "us per launch", "n_gpus": 1,
+                      "steps": steps, "data": "16 rotating device buffers", "peak_gbs": 8000.0,
+                      "kernel": "k_read_probe (one 16-byte load per thread, 1024-thread "
+                                "workgroups; a search for a 32-bit value absent from the buffers)",
+                      "sizes": rows}), flush=True)
 
 
 CLUSTER_SOURCES = ("fh_cluster.hip",)  # the offline clustering, its own translation unit
@@ -492,6 +553,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.burst:
+        burst_main(args)
         return
     if args.cluster:
         cluster_main(args)

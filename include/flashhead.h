@@ -224,7 +224,6 @@ fh_status fh_spec_verify(fh_engine* e, const void* h, int64_t B, int64_t p,
                          void* stream);
 
 /*
- * Per-kernel timing./*
  * Per-kernel timing.  fh_profile_begin(e, n) makes the engine record a HIP
  * event pair on the launch stream around each of its next n kernel launches.
  * fh_profile_end waits for those events and fills up to `max` records
@@ -239,6 +238,25 @@ typedef struct {
 
 fh_status fh_profile_begin(fh_engine* e, int64_t max_launches);
 fh_status fh_profile_end(fh_engine* e, fh_kernel_time* out, int max, int* count);
+
+/*
+ * fh_read_probe — a plain one-shot read of a device buffer, for measuring the
+ * memory system the head runs on; it computes nothing of the head.  One
+ * 16-byte load per thread in 1024-thread workgroups; a thread that finds a
+ * 32-bit word equal to `key` stores 1 to *found, so the call is a search and
+ * every load is used, with almost no work after the loads.  The head's phases
+ * are one-shot reads of tens of MB each (stage 1 and stage 2 of a batch-1
+ * call, about 33 MB apiece at the Llama-3.2-1B shape); this times how fast the
+ * part streams a buffer of the same size in one launch.
+ *   buf     device, 16-byte aligned, `bytes` bytes.
+ *   bytes   a positive multiple of 16, at most 2^40.
+ *   key     the 32-bit value searched for.
+ *   found   device uint32 [1]: set to 1 if some word equals key, else left as
+ *           it was (the caller clears it).
+ *   stream  HIP stream (NULL = default); asynchronous, allocates nothing.
+ * FH_EINVAL on a NULL pointer, a misaligned buffer or a bad size.
+ */
+fh_status fh_read_probe(const void* buf, int64_t bytes, uint32_t key, uint32_t* found, void* stream);
 
 /*
  * fh_set_path — choose how fh_forward runs a batch-1 call.

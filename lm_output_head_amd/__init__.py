@@ -13,7 +13,7 @@ def __getattr__(name):
     # the build script stay usable without initialising torch
     if name in ("FlashHead", "fh_create", "fh_destroy", "fh_forward", "fh_score",
                 "fh_dense_forward", "fh_get_int4", "fh_get_int8", "fh_spec_verify", "fh_profile_begin", "fh_profile_end",
-                "fh_set_path", "fh_sync_status", "fh_balanced_assign", "fh_cluster",
+                "fh_set_path", "fh_sync_status", "fh_balanced_assign", "fh_cluster", "fh_read_probe",
                 "fh_last_error", "fh_version"):
         from . import flashhead
         return getattr(flashhead, name)

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstdint>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -611,6 +612,16 @@ fh_status fh_get_int8(fh_engine* e, int8_t* codes, uint16_t* scales, void* strea
     r = hipMemcpyAsync(scales, e->csig, sizeof(uint16_t) * (size_t)(e->c * e->d / 32),
                        hipMemcpyDeviceToDevice, st);
   return r == hipSuccess ? FH_OK : hip_fail(r, "copy INT8 centroids");
+}
+
+fh_status fh_read_probe(const void* buf, int64_t bytes, uint32_t key, uint32_t* found, void* stream) {
+  g_err.clear();
+  if (!buf || !found) return fail(FH_EINVAL, "NULL pointer");
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return fail(FH_EINVAL, "buf is not 16-byte aligned");
+  if (bytes < 16 || bytes % 16 != 0 || bytes > ((int64_t)1 << 40))
+    return fail(FH_EINVAL, "bytes must be a positive multiple of 16, at most 2^40");
+  hipError_t r = fh::launch_read_probe(buf, bytes / 16, key, found, static_cast<hipStream_t>(stream));
+  return r == hipSuccess ? FH_OK : hip_fail(r, "read probe launch");
 }
 
 fh_status fh_profile_begin(fh_engine* e, int64_t max_launches) {

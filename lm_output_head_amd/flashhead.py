@@ -127,6 +127,15 @@ def fh_profile_end(eng) -> dict:
     return {recs[i].name.decode(): (recs[i].launches, recs[i].total_ms) for i in range(n.value)}
 
 
+def fh_read_probe(buf: torch.Tensor, key: int, found: torch.Tensor, stream=None) -> None:
+    """One-shot read of buf (any GPU tensor, nbytes a multiple of 16): sets
+    found (int32 [1] on the GPU, cleared by the caller) to 1 if some 32-bit
+    word of buf equals key (taken mod 2^32)."""
+    _require(found, torch.int32, (1,), "found")
+    check(_abi.load().fh_read_probe(_ptr(buf), buf.numel() * buf.element_size(), key & 0xFFFFFFFF,
+                                    _ptr(found), _stream(stream)))
+
+
 def fh_balanced_assign(sims: torch.Tensor, out_assign: torch.Tensor, stream=None) -> int:
     """Balanced assignment of v tokens to c clusters of v / c: sims [v x c]
     float32 on the GPU, out_assign [v] int32 on the GPU.  Returns the number

@@ -92,3 +92,15 @@ def test_calls_on_null_engine_fail_cleanly(lib):
     assert lib.fh_profile_end(None, None, 0, ctypes.byref(n)) == -1
     lib.fh_destroy(None)
     assert "NULL" in lib.fh_last_error().decode()
+
+
+def test_read_probe_rejects_bad_arguments(lib):
+    """Checked before anything is launched: NULL pointers, a misaligned
+    buffer, and sizes that are not a positive multiple of 16."""
+    buf, out = P(4096), P(4096)
+    for args, needle in [((None, 4096, 7, out), "NULL"), ((buf, 4096, 7, None), "NULL"),
+                         ((P(4104), 4096, 7, out), "aligned"), ((buf, 0, 7, out), "multiple of 16"),
+                         ((buf, 4100, 7, out), "multiple of 16"),
+                         ((buf, 1 << 41, 7, out), "multiple of 16")]:
+        assert lib.fh_read_probe(*args, None) == -1, args
+        assert needle in lib.fh_last_error().decode(), args
