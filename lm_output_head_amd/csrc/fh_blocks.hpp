@@ -668,12 +668,21 @@ __device__ __forceinline__ void emit_selected(int c, Emit emit, SelShared& sh) {
 // ======================================================================
 // Finisher: merge n Parts in a fixed order (threads stride, then a tree).
 // ======================================================================
-// Merge n Parts: each thread folds a strided subset in index order, the
-// waves merge their lanes, and thread 0 merges the waves in order.
+// Merge n Parts: each thread folds a strided subset in index order (eight
+// loads in flight, then eight merges: one memory round trip per eight
+// partials, not per partial; past n the slots hold part_empty(), which
+// part_merge leaves the running partial unchanged by, bit for bit), the waves
+// merge their lanes, and thread 0 merges the waves in order.
 template <int NT>
 __device__ __forceinline__ Part merge_parts_block(const Part* __restrict__ pq, int n, Part* sh) {
   Part acc = part_empty();
-  for (int i = threadIdx.x; i < n; i += NT) acc = part_merge(acc, pq[i]);
+  for (int i = threadIdx.x; i < n; i += 8 * NT) {
+    Part x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = i + u * NT < n ? pq[i + u * NT] : part_empty();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = part_merge(acc, x[u]);
+  }
   acc = wave_merge_part(acc);
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = acc;
   __syncthreads();
