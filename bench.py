@@ -12,7 +12,7 @@ between two uses of one replica is R * (|C| + |E rows read|), several times
 the cache.
 
 Output: one JSON line (see the keys below).  --gpus N > 1 is not supported:
-this build runs on one GPU.
+this benchmark runs on one GPU.
 """
 
 from __future__ import annotations
@@ -548,7 +548,7 @@ def spec_main(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
     if args.copy_calibration:

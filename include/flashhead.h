@@ -47,7 +47,7 @@ typedef enum {
   FH_EINVAL = -1,       /* invalid argument                                 */
   FH_ENOMEM = -2,       /* device or host allocation failed                 */
   FH_EHIP = -3,         /* a HIP runtime call or kernel launch failed       */
-  FH_EUNSUPPORTED = -4  /* valid, but outside what this build implements    */
+  FH_EUNSUPPORTED = -4  /* valid, but outside what this library implements  */
 } fh_status;
 
 /* Storage type shared by E, C and h. */

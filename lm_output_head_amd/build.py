@@ -1,6 +1,6 @@
 """Build libflashhead.so in-tree with hipcc for gfx950.
 
-Usage: ``python -m lm_output_head_amd.build`` (or ``__graft_entry__.build()``).
+Usage: ``python -m lm_output_head_amd.build``.
 Every call compiles from source; object files go to ``lm_output_head_amd/_build``.
 """
 

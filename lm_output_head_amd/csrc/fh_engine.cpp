@@ -263,7 +263,7 @@ fh_status fh_cluster(const void* E, fh_dtype dtype, int64_t v, int64_t d, int64_
   const int64_t epc = dtype == FH_BF16 ? 8 : 4;  // elements per 16-byte chunk
   if (d < 1 || d % epc != 0)
     return fail(FH_EINVAL, dtype == FH_BF16 ? "bf16 needs d % 8 == 0" : "f32 needs d % 4 == 0");
-  if (d > 64 * 8 * epc) return fail(FH_EUNSUPPORTED, "d too large for this build");
+  if (d > 64 * 8 * epc) return fail(FH_EUNSUPPORTED, "d too large for this library");
   if (iters < 1) return fail(FH_EINVAL, "iters must be >= 1");
   for (int64_t i = 0; i < c; ++i)
     if (!(u[i] >= 0.0 && u[i] < 1.0))
@@ -302,7 +302,7 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   const int epc = dtype == FH_BF16 ? 8 : 4;
   if (d % epc != 0)
     return fail(FH_EINVAL, dtype == FH_BF16 ? "bf16 needs d % 8 == 0" : "f32 needs d % 4 == 0");
-  if (d > 64 * 8 * epc) return fail(FH_EUNSUPPORTED, "d too large for this build");
+  if (d > 64 * 8 * epc) return fail(FH_EUNSUPPORTED, "d too large for this library");
   if (quant != FH_QUANT_NONE && d % 32 != 0)
     return fail(FH_EUNSUPPORTED, "g32 quantisation needs d % 32 == 0");
   if (max_batch < 1 || max_batch > 65535) return fail(FH_EINVAL, "max_batch outside [1, 65535]");
