@@ -157,6 +157,13 @@ __device__ __forceinline__ float gumbel_at(uint64_t seed, uint32_t row, uint32_t
   return gumbel_from_word(u4_word(blk, index & 3));
 }
 
+// The stage-1 value of query q and cluster k: the score, or the selection
+// key s / T + G(seed, q, k, 0) (the same float operations as k_select's).
+__device__ __forceinline__ float stage1_value(float s, int sample, float temperature,
+                                              uint64_t seed, uint32_t q, uint32_t k) {
+  return sample ? s / temperature + gumbel_at(seed, q, k, 0u) : s;
+}
+
 // -------------------------------------------- device-coherent accesses ----
 // Agent-scope relaxed atomics compile to sc1 loads/stores on gfx950: they
 // reach the device coherence point, so workgroups on other XCDs see them

@@ -151,25 +151,26 @@ void free_engine(fh_engine* e) {
   delete e;
 }
 
-// Stage-1 scores for B queries: matrix cores for batches of bf16 queries,
-// the row GEMV otherwise.
+// Stage-1 scores for B queries (or, with kx.sample, the sampled-probe
+// selection keys): matrix cores for batches of bf16 queries, the row GEMV
+// otherwise.
 hipError_t launch_stage1(fh_engine* e, hipStream_t st, const fh::KernelCtx& k, const void* h,
-                         int64_t B, float* out) {
+                         int64_t B, float* out, const fh::KeyXform& kx = fh::KeyXform{}) {
   const bool int4 = e->quant == FH_QUANT_INT4_G32;
   const bool int8 = e->quant == FH_QUANT_INT8_G32;
   const bool bf16 = e->dtype == FH_BF16;
   if (bf16 && int4 && B >= fh::kMfmaMinBatchInt4)
     return timed(e, st, "score_int4_mfma",
-                 [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out); });
+                 [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out, kx); });
   if (bf16 && int8 && B >= fh::kMfmaMinBatchInt8)
     return timed(e, st, "score_int8_mfma",
-                 [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out); });
+                 [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out, kx); });
   if (bf16 && e->quant == FH_QUANT_NONE && B >= fh::kMfmaMinBatchBf16)
-    return timed(e, st, "score_mfma", [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out); });
+    return timed(e, st, "score_mfma", [&] { return fh::launch_score_mfma(k, e->cus, h, (int)B, out, kx); });
   if (int4 || int8)
     return timed(e, st, int4 ? "score_int4" : "score_int8",
-                 [&] { return fh::launch_score_quant(k, h, (int)B, out); });
-  return timed(e, st, "score", [&] { return fh::launch_score(k, h, (int)B, out); });
+                 [&] { return fh::launch_score_quant(k, h, (int)B, out, kx); });
+  return timed(e, st, "score", [&] { return fh::launch_score(k, h, (int)B, out, kx); });
 }
 
 fh_status check_common(const fh_engine* e, const void* h, int64_t B) {
@@ -478,11 +479,15 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
   // batches of bf16 queries that share probes: stage 2 cluster-major on the
   // matrix cores, each probed cluster's rows read once for all its queries
   const bool cm = e->dtype == FH_BF16 && fh::gather_cm_fits((int)B, p, e->c);
-  hipError_t r = launch_stage1(e, st, k, h, B, e->scores);
+  // with sampled probes stage 1 stores the selection keys (the Gumbel draws
+  // spread over its grid) and the selection takes them as they are
+  fh::KeyXform kx;
+  kx.sample = probe_sample; kx.temperature = temperature; kx.seed = seed;
+  hipError_t r = launch_stage1(e, st, k, h, B, e->scores, kx);
   if (r != hipSuccess) return hip_fail(r, "score launch");
   r = timed(e, st, "select", [&] {
-    return fh::launch_select(k, e->scores, (int)B, (int)p, probe_sample, temperature, seed, S,
-                             (int)p, cm ? e->mbits : nullptr, cm ? e->mpre : nullptr);
+    return fh::launch_select(k, e->scores, (int)B, (int)p, 0, 1.f, seed, S, (int)p,
+                             cm ? e->mbits : nullptr, cm ? e->mpre : nullptr);
   });
   if (r != hipSuccess) return hip_fail(r, "select launch");
   int64_t nparts = 0;

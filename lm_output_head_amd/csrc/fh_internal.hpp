@@ -42,12 +42,25 @@ struct KernelCtx {
 
 int64_t rows_blocks(int64_t nrows, int rpw);
 
+// What a stage-1 launch stores: the score s, or with sampled probes the
+// selection key s / T + G(seed, q, k, 0) of query q and cluster k (k_select
+// then takes the keys as they are).  Computing the keys in the stage-1
+// epilogue spreads the Gumbel draws over the whole grid instead of one
+// workgroup per query.
+struct KeyXform {
+  int sample = 0;
+  float temperature = 1.f;
+  uint64_t seed = 0;
+};
+
 // g32 quantisation of C into cq / csig (k.qbits = 4 or 8)
 hipError_t launch_quant(const KernelCtx& k, int* bad);
 hipError_t launch_permute_rows(const KernelCtx& k, void* out);
-hipError_t launch_score(const KernelCtx& k, const void* h, int B, float* out);
+hipError_t launch_score(const KernelCtx& k, const void* h, int B, float* out,
+                        const KeyXform& kx = KeyXform{});
 // stage-1 scores from the g32 codes (k.qbits = 4 or 8), on the vector units
-hipError_t launch_score_quant(const KernelCtx& k, const void* h, int B, float* out);
+hipError_t launch_score_quant(const KernelCtx& k, const void* h, int B, float* out,
+                              const KeyXform& kx = KeyXform{});
 float select_quantile(int64_t c, int64_t p);
 // S [B x ldS]: the p probes of each query, ascending.  With mbits/mpre non-
 // null also the probe bitsets word-major, mbits[w * B + q], and the probes of
@@ -76,7 +89,8 @@ int64_t mfma_int4_row_bytes(int d);
 int64_t mfma_blocks(int64_t R);  // row blocks (partials per query) of the MFMA dense head
 int64_t mfma_sig_ld(int64_t c);
 hipError_t launch_mfma_relayout(const KernelCtx& k, uint8_t* cq_mfma, uint16_t* sigT);
-hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, float* out);
+hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, float* out,
+                             const KeyXform& kx = KeyXform{});
 // Cluster-major stage 2 on the matrix cores (bf16 engines, B >= 2): every
 // probed cluster's rows are read once for all queries that probe it.
 int64_t gather_cm_blocks(int64_t c, int cus);

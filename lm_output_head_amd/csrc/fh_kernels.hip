@@ -113,6 +113,7 @@ struct RowsArgs {
   float tprime;  // T' (1 unless tokens are sampled)
   uint64_t seed;
   Part* parts;  // [B x gridDim.x] (EPI)
+  KeyXform key;  // stage 1 (neither GATHER nor EPI): scores or selection keys
 };
 
 template <typename T, int MAXM, int NQ, int RPW, bool GATHER, bool EPI>
@@ -149,7 +150,11 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   auto sink = [&](int q, int64_t r, int64_t src, float z) {
     const int64_t oq = q0 + q;
     if (lane == 0) {
-      if (a.out_vals) a.out_vals[oq * a.ld_vals + r] = z;
+      if (a.out_vals)
+        a.out_vals[oq * a.ld_vals + r] =
+            GATHER || EPI ? z
+                          : stage1_value(z, a.key.sample, a.key.temperature, a.key.seed,
+                                         (uint32_t)oq, (uint32_t)r);
       if (GATHER && a.out_ids) a.out_ids[oq * a.ld_vals + r] = (int32_t)src;
     }
     if (EPI)
@@ -168,7 +173,7 @@ template <typename T, int BITS, int MAXG, int NQ, int RPW>
 __global__ __launch_bounds__(256) void k_score_q(const uint8_t* __restrict__ Q,
                                                     const uint16_t* __restrict__ SG, int64_t c,
                                                     int d, const T* __restrict__ H, int B,
-                                                    float* __restrict__ out) {
+                                                    float* __restrict__ out, KeyXform kx) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int q0 = blockIdx.y * NQ;
@@ -180,7 +185,9 @@ __global__ __launch_bounds__(256) void k_score_q(const uint8_t* __restrict__ Q,
   const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
   const int64_t r1 = min(r0 + RPW, c);
   auto sink = [&](int q, int64_t r, int64_t, float s) {
-    if (lane == 0) out[(int64_t)(q0 + q) * c + r] = s;
+    if (lane == 0)
+      out[(int64_t)(q0 + q) * c + r] =
+          stage1_value(s, kx.sample, kx.temperature, kx.seed, (uint32_t)(q0 + q), (uint32_t)r);
   };
   wave_rows_q<BITS, MAXG, NQ>(Q, SG, d, lane, hg, nq, r0, r1, 1, sink);
 }
@@ -279,21 +286,25 @@ static hipError_t launch_rows(const RowsArgs& a, hipStream_t st, int64_t* nblock
 }
 
 template <typename T>
-static hipError_t score_dispatch(const KernelCtx& k, const void* h, int B, float* out) {
+static hipError_t score_dispatch(const KernelCtx& k, const void* h, int B, float* out,
+                                const KeyXform& kx) {
   RowsArgs a{};
   a.M = k.C; a.nrows = k.c; a.d = k.d; a.H = h; a.B = B; a.out_vals = out; a.ld_vals = k.c;
-  a.tprime = 1.f;
+  a.tprime = 1.f; a.key = kx;
   if (B == 1) return launch_rows<T, 1, kScoreRPW, false, false>(a, k.stream, nullptr);
   if (B == 2) return launch_rows<T, 2, kScoreRPW, false, false>(a, k.stream, nullptr);
   return launch_rows<T, 4, kScoreRPW, false, false>(a, k.stream, nullptr);
 }
 
-hipError_t launch_score(const KernelCtx& k, const void* h, int B, float* out) {
-  return k.bf16 ? score_dispatch<uint16_t>(k, h, B, out) : score_dispatch<float>(k, h, B, out);
+hipError_t launch_score(const KernelCtx& k, const void* h, int B, float* out,
+                        const KeyXform& kx) {
+  return k.bf16 ? score_dispatch<uint16_t>(k, h, B, out, kx)
+                : score_dispatch<float>(k, h, B, out, kx);
 }
 
 template <typename T, int BITS, int NQ>
-static hipError_t quant_score_launch(const KernelCtx& k, const void* h, int B, float* out) {
+static hipError_t quant_score_launch(const KernelCtx& k, const void* h, int B, float* out,
+                                     const KeyXform& kx) {
   const int G = k.d / 32;
   const int maxg = (G + 63) / 64;
   const int64_t gx = (k.c + 4 * kInt4RPW - 1) / (4 * kInt4RPW);
@@ -301,7 +312,7 @@ static hipError_t quant_score_launch(const KernelCtx& k, const void* h, int B, f
   const T* hp = static_cast<const T*>(h);
   switch (maxg) {
 #define FH_CASE(MG) \
-  case MG: hipLaunchKernelGGL((k_score_q<T, BITS, MG, NQ, kInt4RPW>), grid, dim3(256), 0, k.stream, k.cq, k.csig, k.c, k.d, hp, B, out); break;
+  case MG: hipLaunchKernelGGL((k_score_q<T, BITS, MG, NQ, kInt4RPW>), grid, dim3(256), 0, k.stream, k.cq, k.csig, k.c, k.d, hp, B, out, kx); break;
     FH_CASE(1) FH_CASE(2) FH_CASE(3) FH_CASE(4)
 #undef FH_CASE
     default: return hipErrorInvalidValue;
@@ -310,17 +321,19 @@ static hipError_t quant_score_launch(const KernelCtx& k, const void* h, int B, f
 }
 
 template <int BITS>
-static hipError_t quant_score(const KernelCtx& k, const void* h, int B, float* out) {
+static hipError_t quant_score(const KernelCtx& k, const void* h, int B, float* out,
+                              const KeyXform& kx) {
   if (k.bf16)
-    return B == 1 ? quant_score_launch<uint16_t, BITS, 1>(k, h, B, out)
-                  : quant_score_launch<uint16_t, BITS, 2>(k, h, B, out);
-  return B == 1 ? quant_score_launch<float, BITS, 1>(k, h, B, out)
-                : quant_score_launch<float, BITS, 2>(k, h, B, out);
+    return B == 1 ? quant_score_launch<uint16_t, BITS, 1>(k, h, B, out, kx)
+                  : quant_score_launch<uint16_t, BITS, 2>(k, h, B, out, kx);
+  return B == 1 ? quant_score_launch<float, BITS, 1>(k, h, B, out, kx)
+                : quant_score_launch<float, BITS, 2>(k, h, B, out, kx);
 }
 
-hipError_t launch_score_quant(const KernelCtx& k, const void* h, int B, float* out) {
-  if (k.qbits == 4) return quant_score<4>(k, h, B, out);
-  if (k.qbits == 8) return quant_score<8>(k, h, B, out);
+hipError_t launch_score_quant(const KernelCtx& k, const void* h, int B, float* out,
+                              const KeyXform& kx) {
+  if (k.qbits == 4) return quant_score<4>(k, h, B, out, kx);
+  if (k.qbits == 8) return quant_score<8>(k, h, B, out, kx);
   return hipErrorInvalidValue;
 }
 

@@ -115,6 +115,7 @@ struct MfmaArgs {
   int bsz;
   const int32_t* c2t;
   int32_t* out_ids;
+  KeyXform key;  // stage 1 (not EPI): scores or selection keys into out
 };
 
 constexpr int kHRow = 128 + 8;  // LDS row of a staged h block (bf16), padded
@@ -368,7 +369,9 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int64_t r = rbase + 16 * m + 4 * g + i;
-            if (r < a.R) a.out[(int64_t)q * a.ld_out + r] = acc[m][n][i];
+            if (r < a.R)
+              a.out[(int64_t)q * a.ld_out + r] = stage1_value(
+                  acc[m][n][i], a.key.sample, a.key.temperature, a.key.seed, (uint32_t)q, (uint32_t)r);
           }
       }
     }
@@ -690,10 +693,11 @@ static hipError_t mfma_dispatch(const MfmaArgs& a, int cus, hipStream_t st, int6
 
 int64_t mfma_blocks(int64_t R) { return (R + 63) / 64; }
 
-hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, float* out) {
+hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, float* out,
+                             const KeyXform& kx) {
   MfmaArgs a{};
   a.R = k.c; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
-  a.out = out; a.ld_out = k.c;
+  a.out = out; a.ld_out = k.c; a.key = kx;
   if (k.qbits == 4) {
     a.A = k.cq_mfma; a.sigT = k.sig_mfma; a.ldsig = mfma_sig_ld(k.c);
     a.a_row_bytes = mfma_int4_row_bytes(k.d);
