@@ -84,7 +84,7 @@ hipError_t launch_dense(const KernelCtx& k, const void* h, int B, int token_samp
 constexpr int kMfmaMinBatchBf16 = 8;  // bf16 stage 1
 constexpr int kMfmaMinBatchDense = 2;  // the dense head and the speculative verification (bf16)
 constexpr int kMfmaMinBatchInt4 = 2;  // INT4 stage 1
-constexpr int kMfmaMinBatchInt8 = 16;  // INT8 stage 1 (measured: vector units 21 us at B = 8, MFMA 27 us)
+constexpr int kMfmaMinBatchInt8 = 2;  // INT8 stage 1 (split over d up to 16 queries: 13.7 us at B = 16)
 int64_t mfma_int4_row_bytes(int d);
 int64_t mfma_blocks(int64_t R);  // row blocks (partials per query) of the MFMA dense head
 int64_t mfma_sig_ld(int64_t c);

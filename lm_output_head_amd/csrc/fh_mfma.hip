@@ -420,6 +420,139 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
 }
 
 // ======================================================================
+// Stage 1 for at most 16 queries (one query tile), split over d.  With one
+// query tile the GEMM above has one workgroup per 64 rows (126 at the
+// Llama-3.2-1B shape's 8016 centroids), each walking all of d; its time is
+// the chain of d / 128 dependent block steps.  Here the four waves of a
+// workgroup take the same 16 rows and consecutive quarters of d, so there
+// are four times the workgroups and a quarter of the chain per wave.  Each
+// lane loads its queries' h fragments itself (the [B x d] queries are a few
+// KB and stay in cache), so the waves never synchronise until the end, where
+// waves 1..3 hand their tiles to wave 0 through LDS and it adds them in wave
+// order.  Rows and scale layout as in k_mfma_gemm (MT = 1, no row map).
+// ======================================================================
+template <int QB>
+__global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
+  __shared__ f32x4 red[3][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t rbase = (int64_t)blockIdx.x * 16;
+  const int nkb = (a.d + 127) / 128;
+  const int kb0 = wave * nkb / 4, kb1 = (wave + 1) * nkb / 4;
+  const uint16_t* Hq = a.H + (int64_t)min(col, a.B - 1) * a.d;
+  const int64_t ra = min(rbase + col, a.R - 1);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the queries' fragments of block kb: step s holds elements 128 kb + 32 s + 8 g .. + 7
+  auto load_h = [&](int kb, uint4 (&hb)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = 128 * kb + 32 * s + 8 * g;
+      hb[s] = k < a.d ? *reinterpret_cast<const uint4*>(Hq + k) : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  if constexpr (QB == 0) {
+    const uint16_t* A = static_cast<const uint16_t*>(a.A);
+    struct Blk {
+      uint4 v[4], hb[4];
+    };
+    auto load = [&](int kb, Blk& x) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int k = 128 * kb + 32 * s + 8 * g;
+        x.v[s] = k < a.d ? *reinterpret_cast<const uint4*>(A + ra * a.d + k) : uint4{0u, 0u, 0u, 0u};
+      }
+      load_h(kb, x.hb);
+    };
+    auto compute = [&](int, const Blk& x) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = mfma16(x.v[s], x.hb[s], acc);
+    };
+    Blk b0, b1;
+    if (kb0 < kb1) load(kb0, b0);
+    for (int kb = kb0; kb < kb1; kb += 2) {
+      if (kb + 1 < kb1) load(kb + 1, b1);
+      compute(kb, b0);
+      if (kb + 1 < kb1) {
+        if (kb + 2 < kb1) load(kb + 2, b0);
+        compute(kb + 1, b1);
+      }
+    }
+  } else {
+    const uint8_t* A = static_cast<const uint8_t*>(a.A);
+    const int G = a.d / 32;
+    const uint4 neg136 = uint4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
+    struct Blk {
+      uint4 w4;       // INT4: lane group g's bytes of the block's four groups
+      uint2 w8[4];    // INT8: lane group g's 8 bytes of each group
+      uint2 sg[4];
+      uint4 hb[4];
+    };
+    auto load = [&](int kb, Blk& x) {
+      if constexpr (QB == 4)
+        x.w4 = *reinterpret_cast<const uint4*>(A + ra * a.a_row_bytes + 64 * kb + 16 * g);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int grp = min(4 * kb + s, G - 1);
+        if constexpr (QB == 8)
+          x.w8[s] = *reinterpret_cast<const uint2*>(A + ra * a.d + 32 * grp + 8 * g);
+        x.sg[s] = *reinterpret_cast<const uint2*>(a.sigT + (int64_t)grp * a.ldsig + rbase + 4 * g);
+      }
+      load_h(kb, x.hb);
+    };
+    auto compute = [&](int kb, const Blk& x) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (4 * kb + s >= G) break;
+        f32x4 part;
+        if constexpr (QB == 4) {
+          const uint32_t wv[4] = {x.w4.x, x.w4.y, x.w4.z, x.w4.w};
+          part = mfma16(int4_fragment(wv[s]), x.hb[s], f32x4{0.f, 0.f, 0.f, 0.f});
+          part = mfma16(neg136, x.hb[s], part);
+        } else {
+          part = mfma16(int8_fragment(x.w8[s]), x.hb[s], f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        const float sig[4] = {
+            __half2float(__ushort_as_half((uint16_t)(x.sg[s].x & 0xFFFFu))),
+            __half2float(__ushort_as_half((uint16_t)(x.sg[s].x >> 16))),
+            __half2float(__ushort_as_half((uint16_t)(x.sg[s].y & 0xFFFFu))),
+            __half2float(__ushort_as_half((uint16_t)(x.sg[s].y >> 16)))};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(sig[i], part[i], acc[i]);
+      }
+    };
+    Blk b0, b1;
+    if (kb0 < kb1) load(kb0, b0);
+    for (int kb = kb0; kb < kb1; kb += 2) {
+      if (kb + 1 < kb1) load(kb + 1, b1);
+      compute(kb, b0);
+      if (kb + 1 < kb1) {
+        if (kb + 2 < kb1) load(kb + 2, b0);
+        compute(kb + 1, b1);
+      }
+    }
+  }
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    const f32x4 o = red[w][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += o[i];
+  }
+  // lane holds rows rbase + 4 g + i of query col
+  const int q = col;
+  if (q >= a.B) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = rbase + 4 * g + i;
+    if (r < a.R)
+      a.out[(int64_t)q * a.ld_out + r] =
+          stage1_value(acc[i], a.key.sample, a.key.temperature, a.key.seed, (uint32_t)q, (uint32_t)r);
+  }
+}
+
+// ======================================================================
 // Cluster-major stage 2 (explainer §1.2.1, §1.2.4; batch semantics: each
 // query still takes only its own probes).  Workgroup x owns clusters
 // [8x, 8x + 8).  For each of them the workgroup lists the queries whose
@@ -693,6 +826,18 @@ static hipError_t mfma_dispatch(const MfmaArgs& a, int cus, hipStream_t st, int6
 
 int64_t mfma_blocks(int64_t R) { return (R + 63) / 64; }
 
+// Stage 1 split over d (one query tile) when the GEMM would leave fewer than
+// four workgroups per CU.
+template <int QB>
+static hipError_t score_mfma_go(const MfmaArgs& a, int cus, hipStream_t st) {
+  if (a.B <= 16 && (a.R + 63) / 64 < 4 * (int64_t)cus) {
+    hipLaunchKernelGGL((k_mfma_stage1_splitd<QB>), dim3((unsigned)((a.R + 15) / 16)), dim3(256), 0,
+                       st, a);
+    return hipGetLastError();
+  }
+  return mfma_dispatch<QB, false>(a, cus, st, nullptr);
+}
+
 hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, float* out,
                              const KeyXform& kx) {
   MfmaArgs a{};
@@ -701,14 +846,14 @@ hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, 
   if (k.qbits == 4) {
     a.A = k.cq_mfma; a.sigT = k.sig_mfma; a.ldsig = mfma_sig_ld(k.c);
     a.a_row_bytes = mfma_int4_row_bytes(k.d);
-    return mfma_dispatch<4, false>(a, cus, k.stream, nullptr);
+    return score_mfma_go<4>(a, cus, k.stream);
   }
   if (k.qbits == 8) {
     a.A = k.cq; a.sigT = k.sig_mfma; a.ldsig = mfma_sig_ld(k.c);
-    return mfma_dispatch<8, false>(a, cus, k.stream, nullptr);
+    return score_mfma_go<8>(a, cus, k.stream);
   }
   a.A = k.C;
-  return mfma_dispatch<0, false>(a, cus, k.stream, nullptr);
+  return score_mfma_go<0>(a, cus, k.stream);
 }
 
 int64_t gather_cm_blocks(int64_t c, int) { return (c + kCmClusters - 1) / kCmClusters; }
