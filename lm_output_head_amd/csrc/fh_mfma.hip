@@ -420,12 +420,13 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
 }
 
 // ======================================================================
-// Stage 1 for at most 16 queries (one query tile), split over d.  With one
-// query tile the GEMM above has one workgroup per 64 rows (126 at the
-// Llama-3.2-1B shape's 8016 centroids), each walking all of d; its time is
-// the chain of d / 128 dependent block steps.  Here the four waves of a
-// workgroup take the same 16 rows and consecutive quarters of d, so there
-// are four times the workgroups and a quarter of the chain per wave.  Each
+// Stage 1 split over d, one 16-query tile per workgroup row (grid.y).  With
+// one query tile per workgroup the GEMM above has one workgroup per 64 rows
+// and tile (126 per tile at the Llama-3.2-1B shape's 8016 centroids), each
+// walking all of d; its time is the chain of d / 128 dependent block steps.
+// Here the four waves of a workgroup take the same 16 rows and consecutive
+// quarters of d, so there are four times the workgroups and a quarter of the
+// chain per wave.  Each
 // lane loads its queries' h fragments itself (the [B x d] queries are a few
 // KB and stay in cache), so the waves never synchronise until the end, where
 // waves 1..3 hand their tiles to wave 0 through LDS and it adds them in wave
@@ -437,9 +438,10 @@ __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int64_t rbase = (int64_t)blockIdx.x * 16;
+  const int q0 = 16 * blockIdx.y;
   const int nkb = (a.d + 127) / 128;
   const int kb0 = wave * nkb / 4, kb1 = (wave + 1) * nkb / 4;
-  const uint16_t* Hq = a.H + (int64_t)min(col, a.B - 1) * a.d;
+  const uint16_t* Hq = a.H + (int64_t)min(q0 + col, a.B - 1) * a.d;
   const int64_t ra = min(rbase + col, a.R - 1);
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   // the queries' fragments of block kb: step s holds elements 128 kb + 32 s + 8 g .. + 7
@@ -540,8 +542,8 @@ __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += o[i];
   }
-  // lane holds rows rbase + 4 g + i of query col
-  const int q = col;
+  // lane holds rows rbase + 4 g + i of query q0 + col
+  const int q = q0 + col;
   if (q >= a.B) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -826,13 +828,19 @@ static hipError_t mfma_dispatch(const MfmaArgs& a, int cus, hipStream_t st, int6
 
 int64_t mfma_blocks(int64_t R) { return (R + 63) / 64; }
 
-// Stage 1 split over d (one query tile) when the GEMM would leave fewer than
-// four workgroups per CU.
+// Stage 1 split over d up to 32 queries, where the GEMM's shape rule finds
+// too few workgroups for more than one query tile per workgroup.  Measured at
+// the Llama-3.2-1B shape (INT4 / bf16 stage 1): B = 8 10.4 / 11.6 us against
+// 21.4 / 23.2 us, B = 32 18.0 / 20.9 us against 22.3 / 24.3 us; at B = 64 the
+// GEMM is faster (22.8 / 30.8 us against 28.3 / 34.8 us), its rows being read
+// once per workgroup for more queries.
 template <int QB>
 static hipError_t score_mfma_go(const MfmaArgs& a, int cus, hipStream_t st) {
-  if (a.B <= 16 && (a.R + 63) / 64 < 4 * (int64_t)cus) {
-    hipLaunchKernelGGL((k_mfma_stage1_splitd<QB>), dim3((unsigned)((a.R + 15) / 16)), dim3(256), 0,
-                       st, a);
+  const GemmShape s = gemm_shape(a.R, a.B, cus);
+  const bool splitd = a.B <= 32 && s.nt == 1 && s.mt == 1;
+  if (splitd) {
+    const dim3 grid((unsigned)((a.R + 15) / 16), (unsigned)((a.B + 15) / 16));
+    hipLaunchKernelGGL((k_mfma_stage1_splitd<QB>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
   return mfma_dispatch<QB, false>(a, cus, st, nullptr);

@@ -193,6 +193,10 @@ def test_batches_at_the_cluster_major_limit(B):
                   f"cm limit dense B={B}")
     s = host({"s": head.score(H[:B])})["s"]
     assert_report(parity.check_scores(ref.C_hat, pb.H[rows], s[rows]), f"cm limit scores B={B}")
+    # stage 1 split over d with one and two 16-query tiles (ragged second tile)
+    for nb in (16, 24, 32):
+        s = host({"s": head.score(H[:nb])})["s"]
+        assert_report(parity.check_scores(ref.C_hat, pb.H[:nb], s), f"split-d scores B={nb}")
     head.close()
 
 
