@@ -241,7 +241,9 @@ fh_status fh_profile_end(fh_engine* e, fh_kernel_time* out, int max, int* count)
 
 /*
  * fh_read_probe — a plain one-shot read of a device buffer, for measuring the
- * memory system the head runs on; it computes nothing of the head.  One
+ * memory system the head runs on; it computes nothing of the head (whose
+ * cost the pages place in reading the embedding table from memory: FlashHead
+ * technical explainer, framerc.cn, §1.1).  One
  * 16-byte load per thread in 1024-thread workgroups; a thread that finds a
  * 32-bit word equal to `key` stores 1 to *found, so the call is a search and
  * every load is used, with almost no work after the loads.  The head's phases
