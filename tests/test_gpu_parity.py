@@ -200,6 +200,22 @@ def test_batches_at_the_cluster_major_limit(B):
     head.close()
 
 
+@pytest.mark.parametrize("quant", ["none", "int4", "int8"])
+def test_sampled_probes_over_two_query_tiles(quant):
+    """24 queries with sampled probes and tokens: stage 1 split over d in two
+    16-query tiles forms the Gumbel keys itself, keyed by each query's index
+    in the batch (the second tile's 8 queries included)."""
+    pb = _custom_problem(8192, 128, 512, "bf16", 24, seed=29)
+    head, H = _engine(pb, quant=quant, max_batch=24)
+    ref = _oracle(pb, quant)
+    say("sampled probes two tiles", quant)
+    out = host(head.forward(H, 32, mode=PSAMPLE | TSAMPLE, temperature=0.9, seed=11,
+                            want_clusters=True, want_retrieved=True))
+    assert_report(parity.check_forward(ref, pb.H, 32, PSAMPLE | TSAMPLE, 0.9, 11, out),
+                  f"sampled probes B=24 {quant}")
+    head.close()
+
+
 @pytest.mark.parametrize("shape,quant,B,p,mode,T", [
     ("tiny", "none", 8, 16, SHARED, 1.0),               # fp32: query-major, one probe row
     ("tiny", "none", 64, 16, SHARED | TSAMPLE, 0.8),
