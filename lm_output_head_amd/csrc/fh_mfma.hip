@@ -432,7 +432,7 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
 // waves 1..3 hand their tiles to wave 0 through LDS and it adds them in wave
 // order.  Rows and scale layout as in k_mfma_gemm (MT = 1, no row map).
 // ======================================================================
-template <int QB>
+template <int QB, bool EPI>
 __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
   __shared__ f32x4 red[3][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -544,6 +544,35 @@ __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
   }
   // lane holds rows rbase + 4 g + i of query q0 + col
   const int q = q0 + col;
+  if constexpr (EPI) {
+    // the dense head's epilogue (as in k_mfma_gemm, rows are tokens): one
+    // partial per query and workgroup, the four lane groups folded in order
+    Part p = part_empty();
+    const bool qok = q < a.B;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = rbase + 4 * g + i;
+      if (qok && r < a.R) {
+        if (a.out) a.out[(int64_t)q * a.ld_out + r] = acc[i];
+        Part pt = part_of(acc[i], (int32_t)r, a.token_sample, a.tprime, a.seed, (uint32_t)q);
+        if (a.bits) {
+          const int k = a.t2c[r];
+          const bool probed = (a.bits[(int64_t)q * a.W + (k >> 5)] >> (k & 31)) & 1u;
+          pt.key = probed ? -INFINITY
+                          : acc[i] / a.tprime + gumbel_at(a.seed, (uint32_t)q, (uint32_t)r, 3u);
+        }
+        p = part_merge(p, pt);
+      }
+    }
+#pragma unroll
+    for (int msk = 16; msk <= 32; msk *= 2) {
+      const Part o{__shfl_xor(p.key, msk), __shfl_xor(p.z, msk), __shfl_xor(p.m, msk),
+                   __shfl_xor(p.s, msk), __shfl_xor(p.id, msk)};
+      p = (lane & msk) ? part_merge(o, p) : part_merge(p, o);
+    }
+    if (g == 0 && qok) a.parts[(int64_t)q * gridDim.x + blockIdx.x] = p;
+    return;
+  }
   if (q >= a.B) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -840,7 +869,7 @@ static hipError_t score_mfma_go(const MfmaArgs& a, int cus, hipStream_t st) {
   const bool splitd = a.B <= 32 && s.nt == 1 && s.mt == 1;
   if (splitd) {
     const dim3 grid((unsigned)((a.R + 15) / 16), (unsigned)((a.B + 15) / 16));
-    hipLaunchKernelGGL((k_mfma_stage1_splitd<QB>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_mfma_stage1_splitd<QB, false>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
   return mfma_dispatch<QB, false>(a, cus, st, nullptr);
@@ -891,6 +920,22 @@ hipError_t launch_gather_cm(const KernelCtx& k, int cus, const void* h, int B, i
   return hipGetLastError();
 }
 
+// The dense head's passes over all of E (the dense head itself and the
+// verification's): split over d for up to kDenseSplitdMaxB queries, the GEMM
+// beyond.  Every 16-row workgroup of the split reads its queries' h, so the
+// cache traffic grows with B: measured at the Llama-3.2-1B shape, B = 2 takes
+// 101 us against the GEMM's 116 us, but B = 8 122 us against 118 us.
+constexpr int kDenseSplitdMaxB = 4;
+static hipError_t dense_mfma_go(const MfmaArgs& a, int cus, hipStream_t st, int64_t* nparts) {
+  if (a.B <= kDenseSplitdMaxB) {
+    const dim3 grid((unsigned)((a.R + 15) / 16), 1);
+    *nparts = grid.x;
+    hipLaunchKernelGGL((k_mfma_stage1_splitd<0, true>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  return mfma_dispatch<0, true>(a, cus, st, nparts);
+}
+
 hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, int token_sample,
                              float tprime, uint64_t seed, float* out_logits, Part* parts,
                              int64_t* nparts) {
@@ -898,7 +943,7 @@ hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, 
   a.A = k.E; a.R = k.v; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
   a.out = out_logits; a.ld_out = k.v;
   a.token_sample = token_sample; a.tprime = tprime; a.seed = seed; a.parts = parts;
-  return mfma_dispatch<0, true>(a, cus, k.stream, nparts);
+  return dense_mfma_go(a, cus, k.stream, nparts);
 }
 
 hipError_t launch_gather_shared_mfma(const KernelCtx& k, int cus, const void* h, int B,
@@ -920,7 +965,7 @@ hipError_t launch_spec_mfma(const KernelCtx& k, int cus, const void* h, int B, f
   a.A = k.E; a.R = k.v; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
   a.token_sample = 0; a.tprime = T; a.seed = seed; a.parts = parts;
   a.t2c = t2c; a.bits = bits; a.W = W;
-  return mfma_dispatch<0, true>(a, cus, k.stream, nparts);
+  return dense_mfma_go(a, cus, k.stream, nparts);
 }
 
 }  // namespace fh
