@@ -339,7 +339,7 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
 
   e->parts_per_q = std::max<int64_t>(
       {fh::rows_blocks(v, fh::kGatherRPW), fh::rows_blocks(v, fh::kDenseRPW),
-       fh::gather_cm_blocks(c, e->cus), fh::mfma_blocks(v), 4096});
+       fh::gather_cm_blocks(c, e->cus), fh::mfma_blocks(v), fh::splitd_blocks(v), 4096});
   struct Alloc { void** p; size_t bytes; const char* what; };
   const Alloc allocs[] = {
       {(void**)&e->c2t, sizeof(int32_t) * (size_t)v, "C2T"},

@@ -84,9 +84,10 @@ hipError_t launch_dense(const KernelCtx& k, const void* h, int B, int token_samp
 constexpr int kMfmaMinBatchBf16 = 8;  // bf16 stage 1
 constexpr int kMfmaMinBatchDense = 2;  // the dense head and the speculative verification (bf16)
 constexpr int kMfmaMinBatchInt4 = 2;  // INT4 stage 1
-constexpr int kMfmaMinBatchInt8 = 2;  // INT8 stage 1 (split over d up to 16 queries: 13.7 us at B = 16)
+constexpr int kMfmaMinBatchInt8 = 2;  // INT8 stage 1 (split over d at small B: 13.7 us at B = 16)
 int64_t mfma_int4_row_bytes(int d);
-int64_t mfma_blocks(int64_t R);  // row blocks (partials per query) of the MFMA dense head
+int64_t mfma_blocks(int64_t R);    // row blocks (partials per query) of the MFMA dense head
+int64_t splitd_blocks(int64_t R);  // the same for the dense pass split over d (16 rows each)
 int64_t mfma_sig_ld(int64_t c);
 hipError_t launch_mfma_relayout(const KernelCtx& k, uint8_t* cq_mfma, uint16_t* sigT);
 hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, float* out,

@@ -856,6 +856,7 @@ static hipError_t mfma_dispatch(const MfmaArgs& a, int cus, hipStream_t st, int6
 }
 
 int64_t mfma_blocks(int64_t R) { return (R + 63) / 64; }
+int64_t splitd_blocks(int64_t R) { return (R + 15) / 16; }
 
 // Stage 1 split over d up to 32 queries, where the GEMM's shape rule finds
 // too few workgroups for more than one query tile per workgroup.  Measured at
@@ -928,7 +929,7 @@ hipError_t launch_gather_cm(const KernelCtx& k, int cus, const void* h, int B, i
 constexpr int kDenseSplitdMaxB = 4;
 static hipError_t dense_mfma_go(const MfmaArgs& a, int cus, hipStream_t st, int64_t* nparts) {
   if (a.B <= kDenseSplitdMaxB) {
-    const dim3 grid((unsigned)((a.R + 15) / 16), 1);
+    const dim3 grid((unsigned)splitd_blocks(a.R), 1);
     *nparts = grid.x;
     hipLaunchKernelGGL((k_mfma_stage1_splitd<0, true>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
