@@ -74,15 +74,16 @@ def test_tiny_matches_oracle(mode):
     head.close()
 
 
-@pytest.mark.parametrize("T", [1.0, 0.25])
-def test_llama_matches_oracle(T):
+@pytest.mark.parametrize("T,B", [(1.0, 8), (0.25, 8), (1.0, 3)])
+def test_llama_matches_oracle(T, B):
     """Full size: at T = 1 the probes hold little of the target's mass (most
-    drafts are refused and redrawn outside them); at T = 0.25 most are kept."""
+    drafts are refused and redrawn outside them); at T = 0.25 most are kept.
+    B = 8 runs the dense pass as the matrix-core GEMM, B = 3 split over d."""
     from lm_output_head_amd import FlashHead
-    pb = make_problem("llama32_1b", nq=8)
+    pb = make_problem("llama32_1b", nq=B)
     E, C, H = problem_tensors(pb)
-    head = FlashHead(E, C, pb.C2T, max_batch=8)
-    say("spec llama B=8 T", T)
+    head = FlashHead(E, C, pb.C2T, max_batch=B)
+    say("spec llama B", B, "T", T)
     draft, ver = _run(head, H, 512, PSAMPLE | TSAMPLE, T, 21, 22)
     _check(pb, pb.H, draft, ver, T, 22)
     head.close()
