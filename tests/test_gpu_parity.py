@@ -148,7 +148,7 @@ def test_ragged_shapes(v, d, c, dtype):
     (2048, 2048, 128, "f32", "none"),   # the largest fp32 d
 ])
 def test_maximum_hidden_size(v, d, c, dtype, quant):
-    """d at the build's limit, through every path: the single launch (B = 1),
+    """d at the library's limit, through every path: the single launch (B = 1),
     per-stage launches, the matrix cores for stage 1 (INT4 and INT8 from B = 2, bf16
     from 8) and the dense head (from 2)."""
     pb = _custom_problem(v, d, c, dtype, 8, seed=13)
