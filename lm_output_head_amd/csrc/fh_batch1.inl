@@ -37,8 +37,12 @@ namespace fh {
 // already running and never waits for its waiter; the grid need not be
 // co-resident.  Sizes keep G1 < CUs and G2 < CUs so that at one workgroup
 // per CU the selector starts at once and every stage-2 workgroup and the
-// finisher are resident when stage 1 retires.  Every wait is bounded: past kSpinLimit polls the waiter sets
-// *err and goes on with what it has, so the grid always drains.
+// finisher are resident when stage 1 retires.  Every wait is bounded: past
+// kSpinLimit polls the waiter sets *err and goes on with what it has, so the
+// grid always drains; indices derived from a word that never arrived are
+// clamped to valid rows, a stage-2 workgroup that gave up (the selector's
+// key poll included) publishes its partial with id kBadPart, and the
+// finisher then writes token -1 with a NaN logit and LSE.
 // ======================================================================
 struct FusedArgs {
   const void* E;
@@ -87,7 +91,7 @@ __device__ __forceinline__ void st_tagged(unsigned long long* p, unsigned long l
 // round in flight together; out[i] gets word i's low 32 bits.  Words with
 // live[i] false are skipped.
 template <int N>
-__device__ __forceinline__ void poll_tagged(unsigned long long* const (&p)[N],
+__device__ __forceinline__ bool poll_tagged(unsigned long long* const (&p)[N],
                                             const bool (&live)[N], unsigned epoch,
                                             unsigned* err, uint32_t (&out)[N]) {
   unsigned long long v[N];
@@ -102,7 +106,9 @@ __device__ __forceinline__ void poll_tagged(unsigned long long* const (&p)[N],
     if (done) break;
     if (n >= kSpinLimit) {
       __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
+#pragma unroll
+      for (int i = 0; i < N; ++i) out[i] = (uint32_t)v[i];
+      return false;
     }
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
@@ -112,7 +118,12 @@ __device__ __forceinline__ void poll_tagged(unsigned long long* const (&p)[N],
   }
 #pragma unroll
   for (int i = 0; i < N; ++i) out[i] = (uint32_t)v[i];
+  return true;
 }
+
+// A stage-2 partial whose workgroup gave up a poll carries this id (never a
+// token id, nor part_empty's), so that the finisher can mark the outputs.
+constexpr int32_t kBadPart = -1;
 
 union Batch1Shared {
   SelShared sel;
@@ -161,31 +172,37 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   }
 
   if (w == a.g1 + a.g2) {  // ---- finisher: the stage-2 partials in a fixed order
-    // waves [0, nwv) hold partials: part i goes to thread i mod 1024
-    const int nwv = min(16, (a.g2 + 63) / 64);
+    // part i goes to thread i mod 1024 (threads past g2 hold part_empty)
     Part acc = part_empty();
+    bool bad = false;
     for (int i = threadIdx.x; i < a.g2; i += 1024) {
       unsigned long long* tp = a.tparts + 5 * (int64_t)i;
       unsigned long long* const ptr[5] = {tp, tp + 1, tp + 2, tp + 3, tp + 4};
       const bool live[5] = {true, true, true, true, true};
       uint32_t wv[5];
-      poll_tagged<5>(ptr, live, a.epoch, a.err, wv);
+      if (!poll_tagged<5>(ptr, live, a.epoch, a.err, wv) || (int32_t)wv[4] == kBadPart) bad = true;
       acc = part_merge(acc, Part{__uint_as_float(wv[0]), __uint_as_float(wv[1]),
                                  __uint_as_float(wv[2]), __uint_as_float(wv[3]), (int32_t)wv[4]});
     }
-    if (wave < nwv) {
-      acc = wave_merge_part(acc);
-      if (lane == 0) sh.parts[wave] = acc;
+    const bool anybad = __syncthreads_or(bad);
+    // the waves' partials, then a 16-lane DPP tree over them (fixed order)
+    acc = wave_merge_part(acc);
+    const Part r = block_merge_parts<16, 1>({acc}, 1, sh.parts);
+    if (threadIdx.x == 0) {
+      if (anybad) {
+        if (a.out_token) a.out_token[0] = -1;
+        if (a.out_logit) a.out_logit[0] = __int_as_float(0x7FC00000);
+        if (a.out_lse) a.out_lse[0] = __int_as_float(0x7FC00000);
+      } else {
+        write_outputs(r, 0, a.out_token, a.out_logit, a.out_lse);
+      }
     }
-    __syncthreads();
-    Part r = sh.parts[0];
-    for (int w2 = 1; w2 < nwv; ++w2) r = part_merge(r, sh.parts[w2]);
-    if (threadIdx.x == 0) write_outputs(r, 0, a.out_token, a.out_logit, a.out_lse);
     FH_TRACE(14);
     return;
   }
 
   const int j = w - a.g1;  // stage-2 workgroup index
+  bool gave_up = false;    // a poll of this thread gave up
   if (j == 0) {            // ---- selector
     FH_TRACE(2);
     // every thread waits for the keys of clusters k = tid + 1024 i, which
@@ -200,7 +217,7 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
       live[i] = k < a.c;
       ptr[i] = a.tscores + (live[i] ? k : 0);
     }
-    poll_tagged<KP>(ptr, live, a.epoch, a.err, raw);
+    if (!poll_tagged<KP>(ptr, live, a.epoch, a.err, raw)) gave_up = true;
     float x[KP];
 #pragma unroll
     for (int i = 0; i < KP; ++i) x[i] = live[i] ? __uint_as_float(raw[i]) : -FLT_MAX;
@@ -227,13 +244,18 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   if (npos > 0) {
     const int nw = (a.c + 31) / 32;
     const int t = threadIdx.x;
+    // every listed probe starts as a valid cluster: if a bitset word never
+    // arrives, the popcounts need not reach p and some positions stay unset
+    for (int i = t; i < npos; i += 1024) sh.probes[i] = 0;
     uint32_t word = 0u;
     if (t < nw) {
       unsigned long long* const ptr[1] = {a.tsel + t};
       const bool live[1] = {true};
       uint32_t got[1];
-      poll_tagged<1>(ptr, live, a.epoch, a.err, got);
+      if (!poll_tagged<1>(ptr, live, a.epoch, a.err, got)) gave_up = true;
       word = got[0];
+      // bits past c (a stale or foreign word) name no cluster
+      if (t == nw - 1 && (a.c & 31)) word &= (1u << (a.c & 31)) - 1u;
     }
     int tot;
     int pos = block_exclusive_scan(__popc(word), sh.sel.red_scan, &tot);
@@ -267,8 +289,10 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   // four rows in flight per wave when the register slice allows it
   wave_rows<T, MAXM, 1, (MAXM <= 4 ? 4 : 2)>(static_cast<const T*>(a.Ec ? a.Ec : a.E), a.d, lane,
                                              hv, 1, r_lo + wave, r_hi, 16, src_of, tok_of, sink);
-  __syncthreads();  // sh.probes is read above; sh.parts aliases it
-  const Part wg = block_merge_parts<16, 1>(part, 1, sh.parts);
+  // sh.probes is read above; sh.parts aliases it
+  const bool wg_bad = __syncthreads_or(gave_up);
+  Part wg = block_merge_parts<16, 1>(part, 1, sh.parts);
+  if (wg_bad) wg.id = kBadPart;
   if (threadIdx.x == 0) {
     unsigned long long* tp = a.tparts + 5 * (int64_t)j;
     st_tagged(tp + 0, tag(a.epoch, __float_as_uint(wg.key)));

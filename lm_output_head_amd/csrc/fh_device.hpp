@@ -200,13 +200,13 @@ __device__ __forceinline__ Part part_merge(const Part& a, const Part& b) {
   } else {
     r.key = a.key; r.id = a.id; r.z = a.z;
   }
-  const float m = fmaxf(a.m, b.m);
-  if (m == -INFINITY) {
-    r.m = m; r.s = 0.f;
-  } else {
-    r.m = m;
-    r.s = a.s * expf(a.m - m) + b.s * expf(b.m - m);
-  }
+  // (m, s): the larger max keeps its sum, the other's sum is rescaled by
+  // one exponential (commutative: equal maxima add the sums either way)
+  const bool ab = a.m >= b.m;
+  const float hm = ab ? a.m : b.m, lm = ab ? b.m : a.m;
+  const float hs = ab ? a.s : b.s, ls = ab ? b.s : a.s;
+  r.m = hm;
+  r.s = hm == -INFINITY ? 0.f : fmaf(ls, __expf(lm - hm), hs);
   return r;
 }
 

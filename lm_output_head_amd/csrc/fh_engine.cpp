@@ -65,7 +65,7 @@ struct fh_engine {
   fh::Part* parts = nullptr;  // [max_batch x parts_per_q]
   int64_t parts_per_q = 0;
   unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up
-  unsigned long long* tagged = nullptr;  // batch-1 hand-over words: c scores + 5 per partial
+  unsigned long long* tagged = nullptr;  // batch-1 hand-over words (fh_batch1_sizing.hpp layout)
   unsigned epoch = 0;
   int cus = 0;                // compute units of the device
   int path = FH_PATH_AUTO;
@@ -335,7 +335,9 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "hipGetDevice"); }
   r = hipDeviceGetAttribute(&e->cus, hipDeviceAttributeMultiprocessorCount, e->device);
   if (r != hipSuccess || e->cus <= 0) { free_engine(e); return hip_fail(r, "device attributes"); }
-  const int64_t ntag = 2 * c + 5 * (int64_t)fh::batch1_stage2_blocks(c, b, e->cus);
+  // batch-1 hand-over words: enough partials for the largest stage-2 grid of
+  // any p (batch1_stage2_blocks never exceeds batch1_slots2)
+  const int64_t ntag = fh::batch1_tag_words(c, e->cus);
 
   e->parts_per_q = std::max<int64_t>(
       {fh::rows_blocks(v, fh::kGatherRPW), fh::rows_blocks(v, fh::kDenseRPW),
@@ -459,8 +461,8 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
     e->epoch = e->epoch == 0xFFFFFFFFu ? 1u : e->epoch + 1u;
     f.epoch = e->epoch;
     f.tscores = e->tagged;
-    f.tsel = e->tagged + e->c;
-    f.tparts = e->tagged + 2 * e->c;
+    f.tsel = e->tagged + fh::batch1_off_sel(e->c);
+    f.tparts = e->tagged + fh::batch1_off_parts(e->c);
     f.out_clusters = out_clusters;
     f.out_ids = out_ids;
     f.out_logits = out_logits;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fh_batch1_sizing.hpp"
+
 namespace fh {
 
 // A partial epilogue result over a set of candidate tokens: the best
@@ -127,7 +129,7 @@ struct FusedLaunch {
   unsigned epoch;                 // this call's tag, never 0
   unsigned long long* tscores;    // [c] tagged scores (zeroed at create)
   unsigned long long* tsel;       // [ceil(c/32)] tagged probe bitset (zeroed at create)
-  unsigned long long* tparts;     // [5 x batch1_stage2_blocks(c, b, cus)] (zeroed at create)
+  unsigned long long* tparts;     // [5 x batch1_slots2(cus)] (zeroed at create)
   int32_t* out_clusters;          // [p] or null
   int32_t* out_ids;
   float* out_logits;
@@ -171,21 +173,5 @@ hipError_t launch_batch1_f32(const FusedLaunch& f);
 hipError_t launch_batch1_f32_int4(const FusedLaunch& f);
 hipError_t launch_batch1_bf16_int8(const FusedLaunch& f);
 hipError_t launch_batch1_f32_int8(const FusedLaunch& f);
-
-// Batch-1 sizing: rows per workgroup are a multiple of kBatch1RowsUnit
-// (one row for each of the 16 waves), large enough that a stage needs at
-// most `slots` workgroups.
-#ifndef FH_BATCH1_ROWS_UNIT
-#define FH_BATCH1_ROWS_UNIT 16
-#endif
-constexpr int kBatch1RowsUnit = FH_BATCH1_ROWS_UNIT;
-int64_t batch1_rows(int64_t n, int64_t slots);
-int64_t batch1_slots1(int cus);  // stage-1 workgroup budget
-int64_t batch1_slots2(int cus);  // stage-2 workgroup budget (one CU left for the finisher)
-int batch1_stage1_blocks(int64_t c, int cus);
-int batch1_stage2_blocks(int64_t p, int64_t b, int cus);
-// Whether a batch-1 call with p probes fits the single launch (a stage-2
-// workgroup holds the probes of its rows in a 1024-entry LDS list).
-bool batch1_fits(int64_t p, int64_t b, int cus);
 
 }  // namespace fh

@@ -486,35 +486,7 @@ hipError_t launch_finish(const KernelCtx& k, const Part* parts, int B, int64_t n
   return hipGetLastError();
 }
 
-// ---- batch-1 path: one launch
-
-// Rows per workgroup: a multiple of kBatch1RowsUnit (a row per wave) large
-// enough that a stage needs at most `slots` workgroups: cus - 4 for stage 1
-// (so the selector and a few stage-2 workgroups start at once), cus - 1 for
-// stage 2 (one CU for the finisher).
-int64_t batch1_rows(int64_t n, int64_t slots) {
-  slots = std::max<int64_t>(slots, 1);
-  const int64_t units = (n + kBatch1RowsUnit - 1) / kBatch1RowsUnit;
-  return kBatch1RowsUnit * std::max<int64_t>(1, (units + slots - 1) / slots);
-}
-int64_t batch1_slots1(int cus) { return cus > 8 ? cus - 4 : 4; }
-int batch1_stage1_blocks(int64_t c, int cus) {
-  const int64_t r = batch1_rows(c, batch1_slots1(cus));
-  return (int)((c + r - 1) / r);
-}
-#ifndef FH_STAGE2_SLOTS_DIV
-#define FH_STAGE2_SLOTS_DIV 1  // stage-2 workgroup budget = (CUs - 1) / this
-#endif
-int64_t batch1_slots2(int cus) { return std::max(1, (cus - 1) / FH_STAGE2_SLOTS_DIV); }
-int batch1_stage2_blocks(int64_t p, int64_t b, int cus) {
-  const int64_t r = batch1_rows(p * b, batch1_slots2(cus));
-  return (int)std::max<int64_t>(1, (p * b + r - 1) / r);
-}
-
-bool batch1_fits(int64_t p, int64_t b, int cus) {
-  const int64_t rows2 = batch1_rows(p * b, batch1_slots2(cus));
-  return rows2 / b + 2 <= 1024;
-}
+// ---- batch-1 path: one launch (sizing in fh_batch1_sizing.hpp)
 
 hipError_t launch_batch1(const FusedLaunch& f) {
   switch (f.ctx->qbits) {
