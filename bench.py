@@ -67,7 +67,7 @@ def parse():
                     help="time the speculative verification of K draft positions (fh_spec_verify) "
                          "beside K single-position drafts and the dense head at B=K; one JSON line")
     ap.add_argument("--burst", action="store_true",
-                    help="time the plain one-shot read probe (fh_read_probe) at the sizes of a "
+                    help="time the plain one-shot read probe (fhb_read_probe) at the sizes of a "
                          "batch-1 call's phases, the whole call and the dense head; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of known size (to scale the "
@@ -97,6 +97,19 @@ BURST_SIZES = (("stage 1", 32_869_696), ("stage 2", 33_593_344), ("batch-1 call"
                ("dense head", 525_340_672))
 
 
+def load_bench_lib():
+    """bench.py's own library (the plain read probe, fhb_read_probe), built
+    beside libflashhead.so by lm_output_head_amd.build."""
+    path = os.path.join(ROOT, "lm_output_head_amd", "libflashhead_bench.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build with `python -m lm_output_head_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.fhb_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.fhb_read_probe.restype = ctypes.c_int
+    return lib
+
+
 def burst_main(args):
     """How fast the part streams a buffer of each size in one launch: the
     library's plain read probe over 16 rotating buffers (their 8.4 GB exceed the
@@ -108,8 +121,7 @@ def burst_main(args):
 
     import torch
 
-    from lm_output_head_amd import _abi
-    lib = _abi.load()
+    lib = load_bench_lib()
     nbuf, steps = 16, max(50, min(args.steps, 400))
     big = max(n for _, n in BURST_SIZES)
     bufs = [torch.full((big // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(nbuf)]
@@ -117,11 +129,11 @@ def burst_main(args):
     stream = torch.cuda.current_stream()
     ptrs = [ctypes.c_void_p(b.data_ptr()) for b in bufs]
     fptr, sptr = ctypes.c_void_p(found.data_ptr()), ctypes.c_void_p(stream.cuda_stream)
-    probe = lib.fh_read_probe
+    probe = lib.fhb_read_probe
     rows = []
     for what, n in BURST_SIZES:
         for i in range(20):
-            assert probe(ptrs[i % nbuf], n, 0, fptr, sptr) == 0, lib.fh_last_error()
+            assert probe(ptrs[i % nbuf], n, 0, fptr, sptr) == 0
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(stream)

@@ -21,7 +21,7 @@ FH_PATH_AUTO, FH_PATH_MULTI = 0, 1
 # Every symbol the header declares.
 EXPORTS = (
     "fh_create", "fh_destroy", "fh_forward", "fh_score", "fh_dense_forward",
-    "fh_get_int4", "fh_get_int8", "fh_spec_verify", "fh_profile_begin", "fh_profile_end", "fh_read_probe",
+    "fh_get_int4", "fh_get_int8", "fh_spec_verify", "fh_profile_begin", "fh_profile_end",
     "fh_set_path", "fh_sync_status",
     "fh_balanced_assign", "fh_cluster", "fh_last_error", "fh_version",
 )
@@ -63,7 +63,6 @@ _SIGS = {
     "fh_spec_verify": ([_p, _p, _i64, _i64, _p, _p, _p, _f, _u64, _p, _p, _p, _p], _int),
     "fh_profile_begin": ([_p, _i64], _int),
     "fh_profile_end": ([_p, ctypes.POINTER(FhKernelTime), _int, ctypes.POINTER(_int)], _int),
-    "fh_read_probe": ([_p, _i64, ctypes.c_uint32, _p, _p], _int),
     "fh_set_path": ([_p, _int], _int),
     "fh_sync_status": ([_p, _p], _int),
     "fh_balanced_assign": ([_p, _i64, _i64, _p, ctypes.POINTER(_int), _p], _int),

@@ -1,4 +1,5 @@
-"""Build libflashhead.so in-tree with hipcc for gfx950.
+"""Build libflashhead.so (and bench.py's libflashhead_bench.so) in-tree with
+hipcc for gfx950.
 
 Usage: ``python -m lm_output_head_amd.build``.
 Every call compiles from source; object files go to ``lm_output_head_amd/_build``.
@@ -18,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashhead.so")
+# bench.py --burst only: the plain read probe, outside the product's C ABI
+BENCH_LIB = os.path.join(PKG, "libflashhead_bench.so")
+BENCH_SOURCE = os.path.join(PKG, "bench_read_probe.hip")
 
 SOURCES = ["fh_kernels.hip", "fh_mfma.hip", "fh_cluster.hip", "fh_batch1_bf16.hip", "fh_batch1_bf16_int4.hip",
            "fh_batch1_bf16_int8.hip", "fh_batch1_f32.hip", "fh_batch1_f32_int8.hip",
@@ -61,8 +65,14 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}")
     os.replace(tmp, LIB)
+    tmp = BENCH_LIB + ".tmp"
+    cmd = [_hipcc(), *COMMON, *extra, "-shared", "-x", "hip", BENCH_SOURCE, "-o", tmp]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"bench library build failed: {' '.join(cmd)}\n{r.stdout}")
+    os.replace(tmp, BENCH_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {BENCH_LIB}")
     return LIB
 
 

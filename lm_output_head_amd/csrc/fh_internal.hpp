@@ -67,8 +67,6 @@ float select_quantile(int64_t c, int64_t p);
 // S [B x ldS]: the p probes of each query, ascending.  With mbits/mpre non-
 // null also the probe bitsets word-major, mbits[w * B + q], and the probes of
 // q in words before w, mpre[w * B + q] (W = ceil(c/32) words).
-hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t key, uint32_t* found,
-                             hipStream_t st);
 hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, int sample,
                          float temperature, uint64_t seed, int32_t* S, int ldS,
                          uint32_t* mbits = nullptr, int32_t* mpre = nullptr);

@@ -232,23 +232,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   }
 }
 
-// A plain one-shot read of n16 16-byte words: thread i loads word i and, if
-// one of its four 32-bit values equals key, stores 1 to *found (a search, so
-// every load is used; equal stores from several threads are benign).  No part
-// of the head's arithmetic: it measures how fast the part streams a buffer of
-// a given size in one launch, with almost nothing after the loads.
-__global__ __launch_bounds__(1024) void k_read_probe(const uint4* __restrict__ p, int64_t n16,
-                                                     uint32_t key, uint32_t* __restrict__ found) {
-  const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
-  if (i >= n16) return;
-  const uint4 v = p[i];
-  // no short-circuit: with || the compiler loads one word first and the rest
-  // only after comparing it, two dependent memory round trips
-  const uint32_t hit = (uint32_t)(v.x == key) | (uint32_t)(v.y == key) | (uint32_t)(v.z == key) |
-                       (uint32_t)(v.w == key);
-  if (hit) *found = 1u;
-}
-
 __global__ __launch_bounds__(256) void k_finish(const Part* __restrict__ parts, int nparts,
                                                 int32_t* __restrict__ out_token,
                                                 float* __restrict__ out_logit,
@@ -381,13 +364,6 @@ hipError_t launch_permute_rows(const KernelCtx& k, void* out) {
   const unsigned blocks = (unsigned)((k.v + 3) / 4);
   hipLaunchKernelGGL(k_permute_rows, dim3(blocks), dim3(256), 0, k.stream,
                      static_cast<const uint4*>(k.E), k.c2t, static_cast<uint4*>(out), k.v, nch);
-  return hipGetLastError();
-}
-
-hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t key, uint32_t* found,
-                             hipStream_t st) {
-  hipLaunchKernelGGL(k_read_probe, dim3((unsigned)((n16 + 1023) / 1024)), dim3(1024), 0, st,
-                     static_cast<const uint4*>(buf), n16, key, found);
   return hipGetLastError();
 }
 

@@ -42,6 +42,25 @@ def _require(t, dtype, shape, name):
         raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
 
 
+# What each engine was created with: h must have the engine's dtype and d
+# columns and every output its size, or the kernels would read or write past
+# them.  Keyed by the handle's value: (dtype, v, d, c).
+_ENGINES = {}
+
+
+def _engine_h(eng, h):
+    """Check h [B x d] against the engine; returns (B, v, d, c)."""
+    key = eng.value if isinstance(eng, ctypes.c_void_p) else eng
+    info = _ENGINES.get(key)
+    if info is None:
+        raise ValueError("unknown engine handle (not created by fh_create, or destroyed)")
+    dtype, v, d, c = info
+    if h.dim() != 2:
+        raise ValueError(f"h must be [B x d], got shape {tuple(h.shape)}")
+    _require(h, dtype, (h.shape[0], d), "h")
+    return h.shape[0], v, d, c
+
+
 def fh_version() -> str:
     return _abi.load().fh_version().decode()
 
@@ -65,15 +84,25 @@ def fh_create(E: torch.Tensor, C: torch.Tensor, C2T, quant: str = "none", max_ba
     eng = ctypes.c_void_p()
     check(lib.fh_create(_ptr(E), _ptr(C), c2t.ctypes.data_as(ctypes.c_void_p), _DTYPES[E.dtype],
                         v, d, c, _QUANTS[quant], max_batch, _stream(stream), ctypes.byref(eng)))
+    _ENGINES[eng.value] = (E.dtype, v, d, c)
     return eng
 
 
 def fh_destroy(eng) -> None:
     _abi.load().fh_destroy(eng)
+    _ENGINES.pop(eng.value if isinstance(eng, ctypes.c_void_p) else eng, None)
 
 
 def fh_forward(eng, h, p, mode, temperature, seed, out_token, out_token_logit=None, out_lse=None,
                out_clusters=None, out_ids=None, out_logits=None, stream=None) -> None:
+    B, v, _, c = _engine_h(eng, h)
+    b = v // c
+    _require(out_token, torch.int32, (B,), "out_token")
+    _require(out_token_logit, torch.float32, (B,), "out_token_logit")
+    _require(out_lse, torch.float32, (B,), "out_lse")
+    _require(out_clusters, torch.int32, (B, p), "out_clusters")
+    _require(out_ids, torch.int32, (B, p * b), "out_ids")
+    _require(out_logits, torch.float32, (B, p * b), "out_logits")
     check(_abi.load().fh_forward(eng, _ptr(h), h.shape[0], p, mode, temperature, seed,
                                  _ptr(out_token), _ptr(out_token_logit), _ptr(out_lse),
                                  _ptr(out_clusters), _ptr(out_ids), _ptr(out_logits),
@@ -81,11 +110,18 @@ def fh_forward(eng, h, p, mode, temperature, seed, out_token, out_token_logit=No
 
 
 def fh_score(eng, h, out_scores, stream=None) -> None:
+    B, _, _, c = _engine_h(eng, h)
+    _require(out_scores, torch.float32, (B, c), "out_scores")
     check(_abi.load().fh_score(eng, _ptr(h), h.shape[0], _ptr(out_scores), _stream(stream)))
 
 
 def fh_dense_forward(eng, h, mode, temperature, seed, out_token, out_token_logit=None,
                      out_lse=None, out_logits=None, stream=None) -> None:
+    B, v, _, _ = _engine_h(eng, h)
+    _require(out_token, torch.int32, (B,), "out_token")
+    _require(out_token_logit, torch.float32, (B,), "out_token_logit")
+    _require(out_lse, torch.float32, (B,), "out_lse")
+    _require(out_logits, torch.float32, (B, v), "out_logits")
     check(_abi.load().fh_dense_forward(eng, _ptr(h), h.shape[0], mode, temperature, seed,
                                        _ptr(out_token), _ptr(out_token_logit), _ptr(out_lse),
                                        _ptr(out_logits), _stream(stream)))
@@ -101,6 +137,13 @@ def fh_get_int8(eng, codes, scales, stream=None) -> None:
 
 def fh_spec_verify(eng, h, p, draft_clusters, draft_token, draft_lse, temperature, seed,
                    out_token, out_accepted=None, out_lse=None, stream=None) -> None:
+    B, _, _, _ = _engine_h(eng, h)
+    _require(draft_clusters, torch.int32, (B, p), "draft_clusters")
+    _require(draft_token, torch.int32, (B,), "draft_token")
+    _require(draft_lse, torch.float32, (B,), "draft_lse")
+    _require(out_token, torch.int32, (B,), "out_token")
+    _require(out_accepted, torch.int32, (B,), "out_accepted")
+    _require(out_lse, torch.float32, (B,), "out_lse")
     check(_abi.load().fh_spec_verify(eng, _ptr(h), h.shape[0], p, _ptr(draft_clusters),
                                      _ptr(draft_token), _ptr(draft_lse), temperature, seed,
                                      _ptr(out_token), _ptr(out_accepted), _ptr(out_lse),
@@ -125,15 +168,6 @@ def fh_profile_end(eng) -> dict:
     n = ctypes.c_int(0)
     check(_abi.load().fh_profile_end(eng, recs, 64, ctypes.byref(n)))
     return {recs[i].name.decode(): (recs[i].launches, recs[i].total_ms) for i in range(n.value)}
-
-
-def fh_read_probe(buf: torch.Tensor, key: int, found: torch.Tensor, stream=None) -> None:
-    """One-shot read of buf (any GPU tensor, nbytes a multiple of 16): sets
-    found (int32 [1] on the GPU, cleared by the caller) to 1 if some 32-bit
-    word of buf equals key (taken mod 2^32)."""
-    _require(found, torch.int32, (1,), "found")
-    check(_abi.load().fh_read_probe(_ptr(buf), buf.numel() * buf.element_size(), key & 0xFFFFFFFF,
-                                    _ptr(found), _stream(stream)))
 
 
 def fh_balanced_assign(sims: torch.Tensor, out_assign: torch.Tensor, stream=None) -> int:

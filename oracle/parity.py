@@ -56,15 +56,30 @@ def _logit_tol(E, ids, h, z_ref, rel):
     return rel * np.maximum(np.abs(z_ref), floor)
 
 
+FORWARD_KEYS = ("clusters", "ids", "logits", "token", "token_logit", "lse")
+DENSE_KEYS = ("token", "token_logit", "lse")
+
+
+def _missing(rep, gpu, keys):
+    miss = [k for k in keys if k not in gpu]
+    if miss:
+        rep.fail(f"result lacks {', '.join(miss)}: nothing can be certified without them")
+    return bool(miss)
+
+
 def check_forward(head: OracleHead, H, p, mode, temperature, seed, gpu: dict, queries=None,
                   rel=REL, tie_gap=TIE_GAP) -> Report:
     """Compare a GPU forward result (numpy arrays keyed like FlashHead.forward)
-    with the oracle, on all queries or on the listed row indices."""
+    with the oracle, on all queries or on the listed row indices.  Every
+    output is required: the probe set, the retrieved ids and logits, the
+    token, its logit and the LSE (FORWARD_KEYS)."""
     H = np.atleast_2d(np.asarray(H, dtype=np.float64))
     B = H.shape[0]
     rows = range(B) if queries is None else queries
     rep = Report()
     rows = list(rows)
+    if _missing(rep, gpu, FORWARD_KEYS):
+        return rep
     shared = bool(mode & 4)  # a shared probe set depends on every row of the batch
     s = (H if shared else H[rows]) @ head.C_hat.T  # float64 scores
     sel = select(s, p, mode, temperature, seed, rows=None if shared else rows)
@@ -75,7 +90,7 @@ def check_forward(head: OracleHead, H, p, mode, temperature, seed, gpu: dict, qu
         keys_all = sel.key[i]
         S_ref = sel.S[i]
         theta = float(sel.theta[i])
-        S_gpu = np.asarray(gpu["clusters"][r]) if "clusters" in gpu else S_ref
+        S_gpu = np.asarray(gpu["clusters"][r])
         if not np.array_equal(S_gpu, S_ref):
             if (len(S_gpu) != p or np.any(np.diff(S_gpu) <= 0) or S_gpu.min() < 0
                     or S_gpu.max() >= head.c):
@@ -91,15 +106,14 @@ def check_forward(head: OracleHead, H, p, mode, temperature, seed, gpu: dict, qu
         ids, z = gather(head.E, head.c2t, S_gpu[None, :], h[None, :])
         ids, z = ids[0], z[0]
         fin = _finish_row(ids, z, mode, temperature, seed, r)
-        if "ids" in gpu and not np.array_equal(np.asarray(gpu["ids"][r]), ids):
+        if not np.array_equal(np.asarray(gpu["ids"][r]), ids):
             rep.fail(f"row {r}: retrieved ids differ")
             continue
-        if "logits" in gpu:
-            tol = _logit_tol(head.E, ids, h, z, rel)
-            err = np.abs(np.asarray(gpu["logits"][r], dtype=np.float64) - z) / tol
-            rep.max_logit_err = max(rep.max_logit_err, float(err.max()))
-            if err.max() > 1:
-                rep.fail(f"row {r}: retrieved logit error {err.max():.3g} x tol")
+        tol = _logit_tol(head.E, ids, h, z, rel)
+        err = np.abs(np.asarray(gpu["logits"][r], dtype=np.float64) - z) / tol
+        rep.max_logit_err = max(rep.max_logit_err, float(err.max()))
+        if not err.max() <= 1:  # a NaN logit fails too
+            rep.fail(f"row {r}: retrieved logit error {err.max():.3g} x tol")
         _check_token(rep, head.E, ids, z, h, fin, gpu, r, rel, tie_gap)
     return rep
 
@@ -124,26 +138,28 @@ def _check_token(rep, E, ids, z, h, fin, gpu, r, rel, tie_gap):
             rep.fail(f"row {r}: token {y} != {fin['token']} beyond near-tie")
             return
     zi = float(z[np.nonzero(ids == y)[0][0]])
-    if "token_logit" in gpu:
-        tol = _logit_tol(E, np.array([y]), h, np.array([zi]), rel)[0]
-        err = abs(float(gpu["token_logit"][r]) - zi) / tol
-        rep.max_logit_err = max(rep.max_logit_err, err)
-        if err > 1:
-            rep.fail(f"row {r}: token logit error {err:.3g} x tol")
-    if "lse" in gpu:
-        err = abs(float(gpu["lse"][r]) - fin["lse"]) / (rel * max(1.0, abs(fin["lse"])))
-        rep.max_lse_err = max(rep.max_lse_err, err)
-        if err > 1:
-            rep.fail(f"row {r}: lse error {err:.3g} x tol")
+    tol = _logit_tol(E, np.array([y]), h, np.array([zi]), rel)[0]
+    err = abs(float(gpu["token_logit"][r]) - zi) / tol
+    rep.max_logit_err = max(rep.max_logit_err, err)
+    if not err <= 1:
+        rep.fail(f"row {r}: token logit error {err:.3g} x tol")
+    err = abs(float(gpu["lse"][r]) - fin["lse"]) / (rel * max(1.0, abs(fin["lse"])))
+    rep.max_lse_err = max(rep.max_lse_err, err)
+    if not err <= 1:
+        rep.fail(f"row {r}: lse error {err:.3g} x tol")
 
 
 def check_dense(E, H, mode, temperature, seed, gpu: dict, queries=None, rel=REL,
                 tie_gap=TIE_GAP) -> Report:
-    """Compare a GPU dense-head result with the oracle's dense head."""
+    """Compare a GPU dense-head result with the oracle's dense head.  The
+    token, its logit and the LSE are required (DENSE_KEYS); the v logits are
+    checked when the call asked for them."""
     H = np.atleast_2d(np.asarray(H, dtype=np.float64))
     B = H.shape[0]
     rows = list(range(B) if queries is None else queries)
     rep = Report()
+    if _missing(rep, gpu, DENSE_KEYS):
+        return rep
     E64 = np.asarray(E, dtype=np.float64)
     v = E64.shape[0]
     ids = np.arange(v)
@@ -156,7 +172,7 @@ def check_dense(E, H, mode, temperature, seed, gpu: dict, queries=None, rel=REL,
             tol = _logit_tol(E, ids, h, z, rel)
             err = np.abs(np.asarray(gpu["logits"][r], dtype=np.float64) - z) / tol
             rep.max_logit_err = max(rep.max_logit_err, float(err.max()))
-            if err.max() > 1:
+            if not err.max() <= 1:
                 rep.fail(f"row {r}: dense logit error {err.max():.3g} x tol")
         _check_token(rep, E, ids, z, h, fin, gpu, r, rel, tie_gap)
     return rep
@@ -172,6 +188,6 @@ def check_scores(C_hat, H, s_gpu, rel=REL) -> Report:
         tol = rel * np.maximum(np.abs(s[r]), 2.0 ** -8 * Cn * np.linalg.norm(H[r]))
         err = np.abs(np.asarray(s_gpu[r], dtype=np.float64) - s[r]) / tol
         rep.max_logit_err = max(rep.max_logit_err, float(err.max()))
-        if err.max() > 1:
+        if not err.max() <= 1:
             rep.fail(f"row {r}: score error {err.max():.3g} x tol")
     return rep

@@ -1,4 +1,4 @@
-"""The plain read probe (fh_read_probe) behind bench.py --burst: a search for
+"""The plain read probe (bench.py's fhb_read_probe) behind --burst: a search for
 one 32-bit value, so it must see every word of the buffer, including the last
 one of a ragged final workgroup."""
 
@@ -14,7 +14,15 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("nbytes", [16, 16384, 16384 * 3 + 48, 32_869_696])
 def test_read_probe_finds_every_word(nbytes):
     need_gpu()
-    from lm_output_head_amd import fh_read_probe
+    import ctypes
+
+    import bench
+    blib = bench.load_bench_lib()
+
+    def fh_read_probe(b, key, f):
+        st = torch.cuda.current_stream().cuda_stream
+        assert blib.fhb_read_probe(ctypes.c_void_p(b.data_ptr()), b.numel() * 4, key & 0xFFFFFFFF,
+                                   ctypes.c_void_p(f.data_ptr()), ctypes.c_void_p(st)) == 0
     say("read probe", nbytes)
     n = nbytes // 4
     # distinct words 1 .. n (a permutation), so a key is present exactly once
