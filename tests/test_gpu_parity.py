@@ -364,16 +364,23 @@ def test_int4_codes_bit_exact(llama):
     head.close()
 
 
-@pytest.mark.parametrize("B,p", [(1, 128), (1, 1024), (8, 256), (8, 512)])
-def test_int4_batched_probe_sweep(llama, B, p):
+@pytest.mark.parametrize("quant,B,p", [
+    ("int4", 1, 128), ("int4", 1, 1024), ("int4", 8, 256), ("int4", 8, 512),
+    ("int4", 32, 128), ("int4", 32, 512), ("int4", 64, 512), ("int4", 64, 1024),
+    ("none", 32, 512), ("none", 64, 512), ("none", 64, 1024),
+])
+def test_llama_batch_probe_sweep_every_row(llama, quant, B, p):
+    """The batch sweep at the Llama-3.2-1B shape, B in {1, 8, 32, 64} x p in
+    {128 ... 1024}, INT4 and bf16 centroids: every query of every call
+    against the oracle (per-query probes; cluster-major stage 2 from B = 32)."""
     pb = llama
-    head, H = _engine(pb, quant="int4", max_batch=8)
-    ref = _oracle(pb, "int4")
-    say("int4 B", B, "p", p)
+    head, H = _engine(pb, quant=quant, max_batch=64)
+    ref = _oracle(pb, quant)
+    say(quant, "B", B, "p", p)
     out = host(head.forward(H[:B], p, want_clusters=True, want_retrieved=True))
-    assert_report(parity.check_forward(ref, pb.H[:B], p, TOPK, 1.0, 0, out), f"int4 B={B} p={p}")
+    assert_report(parity.check_forward(ref, pb.H[:B], p, TOPK, 1.0, 0, out), f"{quant} B={B} p={p}")
     s = host({"s": head.score(H[:B])})["s"]
-    assert_report(parity.check_scores(ref.C_hat, pb.H[:B], s), "int4 scores")
+    assert_report(parity.check_scores(ref.C_hat, pb.H[:B], s), f"{quant} scores B={B}")
     head.close()
 
 
@@ -444,9 +451,9 @@ def test_gemma_sampled_probes_and_tokens():
     out = host(head.forward(H, 512, mode=mode, temperature=1.0, seed=0x5EED,
                             want_clusters=True, want_retrieved=True))
     assert_report(parity.check_forward(ref, pb.H, 512, mode, 1.0, 0x5EED, out), "gemma sampled")
-    say("gemma dense sampled B=4")
-    d = host(head.dense(H[:4], mode=TSAMPLE, temperature=1.0, seed=0x5EED))
-    assert_report(parity.check_dense(pb.E, pb.H[:4], TSAMPLE, 1.0, 0x5EED, d), "gemma dense")
+    say("gemma dense sampled B=16")
+    d = host(head.dense(H, mode=TSAMPLE, temperature=1.0, seed=0x5EED))
+    assert_report(parity.check_dense(pb.E, pb.H, TSAMPLE, 1.0, 0x5EED, d), "gemma dense")
     head.close()
 
 
@@ -456,7 +463,7 @@ def test_qwen_int4_batch128_greedy_and_t07():
     pb = make_problem("qwen3_4b", nq=128)
     head, H = _engine(pb, quant="int4", max_batch=128)
     ref = _oracle(pb, "int4")
-    rows = list(range(0, 128, 9))
+    rows = None  # every one of the 128 queries
     say("qwen B=128 greedy")
     out = host(head.forward(H, 1024, want_clusters=True, want_retrieved=True))
     assert_report(parity.check_forward(ref, pb.H, 1024, TOPK, 1.0, 0, out, queries=rows),
