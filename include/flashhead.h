@@ -150,6 +150,37 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
                      int32_t* out_ids, float* out_logits, void* stream);
 
 /*
+ * fh_forward_noalloc — fh_forward without an engine and without allocating:
+ * for callers that cannot call hipMalloc (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid it).  It runs the per-stage
+ * launches (stage-1 scores, selection, stage 2, finish) on caller-owned
+ * tables and keeps its workspace (scores, probe lists, stage-2 partials) in
+ * a fixed 8 MiB device array of the library, one per GPU, held until the
+ * process ends; it calls no hipMalloc, hipFree or allocating routine.
+ *
+ *   E, C     device [v x d] and [c x d] of dtype, 16-byte aligned (as for
+ *            fh_create; C as stored, no quantisation).
+ *   c2t      device int32 [c x b], b = v / c: a permutation of [0, v) (the
+ *            caller's responsibility; fh_create checks it, this does not).
+ *   h        device [B x d] of dtype, 16-byte aligned; 1 <= B <= 65535.
+ *   p, mode, temperature, seed, outputs: as for fh_forward, except that
+ *            FH_PROBE_SHARED is not offered (FH_EUNSUPPORTED).
+ * Results equal fh_forward's per-stage path (fh_set_path FH_PATH_MULTI)
+ * bit for bit.  FH_EINVAL, before anything is launched, when the call's
+ * workspace, 4 B c + 4 B p + 20 B ceil(p b / 8) bytes (each term rounded up
+ * to 256), exceeds 8 MiB, and for the argument errors of fh_create and
+ * fh_forward.  Every call on a GPU shares that GPU's array, and the array
+ * keeps the last call's contents (each call writes all it reads, so nothing
+ * needs clearing): calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.
+ */
+fh_status fh_forward_noalloc(const void* E, const void* C, const int32_t* c2t, fh_dtype dtype,
+                             int64_t v, int64_t d, int64_t c, const void* h, int64_t B, int64_t p,
+                             int mode, float temperature, uint64_t seed, int32_t* out_token,
+                             float* out_token_logit, float* out_lse, int32_t* out_clusters,
+                             int32_t* out_ids, float* out_logits, void* stream);
+
+/*
  * fh_score — stage 1 alone: out_scores[b*c + k] = C_hat[k] . h[b] in float32
  * accumulation, with C_hat the centroids as stored (INT4: sigma * q)
  * ([X] §1.2.4 stage 1).

@@ -17,6 +17,7 @@
 #include <algorithm>
 #include <new>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -232,6 +233,39 @@ fh_status shared_forward(fh_engine* e, hipStream_t st, const fh::KernelCtx& k, c
   });
   return r == hipSuccess ? FH_OK : hip_fail(r, "finish launch");
 }
+
+}  // namespace
+
+// ---- workspace of fh_forward_noalloc: a file-scope device array (one copy
+// per GPU, held until the process ends), for callers that cannot allocate.
+// Host code never passes the array's name to a kernel: it takes the device
+// address once per device (hipGetSymbolAddress, with that device current)
+// and uses that address everywhere.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;  // 8 MiB
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices] = {};  // device -> address of its scratch
+
+// The current device's scratch address (set up on first use on the device).
+hipError_t scratch_for(int dev, void** out) {
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (r != hipSuccess) return r;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 }  // namespace
 
@@ -509,6 +543,85 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
   });
   if (r != hipSuccess) return hip_fail(r, "finish launch");
   return FH_OK;
+}
+
+fh_status fh_forward_noalloc(const void* E, const void* C, const int32_t* c2t, fh_dtype dtype,
+                             int64_t v, int64_t d, int64_t c, const void* h, int64_t B, int64_t p,
+                             int mode, float temperature, uint64_t seed, int32_t* out_token,
+                             float* out_token_logit, float* out_lse, int32_t* out_clusters,
+                             int32_t* out_ids, float* out_logits, void* stream) {
+  g_err.clear();
+  if (!E || !C || !c2t || !h) return fail(FH_EINVAL, "E, C, C2T and h must be non-NULL");
+  if (dtype != FH_F32 && dtype != FH_BF16) return fail(FH_EINVAL, "unknown dtype");
+  if (v <= 0 || d <= 0 || c <= 0) return fail(FH_EINVAL, "v, d and c must be positive");
+  if (v % c != 0) return fail(FH_EINVAL, "v must be a multiple of c (balanced clusters)");
+  if (v >= (int64_t(1) << 31)) return fail(FH_EUNSUPPORTED, "v must be below 2^31");
+  if (c > kMaxC) return fail(FH_EUNSUPPORTED, "c above 16384 is not supported");
+  const int epc = dtype == FH_BF16 ? 8 : 4;
+  if (d % epc != 0)
+    return fail(FH_EINVAL, dtype == FH_BF16 ? "bf16 needs d % 8 == 0" : "f32 needs d % 4 == 0");
+  if (d > 64 * 8 * epc) return fail(FH_EUNSUPPORTED, "d too large for this library");
+  if (!aligned16(E) || !aligned16(C) || !aligned16(h))
+    return fail(FH_EINVAL, "E, C and h must be 16-byte aligned");
+  if (B < 1 || B > 65535) return fail(FH_EINVAL, "B outside [1, 65535]");
+  if (p < 1 || p > c)
+    return fail(FH_EINVAL, "p=" + std::to_string(p) + " outside [1, c=" + std::to_string(c) + "]");
+  if (mode & FH_PROBE_SHARED) return fail(FH_EUNSUPPORTED, "FH_PROBE_SHARED is not offered here");
+  fh_status s = check_mode(mode, temperature);
+  if (s != FH_OK) return s;
+  const int64_t b = v / c;
+  // workspace: scores [B x c] fp32, probe lists [B x p] (unless out_clusters
+  // takes them), stage-2 partials [B x rows_blocks(p b)]
+  const int64_t nparts = fh::rows_blocks(p * b, fh::kGatherRPW);
+  const size_t off_sel = align256(sizeof(float) * (size_t)(B * c));
+  const size_t off_parts = off_sel + align256(sizeof(int32_t) * (size_t)(B * p));
+  const size_t need = off_parts + sizeof(fh::Part) * (size_t)(B * nparts);
+  if (need > kNoAllocScratchBytes)
+    return fail(FH_EINVAL, "this call needs " + std::to_string(need) +
+                               " bytes of workspace; fh_forward_noalloc has " +
+                               std::to_string(kNoAllocScratchBytes) + " (use fh_forward)");
+  int dev = -1;
+  hipError_t r = hipGetDevice(&dev);
+  if (r != hipSuccess) return hip_fail(r, "hipGetDevice");
+  unsigned char* ws = nullptr;
+  r = scratch_for(dev, reinterpret_cast<void**>(&ws));
+  if (r != hipSuccess) return hip_fail(r, "workspace address (hipGetSymbolAddress)");
+  float* scores = reinterpret_cast<float*>(ws);
+  int32_t* S = out_clusters ? out_clusters : reinterpret_cast<int32_t*>(ws + off_sel);
+  fh::Part* parts = reinterpret_cast<fh::Part*>(ws + off_parts);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  fh::KernelCtx k;
+  k.bf16 = dtype == FH_BF16;
+  k.E = E;
+  k.Ec = nullptr;  // rows of E are found through C2T
+  k.C = C;
+  k.c2t = c2t;
+  k.cq = nullptr;
+  k.csig = nullptr;
+  k.cq_mfma = nullptr;
+  k.sig_mfma = nullptr;
+  k.v = v;
+  k.c = c;
+  k.b = b;
+  k.d = (int)d;
+  k.stream = st;
+  k.qbits = 0;
+  const int probe_sample = mode & FH_PROBE_SAMPLE;
+  const int token_sample = (mode & FH_TOKEN_SAMPLE) ? 1 : 0;
+  const float tprime = token_sample ? temperature : 1.f;
+  fh::KeyXform kx;
+  kx.sample = probe_sample; kx.temperature = temperature; kx.seed = seed;
+  r = fh::launch_score(k, h, (int)B, scores, kx);
+  if (r != hipSuccess) return hip_fail(r, "score launch");
+  r = fh::launch_select(k, scores, (int)B, (int)p, 0, 1.f, seed, S, (int)p);
+  if (r != hipSuccess) return hip_fail(r, "select launch");
+  int64_t np = 0;
+  r = fh::launch_gather(k, h, (int)B, S, (int)p, token_sample, tprime, seed, out_ids, out_logits,
+                        parts, &np);
+  if (r != hipSuccess) return hip_fail(r, "gather launch");
+  r = fh::launch_finish(k, parts, (int)B, np, out_token, out_token_logit, out_lse);
+  return r == hipSuccess ? FH_OK : hip_fail(r, "finish launch");
 }
 
 fh_status fh_dense_forward(fh_engine* e, const void* h, int64_t B, int mode, float temperature,

@@ -109,6 +109,31 @@ def fh_forward(eng, h, p, mode, temperature, seed, out_token, out_token_logit=No
                                  _stream(stream)))
 
 
+def fh_forward_noalloc(E, C, c2t, h, p, mode, temperature, seed, out_token, out_token_logit=None,
+                       out_lse=None, out_clusters=None, out_ids=None, out_logits=None,
+                       stream=None) -> None:
+    """fh_forward without an engine, on caller-owned tables (c2t: a device
+    int32 [c x b] permutation of [0, v)), with the library's fixed workspace."""
+    if E.dtype not in _DTYPES or C.dtype != E.dtype or h.dtype != E.dtype:
+        raise ValueError("E, C and h must share dtype float32 or bfloat16")
+    v, d = E.shape
+    c = C.shape[0]
+    if C.shape[1] != d or h.dim() != 2 or h.shape[1] != d or c < 1 or v % c:
+        raise ValueError("inconsistent shapes of E, C and h")
+    B, b = h.shape[0], v // c
+    _require(c2t, torch.int32, (c, b), "c2t")
+    _require(out_token, torch.int32, (B,), "out_token")
+    _require(out_token_logit, torch.float32, (B,), "out_token_logit")
+    _require(out_lse, torch.float32, (B,), "out_lse")
+    _require(out_clusters, torch.int32, (B, p), "out_clusters")
+    _require(out_ids, torch.int32, (B, p * b), "out_ids")
+    _require(out_logits, torch.float32, (B, p * b), "out_logits")
+    check(_abi.load().fh_forward_noalloc(_ptr(E), _ptr(C), _ptr(c2t), _DTYPES[E.dtype], v, d, c,
+                                         _ptr(h), B, p, mode, temperature, seed, _ptr(out_token),
+                                         _ptr(out_token_logit), _ptr(out_lse), _ptr(out_clusters),
+                                         _ptr(out_ids), _ptr(out_logits), _stream(stream)))
+
+
 def fh_score(eng, h, out_scores, stream=None) -> None:
     B, _, _, c = _engine_h(eng, h)
     _require(out_scores, torch.float32, (B, c), "out_scores")
