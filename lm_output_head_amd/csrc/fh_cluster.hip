@@ -667,8 +667,10 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
   uint16_t* pieces = nullptr;  // bf16 tables: the three bf16 pieces of C
   ClusterWork w;
   hipEvent_t ev[5] = {};
-  for (auto& e : ev) (void)hipEventCreate(&e);
-  hipError_t r = hipMalloc((void**)&X, sizeof(float) * v * d);
+  hipError_t r = hipSuccess;
+  for (auto& e : ev)
+    if (r == hipSuccess) r = hipEventCreate(&e);
+  if (r == hipSuccess) r = hipMalloc((void**)&X, sizeof(float) * v * d);
   const int64_t nb = (v + kPpRows - 1) / kPpRows;
   if (r == hipSuccess) r = hipMalloc((void**)&inv, sizeof(float) * v);
   if (r == hipSuccess) r = hipMalloc((void**)&D, sizeof(float) * v);
@@ -680,29 +682,39 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
   if (r == hipSuccess && bf16) r = hipMalloc((void**)&pieces, sizeof(uint16_t) * 3 * c * d);
   if (r == hipSuccess) r = work_alloc(w, v, c, st);
   int total_rounds = 0;
+  if (r == hipSuccess) r = hipEventRecord(ev[0], st);
   if (r == hipSuccess) {
-    (void)hipEventRecord(ev[0], st);
     if (bf16)
       hipLaunchKernelGGL((k_normalize_rows<uint16_t>), dim3(blocks_for(v, 4)), dim3(256), 0, st,
                          static_cast<const uint16_t*>(E), v, d, X, inv);
     else
       hipLaunchKernelGGL((k_normalize_rows<float>), dim3(blocks_for(v, 4)), dim3(256), 0, st,
                          static_cast<const float*>(E), v, d, X, inv);
+    r = hipGetLastError();
     const int32_t first = (int32_t)std::min<int64_t>((int64_t)(u[0] * (double)v), v - 1);
-    r = hipMemcpyAsync(centers, &first, sizeof(int32_t), hipMemcpyHostToDevice, st);
+    if (r == hipSuccess)
+      r = hipMemcpyAsync(centers, &first, sizeof(int32_t), hipMemcpyHostToDevice, st);
     // every 16th distance refresh is bracketed by an event pair
     constexpr int64_t kSample = 16;
+    // the host waits for the stream every kDrain centres, so that at most
+    // 2 kDrain launches and kDrain / 8 event records are ever queued (a
+    // single wait after all c centres queued 2c launches: 16 000 at the
+    // Llama-3.2-1B shape, too many for tools that instrument each launch)
+    constexpr int64_t kDrain = 256;
     std::vector<hipEvent_t> sev(2 * ((c + kSample - 1) / kSample), nullptr);
-    for (auto& e : sev) (void)hipEventCreate(&e);
+    for (auto& e : sev)
+      if (r == hipSuccess) r = hipEventCreate(&e);
     for (int64_t i = 0; r == hipSuccess && i < c; ++i) {
       if (i > 0) {
         hipLaunchKernelGGL(k_pp_pick, dim3(1), dim3(1024), 0, st, D, part, nb, v, u[i],
                            centers, (int)i);
+        r = hipGetLastError();
       }
       const bool sample = i % kSample == 0;
-      if (sample) (void)hipEventRecord(sev[2 * (i / kSample)], st);
-      r = launch_pp_step(E, bf16, inv, v, d, centers, (int)i, D, part, nb, st);
-      if (sample) (void)hipEventRecord(sev[2 * (i / kSample) + 1], st);
+      if (r == hipSuccess && sample) r = hipEventRecord(sev[2 * (i / kSample)], st);
+      if (r == hipSuccess) r = launch_pp_step(E, bf16, inv, v, d, centers, (int)i, D, part, nb, st);
+      if (r == hipSuccess && sample) r = hipEventRecord(sev[2 * (i / kSample) + 1], st);
+      if (r == hipSuccess && (i + 1) % kDrain == 0) r = hipStreamSynchronize(st);
     }
     if (r == hipSuccess) r = hipStreamSynchronize(st);
     double step_ms = 0.0;
@@ -711,18 +723,20 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
       if (hipEventElapsedTime(&ms, sev[j], sev[j + 1]) == hipSuccess) step_ms += ms;
     }
     if (times) times->pp_step_us = (float)(1e3 * step_ms / (double)(sev.size() / 2));
-    for (auto& e : sev) (void)hipEventDestroy(e);
+    for (auto& e : sev)
+      if (e) (void)hipEventDestroy(e);
     if (r == hipSuccess) {
       hipLaunchKernelGGL(k_gather_rows, dim3(blocks_for(c * d, 256)), dim3(256), 0, st, X, d,
                          centers, c, C);
       r = hipGetLastError();
     }
-    (void)hipEventRecord(ev[1], st);
+    if (r == hipSuccess) r = hipEventRecord(ev[1], st);
     if (r == hipSuccess && init)
       r = hipMemcpyAsync(init, centers, sizeof(int32_t) * c, hipMemcpyDeviceToDevice, st);
     float sims_ms = 0.f;
     for (int it = 0; r == hipSuccess && it < iters; ++it) {
-      (void)hipEventRecord(ev[2], st);
+      r = hipEventRecord(ev[2], st);
+      if (r != hipSuccess) break;
       if (bf16) {
         hipLaunchKernelGGL(k_split_pieces, dim3(blocks_for(c * d, 256)), dim3(256), 0, st, C, c * d,
                            pieces);
@@ -733,7 +747,9 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
         hipLaunchKernelGGL(k_sims, dim3(blocks_for(v, 64), blocks_for(c, 64)), dim3(256), 0, st, X,
                            v, C, c, d, S);
       }
-      (void)hipEventRecord(ev[3], st);
+      r = hipGetLastError();
+      if (r == hipSuccess) r = hipEventRecord(ev[3], st);
+      if (r != hipSuccess) break;
       hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(v, 256)), dim3(256), 0, st, asg, v, -1);
       r = hipGetLastError();
       int rounds = 0;
@@ -745,7 +761,7 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
     }
     if (r == hipSuccess && asg_out)
       r = hipMemcpyAsync(asg_out, asg, sizeof(int32_t) * v, hipMemcpyDeviceToDevice, st);
-    (void)hipEventRecord(ev[4], st);
+    if (r == hipSuccess) r = hipEventRecord(ev[4], st);
     if (r == hipSuccess) r = hipStreamSynchronize(st);
     if (times && r == hipSuccess) {
       float ms = 0.f;
@@ -758,7 +774,8 @@ hipError_t kmeans_device(const void* E, bool bf16, int64_t v, int d, int64_t c, 
       times->rounds = total_rounds;
     }
   }
-  for (auto& e : ev) (void)hipEventDestroy(e);
+  for (auto& e : ev)
+    if (e) (void)hipEventDestroy(e);
   work_free(w);
   for (void* p : {(void*)X, (void*)inv, (void*)D, (void*)part, (void*)S,
                   (void*)centers, (void*)asg, (void*)pieces})

@@ -10,6 +10,7 @@ with output allocation for convenience.
 from __future__ import annotations
 
 import ctypes
+import sys
 
 import numpy as np
 import torch
@@ -260,6 +261,11 @@ class FlashHead:
             self.eng = None
 
     def __del__(self):
+        # not while the interpreter shuts down: the HIP runtime (and any
+        # profiler wrapping it) may already be torn down, and a process that
+        # ends frees the engine's memory anyway.  Close engines explicitly.
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
