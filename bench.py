@@ -225,17 +225,49 @@ def traffic_from_profiles(kernel: str, src_hash: str, workload_key: str,
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(pb, p, quant, mode, temperature, seconds):
-    """The oracle as it stands, on host cores, over a bounded query sample."""
-    import numpy as np
+def kernel_us_from_profiles(kernel: str, src_hash: str, workload_key: str, nbytes: int) -> dict:
+    """The rocprofv3 kernel-trace mean of `kernel` for this workload, if the
+    summary under profiles/ was taken from the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if rec.get("source_hash") != src_hash:
+        return {}
+    us = rec.get("workloads", {}).get(workload_key, {}).get(kernel)
+    if not us:
+        return {}
+    return {"rocprof_kernel_us": us, "rocprof_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    import oracle
+
+def cpu_info():
+    """The host's CPU model, its BLAS libraries and the thread variables."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    blas = []
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = [{"api": i.get("internal_api"), "version": i.get("version"),
+                 "threads": i.get("num_threads"), "library": os.path.basename(i.get("filepath", ""))}
+                for i in threadpool_info()]
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    head = oracle.OracleHead(pb.E, pb.C, pb.C2T, quant)
+        pass
+    env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                          "MKL_NUM_THREADS") if os.environ.get(k) is not None}
+    return {"cpu_model": model, "logical_cpus": len(os.sched_getaffinity(0)), "blas": blas,
+            "thread_env": env}
+
+
+def _oracle_rate(head, pb, p, mode, temperature, seconds):
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -244,10 +276,71 @@ def cpu_baseline(pb, p, quant, mode, temperature, seconds):
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds:
+            return n, el
+
+
+def cpu_fp32_two_stage(pb, p, seconds):
+    """A plain float32 numpy two-stage head (scores, top-p by argpartition,
+    gathered rows, argmax) on host cores: what BLAS-speed CPU code does on
+    the same workload, greedy top-p only.  Its tokens are certified against
+    the float64 oracle on the timed sample."""
+    import numpy as np
+
+    import oracle
+    E32 = np.ascontiguousarray(pb.E, dtype=np.float32)
+    C32 = np.ascontiguousarray(pb.C, dtype=np.float32)
+    c2t = np.asarray(pb.C2T)
+    H32 = np.asarray(pb.H, dtype=np.float32)
+
+    def call(h):
+        s = C32 @ h
+        probes = np.argpartition(-s, p - 1)[:p]
+        ids = c2t[probes].reshape(-1)
+        z = E32[ids] @ h
+        return int(ids[int(np.argmax(z))])
+
+    toks, n = [], 0
+    t0 = time.perf_counter()
+    while True:
+        toks.append(call(H32[n % H32.shape[0]]))
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
             break
-    return {"value": round(n / el, 3), "unit": "calls/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} single-query calls of the same workload in {el:.1f} s "
-                      f"(float64 numpy oracle, BLAS threads={cores})"}
+    head = oracle.OracleHead(pb.E, pb.C, pb.C2T)
+    m = min(n, H32.shape[0], 32)
+    ref = head.forward(pb.H[:m], p).fin.token
+    agree = int(sum(int(ref[i]) == toks[i] for i in range(m)))
+    return {"value": round(n / el, 3), "unit": "calls/s",
+            "sample": f"{n} single-query calls in {el:.1f} s (float32 numpy, E and C widened to float32)",
+            "tokens_equal_to_oracle": f"{agree}/{m}"}
+
+
+def cpu_baseline(pb, p, quant, mode, temperature, seconds):
+    """The oracle as it stands, on host cores, over a bounded query sample;
+    beside it the same oracle on one thread, a float32 numpy two-stage head
+    (greedy top-p), and the host's CPU model and BLAS."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+        cores = os.cpu_count() or 1
+    head = oracle.OracleHead(pb.E, pb.C, pb.C2T, quant)
+    n, el = _oracle_rate(head, pb, p, mode, temperature, seconds)
+    res = {"value": round(n / el, 3), "unit": "calls/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{n} single-query calls of the same workload in {el:.1f} s "
+                     f"(float64 numpy oracle, BLAS threads={cores})"}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            n1, el1 = _oracle_rate(head, pb, p, mode, temperature, seconds / 2)
+        res["single_thread"] = {"value": round(n1 / el1, 3), "unit": "calls/s",
+                                "sample": f"{n1} calls in {el1:.1f} s on one BLAS thread"}
+    if quant == "none" and mode == 0:
+        res["fp32_two_stage"] = cpu_fp32_two_stage(pb, p, seconds / 2)
+    res["host"] = cpu_info()
+    return res
 
 
 def cluster_cpu_baseline(E, c, seconds):
@@ -680,7 +773,15 @@ def main():
     dominant = max((k for k in kern if k in algo),
                    key=lambda k: kern[k]["avg_us"] * kern[k]["launches"] * (algo[k] > 1e6))
     dom_bytes = algo[dominant]
-    dom_us = kern[dominant]["avg_us"]
+    # the kernel's duration: a step of one launch (the batch-1 call) is timed
+    # by the events around the whole timed region divided by the steps, which
+    # cannot exceed the step; an event pair around each launch also holds the
+    # launch's own latency and is kept beside it
+    one_launch = len(kern) == 1 and kern[dominant]["launches"] == args.steps
+    pair_us = kern[dominant]["avg_us"]
+    dom_us = min(pair_us, ms * 1e3) if one_launch else pair_us
+    dur_src = ("HIP events around the timed region / steps (one launch per step)" if one_launch
+               else "HIP event pair around each launch, on its stream")
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     src_hash = kernel_source_hash()
     wkey = f"{shape.name}/B{B}/p{p}/{args.quant}/m{args.mode}"
@@ -719,8 +820,31 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes": dom_bytes, "source_hash": src_hash},
+                     "algorithmic_bytes": dom_bytes, "duration_us": round(dom_us, 3),
+                     "duration_source": dur_src, "event_pair_us": pair_us,
+                     "source_hash": src_hash, **kernel_us_from_profiles(dominant, src_hash, wkey,
+                                                                        dom_bytes)},
     }
+    # the same call writing every output fh_forward offers (the probe list,
+    # the retrieved ids and logits), as the method's call returns them
+    b = shape.b
+    o_cl = torch.empty(B * p, dtype=torch.int32, device="cuda")
+    o_ids = torch.empty(B * p * b, dtype=torch.int32, device="cuda")
+    o_lg = torch.empty(B * p * b, dtype=torch.float32, device="cuda")
+    ocl, oids, olg = ptr(o_cl), ptr(o_ids), ptr(o_lg)
+
+    def step_all(i):
+        st = lib.fh_forward(engs[i % R], hptr[i % len(hptr)], B, p, args.mode, args.temperature,
+                            0x5EED + i, otok, olog, olse, ocl, oids, olg, sp)
+        if st != 0:
+            raise RuntimeError(lib.fh_last_error().decode())
+
+    print(f"[bench] timing {args.steps} steps with every output", file=sys.stderr, flush=True)
+    ms_all, _ = timed(step_all, args.steps, 10)
+    res["with_retrieved_outputs"] = {
+        "ms_per_step": round(ms_all, 5), "calls_per_s": round(1000.0 / ms_all, 2),
+        "extra_output_bytes": B * p * 4 + 2 * B * p * b * 4,
+        "outputs": "token, token logit, LSE, probe list, retrieved ids and logits"}
     if not args.no_dense:
         print(f"[bench] timing {args.dense_steps} dense steps", file=sys.stderr, flush=True)
         dms, _ = timed(dense_step, args.dense_steps, 10)
