@@ -31,6 +31,7 @@ from .flashhead_oracle import (  # noqa: F401
     quantize_int8_g32,
     score,
     select,
+    select_adaptive,
     select_shared,
     unpack_int4,
     validate_c2t,

@@ -238,6 +238,62 @@ def select(s: np.ndarray, p: int, mode: int = 0, temperature: float = 1.0,
     return Selection(S, key, key32, theta)
 
 
+@dataclass
+class AdaptiveSelection:
+    S: np.ndarray  # int64 [B x p_max]: the n[b] probes of row b ascending, then -1
+    n: np.ndarray  # int64 [B] probes per row
+    order: np.ndarray  # int64 [B x c] every cluster by key32 descending, ties to the smaller id
+    key: np.ndarray  # float64 [B x c] selection keys (as select)
+    key32: np.ndarray  # float32 [B x c] the keys the order is taken on
+    mass: np.ndarray  # float64 [B x c] softmax(s / T) mass of the first j+1 clusters of `order`
+
+
+def select_adaptive(s: np.ndarray, p_max: int, tau: float, p_min: int = 1, mode: int = 0,
+                    temperature: float = 1.0, seed: int = 0, rows=None) -> AdaptiveSelection:
+    """Per-query probe count (explainer §1.2.2, dynamic adjustment: the number
+    of probes follows the distribution of h; §4.2: fewer probes where the
+    query is confident, e.g. for frequent tokens).
+
+    The pages give no formula.  The reading here: the clusters are taken one
+    after another in the order of the selection keys (the scores, or with
+    MODE_PROBE_SAMPLE the Gumbel-perturbed keys, i.e. draws without
+    replacement from softmax(s/T)), and a row stops at the first count n whose
+    clusters together hold at least tau of the centroid distribution
+    softmax(s/T) over all c clusters; n is then clamped to [p_min, p_max].
+    A peaked distribution stops after few clusters, a flat one probes up to
+    p_max.  The order is decided on float32 keys like select (ties to the
+    smaller id); the mass is float64.
+    """
+    if mode & MODE_PROBE_SHARED:
+        raise ValueError("the adaptive count is per query; shared probes are not adaptive")
+    s = np.atleast_2d(np.asarray(s, dtype=np.float64))
+    B, c = s.shape
+    if not 1 <= p_min <= p_max <= c:
+        raise ValueError(f"need 1 <= p_min={p_min} <= p_max={p_max} <= c={c}")
+    if not 0.0 < tau <= 1.0:
+        raise ValueError(f"tau={tau} outside (0, 1]")
+    if not temperature > 0:
+        raise ValueError("the mass needs temperature > 0")
+    key = probe_keys(s, mode, temperature, seed, rows)
+    key32 = key.astype(np.float32)
+    x = s / float(temperature)
+    w = np.exp(x - x.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    ids = np.arange(c)
+    order = np.empty((B, c), dtype=np.int64)
+    mass = np.empty((B, c), dtype=np.float64)
+    n = np.empty(B, dtype=np.int64)
+    S = np.full((B, p_max), -1, dtype=np.int64)
+    for r in range(B):
+        order[r] = _top_ids(key32[r], ids, c)
+        mass[r] = np.cumsum(w[r, order[r]])
+        reach = np.nonzero(mass[r] >= tau)[0]
+        n_raw = int(reach[0]) + 1 if reach.size else c
+        n[r] = min(max(n_raw, p_min), p_max)
+        S[r, :n[r]] = np.sort(order[r, :n[r]])
+    return AdaptiveSelection(S, n, order, key, key32, mass)
+
+
 # ---------------------------------------------------------------------------
 # Stage 2: token scores of the probed clusters (explainer §1.2.4: E[top] h)
 # ---------------------------------------------------------------------------

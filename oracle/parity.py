@@ -17,8 +17,11 @@ near-ties certified on the oracle's own keys):
   differ by less than ``tie_gap``; the GPU's token must be a retrieved one.
 * LSE: |lse_gpu - lse_ref| <= rel * max(1, |lse_ref|).
 
+* Adaptive probe count: the GPU's count must be one that a cut within
+  ``mass_gap`` of tau on the oracle's mass gives (check_adaptive).
+
 Defaults follow the stated targets: rel = 2e-3 (bfloat16 inputs, float32
-accumulation) and tie_gap = 1e-3.
+accumulation), tie_gap = 1e-3 and mass_gap = 1e-4.
 """
 
 from __future__ import annotations
@@ -27,10 +30,14 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .flashhead_oracle import OracleHead, finish, gather, select
+from .flashhead_oracle import OracleHead, finish, gather, select, select_adaptive
 
 REL = 2e-3
 TIE_GAP = 1e-3
+# adaptive probe count: the GPU accumulates the softmax mass in float32 from
+# float32 scores; a count is certified when the oracle's mass at the GPU's cut
+# lies within MASS_GAP of tau
+MASS_GAP = 1e-4
 
 
 @dataclass
@@ -38,6 +45,7 @@ class Report:
     queries: int = 0
     cluster_ties: int = 0  # queries whose probe set differed only at certified near-ties
     token_ties: int = 0
+    count_ties: int = 0  # adaptive rows whose count differs at a certified mass near-tie
     max_logit_err: float = 0.0  # in units of the tolerance (<= 1 passes)
     max_lse_err: float = 0.0
     failures: list = field(default_factory=list)
@@ -57,6 +65,7 @@ def _logit_tol(E, ids, h, z_ref, rel):
 
 
 FORWARD_KEYS = ("clusters", "ids", "logits", "token", "token_logit", "lse")
+ADAPTIVE_KEYS = FORWARD_KEYS + ("nprobe",)
 DENSE_KEYS = ("token", "token_logit", "lse")
 
 
@@ -113,6 +122,80 @@ def check_forward(head: OracleHead, H, p, mode, temperature, seed, gpu: dict, qu
         err = np.abs(np.asarray(gpu["logits"][r], dtype=np.float64) - z) / tol
         rep.max_logit_err = max(rep.max_logit_err, float(err.max()))
         if not err.max() <= 1:  # a NaN logit fails too
+            rep.fail(f"row {r}: retrieved logit error {err.max():.3g} x tol")
+        _check_token(rep, head.E, ids, z, h, fin, gpu, r, rel, tie_gap)
+    return rep
+
+
+def _plausible_counts(mass, tau, p_min, p_max, gap):
+    """Counts a float32 accumulation of the mass may stop at: the cut lands
+    where the oracle's mass is within gap of tau, then the clamp."""
+    lo = np.nonzero(mass >= tau - gap)[0]
+    hi = np.nonzero(mass >= tau + gap)[0]
+    n_lo = int(lo[0]) + 1 if lo.size else mass.size
+    n_hi = int(hi[0]) + 1 if hi.size else mass.size
+    return min(max(n_lo, p_min), p_max), min(max(n_hi, p_min), p_max)
+
+
+def check_adaptive(head: OracleHead, H, p_max, p_min, tau, mode, temperature, seed, gpu: dict,
+                   queries=None, rel=REL, tie_gap=TIE_GAP, mass_gap=MASS_GAP) -> Report:
+    """Compare a GPU adaptive forward (FlashHead.forward_adaptive) with the
+    oracle's select_adaptive.  Per row: the count n must lie in the range of
+    counts the oracle's mass allows within mass_gap of tau; the first n
+    entries of the probe row must be n ascending valid ids, equal to the
+    oracle's first n clusters in key order up to certified key near-ties at
+    the n-th key, and the rest -1; retrieved slots past n b hold id -1.  Stage
+    2 and the finish are then checked on the GPU's probe set, as in
+    check_forward.  Every output is required (ADAPTIVE_KEYS)."""
+    H = np.atleast_2d(np.asarray(H, dtype=np.float64))
+    B = H.shape[0]
+    rows = list(range(B) if queries is None else queries)
+    rep = Report()
+    if _missing(rep, gpu, ADAPTIVE_KEYS):
+        return rep
+    s = H[rows] @ head.C_hat.T
+    a = select_adaptive(s, p_max, tau, p_min, mode, temperature, seed, rows=rows)
+    b = head.b
+    for pos, r in enumerate(rows):
+        rep.queries += 1
+        h = H[r]
+        n = int(gpu["nprobe"][r])
+        lo, hi = _plausible_counts(a.mass[pos], tau, p_min, p_max, mass_gap)
+        if not lo <= n <= hi:
+            rep.fail(f"row {r}: {n} probes, the oracle's mass allows {lo}..{hi}")
+            continue
+        if n != int(a.n[pos]):
+            rep.count_ties += 1
+        row = np.asarray(gpu["clusters"][r])
+        S_gpu = row[:n]
+        if (np.any(row[n:] != -1) or np.any(np.diff(S_gpu) <= 0) or S_gpu.min() < 0
+                or S_gpu.max() >= head.c):
+            rep.fail(f"row {r}: probe row is not {n} ascending valid ids followed by -1")
+            continue
+        S_ref = np.sort(a.order[pos, :n])
+        if not np.array_equal(S_gpu, S_ref):
+            theta = float(a.key32[pos, a.order[pos, n - 1]])
+            diff = np.setxor1d(S_gpu, S_ref)
+            if np.all(np.abs(a.key[pos, diff] - theta) < tie_gap):
+                rep.cluster_ties += 1
+            else:
+                rep.fail(f"row {r}: probe sets differ beyond near-ties at {diff[:8]}")
+                continue
+        ids, z = gather(head.E, head.c2t, S_gpu[None, :], h[None, :])
+        ids, z = ids[0], z[0]
+        fin = _finish_row(ids, z, mode, temperature, seed, r)
+        gid = np.asarray(gpu["ids"][r])
+        if not np.array_equal(gid[:n * b], ids) or np.any(gid[n * b:] != -1):
+            rep.fail(f"row {r}: retrieved ids differ")
+            continue
+        zg = np.asarray(gpu["logits"][r], dtype=np.float64)
+        if not np.all(np.isneginf(zg[n * b:])):
+            rep.fail(f"row {r}: retrieved logits past the {n} probes are not -inf")
+            continue
+        tol = _logit_tol(head.E, ids, h, z, rel)
+        err = np.abs(zg[:n * b] - z) / tol
+        rep.max_logit_err = max(rep.max_logit_err, float(err.max()))
+        if not err.max() <= 1:
             rep.fail(f"row {r}: retrieved logit error {err.max():.3g} x tol")
         _check_token(rep, head.E, ids, z, h, fin, gpu, r, rel, tie_gap)
     return rep

@@ -184,3 +184,89 @@ def test_dense_checker_requires_the_token_and_rejects_a_wrong_one(head):
     assert not parity.check_dense(E, H, 0, 1.0, 0, bad).ok()
     for key in parity.DENSE_KEYS:
         assert not parity.check_dense(E, H, 0, 1.0, 0, {k: v for k, v in gpu.items() if k != key}).ok()
+
+
+# ---- adaptive probe count (check_adaptive): a count is certified when the
+# oracle's mass at the GPU's cut is within mass_gap (1e-4) of tau
+
+PMAX = 6
+
+
+def adaptive_result(head, n, tau, p_max=PMAX):
+    """The exact answer with the first n clusters of the oracle's key order."""
+    a = oracle.select_adaptive(H @ head.C_hat.T, p_max, tau)
+    S = np.sort(a.order[0, :n])
+    out = result_for(head, S)
+    b = head.b
+    row = np.full((1, p_max), -1, np.int32)
+    row[0, :n] = S
+    ids = np.full((1, p_max * b), -1, np.int32)
+    ids[0, :n * b] = out["ids"][0]
+    z = np.full((1, p_max * b), -np.inf, np.float32)
+    z[0, :n * b] = out["logits"][0]
+    out.update(clusters=row, ids=ids, logits=z, nprobe=np.array([n], np.int32))
+    return out, a
+
+
+def check_a(head, gpu, tau):
+    return parity.check_adaptive(head, H, PMAX, 1, tau, 0, 1.0, 0, gpu)
+
+
+def test_adaptive_exact_answer_passes(head):
+    a = oracle.select_adaptive(H @ head.C_hat.T, PMAX, 0.5)
+    gpu, _ = adaptive_result(head, int(a.n[0]), 0.5)
+    rep = check_a(head, gpu, 0.5)
+    assert rep.ok(), rep.failures
+    assert rep.count_ties == 0
+
+
+def test_adaptive_count_off_by_one_fails(head):
+    a = oracle.select_adaptive(H @ head.C_hat.T, PMAX, 0.5)
+    n = int(a.n[0])
+    for m in (n - 1, n + 1):
+        gpu, _ = adaptive_result(head, m, 0.5)
+        rep = check_a(head, gpu, 0.5)
+        assert not rep.ok()
+        assert "the oracle's mass allows" in rep.failures[0]
+
+
+def test_adaptive_count_at_a_mass_near_tie_passes(head):
+    a = oracle.select_adaptive(H @ head.C_hat.T, PMAX, 0.5)
+    j = 1
+    tau = float(a.mass[0, j]) + 5e-5  # the oracle needs j + 2; j + 1 falls short by 5e-5
+    assert int(oracle.select_adaptive(H @ head.C_hat.T, PMAX, tau).n[0]) == j + 2
+    gpu, _ = adaptive_result(head, j + 1, tau)
+    rep = check_a(head, gpu, tau)
+    assert rep.ok(), rep.failures
+    assert rep.count_ties == 1
+    tau = float(a.mass[0, j]) + 5e-4  # short by 5e-4: beyond the band
+    gpu, _ = adaptive_result(head, j + 1, tau)
+    assert not check_a(head, gpu, tau).ok()
+
+
+@pytest.mark.parametrize("what", ["clusters", "ids", "logits", "set"])
+def test_adaptive_planted_mistakes_fail(head, what):
+    a = oracle.select_adaptive(H @ head.C_hat.T, PMAX, 0.5)
+    n = int(a.n[0])
+    gpu, _ = adaptive_result(head, n, 0.5)
+    if what == "clusters":
+        gpu["clusters"][0, n] = 0  # padding must be -1
+    elif what == "ids":
+        gpu["ids"][0, -1] = 0
+    elif what == "logits":
+        gpu["logits"][0, -1] = 0.0  # padding must be -inf
+    else:  # a cluster far below the n-th key instead of the n-th
+        S = np.sort(np.r_[a.order[0, :n - 1], 7])
+        gpu2 = result_for(head, S)
+        gpu["clusters"][0, :n] = S
+        gpu["ids"][0, :n * head.b] = gpu2["ids"][0]
+        gpu["logits"][0, :n * head.b] = gpu2["logits"][0]
+    rep = check_a(head, gpu, 0.5)
+    assert not rep.ok(), what
+
+
+def test_adaptive_needs_the_count(head):
+    gpu, _ = adaptive_result(head, 2, 0.5)
+    del gpu["nprobe"]
+    rep = check_a(head, gpu, 0.5)
+    assert not rep.ok() and "nprobe" in rep.failures[0]
