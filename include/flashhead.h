@@ -150,6 +150,37 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
                      int32_t* out_ids, float* out_logits, void* stream);
 
 /*
+ * fh_forward_adaptive — fh_forward with a probe count per query ([X] §1.2.2:
+ * the number of probes adapts to the distribution of h; §4.2: fewer probes
+ * for confident queries, such as frequent tokens).  The pages give no
+ * formula; this library's reading: the clusters are taken in the order of the
+ * selection keys (by score, or with FH_PROBE_SAMPLE the draws without
+ * replacement from softmax(s/T)), and query b stops at the first count n whose
+ * clusters hold at least tau of softmax(s/T) over all c clusters; n is then
+ * clamped to [p_min, p_max].  The mass is accumulated in float32.
+ *   p_min, p_max  1 <= p_min <= p_max <= min(c, 1024).
+ *   tau           in (0, 1].
+ *   mode          FH_PROBE_TOPK or FH_PROBE_SAMPLE | FH_TOKEN_*; not
+ *                 FH_PROBE_SHARED (FH_EINVAL).  temperature > 0 always (it
+ *                 sets the mass even for greedy calls).
+ *   out_nprobe    device [B] int32: n per query, or NULL.
+ *   out_clusters  device [B x p_max] int32 or NULL: the n probes ascending,
+ *                 then -1.
+ *   out_ids, out_logits  device [B x p_max b] or NULL: the n b retrieved
+ *                 tokens (cluster ascending, slot order), then id -1 and
+ *                 logit -inf.
+ *   out_token, out_token_logit, out_lse: as for fh_forward, over the n b
+ *                 retrieved tokens.
+ * Per-stage launches only (stage 1, selection of p_max, the count, stage 2
+ * over n probes, finish); stream-ordered, no host synchronisation.
+ */
+fh_status fh_forward_adaptive(fh_engine* e, const void* h, int64_t B, int64_t p_max,
+                              int64_t p_min, float tau, int mode, float temperature,
+                              uint64_t seed, int32_t* out_nprobe, int32_t* out_token,
+                              float* out_token_logit, float* out_lse, int32_t* out_clusters,
+                              int32_t* out_ids, float* out_logits, void* stream);
+
+/*
  * fh_forward_noalloc — fh_forward without an engine and without allocating:
  * for callers that cannot call hipMalloc (code under HIP graph capture,
  * tight serving loops, harnesses that forbid it).  It runs the per-stage

@@ -63,6 +63,7 @@ struct fh_engine {
   uint32_t* mbits = nullptr;  // [ceil(c/32) x max_batch] probe bitsets, word-major
   int32_t* mpre = nullptr;    // [ceil(c/32) x max_batch] probes in earlier words
   float* sumscores = nullptr;  // [c] summed scores of a batch (shared probes)
+  int32_t* nprobe = nullptr;   // [max_batch] adaptive probe counts
   fh::Part* parts = nullptr;  // [max_batch x parts_per_q]
   int64_t parts_per_q = 0;
   unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up
@@ -137,6 +138,7 @@ void free_engine(fh_engine* e) {
   (void)hipFree(e->Ec);
   (void)hipFree(e->t2c);
   (void)hipFree(e->sumscores);
+  (void)hipFree(e->nprobe);
   (void)hipFree(e->cq);
   (void)hipFree(e->csig);
   (void)hipFree(e->cq_mfma);
@@ -381,6 +383,7 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
       {(void**)&e->c2t, sizeof(int32_t) * (size_t)v, "C2T"},
       {(void**)&e->t2c, sizeof(int32_t) * (size_t)v, "token clusters"},
       {(void**)&e->sumscores, sizeof(float) * (size_t)c, "summed scores"},
+      {(void**)&e->nprobe, sizeof(int32_t) * (size_t)max_batch, "probe counts"},
       {(void**)&e->Ec, (size_t)(v * d) * (dtype == FH_BF16 ? 2 : 4), "cluster-contiguous E"},
       {(void**)&e->scores, sizeof(float) * (size_t)(max_batch * c), "scores"},
       {(void**)&e->sel, sizeof(int32_t) * (size_t)(max_batch * c), "selection"},
@@ -543,6 +546,60 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
   });
   if (r != hipSuccess) return hip_fail(r, "finish launch");
   return FH_OK;
+}
+
+fh_status fh_forward_adaptive(fh_engine* e, const void* h, int64_t B, int64_t p_max,
+                              int64_t p_min, float tau, int mode, float temperature,
+                              uint64_t seed, int32_t* out_nprobe, int32_t* out_token,
+                              float* out_token_logit, float* out_lse, int32_t* out_clusters,
+                              int32_t* out_ids, float* out_logits, void* stream) {
+  g_err.clear();
+  fh_status s = check_common(e, h, B);
+  if (s != FH_OK) return s;
+  const int64_t pcap = std::min<int64_t>(e->c, 1024);
+  if (p_min < 1 || p_min > p_max || p_max > pcap)
+    return fail(FH_EINVAL, "need 1 <= p_min <= p_max <= min(c, 1024) (p_min=" +
+                               std::to_string(p_min) + ", p_max=" + std::to_string(p_max) + ")");
+  if (!(tau > 0.f && tau <= 1.f)) return fail(FH_EINVAL, "tau must lie in (0, 1]");
+  if (mode & FH_PROBE_SHARED)
+    return fail(FH_EINVAL, "the adaptive count is per query; FH_PROBE_SHARED does not apply");
+  s = check_mode(mode, temperature);
+  if (s != FH_OK) return s;
+  if (!(temperature > 0.f && std::isfinite(temperature)))
+    return fail(FH_EINVAL, "the probe mass needs a finite temperature > 0");
+  DeviceGuard g(e->device);
+  if (!g.ok) return fail(FH_EHIP, "cannot select the engine's device");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const fh::KernelCtx k = e->ctx(st);
+  const int probe_sample = mode & FH_PROBE_SAMPLE;
+  const int token_sample = (mode & FH_TOKEN_SAMPLE) ? 1 : 0;
+  const float tprime = token_sample ? temperature : 1.f;
+  int32_t* S = out_clusters ? out_clusters : e->sel;
+  int32_t* np = out_nprobe ? out_nprobe : e->nprobe;
+  // stage 1 keeps the raw scores (the mass needs them); the selection forms
+  // the keys itself
+  hipError_t r = launch_stage1(e, st, k, h, B, e->scores);
+  if (r != hipSuccess) return hip_fail(r, "score launch");
+  r = timed(e, st, "select", [&] {
+    return fh::launch_select(k, e->scores, (int)B, (int)p_max, probe_sample, temperature, seed, S,
+                             (int)p_max);
+  });
+  if (r != hipSuccess) return hip_fail(r, "select launch");
+  r = timed(e, st, "adapt", [&] {
+    return fh::launch_adapt(k, e->scores, (int)B, (int)p_max, (int)p_min, tau, probe_sample,
+                            temperature, seed, S, np, out_ids, out_logits);
+  });
+  if (r != hipSuccess) return hip_fail(r, "adaptive count launch");
+  int64_t nparts = 0;
+  r = timed(e, st, "gather", [&] {
+    return fh::launch_gather(k, h, (int)B, S, (int)p_max, token_sample, tprime, seed, out_ids,
+                             out_logits, e->parts, &nparts, -1, np);
+  });
+  if (r != hipSuccess) return hip_fail(r, "gather launch");
+  r = timed(e, st, "finish", [&] {
+    return fh::launch_finish(k, e->parts, (int)B, nparts, out_token, out_token_logit, out_lse);
+  });
+  return r == hipSuccess ? FH_OK : hip_fail(r, "finish launch");
 }
 
 fh_status fh_forward_noalloc(const void* E, const void* C, const int32_t* c2t, fh_dtype dtype,

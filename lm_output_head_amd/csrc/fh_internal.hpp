@@ -70,10 +70,21 @@ float select_quantile(int64_t c, int64_t p);
 hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, int sample,
                          float temperature, uint64_t seed, int32_t* S, int ldS,
                          uint32_t* mbits = nullptr, int32_t* mpre = nullptr);
+// Stage 2 over the probe lists S [B x ldS] (ldS < 0: p).  With nprobe non-null
+// query q scores only its first nprobe[q] probes (the adaptive count).
 hipError_t launch_gather(const KernelCtx& k, const void* h, int B, const int32_t* S, int p,
                          int token_sample, float tprime, uint64_t seed, int32_t* out_ids,
                          float* out_logits, Part* parts, int64_t* nparts,
-                         int ldS = -1);
+                         int ldS = -1, const int32_t* nprobe = nullptr);
+// Adaptive probe count: per query, of the pmax probes in S [B x pmax]
+// (ascending, from launch_select over raw scores with the same sample,
+// temperature and seed), keep the first n in key order whose softmax(s/T)
+// mass reaches tau of all c clusters, n clamped to [pmin, pmax] (pmax <= 1024).
+// Rewrites S (n ascending, then -1), writes nprobe [B], and pads the retrieved
+// outputs [B x pmax b] (if non-null) past n b with id -1 and logit -inf.
+hipError_t launch_adapt(const KernelCtx& k, const float* scores, int B, int pmax, int pmin,
+                        float tau, int sample, float temperature, uint64_t seed, int32_t* S,
+                        int32_t* nprobe, int32_t* out_ids, float* out_logits);
 // batch-shared probes: summed scores, and one probe list broadcast to every row
 hipError_t launch_sum_rows(const KernelCtx& k, const float* scores, int B, float* out);
 hipError_t launch_broadcast_row(const KernelCtx& k, const int32_t* src, int n, int B,

@@ -114,6 +114,7 @@ struct RowsArgs {
   uint64_t seed;
   Part* parts;  // [B x gridDim.x] (EPI)
   KeyXform key;  // stage 1 (neither GATHER nor EPI): scores or selection keys
+  const int32_t* nprobe;  // GATHER: probes of each query (its first nprobe[q] of S), or null
 };
 
 template <typename T, int MAXM, int NQ, int RPW, bool GATHER, bool EPI>
@@ -134,7 +135,9 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   for (int q = 0; q < NQ; ++q) part[q] = part_empty();
 
   const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
-  const int64_t r1 = min(r0 + RPW, a.nrows);
+  int64_t nrows = a.nrows;
+  if (GATHER && a.nprobe) nrows = min(nrows, (int64_t)max(a.nprobe[q0], 0) * a.bsz);
+  const int64_t r1 = min(r0 + RPW, nrows);
   const int32_t* Sq = GATHER ? a.S + (int64_t)q0 * a.ldS : nullptr;
   // slot f = S[q, r / b] * b + r % b of the clustering; with the
   // cluster-contiguous copy of E that slot is also the row, else the row is
@@ -229,6 +232,138 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
       mbits[(int64_t)t * gridDim.x + q] = word;
       mpre[(int64_t)t * gridDim.x + q] = before;
     }
+  }
+}
+
+// ---- adaptive probe count (explainer §1.2.2, dynamic adjustment of the
+// probe count to the query; §4.2, fewer probes for confident queries).
+// One workgroup per query, after k_select has taken the top pmax keys.  The
+// pmax probes are sorted by selection key (descending, ties to the smaller
+// id) with a bitonic sort of 64-bit images (key image << 32 | ~id) in LDS; the
+// softmax(s/T) weights are scanned in that order, and the count n is the
+// first prefix holding tau of the total weight over all c clusters, clamped
+// to [pmin, pmax].  S is rewritten in place: the n kept probes ascending,
+// then -1; nprobe[q] = n; retrieved slots past n b get id -1 and logit -inf.
+struct AdaptShared {
+  unsigned long long key[kSelThreads];
+  uint32_t keep[kSelMaxC / 32];
+  float redf[kSelWaves];
+  int red_scan[kSelWaves];
+  int red_cnt[kSelWaves];
+};
+
+// Inclusive prefix sum of x over the 1024 threads in index order (float; the
+// same fixed pattern as block_exclusive_scan).
+__device__ __forceinline__ float block_inclusive_scan_f(float x, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x += dpp_f<0x111>(x);
+  x += dpp_f<0x112>(x);
+  x += dpp_f<0x114>(x);
+  x += dpp_f<0x118>(x);
+  const float t0 = readlane_f(x, 15), t1 = readlane_f(x, 31), t2 = readlane_f(x, 47);
+  const int row = lane >> 4;
+  x = x + (row >= 1 ? t0 : 0.f) + (row >= 2 ? t1 : 0.f) + (row >= 3 ? t2 : 0.f);
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  float t = lane < kSelWaves ? red[lane] : 0.f;
+  t += dpp_f<0x111>(t);
+  t += dpp_f<0x112>(t);
+  t += dpp_f<0x114>(t);
+  t += dpp_f<0x118>(t);
+  const float before = wave > 0 ? readlane_f(t, wave - 1) : 0.f;
+  return before + x;
+}
+
+// Max (or sum) over the 1024 threads: waves first, then the 16 wave values
+// in one row; the result is uniform.  `red` is free again on return.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce_f(float x, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = MAX ? wave_max(x) : wave_sum(x);
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  float t = lane < kSelWaves ? red[lane] : (MAX ? -INFINITY : 0.f);
+  t = MAX ? row_allreduce(t, [](float a, float b) { return fmaxf(a, b); })
+          : row_allreduce(t, [](float a, float b) { return a + b; });
+  const float r = readlane_f(t, 0);
+  __syncthreads();
+  return r;
+}
+
+template <int KP>
+__global__ __launch_bounds__(kSelThreads) void k_adapt(
+    const float* __restrict__ scores, int c, int pmax, int pmin, float tau, int sample,
+    float temperature, uint64_t seed, int32_t* __restrict__ S, int32_t* __restrict__ nprobe,
+    int b, int32_t* __restrict__ out_ids, float* __restrict__ out_logits) {
+  __shared__ AdaptShared sh;
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const float* sq = scores + (int64_t)q * c;
+  int32_t* Sq = S + (int64_t)q * pmax;
+  for (int w = tid; w < (c + 31) / 32; w += kSelThreads) sh.keep[w] = 0u;
+  // total weight W = sum_k exp(s_k / T - M), M = max_k s_k / T
+  float x[KP];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int k = tid + kSelThreads * i;
+    x[i] = k < c ? sq[k] / temperature : -INFINITY;
+    mx = fmaxf(mx, x[i]);
+  }
+  const float M = block_reduce_f<true>(mx, sh.redf);
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) acc += tid + kSelThreads * i < c ? __expf(x[i] - M) : 0.f;
+  const float W = block_reduce_f<false>(acc, sh.redf);
+  // the selected probes by key: the same key as k_select takes
+  int P2 = 1;
+  while (P2 < pmax) P2 <<= 1;
+  int kj = -1;
+  if (tid < pmax) {
+    kj = min(max(Sq[tid], 0), c - 1);
+    float v = sq[kj];
+    if (sample) v = v / temperature + gumbel_at(seed, (uint32_t)q, (uint32_t)kj, 0u);
+    sh.key[tid] = ((unsigned long long)ordered_bits(saturate_key(v)) << 32) |
+                  (unsigned long long)(0xFFFFFFFFu - (uint32_t)kj);
+  } else if (tid < P2) {
+    sh.key[tid] = 0ull;  // below every real key: sorts last
+  }
+  __syncthreads();
+  for (int k = 2; k <= P2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int i = tid, ixj = tid ^ j;
+      if (i < P2 && ixj > i) {
+        const unsigned long long a = sh.key[i], bb = sh.key[ixj];
+        if ((i & k) == 0 ? a < bb : a > bb) {
+          sh.key[i] = bb;
+          sh.key[ixj] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // weights in key order, their prefix sums, and the count below tau W
+  int id = -1;
+  float w = 0.f;
+  if (tid < pmax) {
+    id = (int)(0xFFFFFFFFu - (uint32_t)(sh.key[tid] & 0xFFFFFFFFull));
+    w = __expf(sq[id] / temperature - M);
+  }
+  const float cum = block_inclusive_scan_f(w, sh.redf);
+  int below;
+  (void)block_exclusive_scan(tid < pmax && cum < tau * W ? 1 : 0, sh.red_cnt, &below);
+  const int n = min(max(below + 1, pmin), pmax);
+  if (tid < n) atomicOr(&sh.keep[id >> 5], 1u << (id & 31));
+  __syncthreads();
+  const int kept = tid < pmax && (sh.keep[kj >> 5] & (1u << (kj & 31))) ? 1 : 0;
+  int tot;
+  const int pos = block_exclusive_scan(kept, sh.red_scan, &tot);
+  if (kept) Sq[pos] = kj;
+  if (tid < pmax && tid >= n) Sq[tid] = -1;
+  if (tid == 0) nprobe[q] = n;
+  const int64_t nr = (int64_t)pmax * b;
+  for (int64_t r = (int64_t)n * b + tid; r < nr; r += kSelThreads) {
+    if (out_ids) out_ids[(int64_t)q * nr + r] = -1;
+    if (out_logits) out_logits[(int64_t)q * nr + r] = -INFINITY;
   }
 }
 
@@ -383,24 +518,42 @@ hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, 
   return hipGetLastError();
 }
 
+hipError_t launch_adapt(const KernelCtx& k, const float* scores, int B, int pmax, int pmin,
+                        float tau, int sample, float temperature, uint64_t seed, int32_t* S,
+                        int32_t* nprobe, int32_t* out_ids, float* out_logits) {
+  if (pmax < 1 || pmax > kSelThreads || pmin < 1 || pmin > pmax) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)B), block(kSelThreads);
+  const int c = (int)k.c, b = (int)k.b;
+  switch (sel_keys_per_thread(k.c)) {
+#define FH_CASE(KK) \
+  case KK: hipLaunchKernelGGL((k_adapt<KK>), grid, block, 0, k.stream, scores, c, pmax, pmin, tau, sample, temperature, seed, S, nprobe, b, out_ids, out_logits); break;
+    FH_CASE(1) FH_CASE(2) FH_CASE(8) FH_CASE(16)
+#undef FH_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t gather_t(const KernelCtx& k, const void* h, int B, const int32_t* S, int p,
                            int token_sample, float tprime, uint64_t seed, int32_t* out_ids,
-                           float* out_logits, Part* parts, int64_t* nparts, int ldS) {
+                           float* out_logits, Part* parts, int64_t* nparts, int ldS,
+                           const int32_t* nprobe) {
   RowsArgs a{};
   a.M = k.Ec ? k.Ec : k.E; a.contiguous = k.Ec != nullptr;
   a.nrows = (int64_t)p * k.b; a.d = k.d; a.c2t = k.c2t; a.bsz = (int)k.b;
   a.S = S; a.ldS = ldS < 0 ? p : ldS; a.H = h; a.B = B; a.out_vals = out_logits; a.ld_vals = a.nrows;
   a.out_ids = out_ids; a.token_sample = token_sample; a.tprime = tprime; a.seed = seed;
-  a.parts = parts;
+  a.parts = parts; a.nprobe = nprobe;
   return launch_rows<T, 1, kGatherRPW, true, true>(a, k.stream, nparts);
 }
 
 hipError_t launch_gather(const KernelCtx& k, const void* h, int B, const int32_t* S, int p,
                          int token_sample, float tprime, uint64_t seed, int32_t* out_ids,
-                         float* out_logits, Part* parts, int64_t* nparts, int ldS) {
-  return k.bf16 ? gather_t<uint16_t>(k, h, B, S, p, token_sample, tprime, seed, out_ids, out_logits, parts, nparts, ldS)
-                : gather_t<float>(k, h, B, S, p, token_sample, tprime, seed, out_ids, out_logits, parts, nparts, ldS);
+                         float* out_logits, Part* parts, int64_t* nparts, int ldS,
+                         const int32_t* nprobe) {
+  return k.bf16 ? gather_t<uint16_t>(k, h, B, S, p, token_sample, tprime, seed, out_ids, out_logits, parts, nparts, ldS, nprobe)
+                : gather_t<float>(k, h, B, S, p, token_sample, tprime, seed, out_ids, out_logits, parts, nparts, ldS, nprobe);
 }
 
 // ---- batch-shared probes (explainer §4.2: share the cluster selection

@@ -110,6 +110,24 @@ def fh_forward(eng, h, p, mode, temperature, seed, out_token, out_token_logit=No
                                  _stream(stream)))
 
 
+def fh_forward_adaptive(eng, h, p_max, p_min, tau, mode, temperature, seed, out_token,
+                        out_nprobe=None, out_token_logit=None, out_lse=None, out_clusters=None,
+                        out_ids=None, out_logits=None, stream=None) -> None:
+    B, v, _, c = _engine_h(eng, h)
+    b = v // c
+    _require(out_nprobe, torch.int32, (B,), "out_nprobe")
+    _require(out_token, torch.int32, (B,), "out_token")
+    _require(out_token_logit, torch.float32, (B,), "out_token_logit")
+    _require(out_lse, torch.float32, (B,), "out_lse")
+    _require(out_clusters, torch.int32, (B, p_max), "out_clusters")
+    _require(out_ids, torch.int32, (B, p_max * b), "out_ids")
+    _require(out_logits, torch.float32, (B, p_max * b), "out_logits")
+    check(_abi.load().fh_forward_adaptive(eng, _ptr(h), B, p_max, p_min, tau, mode, temperature,
+                                          seed, _ptr(out_nprobe), _ptr(out_token),
+                                          _ptr(out_token_logit), _ptr(out_lse), _ptr(out_clusters),
+                                          _ptr(out_ids), _ptr(out_logits), _stream(stream)))
+
+
 def fh_forward_noalloc(E, C, c2t, h, p, mode, temperature, seed, out_token, out_token_logit=None,
                        out_lse=None, out_clusters=None, out_ids=None, out_logits=None,
                        stream=None) -> None:
@@ -288,6 +306,27 @@ class FlashHead:
             out["logits"] = self._alloc((B, p * self.b), torch.float32)
         fh_forward(self.eng, h, p, mode, temperature, seed, out["token"], out["token_logit"],
                    out["lse"], out.get("clusters"), out.get("ids"), out.get("logits"), stream)
+        return out
+
+    def forward_adaptive(self, h: torch.Tensor, p_max: int, tau: float, p_min: int = 1,
+                         mode: int = 0, temperature: float = 1.0, seed: int = 0,
+                         want_clusters: bool = False, want_retrieved: bool = False,
+                         stream=None) -> dict:
+        """forward with a per-query probe count: the first clusters in key
+        order whose softmax(s/T) mass reaches tau, clamped to [p_min, p_max]."""
+        B = h.shape[0]
+        out = {"nprobe": self._alloc((B,), torch.int32),
+               "token": self._alloc((B,), torch.int32),
+               "token_logit": self._alloc((B,), torch.float32),
+               "lse": self._alloc((B,), torch.float32)}
+        if want_clusters:
+            out["clusters"] = self._alloc((B, p_max), torch.int32)
+        if want_retrieved:
+            out["ids"] = self._alloc((B, p_max * self.b), torch.int32)
+            out["logits"] = self._alloc((B, p_max * self.b), torch.float32)
+        fh_forward_adaptive(self.eng, h, p_max, p_min, tau, mode, temperature, seed, out["token"],
+                            out["nprobe"], out["token_logit"], out["lse"], out.get("clusters"),
+                            out.get("ids"), out.get("logits"), stream)
         return out
 
     def score(self, h: torch.Tensor, stream=None) -> torch.Tensor:

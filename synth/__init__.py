@@ -13,5 +13,6 @@ from .clustered import (  # noqa: F401
     Shape,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    make_graded_queries,
     make_problem,
 )

@@ -170,3 +170,21 @@ def _make_problem_cached(shape: Shape, seed_data: int, seed_query: int, nq: int)
     else:
         H_bits, H = None, H32
     return Problem(shape, E, C, c2t, H, tok, E_bits, C_bits, H_bits)
+
+
+def make_graded_queries(pb: Problem, alphas, seed: int = 7):
+    """Queries of graded confidence on pb's head: h_i = alphas[i] E[t_i] +
+    n_i / sqrt(d) for a random token t_i and standard normal n_i (alpha = 0
+    is pure noise, a diffuse query; the shape's own alpha gives pb's queries),
+    rounded to the stored dtype.  Returns (H float32, H_bits or None, tokens)."""
+    alphas = np.asarray(alphas, dtype=np.float32)
+    nq, d = alphas.size, pb.shape.d
+    rq = np.random.default_rng(seed)
+    tok = rq.integers(0, pb.shape.v, nq)
+    H32 = (alphas[:, None] * pb.E[tok]
+           + rq.standard_normal((nq, d), dtype=np.float32) / np.float32(np.sqrt(np.float32(d))))
+    H32 = H32.astype(np.float32)
+    if pb.shape.dtype == "bf16":
+        bits = f32_to_bf16_bits(H32)
+        return bf16_bits_to_f32(bits), bits, tok
+    return H32, None, tok

@@ -85,6 +85,8 @@ def test_calls_on_null_engine_fail_cleanly(lib):
     h = P(4096)
     assert lib.fh_forward(None, h, 1, 1, 0, 1.0, 0, None, None, None, None, None, None, None) == -1
     assert lib.fh_score(None, h, 1, P(4096), None) == -1
+    assert lib.fh_forward_adaptive(None, h, 1, 4, 1, 0.9, 0, 1.0, 0, None, None, None, None, None,
+                                   None, None, None) == -1
     assert lib.fh_dense_forward(None, h, 1, 0, 1.0, 0, None, None, None, None, None) == -1
     assert lib.fh_get_int4(None, P(4096), P(4096), None) == -1
     assert lib.fh_profile_begin(None, 4) == -1

@@ -68,3 +68,19 @@ def test_score_dense_and_verify_refuse_mismatches(eng):
 def test_unknown_engine_is_refused():
     with pytest.raises(ValueError, match="unknown engine"):
         fhb.fh_forward(0xBAD, torch.zeros(1, D, dtype=torch.bfloat16), 1, 0, 1.0, 0, out1(1))
+
+
+@pytest.mark.parametrize("which", ["nprobe", "clusters", "ids", "logits"])
+def test_adaptive_refuses_a_short_output(eng, which):
+    # the adaptive outputs are sized by p_max: [B], [B x p_max], [B x p_max b]
+    B, pmax = 2, 3
+    h = torch.zeros(B, D, dtype=torch.bfloat16)
+    kw = {"out_nprobe": out1(B), "out_clusters": torch.zeros(B, pmax, dtype=torch.int32),
+          "out_ids": torch.zeros(B, pmax * 16, dtype=torch.int32),
+          "out_logits": torch.zeros(B, pmax * 16, dtype=torch.float32)}
+    short = {"nprobe": out1(B + 1), "clusters": torch.zeros(B, pmax - 1, dtype=torch.int32),
+             "ids": torch.zeros(B, pmax * 16 - 16, dtype=torch.int32),
+             "logits": torch.zeros(B, pmax * 16, dtype=torch.float16)}
+    kw["out_" + which] = short[which]
+    with pytest.raises(ValueError, match="out_" + which):
+        fhb.fh_forward_adaptive(eng, h, pmax, 1, 0.9, 0, 1.0, 0, out1(B), **kw)
