@@ -23,10 +23,13 @@ from .flashhead_oracle import (  # noqa: F401
     dequantize_g32,
     dequantize_int4,
     dequantize_int8,
+    e4m3_decode,
+    e4m3_encode,
     finish,
     forward,
     gather,
     pack_int4,
+    probs_fp8,
     quantize_int4_g32,
     quantize_int8_g32,
     score,

@@ -363,6 +363,60 @@ def finish(ids: np.ndarray, z: np.ndarray, mode: int = 0, temperature: float = 1
 
 
 # ---------------------------------------------------------------------------
+# fp8 probability format (explainer §2.3: the quantisation config gives the
+# probability intermediate as fp8)
+# ---------------------------------------------------------------------------
+
+def e4m3_decode(code) -> np.ndarray:
+    """Value of an fp8 E4M3 byte (OCP 8-bit floating point, E4M3: sign, four
+    exponent bits with bias 7, three mantissa bits; exponent field 0 holds
+    the subnormals m/8 * 2^-6; S.1111.111 is NaN; no infinities)."""
+    code = np.asarray(code, dtype=np.int64)
+    sign = np.where(code & 0x80, -1.0, 1.0)
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7F))  # codes 0 .. 126: the finite values >= 0, ascending
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest fp8 E4M3 byte to each x >= 0, ties to the even code, values
+    above the largest finite (448) saturating to it; NaN gives 0x7F.  Written
+    as a search over the code table, not as bit manipulation."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(x < 0):
+        raise ValueError("probabilities are non-negative")
+    out = np.full(x.shape, 0x7F, dtype=np.uint8)
+    ok = ~np.isnan(x)
+    xv = np.minimum(x[ok], _E4M3_POS[-1])
+    hi = np.searchsorted(_E4M3_POS, xv, side="left")  # first value >= x
+    hi = np.minimum(hi, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = xv - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - xv
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    out[ok] = pick.astype(np.uint8)
+    return out
+
+
+def probs_fp8(z, lse, temperature: float = 1.0):
+    """fp8 probabilities of candidates: e4m3_encode(exp(z / T' - LSE)) per row,
+    with LSE the row's log-sum-exp at the same T'.  A logit of -inf (an empty
+    slot) gives probability 0.  Returns (bytes uint8, float64 probabilities)."""
+    z = np.atleast_2d(np.asarray(z, dtype=np.float64))
+    lse = np.asarray(lse, dtype=np.float64).reshape(-1, 1)
+    if not temperature > 0:
+        raise ValueError("temperature must be > 0")
+    with np.errstate(under="ignore"):
+        p = np.exp(z / float(temperature) - lse)
+    return e4m3_encode(p), p
+
+
+# ---------------------------------------------------------------------------
 # Whole paths
 # ---------------------------------------------------------------------------
 

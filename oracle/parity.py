@@ -30,7 +30,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .flashhead_oracle import OracleHead, finish, gather, select, select_adaptive
+from .flashhead_oracle import (OracleHead, e4m3_decode, finish, gather, probs_fp8, select,
+                               select_adaptive)
 
 REL = 2e-3
 TIE_GAP = 1e-3
@@ -38,6 +39,10 @@ TIE_GAP = 1e-3
 # float32 scores; a count is certified when the oracle's mass at the GPU's cut
 # lies within MASS_GAP of tau
 MASS_GAP = 1e-4
+# fp8 probabilities: the GPU's exp runs in float32 (a few ulp); a byte may
+# differ from the oracle's by one code when the probability lies within
+# MID_GAP (relative) of the midpoint between the two codes
+MID_GAP = 1e-5
 
 
 @dataclass
@@ -273,4 +278,29 @@ def check_scores(C_hat, H, s_gpu, rel=REL) -> Report:
         rep.max_logit_err = max(rep.max_logit_err, float(err.max()))
         if not err.max() <= 1:
             rep.fail(f"row {r}: score error {err.max():.3g} x tol")
+    return rep
+
+
+def check_probs_fp8(z, lse, temperature, got, mid_gap=MID_GAP) -> Report:
+    """fp8 E4M3 probabilities against the oracle's encoding of
+    exp(z / T' - LSE), taken on the same logits and LSE the GPU used (its own,
+    already checked against the oracle), so that the byte is decided from the
+    same inputs.  Bytes must be equal, or adjacent codes with the oracle's
+    probability within mid_gap (relative) of their midpoint."""
+    want, p = probs_fp8(z, lse, temperature)
+    got = np.asarray(got, dtype=np.uint8).reshape(want.shape)
+    rep = Report(queries=want.shape[0])
+    bad = got != want
+    if not bad.any():
+        return rep
+    g, w, pv = got[bad].astype(np.int64), want[bad].astype(np.int64), p[bad]
+    adjacent = (np.abs(g - w) == 1) & (g < 0x7F) & (w < 0x7F)
+    mid = (e4m3_decode(np.minimum(g, w)) + e4m3_decode(np.maximum(g, w))) / 2
+    near = adjacent & (np.abs(pv - mid) <= mid_gap * np.maximum(mid, 2.0 ** -10))
+    rep.token_ties = int(near.sum())
+    if not near.all():
+        rows, cols = np.nonzero(bad)
+        i = int(np.nonzero(~near)[0][0])
+        rep.fail(f"row {rows[i]} slot {cols[i]}: fp8 byte {g[i]:#04x} != {w[i]:#04x} "
+                 f"(p = {pv[i]:.6g}), not a midpoint near-tie; {int((~near).sum())} such bytes")
     return rep

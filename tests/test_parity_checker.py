@@ -270,3 +270,43 @@ def test_adaptive_needs_the_count(head):
     del gpu["nprobe"]
     rep = check_a(head, gpu, 0.5)
     assert not rep.ok() and "nprobe" in rep.failures[0]
+
+
+# ---- fp8 probabilities (check_probs_fp8)
+
+def _fp8_case():
+    rng = np.random.default_rng(1)
+    z = rng.normal(0, 2, size=(2, 300))
+    lse = np.log(np.exp(z).sum(1))
+    return z, lse
+
+
+def test_fp8_exact_bytes_pass():
+    z, lse = _fp8_case()
+    want, _ = oracle.probs_fp8(z, lse, 1.0)
+    assert parity.check_probs_fp8(z, lse, 1.0, want).ok()
+
+
+def test_fp8_one_code_off_fails_away_from_a_midpoint():
+    z, lse = _fp8_case()
+    want, p = oracle.probs_fp8(z, lse, 1.0)
+    got = want.copy()
+    i = int(np.argmax(p[0]))
+    got[0, i] += 1
+    rep = parity.check_probs_fp8(z, lse, 1.0, got)
+    assert not rep.ok() and "not a midpoint near-tie" in rep.failures[0]
+
+
+def test_fp8_neighbour_at_a_midpoint_passes():
+    # a probability a hair (1e-7 relative) above the midpoint of codes 0x30 /
+    # 0x31 (0.5 / 0.5625): the oracle rounds up, the other code is certified
+    mid = (oracle.e4m3_decode(0x30) + oracle.e4m3_decode(0x31)) / 2
+    z = np.array([[np.log(mid * (1 + 1e-7))]])
+    lse = np.array([0.0])
+    want, _ = oracle.probs_fp8(z, lse, 1.0)
+    assert int(want[0, 0]) == 0x31
+    rep = parity.check_probs_fp8(z, lse, 1.0, np.array([[0x30]], np.uint8))
+    assert rep.ok() and rep.token_ties == 1
+    # the same swap 1e-3 away from the midpoint fails
+    z = np.array([[np.log(mid * (1 + 1e-3))]])
+    assert not parity.check_probs_fp8(z, lse, 1.0, np.array([[0x30]], np.uint8)).ok()
