@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="latency and agreement with the dense head over B in {1,8,32,64} x p in "
                          "{128,256,512,1024} at --shape / --quant; one JSON line")
+    ap.add_argument("--adaptive", type=float, default=None, metavar="TAU",
+                    help="with --sweep: also rows of the adaptive probe count (mass TAU at "
+                         "--temperature, p_max = --p) on the same queries")
     ap.add_argument("--alpha", type=float, default=None,
                     help="--sweep: query scale on its source token's embedding (default: the "
                          "shape's); smaller is harder for the probes")
@@ -555,6 +558,34 @@ def sweep_main(args):
                          "tokens_per_s": round(B / (us * 1e-6), 1),
                          "top1_agreement": round(agree, 4), "cluster_recall": round(recall, 4)})
             print(f"[bench] B={B} p={p} {us:.1f} us agree {agree:.3f}", file=sys.stderr, flush=True)
+    adaptive = []
+    if args.adaptive is not None:
+        tau, T, pmax = float(args.adaptive), float(args.temperature), int(args.p)
+        toks, hits, ns = [], [], []
+        for i in range(0, nq, 64):
+            o = heads[0].forward_adaptive(Hall[i:i + 64], pmax, tau, mode=0, temperature=T,
+                                          want_clusters=True)
+            toks.append(o["token"].cpu().numpy())
+            ns.append(o["nprobe"].cpu().numpy())
+            cl = o["clusters"].cpu().numpy()
+            dt = dense_tok[i:i + 64]
+            hits.append(np.array([t2c[t] in set(cl[j].tolist()) for j, t in enumerate(dt)]))
+        ns = np.concatenate(ns)
+        agree = float((np.concatenate(toks) == dense_tok).mean())
+        recall = float(np.concatenate(hits).mean())
+        for B in Bs:
+            steps = max(50, 800 // B)
+            us = timed_us(B, lambda e, h, b, i: lib.fh_forward_adaptive(
+                e, h, b, pmax, 1, tau, 0, T, 0x5EED + i, None, ptr(otok), ptr(olog), ptr(olse),
+                None, None, None, sp), steps)
+            adaptive.append({"B": B, "p_max": pmax, "tau": tau, "temperature": T,
+                             "mean_probes": round(float(ns.mean()), 1),
+                             "probes_min_median_max": [int(ns.min()), float(np.median(ns)),
+                                                       int(ns.max())],
+                             "us_per_call": round(us, 2), "tokens_per_s": round(B / (us * 1e-6), 1),
+                             "top1_agreement": round(agree, 4), "cluster_recall": round(recall, 4)})
+            print(f"[bench] adaptive B={B} tau={tau} {us:.1f} us mean n {ns.mean():.1f}",
+                  file=sys.stderr, flush=True)
     dense = []
     for B in Bs:
         us = timed_us(B, lambda e, h, b, i: lib.fh_dense_forward(e, h, b, 0, 1.0, 0x5EED + i,
@@ -569,6 +600,8 @@ def sweep_main(args):
                       "mode": "greedy, probes shared by the batch (top p of the summed scores)"
                       if shared else "greedy (top-p probes, argmax)"},
            "rows": rows, "dense": dense}
+    if adaptive:
+        res["adaptive"] = adaptive
     print(json.dumps(res), flush=True)
     for h in heads:
         h.close()

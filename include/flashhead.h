@@ -181,6 +181,31 @@ fh_status fh_forward_adaptive(fh_engine* e, const void* h, int64_t B, int64_t p_
                               int32_t* out_ids, float* out_logits, void* stream);
 
 /*
+ * fh_probs_fp8 — the candidates' probabilities in fp8 ([X] §2.3: the
+ * quantisation config keeps the probability intermediate as fp8).  Per row
+ * q, p = exp(logits[q*n + i] / T' - lse[q]) (a -inf logit, an empty adaptive
+ * slot, gives 0).  The pages do not say how the fp8 tensor is scaled; here a
+ * power of two per row: k = 8 - e for the row's largest p = f 2^e, f in
+ * [1/2, 1), which puts it in [128, 256) (no saturation, exact scaling, 17
+ * binades below it).  out_probs[q*n + i] = E4M3(p 2^k), the OCP E4M3 byte
+ * (sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 0x7F
+ * NaN) rounded to nearest even; out_scale_exp[q] = k, so p = value(byte)
+ * 2^-k.  Engine-free; stream-ordered.
+ *   logits     device [B x n] float, e.g. fh_forward's out_logits (n = p b)
+ *              or fh_forward_adaptive's (n = p_max b).
+ *   lse        device [B] float: each row's log-sum-exp taken at T'
+ *              (fh_forward's out_lse).
+ *   temperature  T' > 0, the temperature of that LSE: the call's temperature
+ *              when tokens were sampled, else 1.
+ *   out_probs  device [B x n] uint8; out_scale_exp device [B] int32.
+ * FH_EINVAL for NULL pointers, B outside [1, 65535], n outside [1, 2^31] or
+ * a temperature that is not finite and > 0.
+ */
+fh_status fh_probs_fp8(const float* logits, const float* lse, int64_t B, int64_t n,
+                       float temperature, uint8_t* out_probs, int32_t* out_scale_exp,
+                       void* stream);
+
+/*
  * fh_forward_noalloc — fh_forward without an engine and without allocating:
  * for callers that cannot call hipMalloc (code under HIP graph capture,
  * tight serving loops, harnesses that forbid it).  It runs the per-stage

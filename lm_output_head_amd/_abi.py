@@ -20,7 +20,8 @@ FH_PATH_AUTO, FH_PATH_MULTI = 0, 1
 
 # Every symbol the header declares.
 EXPORTS = (
-    "fh_create", "fh_destroy", "fh_forward", "fh_forward_adaptive", "fh_forward_noalloc", "fh_score",
+    "fh_create", "fh_destroy", "fh_forward", "fh_forward_adaptive", "fh_forward_noalloc", "fh_probs_fp8",
+    "fh_score",
     "fh_dense_forward",
     "fh_get_int4", "fh_get_int8", "fh_spec_verify", "fh_profile_begin", "fh_profile_end",
     "fh_set_path", "fh_sync_status",
@@ -59,6 +60,7 @@ _SIGS = {
     "fh_forward": ([_p, _p, _i64, _i64, _int, _f, _u64, _p, _p, _p, _p, _p, _p, _p], _int),
     "fh_forward_adaptive": ([_p, _p, _i64, _i64, _i64, _f, _int, _f, _u64, _p, _p, _p, _p, _p,
                              _p, _p, _p], _int),
+    "fh_probs_fp8": ([_p, _p, _i64, _i64, _f, _p, _p, _p], _int),
     "fh_forward_noalloc": ([_p, _p, _p, _int, _i64, _i64, _i64, _p, _i64, _i64, _int, _f, _u64,
                             _p, _p, _p, _p, _p, _p, _p], _int),
     "fh_score": ([_p, _p, _i64, _p, _p], _int),

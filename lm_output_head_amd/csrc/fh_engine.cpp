@@ -681,6 +681,21 @@ fh_status fh_forward_noalloc(const void* E, const void* C, const int32_t* c2t, f
   return r == hipSuccess ? FH_OK : hip_fail(r, "finish launch");
 }
 
+fh_status fh_probs_fp8(const float* logits, const float* lse, int64_t B, int64_t n,
+                       float temperature, uint8_t* out_probs, int32_t* out_scale_exp,
+                       void* stream) {
+  g_err.clear();
+  if (!logits || !lse || !out_probs || !out_scale_exp)
+    return fail(FH_EINVAL, "logits, lse, out_probs and out_scale_exp must not be NULL");
+  if (B < 1 || B > 65535) return fail(FH_EINVAL, "B outside [1, 65535]");
+  if (n < 1 || n > (int64_t(1) << 31)) return fail(FH_EINVAL, "n outside [1, 2^31]");
+  if (!(temperature > 0.f && std::isfinite(temperature)))
+    return fail(FH_EINVAL, "temperature must be finite and > 0");
+  hipError_t r = fh::launch_probs_fp8(logits, lse, B, n, temperature, out_probs, out_scale_exp,
+                                      static_cast<hipStream_t>(stream));
+  return r == hipSuccess ? FH_OK : hip_fail(r, "fp8 probabilities launch");
+}
+
 fh_status fh_dense_forward(fh_engine* e, const void* h, int64_t B, int mode, float temperature,
                            uint64_t seed, int32_t* out_token, float* out_token_logit,
                            float* out_lse, float* out_logits, void* stream) {

@@ -122,6 +122,11 @@ hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, 
                              float tprime, uint64_t seed, float* out_logits, Part* parts,
                              int64_t* nparts);
 
+// fp8 E4M3 probabilities of [B x n] logits, exp(z / T' - lse[q]) scaled by
+// 2^out_k[q] (fh_probs.hip).
+hipError_t launch_probs_fp8(const float* logits, const float* lse, int64_t B, int64_t n,
+                            float temperature, uint8_t* out, int32_t* out_k, hipStream_t stream);
+
 hipError_t launch_finish(const KernelCtx& k, const Part* parts, int B, int64_t nparts,
                          int32_t* out_token, float* out_logit, float* out_lse);
 

@@ -153,6 +153,22 @@ def fh_forward_noalloc(E, C, c2t, h, p, mode, temperature, seed, out_token, out_
                                          _ptr(out_ids), _ptr(out_logits), _stream(stream)))
 
 
+def fh_probs_fp8(logits, lse, temperature, out_probs, out_scale_exp, stream=None) -> None:
+    """fp8 E4M3 bytes of exp(logits / T' - lse) 2^k per row of [B x n] float32
+    logits, with the row's power-of-two scale exponent k in out_scale_exp."""
+    if logits is None or lse is None or out_probs is None or out_scale_exp is None:
+        raise ValueError("logits, lse, out_probs and out_scale_exp are required")
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be [B x n], got shape {tuple(logits.shape)}")
+    B, n = logits.shape
+    _require(logits, torch.float32, (B, n), "logits")
+    _require(lse, torch.float32, (B,), "lse")
+    _require(out_probs, torch.uint8, (B, n), "out_probs")
+    _require(out_scale_exp, torch.int32, (B,), "out_scale_exp")
+    check(_abi.load().fh_probs_fp8(_ptr(logits), _ptr(lse), B, n, temperature, _ptr(out_probs),
+                                   _ptr(out_scale_exp), _stream(stream)))
+
+
 def fh_score(eng, h, out_scores, stream=None) -> None:
     B, _, _, c = _engine_h(eng, h)
     _require(out_scores, torch.float32, (B, c), "out_scores")
@@ -328,6 +344,17 @@ class FlashHead:
                             out["nprobe"], out["token_logit"], out["lse"], out.get("clusters"),
                             out.get("ids"), out.get("logits"), stream)
         return out
+
+    def probs_fp8(self, out: dict, temperature: float = 1.0, stream=None) -> dict:
+        """fp8 E4M3 probabilities of a forward's retrieved candidates (its
+        "logits" and "lse"; temperature = the LSE's T': the call's temperature
+        when tokens were sampled, else 1): {"probs": uint8 [B x n],
+        "scale_exp": int32 [B]}, p = value(byte) 2^-scale_exp."""
+        B = out["logits"].shape[0]
+        res = {"probs": self._alloc(tuple(out["logits"].shape), torch.uint8),
+               "scale_exp": self._alloc((B,), torch.int32)}
+        fh_probs_fp8(out["logits"], out["lse"], temperature, res["probs"], res["scale_exp"], stream)
+        return res
 
     def score(self, h: torch.Tensor, stream=None) -> torch.Tensor:
         out = self._alloc((h.shape[0], self.c), torch.float32)

@@ -404,16 +404,26 @@ def e4m3_encode(x) -> np.ndarray:
 
 
 def probs_fp8(z, lse, temperature: float = 1.0):
-    """fp8 probabilities of candidates: e4m3_encode(exp(z / T' - LSE)) per row,
-    with LSE the row's log-sum-exp at the same T'.  A logit of -inf (an empty
-    slot) gives probability 0.  Returns (bytes uint8, float64 probabilities)."""
+    """fp8 probabilities of candidates, scaled per row.
+
+    p = exp(z / T' - LSE) per row (LSE the row's log-sum-exp at the same T';
+    a logit of -inf, an empty slot, gives 0).  The pages name fp8 for the
+    probability intermediate but not its scaling; the reading here: a power of
+    two per row, 2^k with k = 8 - e where p_max = f 2^e, f in [1/2, 1) (so the
+    row's largest probability lands in [128, 256), below E4M3's largest finite
+    448, and the scaling itself is exact), then byte = e4m3_encode(p 2^k).
+    A row decodes as e4m3_decode(byte) 2^-k.  Returns (bytes uint8 [B x n],
+    k int64 [B], p float64 [B x n]); a row with no mass gets k = 0."""
     z = np.atleast_2d(np.asarray(z, dtype=np.float64))
     lse = np.asarray(lse, dtype=np.float64).reshape(-1, 1)
     if not temperature > 0:
         raise ValueError("temperature must be > 0")
     with np.errstate(under="ignore"):
         p = np.exp(z / float(temperature) - lse)
-    return e4m3_encode(p), p
+    pmax = p.max(axis=1)
+    _, e = np.frexp(pmax)
+    k = np.where(pmax > 0, 8 - e, 0).astype(np.int64)
+    return e4m3_encode(np.ldexp(p, k[:, None])), k, p
 
 
 # ---------------------------------------------------------------------------

@@ -30,8 +30,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .flashhead_oracle import (OracleHead, e4m3_decode, finish, gather, probs_fp8, select,
-                               select_adaptive)
+from .flashhead_oracle import (OracleHead, e4m3_decode, e4m3_encode, finish, gather, probs_fp8,
+                               select, select_adaptive)
 
 REL = 2e-3
 TIE_GAP = 1e-3
@@ -281,19 +281,32 @@ def check_scores(C_hat, H, s_gpu, rel=REL) -> Report:
     return rep
 
 
-def check_probs_fp8(z, lse, temperature, got, mid_gap=MID_GAP) -> Report:
-    """fp8 E4M3 probabilities against the oracle's encoding of
-    exp(z / T' - LSE), taken on the same logits and LSE the GPU used (its own,
-    already checked against the oracle), so that the byte is decided from the
-    same inputs.  Bytes must be equal, or adjacent codes with the oracle's
-    probability within mid_gap (relative) of their midpoint."""
-    want, p = probs_fp8(z, lse, temperature)
-    got = np.asarray(got, dtype=np.uint8).reshape(want.shape)
-    rep = Report(queries=want.shape[0])
+def check_probs_fp8(z, lse, temperature, got, got_k, mid_gap=MID_GAP) -> Report:
+    """fp8 E4M3 probabilities and their per-row scale exponents against the
+    oracle's probs_fp8, taken on the same logits and LSE the GPU used (its
+    own, already checked against the oracle), so that every byte is decided
+    from the same inputs.  A row's exponent must equal the oracle's, or differ
+    by one where the oracle's largest probability lies within mid_gap
+    (relative) of the power of two between the two choices; bytes (at the
+    GPU's exponent) must be equal, or adjacent codes with the scaled
+    probability within mid_gap of their midpoint."""
+    _, k_ref, p = probs_fp8(z, lse, temperature)
+    got = np.asarray(got, dtype=np.uint8).reshape(p.shape)
+    got_k = np.asarray(got_k, dtype=np.int64).reshape(-1)
+    rep = Report(queries=p.shape[0])
+    pmax = p.max(axis=1)
+    for r in np.nonzero(got_k != k_ref)[0]:
+        edge = 2.0 ** (7 - max(got_k[r], k_ref[r]) + 1)  # the binade boundary between the two
+        if abs(int(got_k[r]) - int(k_ref[r])) != 1 or abs(pmax[r] - edge) > mid_gap * edge:
+            rep.fail(f"row {r}: scale exponent {got_k[r]} != {k_ref[r]} (p_max = {pmax[r]:.8g})")
+            return rep
+        rep.cluster_ties += 1
+    want = e4m3_encode(np.ldexp(p, got_k[:, None]))
+    scaled = np.ldexp(p, got_k[:, None])
     bad = got != want
     if not bad.any():
         return rep
-    g, w, pv = got[bad].astype(np.int64), want[bad].astype(np.int64), p[bad]
+    g, w, pv = got[bad].astype(np.int64), want[bad].astype(np.int64), scaled[bad]
     adjacent = (np.abs(g - w) == 1) & (g < 0x7F) & (w < 0x7F)
     mid = (e4m3_decode(np.minimum(g, w)) + e4m3_decode(np.maximum(g, w))) / 2
     near = adjacent & (np.abs(pv - mid) <= mid_gap * np.maximum(mid, 2.0 ** -10))
@@ -302,5 +315,5 @@ def check_probs_fp8(z, lse, temperature, got, mid_gap=MID_GAP) -> Report:
         rows, cols = np.nonzero(bad)
         i = int(np.nonzero(~near)[0][0])
         rep.fail(f"row {rows[i]} slot {cols[i]}: fp8 byte {g[i]:#04x} != {w[i]:#04x} "
-                 f"(p = {pv[i]:.6g}), not a midpoint near-tie; {int((~near).sum())} such bytes")
+                 f"(scaled p = {pv[i]:.6g}), not a midpoint near-tie; {int((~near).sum())} such bytes")
     return rep

@@ -52,17 +52,34 @@ def test_matches_torch_float8_e4m3fn():
     assert np.array_equal(e4m3_encode(x.astype(np.float64)), ref)
 
 
+def test_probs_hand_worked_row():
+    # p = [1/2, 1/4, 1/4]: p_max = 1/2 = 0.5 * 2^0, so k = 8 and the scaled
+    # row is [128, 64, 64]: codes 1.0 * 2^7 (field 14) and 1.0 * 2^6 (field 13)
+    b, k, p = probs_fp8(np.log([[0.5, 0.25, 0.25]]), np.array([0.0]), 1.0)
+    assert int(k[0]) == 8
+    assert b[0].tolist() == [0x70, 0x68, 0x68]
+    # p_max = 0.3 = 0.6 * 2^-1: k = 9, 0.3 * 512 = 153.6 -> 1.001b * 2^7 = 144
+    # or 1.010b * 2^7 = 160; 153.6 is nearer 160 (field 14, mantissa 2)
+    b, k, _ = probs_fp8(np.log([[0.3, 0.7 / 3, 0.7 / 3, 0.7 / 3]]), np.array([0.0]), 1.0)
+    assert int(k[0]) == 9 and int(b[0, 0]) == 0x72
+
+
 def test_probs_rows_sum_to_one_within_the_format():
     rng = np.random.default_rng(3)
     z = rng.normal(0, 3, size=(4, 5000))
     z[0, :10] = -np.inf
+    z[3] = rng.normal(0, 0.01, size=5000)  # nearly flat: every p near 1/5000
     for T in (1.0, 0.6):
         x = z / T
         lse = x.max(1) + np.log(np.exp(x - x.max(1, keepdims=True)).sum(1))
-        b, p = probs_fp8(z, lse, T)
+        b, k, p = probs_fp8(z, lse, T)
         np.testing.assert_allclose(p.sum(1), 1.0, rtol=1e-12)
         assert np.all(b[0, :10] == 0)
-        q = e4m3_decode(b)
-        # each probability within half a step of its code: relative 2^-4 for
-        # normals, absolute 2^-10 below 2^-6
-        assert np.all(np.abs(q - p) <= np.maximum(p * 2.0 ** -4, 2.0 ** -10))
+        scaled_max = np.ldexp(p.max(1), k)
+        assert np.all((scaled_max >= 128) & (scaled_max < 256))
+        q = np.ldexp(e4m3_decode(b), -k[:, None])
+        # within half a step of the scaled value: relative 2^-4 for normals,
+        # absolute 2^-10 (scaled) below 2^-6
+        assert np.all(np.abs(q - p) <= np.maximum(p * 2.0 ** -4, np.ldexp(2.0 ** -10, -k[:, None])))
+        assert np.all(b[3] > 0)  # a flat row keeps all of its mass
+        np.testing.assert_allclose(q.sum(1), 1.0, atol=0.03)

@@ -283,30 +283,55 @@ def _fp8_case():
 
 def test_fp8_exact_bytes_pass():
     z, lse = _fp8_case()
-    want, _ = oracle.probs_fp8(z, lse, 1.0)
-    assert parity.check_probs_fp8(z, lse, 1.0, want).ok()
+    want, k, _ = oracle.probs_fp8(z, lse, 1.0)
+    assert parity.check_probs_fp8(z, lse, 1.0, want, k).ok()
 
 
 def test_fp8_one_code_off_fails_away_from_a_midpoint():
     z, lse = _fp8_case()
-    want, p = oracle.probs_fp8(z, lse, 1.0)
+    want, k, p = oracle.probs_fp8(z, lse, 1.0)
     got = want.copy()
-    i = int(np.argmax(p[0]))
-    got[0, i] += 1
-    rep = parity.check_probs_fp8(z, lse, 1.0, got)
+    got[0, int(np.argmax(p[0]))] += 1
+    rep = parity.check_probs_fp8(z, lse, 1.0, got, k)
     assert not rep.ok() and "not a midpoint near-tie" in rep.failures[0]
 
 
+def test_fp8_wrong_scale_fails():
+    z, lse = _fp8_case()
+    want, k, _ = oracle.probs_fp8(z, lse, 1.0)
+    rep = parity.check_probs_fp8(z, lse, 1.0, want, k + 1)
+    assert not rep.ok() and "scale exponent" in rep.failures[0]
+
+
 def test_fp8_neighbour_at_a_midpoint_passes():
-    # a probability a hair (1e-7 relative) above the midpoint of codes 0x30 /
-    # 0x31 (0.5 / 0.5625): the oracle rounds up, the other code is certified
-    mid = (oracle.e4m3_decode(0x30) + oracle.e4m3_decode(0x31)) / 2
-    z = np.array([[np.log(mid * (1 + 1e-7))]])
+    # row [1/2, q, 1/2 - q]: p_max = 1/2 gives k = 8, and q 2^8 = 68 (1 + 1e-7)
+    # lies a hair above 68, the midpoint of codes 0x68 (64) and 0x69 (72): the
+    # oracle rounds up, and the other code is certified
+    q = 68.0 / 256 * (1 + 1e-7)
+    z = np.log(np.array([[0.5, q, 0.5 - q]]))
     lse = np.array([0.0])
-    want, _ = oracle.probs_fp8(z, lse, 1.0)
-    assert int(want[0, 0]) == 0x31
-    rep = parity.check_probs_fp8(z, lse, 1.0, np.array([[0x30]], np.uint8))
+    want, k, _ = oracle.probs_fp8(z, lse, 1.0)
+    assert int(k[0]) == 8 and int(want[0, 1]) == 0x69
+    got = want.copy()
+    got[0, 1] = 0x68
+    rep = parity.check_probs_fp8(z, lse, 1.0, got, k)
     assert rep.ok() and rep.token_ties == 1
-    # the same swap 1e-3 away from the midpoint fails
-    z = np.array([[np.log(mid * (1 + 1e-3))]])
-    assert not parity.check_probs_fp8(z, lse, 1.0, np.array([[0x30]], np.uint8)).ok()
+    # the same swap 1e-3 above the midpoint fails
+    q = 68.0 / 256 * (1 + 1e-3)
+    z = np.log(np.array([[0.5, q, 0.5 - q]]))
+    assert not parity.check_probs_fp8(z, lse, 1.0, got, k).ok()
+
+
+def test_fp8_scale_at_a_power_of_two_is_certified():
+    # p_max a hair above 1/2: the oracle takes k = 8; a float32 p_max a hair
+    # below 1/2 would take k = 9, and that is certified
+    row = np.array([[0.5 * (1 + 1e-7), 0.5 * (1 - 1e-7)]])
+    z = np.log(row)
+    lse = np.array([0.0])
+    want, k, p = oracle.probs_fp8(z, lse, 1.0)
+    assert int(k[0]) == 8
+    from oracle.flashhead_oracle import e4m3_encode
+    got = e4m3_encode(np.ldexp(p, 9))
+    rep = parity.check_probs_fp8(z, lse, 1.0, got, k + 1)
+    assert rep.ok(), rep.failures
+    assert rep.cluster_ties == 1
