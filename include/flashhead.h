@@ -171,8 +171,11 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
  *                 logit -inf.
  *   out_token, out_token_logit, out_lse: as for fh_forward, over the n b
  *                 retrieved tokens.
- * Per-stage launches only (stage 1, selection of p_max, the count, stage 2
- * over n probes, finish); stream-ordered, no host synchronisation.
+ * B = 1 runs the single launch of fh_forward (its selector takes the count
+ * and publishes only the kept probes); larger batches, stream capture and
+ * FH_PATH_MULTI run per-stage launches (stage 1, selection of p_max, the
+ * count, stage 2 over the kept probes, finish).  Stream-ordered, no host
+ * synchronisation.
  */
 fh_status fh_forward_adaptive(fh_engine* e, const void* h, int64_t B, int64_t p_max,
                               int64_t p_min, float tau, int mode, float temperature,

@@ -94,6 +94,15 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} is missing: build it with `python -m lm_output_head_amd.build` "
             "(there is no fallback implementation)")
+    # torch ships its own HIP runtime beside the system one this library
+    # links.  Loaded after this library, torch's runtime was the one that saw
+    # the GPU and ours reported no device (build() then smoke() in one
+    # process); loaded first, both work.  Importing torch loads its libraries
+    # without touching the GPU.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     for name, (args, res) in _SIGS.items():
         fn = getattr(lib, name)

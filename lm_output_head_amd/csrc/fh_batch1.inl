@@ -25,7 +25,12 @@ namespace fh {
 //                  selector: before its own rows it waits for the c scores,
 //                  selects the probes and publishes them as a bitset over
 //                  the clusters; each stage-2 workgroup finds the probes of
-//                  its rows by a prefix count over that bitset.
+//                  its rows by a prefix count over that bitset.  With the
+//                  adaptive count (tau > 0) stage 1 publishes raw scores, the
+//                  selector forms the keys, takes the top p, keeps the first
+//                  n of them in key order (adaptive_count) and publishes only
+//                  those; stage 2 then scores the n b rows the bitset's
+//                  total names and pads the rest of its range.
 //   G1+G2          the finisher: polls the G2 stage-2 partials and merges
 //                  them in index order.  G2 <= CUs - 1, so it finds a CU as
 //                  soon as stage 1 retires and its polls overlap stage 2.
@@ -61,6 +66,8 @@ struct FusedArgs {
   float temperature;
   float tprime;
   float zq;  // selection threshold quantile (select_quantile)
+  float tau;  // adaptive probe count: the mass to reach (0: a fixed p)
+  int pmin;   // adaptive: the smallest count
   uint64_t seed;
   int g1, g2;                   // stage-1 and stage-2 workgroup counts
   int rows1, rows2;             // rows per stage-1 / stage-2 workgroup
@@ -69,6 +76,7 @@ struct FusedArgs {
   unsigned long long* tsel;     // [ceil(c/32)] tagged bitset of the probes
   unsigned long long* tparts;   // [5 x g2] tagged Parts
   int32_t* out_clusters;        // [p] or null
+  int32_t* out_nprobe;          // [1] or null (adaptive)
   int32_t* out_ids;
   float* out_logits;
   int32_t* out_token;
@@ -134,6 +142,7 @@ union Batch1Shared {
 template <typename T, int MAXM, int KP, int QB, int MAXG>
 __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   __shared__ Batch1Shared sh;
+  __shared__ unsigned long long s_akey[kSelThreads];  // adaptive: the top p's sort keys
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int w = blockIdx.x;
@@ -148,7 +157,8 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     // the selection)
     auto sink = [&](int, int64_t r, int64_t, float s) {
       if (lane == 0) {
-        if (a.probe_sample) s = s / a.temperature + gumbel_at(a.seed, 0u, (uint32_t)r, 0u);
+        if (a.probe_sample && !(a.tau > 0.f))
+          s = s / a.temperature + gumbel_at(a.seed, 0u, (uint32_t)r, 0u);
         st_tagged(a.tscores + r, tag(a.epoch, __float_as_uint(saturate_key(s))));
       }
     };
@@ -218,14 +228,50 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
       ptr[i] = a.tscores + (live[i] ? k : 0);
     }
     if (!poll_tagged<KP>(ptr, live, a.epoch, a.err, raw)) gave_up = true;
+    const bool adaptive = a.tau > 0.f;
     float x[KP];
 #pragma unroll
     for (int i = 0; i < KP; ++i) x[i] = live[i] ? __uint_as_float(raw[i]) : -FLT_MAX;
+    MassTotal mt{0.f, 0.f};
+    if (adaptive) {  // x holds raw scores: the mass totals, then the keys
+      mt = mass_total<KP>(x, a.c, a.temperature, sh.sel.red[2]);
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const int k = (int)threadIdx.x + kSelThreads * i;
+        if (live[i]) x[i] = probe_key(x[i], a.probe_sample, a.temperature, a.seed, 0u, k);
+      }
+    }
     __syncthreads();
     select_bits<KP>(x, a.c, a.p, a.zq, sh.sel);
+    const uint32_t* pub = sh.sel.selbits;
+    if (adaptive) {
+      // the top p by key, sorted; the score of cluster k is its stage-1 word
+      auto score_of = [&](int k) {
+        return __uint_as_float((uint32_t)__hip_atomic_load(a.tscores + k, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT));
+      };
+      const int P2 = pow2_at_least(a.p);
+      if ((int)threadIdx.x >= a.p && (int)threadIdx.x < P2) s_akey[threadIdx.x] = 0ull;
+      emit_selected<KP>(a.c, [&](int pos, int k) {
+        s_akey[pos] = probe_sort_key(
+            probe_key(score_of(k), a.probe_sample, a.temperature, a.seed, 0u, k), k);
+      }, sh.sel);
+      __syncthreads();
+      bitonic_sort_desc(s_akey, P2);
+      int id;
+      const int n = adaptive_count(s_akey, a.p, a.pmin, a.tau, mt, a.temperature, score_of,
+                                   sh.sel.red[2], sh.sel.red_scan, &id);
+      // the kept set, in the (free) tie bitset
+      for (int t = threadIdx.x; t < (a.c + 31) / 32; t += kSelThreads) sh.sel.tiebits[t] = 0u;
+      __syncthreads();
+      if ((int)threadIdx.x < n) atomicOr(&sh.sel.tiebits[id >> 5], 1u << (id & 31));
+      __syncthreads();
+      pub = sh.sel.tiebits;
+      if (threadIdx.x == 0 && a.out_nprobe) a.out_nprobe[0] = n;
+    }
     // publish the chosen clusters as a bitset, one tagged word per 32
     for (int t = threadIdx.x; t < (a.c + 31) / 32; t += kSelThreads)
-      st_tagged(a.tsel + t, tag(a.epoch, sh.sel.selbits[t]));
+      st_tagged(a.tsel + t, tag(a.epoch, pub[t]));
     FH_TRACE(3);
     __syncthreads();  // sh.sel is reused below
   }
@@ -241,6 +287,7 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   // of the ascending probe list, read off the selector's bitset
   const int pos0 = (int)(r_lo / a.bsz);
   const int npos = r_hi > r_lo ? (int)((r_hi - 1) / a.bsz) - pos0 + 1 : 0;
+  int nkept = a.p;  // probes in the published bitset
   if (npos > 0) {
     const int nw = (a.c + 31) / 32;
     const int t = threadIdx.x;
@@ -259,6 +306,7 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     }
     int tot;
     int pos = block_exclusive_scan(__popc(word), sh.sel.red_scan, &tot);
+    nkept = min(tot, a.p);
     if (pos < pos0 + npos && pos + __popc(word) > pos0) {
       for (uint32_t bitsleft = word; bitsleft; bitsleft &= bitsleft - 1, ++pos) {
         if (pos < pos0 || pos >= pos0 + npos) continue;
@@ -271,6 +319,20 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   }
   __syncthreads();
   FH_TRACE(5);
+  int64_t r_end = r_hi;
+  if (a.tau > 0.f) {
+    // adaptive: only the n b rows of the n kept probes; the rest of this
+    // workgroup's range, and the probe positions past n it owns, are padding
+    const int64_t nr = (int64_t)nkept * a.bsz;
+    r_end = min(r_hi, nr);
+    for (int64_t r = max(r_lo, nr) + threadIdx.x; r < r_hi; r += 1024) {
+      if (a.out_ids) a.out_ids[r] = -1;
+      if (a.out_logits) a.out_logits[r] = -INFINITY;
+    }
+    if (a.out_clusters)
+      for (int pos = max(pos0, nkept) + (int)threadIdx.x; pos < pos0 + npos; pos += 1024)
+        if ((int64_t)pos * a.bsz >= r_lo) a.out_clusters[pos] = -1;
+  }
   Part part[1] = {part_empty()};
   // slot f of the clustering; with the cluster-contiguous copy of E it is
   // also the row, else the row is the token C2T[f]
@@ -288,7 +350,7 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   };
   // four rows in flight per wave when the register slice allows it
   wave_rows<T, MAXM, 1, (MAXM <= 4 ? 4 : 2)>(static_cast<const T*>(a.Ec ? a.Ec : a.E), a.d, lane,
-                                             hv, 1, r_lo + wave, r_hi, 16, src_of, tok_of, sink);
+                                             hv, 1, r_lo + wave, r_end, 16, src_of, tok_of, sink);
   // sh.probes is read above; sh.parts aliases it
   const bool wg_bad = __syncthreads_or(gave_up);
   Part wg = block_merge_parts<16, 1>(part, 1, sh.parts);
@@ -316,6 +378,7 @@ static FusedArgs fused_args(const FusedLaunch& f) {
   a.g1 = batch1_stage1_blocks(k.c, f.cus);
   a.g2 = batch1_stage2_blocks(f.p, k.b, f.cus);
   a.epoch = f.epoch; a.tscores = f.tscores; a.tsel = f.tsel; a.tparts = f.tparts;
+  a.tau = f.tau; a.pmin = f.pmin; a.out_nprobe = f.out_nprobe;
   a.out_clusters = f.out_clusters; a.out_ids = f.out_ids; a.out_logits = f.out_logits;
   a.out_token = f.out_token; a.out_logit = f.out_logit; a.out_lse = f.out_lse;
   a.err = f.err;

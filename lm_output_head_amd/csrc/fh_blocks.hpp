@@ -666,6 +666,144 @@ __device__ __forceinline__ void emit_selected(int c, Emit emit, SelShared& sh) {
 }
 
 // ======================================================================
+// Adaptive probe count (FlashHead explainer §1.2.2: the number of probes
+// follows the distribution of h; §4.2: fewer probes for confident queries).
+// Of the top pmax probes by selection key, keep the first n in key order
+// (descending, ties to the smaller id) whose softmax(s/T) mass reaches tau of
+// the total over all c clusters, n clamped to [pmin, pmax].  Every step has
+// a fixed order (block trees, a bitonic network, a fixed scan), so the count
+// is deterministic.  All helpers are called by all 1024 threads.
+// ======================================================================
+struct MassTotal {
+  float M;  // max_k s_k / T
+  float W;  // sum_k exp(s_k / T - M)
+};
+
+// Max (or sum) over the 1024 threads: waves first, then the 16 wave values
+// in one row; the result is uniform.  `red` (16 floats) is free on return.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce_f(float x, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = MAX ? wave_max(x) : wave_sum(x);
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  float t = lane < kSelWaves ? red[lane] : (MAX ? -INFINITY : 0.f);
+  t = MAX ? row_allreduce(t, [](float a, float b) { return fmaxf(a, b); })
+          : row_allreduce(t, [](float a, float b) { return a + b; });
+  const float r = readlane_f(t, 0);
+  __syncthreads();
+  return r;
+}
+
+// M and W of the scores s[k] of clusters k = tid + 1024 i (entries past c
+// ignored).
+template <int KP>
+__device__ __forceinline__ MassTotal mass_total(const float (&s)[KP], int c, float temperature,
+                                                float* red) {
+  float xs[KP];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const bool live = (int)threadIdx.x + kSelThreads * i < c;
+    xs[i] = live ? s[i] / temperature : -INFINITY;
+    mx = fmaxf(mx, xs[i]);
+  }
+  MassTotal mt;
+  mt.M = block_reduce_f<true>(mx, red);
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < KP; ++i)
+    acc += (int)threadIdx.x + kSelThreads * i < c ? __expf(xs[i] - mt.M) : 0.f;
+  mt.W = block_reduce_f<false>(acc, red);
+  return mt;
+}
+
+// The selection key of cluster k with score s: s, or s/T + G(seed, row, k, 0)
+// for sampled probes, saturated (the key k_select and the batch-1 stage 1
+// form).
+__device__ __forceinline__ float probe_key(float s, int sample, float temperature, uint64_t seed,
+                                           uint32_t row, int k) {
+  if (sample) s = s / temperature + gumbel_at(seed, row, (uint32_t)k, 0u);
+  return saturate_key(s);
+}
+
+// 64-bit sort image of (key, k): larger key first, then the smaller id.  Every
+// image is above 0, which pads a sort.
+__device__ __forceinline__ unsigned long long probe_sort_key(float key, int k) {
+  return ((unsigned long long)ordered_bits(key) << 32) |
+         (unsigned long long)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+__device__ __forceinline__ int pow2_at_least(int n) {
+  int p2 = 1;
+  while (p2 < n) p2 <<= 1;
+  return p2;
+}
+
+// Bitonic sort of key[0 .. P2) into descending order (P2 a power of two,
+// <= 1024); a barrier ends every step.
+__device__ __forceinline__ void bitonic_sort_desc(unsigned long long* key, int P2) {
+  const int i = threadIdx.x;
+  for (int k = 2; k <= P2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int ixj = i ^ j;
+      if (i < P2 && ixj > i) {
+        const unsigned long long a = key[i], b = key[ixj];
+        if ((i & k) == 0 ? a < b : a > b) {
+          key[i] = b;
+          key[ixj] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Inclusive prefix sum of x over the 1024 threads in index order (float; the
+// same fixed pattern as block_exclusive_scan).
+__device__ __forceinline__ float block_inclusive_scan_f(float x, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x += dpp_f<0x111>(x);
+  x += dpp_f<0x112>(x);
+  x += dpp_f<0x114>(x);
+  x += dpp_f<0x118>(x);
+  const float t0 = readlane_f(x, 15), t1 = readlane_f(x, 31), t2 = readlane_f(x, 47);
+  const int row = lane >> 4;
+  x = x + (row >= 1 ? t0 : 0.f) + (row >= 2 ? t1 : 0.f) + (row >= 3 ? t2 : 0.f);
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  float t = lane < kSelWaves ? red[lane] : 0.f;
+  t += dpp_f<0x111>(t);
+  t += dpp_f<0x112>(t);
+  t += dpp_f<0x114>(t);
+  t += dpp_f<0x118>(t);
+  const float before = wave > 0 ? readlane_f(t, wave - 1) : 0.f;
+  __syncthreads();
+  return before + x;
+}
+
+// The count n over skey[0 .. pmax), sorted by bitonic_sort_desc: thread t
+// takes the t-th probe (its id to *id, else -1), the weights exp(s/T - M) are
+// scanned in key order, and n - 1 is the number of prefixes short of tau W.
+template <typename ScoreOf>
+__device__ __forceinline__ int adaptive_count(const unsigned long long* skey, int pmax, int pmin,
+                                              float tau, const MassTotal& mt, float temperature,
+                                              ScoreOf score_of, float* redf, int* red_cnt,
+                                              int* id) {
+  const int t = threadIdx.x;
+  float w = 0.f;
+  *id = -1;
+  if (t < pmax) {
+    *id = (int)(0xFFFFFFFFu - (uint32_t)(skey[t] & 0xFFFFFFFFull));
+    w = __expf(score_of(*id) / temperature - mt.M);
+  }
+  const float cum = block_inclusive_scan_f(w, redf);
+  int below;
+  (void)block_exclusive_scan(t < pmax && cum < tau * mt.W ? 1 : 0, red_cnt, &below);
+  return min(max(below + 1, pmin), pmax);
+}
+
+// ======================================================================
 // Finisher: merge n Parts in a fixed order (threads stride, then a tree).
 // ======================================================================
 // Merge n Parts: each thread folds a strided subset in index order (eight

@@ -576,6 +576,41 @@ fh_status fh_forward_adaptive(fh_engine* e, const void* h, int64_t B, int64_t p_
   const float tprime = token_sample ? temperature : 1.f;
   int32_t* S = out_clusters ? out_clusters : e->sel;
   int32_t* np = out_nprobe ? out_nprobe : e->nprobe;
+
+  // B = 1: the single launch, its selector taking the count (as fh_forward)
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &capture) != hipSuccess) capture = hipStreamCaptureStatusNone;
+  if (B == 1 && e->path == FH_PATH_AUTO && capture == hipStreamCaptureStatusNone &&
+      fh::batch1_fits(p_max, e->b, e->cus)) {
+    fh::FusedLaunch f{};
+    f.ctx = &k;
+    f.cus = e->cus;
+    f.h = h;
+    f.p = (int)p_max;
+    f.probe_sample = probe_sample;
+    f.token_sample = token_sample;
+    f.temperature = temperature;
+    f.tprime = tprime;
+    f.seed = seed;
+    e->epoch = e->epoch == 0xFFFFFFFFu ? 1u : e->epoch + 1u;
+    f.epoch = e->epoch;
+    f.tscores = e->tagged;
+    f.tsel = e->tagged + fh::batch1_off_sel(e->c);
+    f.tparts = e->tagged + fh::batch1_off_parts(e->c);
+    f.tau = tau;
+    f.pmin = (int)p_min;
+    f.out_nprobe = out_nprobe;
+    f.out_clusters = out_clusters;
+    f.out_ids = out_ids;
+    f.out_logits = out_logits;
+    f.out_token = out_token;
+    f.out_logit = out_token_logit;
+    f.out_lse = out_lse;
+    f.err = e->sync;
+    hipError_t r = timed(e, st, "batch1_adaptive", [&] { return fh::launch_batch1(f); });
+    return r == hipSuccess ? FH_OK : hip_fail(r, "batch-1 launch");
+  }
+
   // stage 1 keeps the raw scores (the mass needs them); the selection forms
   // the keys itself
   hipError_t r = launch_stage1(e, st, k, h, B, e->scores);
@@ -585,16 +620,27 @@ fh_status fh_forward_adaptive(fh_engine* e, const void* h, int64_t B, int64_t p_
                              (int)p_max);
   });
   if (r != hipSuccess) return hip_fail(r, "select launch");
+  // batches of bf16 queries: the cluster-major stage 2 over the kept probes'
+  // bitsets, each kept cluster's rows read once for all queries keeping it
+  const bool cm = e->dtype == FH_BF16 && fh::gather_cm_fits((int)B, p_max, e->c);
   r = timed(e, st, "adapt", [&] {
     return fh::launch_adapt(k, e->scores, (int)B, (int)p_max, (int)p_min, tau, probe_sample,
-                            temperature, seed, S, np, out_ids, out_logits);
+                            temperature, seed, S, np, out_ids, out_logits,
+                            cm ? e->mbits : nullptr, cm ? e->mpre : nullptr);
   });
   if (r != hipSuccess) return hip_fail(r, "adaptive count launch");
   int64_t nparts = 0;
-  r = timed(e, st, "gather", [&] {
-    return fh::launch_gather(k, h, (int)B, S, (int)p_max, token_sample, tprime, seed, out_ids,
-                             out_logits, e->parts, &nparts, -1, np);
-  });
+  if (cm)
+    r = timed(e, st, "gather_cm", [&] {
+      return fh::launch_gather_cm(k, e->cus, h, (int)B, (int)p_max, e->mbits, e->mpre,
+                                  token_sample, tprime, seed, out_ids, out_logits, e->parts,
+                                  &nparts);
+    });
+  else
+    r = timed(e, st, "gather", [&] {
+      return fh::launch_gather(k, h, (int)B, S, (int)p_max, token_sample, tprime, seed, out_ids,
+                               out_logits, e->parts, &nparts, -1, np);
+    });
   if (r != hipSuccess) return hip_fail(r, "gather launch");
   r = timed(e, st, "finish", [&] {
     return fh::launch_finish(k, e->parts, (int)B, nparts, out_token, out_token_logit, out_lse);

@@ -82,9 +82,12 @@ hipError_t launch_gather(const KernelCtx& k, const void* h, int B, const int32_t
 // mass reaches tau of all c clusters, n clamped to [pmin, pmax] (pmax <= 1024).
 // Rewrites S (n ascending, then -1), writes nprobe [B], and pads the retrieved
 // outputs [B x pmax b] (if non-null) past n b with id -1 and logit -inf.
+// With mbits/mpre non-null also the kept probes' bitsets and earlier-word
+// counts, word-major [ceil(c/32) x B], for launch_gather_cm.
 hipError_t launch_adapt(const KernelCtx& k, const float* scores, int B, int pmax, int pmin,
                         float tau, int sample, float temperature, uint64_t seed, int32_t* S,
-                        int32_t* nprobe, int32_t* out_ids, float* out_logits);
+                        int32_t* nprobe, int32_t* out_ids, float* out_logits,
+                        uint32_t* mbits = nullptr, int32_t* mpre = nullptr);
 // batch-shared probes: summed scores, and one probe list broadcast to every row
 hipError_t launch_sum_rows(const KernelCtx& k, const float* scores, int B, float* out);
 hipError_t launch_broadcast_row(const KernelCtx& k, const int32_t* src, int n, int B,
@@ -144,6 +147,9 @@ struct FusedLaunch {
   unsigned long long* tscores;    // [c] tagged scores (zeroed at create)
   unsigned long long* tsel;       // [ceil(c/32)] tagged probe bitset (zeroed at create)
   unsigned long long* tparts;     // [5 x batch1_slots2(cus)] (zeroed at create)
+  float tau = 0.f;                // adaptive probe count: mass to reach, or 0 (fixed p)
+  int pmin = 1;                   // adaptive: the smallest count (p is the largest)
+  int32_t* out_nprobe = nullptr;  // adaptive: [1] or null
   int32_t* out_clusters;          // [p] or null
   int32_t* out_ids;
   float* out_logits;

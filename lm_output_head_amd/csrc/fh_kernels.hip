@@ -237,13 +237,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
 
 // ---- adaptive probe count (explainer §1.2.2, dynamic adjustment of the
 // probe count to the query; §4.2, fewer probes for confident queries).
-// One workgroup per query, after k_select has taken the top pmax keys.  The
-// pmax probes are sorted by selection key (descending, ties to the smaller
-// id) with a bitonic sort of 64-bit images (key image << 32 | ~id) in LDS; the
-// softmax(s/T) weights are scanned in that order, and the count n is the
-// first prefix holding tau of the total weight over all c clusters, clamped
-// to [pmin, pmax].  S is rewritten in place: the n kept probes ascending,
-// then -1; nprobe[q] = n; retrieved slots past n b get id -1 and logit -inf.
+// One workgroup per query, after k_select has taken the top pmax keys (see
+// adaptive_count in fh_blocks.hpp for the rule).  S is rewritten in place:
+// the n kept probes ascending, then -1; nprobe[q] = n; retrieved slots past
+// n b get id -1 and logit -inf; with mbits non-null the kept set also goes
+// out as bitset words for the cluster-major stage 2.
 struct AdaptShared {
   unsigned long long key[kSelThreads];
   uint32_t keep[kSelMaxC / 32];
@@ -252,106 +250,38 @@ struct AdaptShared {
   int red_cnt[kSelWaves];
 };
 
-// Inclusive prefix sum of x over the 1024 threads in index order (float; the
-// same fixed pattern as block_exclusive_scan).
-__device__ __forceinline__ float block_inclusive_scan_f(float x, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  x += dpp_f<0x111>(x);
-  x += dpp_f<0x112>(x);
-  x += dpp_f<0x114>(x);
-  x += dpp_f<0x118>(x);
-  const float t0 = readlane_f(x, 15), t1 = readlane_f(x, 31), t2 = readlane_f(x, 47);
-  const int row = lane >> 4;
-  x = x + (row >= 1 ? t0 : 0.f) + (row >= 2 ? t1 : 0.f) + (row >= 3 ? t2 : 0.f);
-  if (lane == 63) red[wave] = x;
-  __syncthreads();
-  float t = lane < kSelWaves ? red[lane] : 0.f;
-  t += dpp_f<0x111>(t);
-  t += dpp_f<0x112>(t);
-  t += dpp_f<0x114>(t);
-  t += dpp_f<0x118>(t);
-  const float before = wave > 0 ? readlane_f(t, wave - 1) : 0.f;
-  return before + x;
-}
-
-// Max (or sum) over the 1024 threads: waves first, then the 16 wave values
-// in one row; the result is uniform.  `red` is free again on return.
-template <bool MAX>
-__device__ __forceinline__ float block_reduce_f(float x, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  x = MAX ? wave_max(x) : wave_sum(x);
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  float t = lane < kSelWaves ? red[lane] : (MAX ? -INFINITY : 0.f);
-  t = MAX ? row_allreduce(t, [](float a, float b) { return fmaxf(a, b); })
-          : row_allreduce(t, [](float a, float b) { return a + b; });
-  const float r = readlane_f(t, 0);
-  __syncthreads();
-  return r;
-}
-
 template <int KP>
 __global__ __launch_bounds__(kSelThreads) void k_adapt(
     const float* __restrict__ scores, int c, int pmax, int pmin, float tau, int sample,
     float temperature, uint64_t seed, int32_t* __restrict__ S, int32_t* __restrict__ nprobe,
-    int b, int32_t* __restrict__ out_ids, float* __restrict__ out_logits) {
+    int b, int32_t* __restrict__ out_ids, float* __restrict__ out_logits,
+    uint32_t* __restrict__ mbits, int32_t* __restrict__ mpre) {
   __shared__ AdaptShared sh;
   const int q = blockIdx.x, tid = threadIdx.x;
   const float* sq = scores + (int64_t)q * c;
   int32_t* Sq = S + (int64_t)q * pmax;
   for (int w = tid; w < (c + 31) / 32; w += kSelThreads) sh.keep[w] = 0u;
-  // total weight W = sum_k exp(s_k / T - M), M = max_k s_k / T
   float x[KP];
-  float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < KP; ++i) {
     const int k = tid + kSelThreads * i;
-    x[i] = k < c ? sq[k] / temperature : -INFINITY;
-    mx = fmaxf(mx, x[i]);
+    x[i] = k < c ? sq[k] : -INFINITY;
   }
-  const float M = block_reduce_f<true>(mx, sh.redf);
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < KP; ++i) acc += tid + kSelThreads * i < c ? __expf(x[i] - M) : 0.f;
-  const float W = block_reduce_f<false>(acc, sh.redf);
-  // the selected probes by key: the same key as k_select takes
-  int P2 = 1;
-  while (P2 < pmax) P2 <<= 1;
+  const MassTotal mt = mass_total<KP>(x, c, temperature, sh.redf);
+  // the selected probes by key (the same key as k_select takes)
+  const int P2 = pow2_at_least(pmax);
   int kj = -1;
   if (tid < pmax) {
     kj = min(max(Sq[tid], 0), c - 1);
-    float v = sq[kj];
-    if (sample) v = v / temperature + gumbel_at(seed, (uint32_t)q, (uint32_t)kj, 0u);
-    sh.key[tid] = ((unsigned long long)ordered_bits(saturate_key(v)) << 32) |
-                  (unsigned long long)(0xFFFFFFFFu - (uint32_t)kj);
+    sh.key[tid] = probe_sort_key(probe_key(sq[kj], sample, temperature, seed, (uint32_t)q, kj), kj);
   } else if (tid < P2) {
     sh.key[tid] = 0ull;  // below every real key: sorts last
   }
   __syncthreads();
-  for (int k = 2; k <= P2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int i = tid, ixj = tid ^ j;
-      if (i < P2 && ixj > i) {
-        const unsigned long long a = sh.key[i], bb = sh.key[ixj];
-        if ((i & k) == 0 ? a < bb : a > bb) {
-          sh.key[i] = bb;
-          sh.key[ixj] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // weights in key order, their prefix sums, and the count below tau W
-  int id = -1;
-  float w = 0.f;
-  if (tid < pmax) {
-    id = (int)(0xFFFFFFFFu - (uint32_t)(sh.key[tid] & 0xFFFFFFFFull));
-    w = __expf(sq[id] / temperature - M);
-  }
-  const float cum = block_inclusive_scan_f(w, sh.redf);
-  int below;
-  (void)block_exclusive_scan(tid < pmax && cum < tau * W ? 1 : 0, sh.red_cnt, &below);
-  const int n = min(max(below + 1, pmin), pmax);
+  bitonic_sort_desc(sh.key, P2);
+  int id;
+  const int n = adaptive_count(sh.key, pmax, pmin, tau, mt, temperature,
+                               [&](int k) { return sq[k]; }, sh.redf, sh.red_cnt, &id);
   if (tid < n) atomicOr(&sh.keep[id >> 5], 1u << (id & 31));
   __syncthreads();
   const int kept = tid < pmax && (sh.keep[kj >> 5] & (1u << (kj & 31))) ? 1 : 0;
@@ -360,6 +290,18 @@ __global__ __launch_bounds__(kSelThreads) void k_adapt(
   if (kept) Sq[pos] = kj;
   if (tid < pmax && tid >= n) Sq[tid] = -1;
   if (tid == 0) nprobe[q] = n;
+  if (mbits) {
+    // the kept probes as bitset words and earlier-word counts, word-major
+    // [W x B], for the cluster-major stage 2
+    const int W = (c + 31) / 32;
+    const uint32_t word = tid < W ? sh.keep[tid] : 0u;
+    int wt;
+    const int before = block_exclusive_scan(__popc(word), sh.red_cnt, &wt);
+    if (tid < W) {
+      mbits[(int64_t)tid * gridDim.x + q] = word;
+      mpre[(int64_t)tid * gridDim.x + q] = before;
+    }
+  }
   const int64_t nr = (int64_t)pmax * b;
   for (int64_t r = (int64_t)n * b + tid; r < nr; r += kSelThreads) {
     if (out_ids) out_ids[(int64_t)q * nr + r] = -1;
@@ -520,13 +462,14 @@ hipError_t launch_select(const KernelCtx& k, const float* scores, int B, int p, 
 
 hipError_t launch_adapt(const KernelCtx& k, const float* scores, int B, int pmax, int pmin,
                         float tau, int sample, float temperature, uint64_t seed, int32_t* S,
-                        int32_t* nprobe, int32_t* out_ids, float* out_logits) {
+                        int32_t* nprobe, int32_t* out_ids, float* out_logits, uint32_t* mbits,
+                        int32_t* mpre) {
   if (pmax < 1 || pmax > kSelThreads || pmin < 1 || pmin > pmax) return hipErrorInvalidValue;
   const dim3 grid((unsigned)B), block(kSelThreads);
   const int c = (int)k.c, b = (int)k.b;
   switch (sel_keys_per_thread(k.c)) {
 #define FH_CASE(KK) \
-  case KK: hipLaunchKernelGGL((k_adapt<KK>), grid, block, 0, k.stream, scores, c, pmax, pmin, tau, sample, temperature, seed, S, nprobe, b, out_ids, out_logits); break;
+  case KK: hipLaunchKernelGGL((k_adapt<KK>), grid, block, 0, k.stream, scores, c, pmax, pmin, tau, sample, temperature, seed, S, nprobe, b, out_ids, out_logits, mbits, mpre); break;
     FH_CASE(1) FH_CASE(2) FH_CASE(8) FH_CASE(16)
 #undef FH_CASE
     default: return hipErrorInvalidValue;

@@ -65,8 +65,14 @@ def test_tiny_graded_batch(mode, T, tau):
 def test_tiny_clamps_and_batch1():
     pb, head, H, Hf, ref = _setup("tiny", 32)
     _run(head, ref, H, Hf, 64, 8, 0.9, 0, 0.3, 0, "tiny clamp [8, 64]")
-    for q in (0, 31):  # B = 1: the per-stage launches, not the single-launch kernel
-        _run(head, ref, H[q:q + 1], Hf[q:q + 1], 128, 1, 0.9, 3, 0.5, 9, f"tiny B=1 row {q}")
+    # B = 1: the single launch (its selector takes the count), then the
+    # per-stage launches
+    for path in ("auto", "multi"):
+        head.set_path(path)
+        for q in (0, 13, 31):
+            for mode, T in ((0, 0.3), (3, 0.5)):
+                _run(head, ref, H[q:q + 1], Hf[q:q + 1], 128, 1, 0.9, mode, T, 9 + q,
+                     f"tiny B=1 {path} row {q}")
     head.close()
 
 
@@ -94,6 +100,22 @@ def test_llama_graded_batch(quant, mode, T, tau):
     n = out["nprobe"]
     if mode == 0:
         assert n.min() == 1 and n.max() == 512  # both kinds of query in the batch
+    head.close()
+
+
+@pytest.mark.parametrize("quant", ["none", "int4"])
+def test_llama_batch1_single_launch(quant):
+    """B = 1 through the single launch at the Llama-3.2-1B shape: graded
+    queries from diffuse (p_max probes) to confident (one probe), greedy and
+    sampled; every row against the oracle."""
+    pb, head, H, Hf, ref = _setup("llama32_1b", 12, quant=quant, max_batch=1)
+    counts = []
+    for q in range(12):
+        mode = (0, 1, 3)[q % 3]
+        out = _run(head, ref, H[q:q + 1], Hf[q:q + 1], 512, 1, 0.5, mode, 0.3, 40 + q,
+                   f"llama {quant} B=1 row {q}")
+        counts.append(int(out["nprobe"][0]))
+    assert min(counts) == 1 and max(counts) == 512, counts
     head.close()
 
 
