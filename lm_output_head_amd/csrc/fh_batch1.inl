@@ -86,6 +86,10 @@ struct FusedArgs {
 };
 
 constexpr unsigned kSpinLimit = 1u << 20;
+// s_sleep argument between polling rounds (units of 64 clocks)
+#ifndef FH_POLL_SLEEP
+#define FH_POLL_SLEEP 1
+#endif
 
 __device__ __forceinline__ unsigned long long tag(unsigned epoch, uint32_t bits) {
   return ((unsigned long long)epoch << 32) | bits;
@@ -118,7 +122,7 @@ __device__ __forceinline__ bool poll_tagged(unsigned long long* const (&p)[N],
       for (int i = 0; i < N; ++i) out[i] = (uint32_t)v[i];
       return false;
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(FH_POLL_SLEEP);
 #pragma unroll
     for (int i = 0; i < N; ++i)
       if ((unsigned)(v[i] >> 32) != epoch)
@@ -142,7 +146,8 @@ union Batch1Shared {
 template <typename T, int MAXM, int KP, int QB, int MAXG>
 __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   __shared__ Batch1Shared sh;
-  __shared__ unsigned long long s_akey[kSelThreads];  // adaptive: the top p's sort keys
+  __shared__ unsigned long long s_akey[kSelThreads];  // adaptive: the top p's sort images
+  __shared__ float s_aval[kSelThreads];               // and their scores
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int w = blockIdx.x;
@@ -229,44 +234,92 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     }
     if (!poll_tagged<KP>(ptr, live, a.epoch, a.err, raw)) gave_up = true;
     const bool adaptive = a.tau > 0.f;
-    float x[KP];
+    float x[KP], sraw[KP];
 #pragma unroll
     for (int i = 0; i < KP; ++i) x[i] = live[i] ? __uint_as_float(raw[i]) : -FLT_MAX;
     MassTotal mt{0.f, 0.f};
     if (adaptive) {  // x holds raw scores: the mass totals, then the keys
       mt = mass_total<KP>(x, a.c, a.temperature, sh.sel.red[2]);
+      FH_TRACE(16);
 #pragma unroll
       for (int i = 0; i < KP; ++i) {
         const int k = (int)threadIdx.x + kSelThreads * i;
+        sraw[i] = x[i];
         if (live[i]) x[i] = probe_key(x[i], a.probe_sample, a.temperature, a.seed, 0u, k);
       }
     }
     __syncthreads();
     select_bits<KP>(x, a.c, a.p, a.zq, sh.sel);
+    FH_TRACE(17);
     const uint32_t* pub = sh.sel.selbits;
     if (adaptive) {
-      // the top p by key, sorted; the score of cluster k is its stage-1 word
-      auto score_of = [&](int k) {
-        return __uint_as_float((uint32_t)__hip_atomic_load(a.tscores + k, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT));
-      };
-      const int P2 = pow2_at_least(a.p);
-      if ((int)threadIdx.x >= a.p && (int)threadIdx.x < P2) s_akey[threadIdx.x] = 0ull;
-      emit_selected<KP>(a.c, [&](int pos, int k) {
-        s_akey[pos] = probe_sort_key(
-            probe_key(score_of(k), a.probe_sample, a.temperature, a.seed, 0u, k), k);
-      }, sh.sel);
-      __syncthreads();
-      bitonic_sort_desc(s_akey, P2);
-      int id;
-      const int n = adaptive_count(s_akey, a.p, a.pmin, a.tau, mt, a.temperature, score_of,
-                                   sh.sel.red[2], sh.sel.red_scan, &id);
-      // the kept set, in the (free) tie bitset
-      for (int t = threadIdx.x; t < (a.c + 31) / 32; t += kSelThreads) sh.sel.tiebits[t] = 0u;
-      __syncthreads();
-      if ((int)threadIdx.x < n) atomicOr(&sh.sel.tiebits[id >> 5], 1u << (id & 31));
-      __syncthreads();
-      pub = sh.sel.tiebits;
+      // this thread's selected probes: their weight and the top sort image
+      uint32_t mine = 0u;
+      float wsel = 0.f, best_s = 0.f;
+      unsigned long long best = 0ull;
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const int k = (int)threadIdx.x + kSelThreads * i;
+        if (live[i] && (sh.sel.selbits[k >> 5] >> (k & 31)) & 1u) {
+          mine |= 1u << i;
+          wsel += __expf(sraw[i] / a.temperature - mt.M);
+          const unsigned long long img = probe_sort_key(x[i], k);
+          if (img > best) {
+            best = img;
+            best_s = sraw[i];
+          }
+        }
+      }
+      unsigned long long top = 0ull;
+      int n = adaptive_fast(wsel, best, best_s, a.p, a.pmin, a.tau, mt, a.temperature,
+                            sh.sel.red[2], s_akey, &top);
+      if (n == 1) {  // the top probe alone
+        for (int t = threadIdx.x; t < (a.c + 31) / 32; t += kSelThreads) sh.sel.tiebits[t] = 0u;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          const int id = (int)(0xFFFFFFFFu - (uint32_t)(top & 0xFFFFFFFFull));
+          sh.sel.tiebits[id >> 5] = 1u << (id & 31);
+        }
+        __syncthreads();
+        pub = sh.sel.tiebits;
+      } else if (n == 0) {
+        // the general case: file the top p's sort images and scores at slots
+        // from a prefix count, sort them, scan the weights in key order
+        const int P2 = pow2_at_least(a.p);
+        int filed;
+        int slot = block_exclusive_scan(__popc(mine), sh.sel.red_out, &filed);
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+          if ((mine >> i) & 1u) {
+            if (slot < a.p) {  // the selection flags exactly p
+              s_akey[slot] = probe_sort_key(x[i], (int)threadIdx.x + kSelThreads * i);
+              s_aval[slot] = sraw[i];
+            }
+            ++slot;
+          }
+        }
+        __syncthreads();
+        unsigned long long skey = 0ull;  // padding sorts below every real key
+        float sval = 0.f;
+        if ((int)threadIdx.x < a.p) {
+          skey = s_akey[threadIdx.x];
+          sval = s_aval[threadIdx.x];
+        }
+        FH_TRACE(20);
+        bitonic_sort_desc(skey, sval, P2, s_akey, s_aval);
+        FH_TRACE(18);
+        int id;
+        n = adaptive_count(skey, sval, a.p, a.pmin, a.tau, mt, a.temperature, sh.sel.red[2],
+                           sh.sel.red_scan, &id);
+        // the kept set, in the (free) tie bitset
+        for (int t = threadIdx.x; t < (a.c + 31) / 32; t += kSelThreads) sh.sel.tiebits[t] = 0u;
+        __syncthreads();
+        if ((int)threadIdx.x < n) atomicOr(&sh.sel.tiebits[id >> 5], 1u << (id & 31));
+        __syncthreads();
+        pub = sh.sel.tiebits;
+      }
+      // n == p: all selected probes, the selection's own bitset
+      FH_TRACE(19);
       if (threadIdx.x == 0 && a.out_nprobe) a.out_nprobe[0] = n;
     }
     // publish the chosen clusters as a bitset, one tagged word per 32
@@ -434,3 +487,12 @@ hipError_t FH_BATCH1_ENTRY(const FusedLaunch& f) {
 }
 
 }  // namespace fh
+
+#ifdef FH_PHASE_TRACE
+// Trace builds only: copy this variant's phase timestamps to the host.
+#define FH_B1_CAT2(a, b) a##b
+#define FH_B1_CAT(a, b) FH_B1_CAT2(a, b)
+extern "C" int FH_B1_CAT(FH_BATCH1_ENTRY, _trace_read)(void* dst, size_t bytes) {
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(fh::g_fh_trace), bytes) == hipSuccess ? 0 : -1;
+}
+#endif

@@ -22,7 +22,7 @@ namespace fh {
 // Optional per-workgroup phase timestamps for performance probes (off in
 // the library build): slot s, workgroup w -> wall clock at phase s.
 #ifdef FH_PHASE_TRACE
-__device__ unsigned long long g_fh_trace[16][4096];
+__device__ unsigned long long g_fh_trace[24][4096];
 #define FH_TRACE(slot) \
   if (threadIdx.x == 0 && blockIdx.x < 4096) g_fh_trace[slot][blockIdx.x] = wall_clock64();
 __device__ __forceinline__ void g_fh_trace_cnt(int n) { g_fh_trace[15][blockIdx.x] = (unsigned long long)n; }
@@ -740,21 +740,43 @@ __device__ __forceinline__ int pow2_at_least(int n) {
   return p2;
 }
 
-// Bitonic sort of key[0 .. P2) into descending order (P2 a power of two,
-// <= 1024); a barrier ends every step.
-__device__ __forceinline__ void bitonic_sort_desc(unsigned long long* key, int P2) {
+// Bitonic sort into descending order of P2 elements (P2 a power of two,
+// <= 1024), one per thread: thread i holds element i in (key, val) and
+// returns holding the i-th largest key with its val.  A compare-exchange at
+// distance j < 64 stays inside the wave (lane shuffles, no barrier); only the
+// steps with j >= 64 exchange through lds_key / lds_val ([P2] each), with a
+// barrier on each side.  Called by all 1024 threads.
+__device__ __forceinline__ void bitonic_sort_desc(unsigned long long& key, float& val, int P2,
+                                                  unsigned long long* lds_key, float* lds_val) {
   const int i = threadIdx.x;
   for (int k = 2; k <= P2; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const int ixj = i ^ j;
-      if (i < P2 && ixj > i) {
-        const unsigned long long a = key[i], b = key[ixj];
-        if ((i & k) == 0 ? a < b : a > b) {
-          key[i] = b;
-          key[ixj] = a;
+      unsigned long long okey;
+      float oval;
+      if (j < 64) {
+        const uint32_t lo = __shfl_xor((uint32_t)key, j);
+        const uint32_t hi = __shfl_xor((uint32_t)(key >> 32), j);
+        okey = ((unsigned long long)hi << 32) | lo;
+        oval = __shfl_xor(val, j);
+      } else {
+        __syncthreads();  // the previous exchange's reads are done
+        if (i < P2) {
+          lds_key[i] = key;
+          lds_val[i] = val;
         }
+        __syncthreads();
+        okey = i < P2 ? lds_key[i ^ j] : 0ull;
+        oval = i < P2 ? lds_val[i ^ j] : 0.f;
       }
-      __syncthreads();
+      // in a descending block (i & k) == 0 the lower index keeps the larger
+      // element; in an ascending one, the smaller
+      const bool lower = (i & j) == 0;
+      const bool want_larger = ((i & k) == 0) == lower;
+      const bool take = want_larger ? okey > key : okey < key;
+      if (i < P2 && take) {
+        key = okey;
+        val = oval;
+      }
     }
   }
 }
@@ -782,20 +804,65 @@ __device__ __forceinline__ float block_inclusive_scan_f(float x, float* red) {
   return before + x;
 }
 
-// The count n over skey[0 .. pmax), sorted by bitonic_sort_desc: thread t
-// takes the t-th probe (its id to *id, else -1), the weights exp(s/T - M) are
-// scanned in key order, and n - 1 is the number of prefixes short of tau W.
-template <typename ScoreOf>
-__device__ __forceinline__ int adaptive_count(const unsigned long long* skey, int pmax, int pmin,
-                                              float tau, const MassTotal& mt, float temperature,
-                                              ScoreOf score_of, float* redf, int* red_cnt,
+// Two cases settle the count without the sort, as the sorted scan would: if
+// all p probes together hold less than tau W, every prefix falls short and
+// n = p (the scan's last prefix is the same sum in another order, so the two
+// can differ only where the total lies within rounding of tau W); if the top
+// probe alone holds tau W (and pmin <= 1), the first prefix -- that same
+// weight -- reaches it and n = 1.
+// Each thread passes the weight sum of its own selected probes and the
+// largest sort image among them with that probe's score.  Returns n (0: no
+// fast case) and, for n = 1, the top probe's image in *top.
+__device__ __forceinline__ int adaptive_fast(float wsel, unsigned long long best, float best_s,
+                                             int p, int pmin, float tau, const MassTotal& mt,
+                                             float temperature, float* redf,
+                                             unsigned long long* redk, unsigned long long* top) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float Wsel = block_reduce_f<false>(wsel, redf);
+  if (Wsel < tau * mt.W) return p;
+  unsigned long long b = best;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)b, m);
+    const uint32_t hi = __shfl_xor((uint32_t)(b >> 32), m);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    b = o > b ? o : b;
+  }
+  // the images are distinct: one lane holds the wave's largest
+  if (best == b && b != 0ull) {
+    redk[wave] = b;
+    redf[wave] = best_s;
+  } else if (lane == 0 && b == 0ull) {
+    redk[wave] = 0ull;
+  }
+  __syncthreads();
+  unsigned long long tb = 0ull;
+  float ts = 0.f;
+  for (int v = 0; v < kSelWaves; ++v)
+    if (redk[v] > tb) {
+      tb = redk[v];
+      ts = redf[v];
+    }
+  __syncthreads();
+  *top = tb;
+  if (pmin <= 1 && tb != 0ull && __expf(ts / temperature - mt.M) >= tau * mt.W) return 1;
+  return 0;
+}
+
+// The count n from the pmax probes sorted by bitonic_sort_desc (thread t
+// holding the t-th: its sort image skey and score s): thread t's id goes to
+// *id (else -1), the weights exp(s/T - M) are scanned in key order, and
+// n - 1 is the number of prefixes short of tau W.
+__device__ __forceinline__ int adaptive_count(unsigned long long skey, float s, int pmax,
+                                              int pmin, float tau, const MassTotal& mt,
+                                              float temperature, float* redf, int* red_cnt,
                                               int* id) {
   const int t = threadIdx.x;
   float w = 0.f;
   *id = -1;
   if (t < pmax) {
-    *id = (int)(0xFFFFFFFFu - (uint32_t)(skey[t] & 0xFFFFFFFFull));
-    w = __expf(score_of(*id) / temperature - mt.M);
+    *id = (int)(0xFFFFFFFFu - (uint32_t)(skey & 0xFFFFFFFFull));
+    w = __expf(s / temperature - mt.M);
   }
   const float cum = block_inclusive_scan_f(w, redf);
   int below;

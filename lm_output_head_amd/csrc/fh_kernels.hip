@@ -244,6 +244,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
 // out as bitset words for the cluster-major stage 2.
 struct AdaptShared {
   unsigned long long key[kSelThreads];
+  float val[kSelThreads];
   uint32_t keep[kSelMaxC / 32];
   float redf[kSelWaves];
   int red_scan[kSelWaves];
@@ -271,18 +272,29 @@ __global__ __launch_bounds__(kSelThreads) void k_adapt(
   // the selected probes by key (the same key as k_select takes)
   const int P2 = pow2_at_least(pmax);
   int kj = -1;
+  unsigned long long skey = 0ull;  // padding sorts below every real key
+  float sval = 0.f;
   if (tid < pmax) {
     kj = min(max(Sq[tid], 0), c - 1);
-    sh.key[tid] = probe_sort_key(probe_key(sq[kj], sample, temperature, seed, (uint32_t)q, kj), kj);
-  } else if (tid < P2) {
-    sh.key[tid] = 0ull;  // below every real key: sorts last
+    sval = sq[kj];
+    skey = probe_sort_key(probe_key(sval, sample, temperature, seed, (uint32_t)q, kj), kj);
   }
-  __syncthreads();
-  bitonic_sort_desc(sh.key, P2);
-  int id;
-  const int n = adaptive_count(sh.key, pmax, pmin, tau, mt, temperature,
-                               [&](int k) { return sq[k]; }, sh.redf, sh.red_cnt, &id);
-  if (tid < n) atomicOr(&sh.keep[id >> 5], 1u << (id & 31));
+  unsigned long long top = 0ull;
+  int n = adaptive_fast(tid < pmax ? __expf(sval / temperature - mt.M) : 0.f, skey, sval, pmax,
+                        pmin, tau, mt, temperature, sh.redf, sh.key, &top);
+  if (n == pmax) {  // every probe
+    if (tid < pmax) atomicOr(&sh.keep[kj >> 5], 1u << (kj & 31));
+  } else if (n == 1) {  // the top probe alone
+    if (tid == 0) {
+      const int id = (int)(0xFFFFFFFFu - (uint32_t)(top & 0xFFFFFFFFull));
+      sh.keep[id >> 5] = 1u << (id & 31);
+    }
+  } else {
+    bitonic_sort_desc(skey, sval, P2, sh.key, sh.val);
+    int id;
+    n = adaptive_count(skey, sval, pmax, pmin, tau, mt, temperature, sh.redf, sh.red_cnt, &id);
+    if (tid < n) atomicOr(&sh.keep[id >> 5], 1u << (id & 31));
+  }
   __syncthreads();
   const int kept = tid < pmax && (sh.keep[kj >> 5] & (1u << (kj & 31))) ? 1 : 0;
   int tot;
