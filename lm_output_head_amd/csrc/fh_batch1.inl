@@ -31,8 +31,8 @@ namespace fh {
 //                  n of them in key order (adaptive_count) and publishes only
 //                  those; stage 2 then scores the n b rows the bitset's
 //                  total names and pads the rest of its range.
-//   G1+G2          the finisher: polls the G2 stage-2 partials and merges
-//                  them in index order.  G2 <= CUs - 1, so it finds a CU as
+//   G1+G2          the finisher: one wave polls the G2 stage-2 partials and
+//                  merges them in a fixed order.  G2 <= CUs - 1, so it finds a CU as
 //                  soon as stage 1 retires and its polls overlap stage 2.
 // Results pass between workgroups as 64-bit words tagged with the call's
 // epoch (epoch << 32 | payload), written and polled with agent-scope (sc1)
@@ -187,23 +187,61 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   }
 
   if (w == a.g1 + a.g2) {  // ---- finisher: the stage-2 partials in a fixed order
-    // part i goes to thread i mod 1024 (threads past g2 hold part_empty)
+    // One wave does it all (block-wide code costs 16 waves' issue slots on
+    // the critical path): lane l takes parts l, l + 64, ... in order, the
+    // lanes merge as a DPP tree, and lane 0 writes the outputs.  The other
+    // waves have nothing to do; no barrier follows.
+    if (wave != 0) return;
     Part acc = part_empty();
     bool bad = false;
-    for (int i = threadIdx.x; i < a.g2; i += 1024) {
-      unsigned long long* tp = a.tparts + 5 * (int64_t)i;
-      unsigned long long* const ptr[5] = {tp, tp + 1, tp + 2, tp + 3, tp + 4};
-      const bool live[5] = {true, true, true, true, true};
-      uint32_t wv[5];
-      if (!poll_tagged<5>(ptr, live, a.epoch, a.err, wv) || (int32_t)wv[4] == kBadPart) bad = true;
-      acc = part_merge(acc, Part{__uint_as_float(wv[0]), __uint_as_float(wv[1]),
-                                 __uint_as_float(wv[2]), __uint_as_float(wv[3]), (int32_t)wv[4]});
+    constexpr int kU = 3;  // parts per lane per round, their 5 words in flight together
+    for (int i0 = 0; i0 < a.g2; i0 += 64 * kU) {
+      unsigned long long* base[kU];
+      bool lv[kU];
+      unsigned long long v[5 * kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = i0 + lane + 64 * u;
+        lv[u] = i < a.g2;
+        base[u] = a.tparts + 5 * (int64_t)(lv[u] ? i : 0);
+#pragma unroll
+        for (int f = 0; f < 5; ++f)
+          v[5 * u + f] = lv[u] ? __hip_atomic_load(base[u] + f, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : tag(a.epoch, 0u);
+      }
+      for (unsigned n = 0;; ++n) {
+        bool done = true;
+#pragma unroll
+        for (int e = 0; e < 5 * kU; ++e) done = done && (unsigned)(v[e] >> 32) == a.epoch;
+        if (done) break;
+        if (n >= kSpinLimit) {
+          __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          bad = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(FH_POLL_SLEEP);
+#pragma unroll
+        for (int e = 0; e < 5 * kU; ++e)
+          if ((unsigned)(v[e] >> 32) != a.epoch)
+            v[e] = __hip_atomic_load(base[e / 5] + e % 5, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (!lv[u]) continue;
+        if ((int32_t)(uint32_t)v[5 * u + 4] == kBadPart) bad = true;
+        acc = part_merge(acc, Part{__uint_as_float((uint32_t)v[5 * u]),
+                                   __uint_as_float((uint32_t)v[5 * u + 1]),
+                                   __uint_as_float((uint32_t)v[5 * u + 2]),
+                                   __uint_as_float((uint32_t)v[5 * u + 3]),
+                                   (int32_t)(uint32_t)v[5 * u + 4]});
+      }
     }
-    const bool anybad = __syncthreads_or(bad);
-    // the waves' partials, then a 16-lane DPP tree over them (fixed order)
-    acc = wave_merge_part(acc);
-    const Part r = block_merge_parts<16, 1>({acc}, 1, sh.parts);
-    if (threadIdx.x == 0) {
+    FH_TRACE(23);
+    const bool anybad = __ballot(bad) != 0ull;
+    const Part r = wave_merge_part(acc);  // fixed DPP pattern, then lanes 0, 16, 32, 48
+    if (lane == 0) {
       if (anybad) {
         if (a.out_token) a.out_token[0] = -1;
         if (a.out_logit) a.out_logit[0] = __int_as_float(0x7FC00000);
@@ -233,6 +271,7 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
       ptr[i] = a.tscores + (live[i] ? k : 0);
     }
     if (!poll_tagged<KP>(ptr, live, a.epoch, a.err, raw)) gave_up = true;
+    FH_TRACE(21);
     const bool adaptive = a.tau > 0.f;
     float x[KP], sraw[KP];
 #pragma unroll
@@ -404,6 +443,7 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   // four rows in flight per wave when the register slice allows it
   wave_rows<T, MAXM, 1, (MAXM <= 4 ? 4 : 2)>(static_cast<const T*>(a.Ec ? a.Ec : a.E), a.d, lane,
                                              hv, 1, r_lo + wave, r_end, 16, src_of, tok_of, sink);
+  FH_TRACE(22);
   // sh.probes is read above; sh.parts aliases it
   const bool wg_bad = __syncthreads_or(gave_up);
   Part wg = block_merge_parts<16, 1>(part, 1, sh.parts);

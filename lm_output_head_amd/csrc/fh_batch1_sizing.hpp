@@ -16,7 +16,10 @@ namespace fh {
 
 // Rows per workgroup are a multiple of this (one row for each of the 16
 // waves of a 1024-thread workgroup).
-constexpr int kBatch1RowsUnit = 16;
+#ifndef FH_B1_ROWS_UNIT
+#define FH_B1_ROWS_UNIT 16
+#endif
+constexpr int kBatch1RowsUnit = FH_B1_ROWS_UNIT;
 // Probes a stage-2 workgroup can list in LDS (its rows' clusters).
 constexpr int kBatch1MaxProbesPerWg = 1024;
 
