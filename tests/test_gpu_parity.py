@@ -114,6 +114,24 @@ def test_tiny_probe_counts_including_p_equals_c(p):
         assert np.array_equal(d["token"], out["token"])
 
 
+@pytest.mark.parametrize("p", [129, 200, 255, 256])
+def test_tiny_batch1_single_launch_large_p(p):
+    """B = 1 through the single launch with the tiny head's p b rows spread
+    over up to CUs - 1 stage-2 workgroups: the regime where the partial slots
+    must cover every p, not only p = c."""
+    pb = make_problem("tiny")
+    head, H = _engine(pb, max_batch=1)
+    ref = _oracle(pb)
+    for q, (mode, T) in enumerate(((0, 1.0), (3, 0.8))):
+        say("tiny B=1 single launch p", p, "mode", mode)
+        out = host(head.forward(H[q:q + 1], p, mode=mode, temperature=T, seed=17,
+                                want_clusters=True, want_retrieved=True))
+        assert_report(parity.check_forward(ref, pb.H[q:q + 1], p, mode, T, 17, out),
+                      f"tiny B=1 p={p} mode={mode}")
+    head.sync_status()
+    head.close()
+
+
 # ------------------------------------------------------- ragged / edge cases --
 
 def _custom_problem(v, d, c, dtype, nq, seed=5):
