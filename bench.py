@@ -164,6 +164,38 @@ def burst_main(args):
                       "sizes": rows}), flush=True)
 
 
+def stream_bandwidth(sizes, nbuf=16, steps=100):
+    """Back-to-back plain reads (the bench library's read probe) over nbuf
+    rotating buffers of each size: the part's streaming rate in GB/s."""
+    import ctypes
+
+    import torch
+
+    lib = load_bench_lib()
+    stream = torch.cuda.current_stream()
+    found = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fptr, sptr = ctypes.c_void_p(found.data_ptr()), ctypes.c_void_p(stream.cuda_stream)
+    out = {}
+    for n in sizes:
+        bufs = [torch.full((n // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(nbuf)]
+        ptrs = [ctypes.c_void_p(b.data_ptr()) for b in bufs]
+        for i in range(nbuf):
+            assert lib.fhb_read_probe(ptrs[i], (n // 4) * 4, 0, fptr, sptr) == 0
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(steps):
+            lib.fhb_read_probe(ptrs[i % nbuf], (n // 4) * 4, 0, fptr, sptr)
+        t1.record(stream)
+        t1.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / steps
+        out[n] = round((n // 4) * 4 / us / 1e3, 1)
+        del bufs
+    assert int(found.item()) == 0
+    torch.cuda.empty_cache()
+    return out
+
+
 CLUSTER_SOURCES = ("fh_cluster.hip",)  # the offline clustering, its own translation unit
 
 
@@ -342,8 +374,30 @@ def cpu_baseline(pb, p, quant, mode, temperature, seconds):
                                 "sample": f"{n1} calls in {el1:.1f} s on one BLAS thread"}
     if quant == "none" and mode == 0:
         res["fp32_two_stage"] = cpu_fp32_two_stage(pb, p, seconds / 2)
+    res["dense"] = cpu_dense(pb, seconds / 4)
     res["host"] = cpu_info()
     return res
+
+
+def cpu_dense(pb, seconds):
+    """The dense head on the host: z = E h in float32 numpy (E widened to
+    float32: numpy has no bfloat16, so it reads twice the bf16 bytes), then
+    the argmax, one query per call."""
+    import numpy as np
+    E32 = np.ascontiguousarray(pb.E, dtype=np.float32)
+    H32 = np.ascontiguousarray(pb.H, dtype=np.float32)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        int(np.argmax(E32 @ H32[n % H32.shape[0]]))
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 200:
+            break
+    v, d = E32.shape
+    return {"value": round(n / el, 3), "unit": "calls/s",
+            "sample": f"{n} single-query calls in {el:.2f} s (float32 numpy E h + argmax)",
+            "bytes_per_call_read": v * d * 4, "algorithmic_bf16_bytes": v * d * 2}
 
 
 def cluster_cpu_baseline(E, c, seconds):
@@ -872,6 +926,30 @@ def main():
         if st != 0:
             raise RuntimeError(lib.fh_last_error().decode())
 
+    # per-call latency: an event pair around each call on the launch stream
+    nlat = min(args.steps, 500)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nlat)]
+    for i, (a0, a1) in enumerate(evs):
+        a0.record(stream)
+        step(i)
+        a1.record(stream)
+    torch.cuda.synchronize()
+    lat = sorted(a0.elapsed_time(a1) * 1e3 for a0, a1 in evs)
+    pick = lambda q: round(lat[min(len(lat) - 1, int(q * len(lat)))], 3)  # noqa: E731
+    res["latency_us"] = {"p10": pick(0.10), "p50": pick(0.50), "p90": pick(0.90), "calls": nlat,
+                         "how": "HIP event pair around each call on its stream, back to back, "
+                                "engine replicas rotated"}
+    # the roofline against the part's measured streaming rate as well
+    print("[bench] measuring the stream bandwidth", file=sys.stderr, flush=True)
+    call_sz = int(total_bytes)
+    sb = stream_bandwidth([call_sz, 525336576])
+    res["roofline"]["stream_gbs"] = sb[525336576]
+    res["roofline"]["stream_call_size_gbs"] = sb[call_sz]
+    res["roofline"]["frac_vs_stream"] = round(achieved / sb[525336576], 4)
+    res["roofline"]["frac_vs_stream_call_size"] = round(achieved / sb[call_sz], 4)
+    res["roofline"]["stream_how"] = ("plain one-shot reads (bench library read probe), 16 rotating "
+                                     "buffers, back to back, at 525,336,576 B and at the call's bytes")
     print(f"[bench] timing {args.steps} steps with every output", file=sys.stderr, flush=True)
     ms_all, _ = timed(step_all, args.steps, 10)
     res["with_retrieved_outputs"] = {
