@@ -177,19 +177,20 @@ def stream_bandwidth(sizes, nbuf=16, steps=100):
     fptr, sptr = ctypes.c_void_p(found.data_ptr()), ctypes.c_void_p(stream.cuda_stream)
     out = {}
     for n in sizes:
+        nb = (n // 16) * 16  # the probe reads whole 16-byte words
         bufs = [torch.full((n // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(nbuf)]
         ptrs = [ctypes.c_void_p(b.data_ptr()) for b in bufs]
         for i in range(nbuf):
-            assert lib.fhb_read_probe(ptrs[i], (n // 4) * 4, 0, fptr, sptr) == 0
+            assert lib.fhb_read_probe(ptrs[i], nb, 0, fptr, sptr) == 0
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(stream)
         for i in range(steps):
-            lib.fhb_read_probe(ptrs[i % nbuf], (n // 4) * 4, 0, fptr, sptr)
+            lib.fhb_read_probe(ptrs[i % nbuf], nb, 0, fptr, sptr)
         t1.record(stream)
         t1.synchronize()
         us = t0.elapsed_time(t1) * 1e3 / steps
-        out[n] = round((n // 4) * 4 / us / 1e3, 1)
+        out[n] = round(nb / us / 1e3, 1)
         del bufs
     assert int(found.item()) == 0
     torch.cuda.empty_cache()
@@ -239,7 +240,8 @@ def algorithmic_bytes(shape, B, p, quant, elem, union=None):
     call = score + select + (gather_cm if (B > 1 and union is not None) else gather)
     return {"score": score, "score_int4": score, "score_int8": score, "score_mfma": score, "score_int4_mfma": score,
             "select": select, "gather": gather, "gather_cm": gather_cm, "dense": dense,
-            "dense_mfma": dense, "batch1": score + select + gather, "call": call}
+            "dense_mfma": dense, "batch1": score + select + gather, "batched": select + gather,
+            "call": call}
 
 
 def traffic_from_profiles(kernel: str, src_hash: str, workload_key: str,

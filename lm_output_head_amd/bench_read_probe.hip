@@ -1,4 +1,5 @@
-// A plain one-shot read of a device buffer, for bench.py --burst only: it
+// A plain one-shot read of a device buffer, for bench.py only (--burst and
+// the stream rate beside the roofline): it
 // measures the memory system the head runs on and computes nothing of the
 // head (whose cost the pages place in reading the embedding table from
 // memory: FlashHead technical explainer, framerc.cn, §1.1).  Built into its

@@ -10,6 +10,7 @@
 // (arXiv 2603.14591), abstract.
 
 #include "fh_blocks.hpp"
+#include "fh_handover.hpp"
 
 namespace fh {
 
@@ -85,63 +86,123 @@ struct FusedArgs {
   unsigned* err;  // sticky: a poll gave up
 };
 
-constexpr unsigned kSpinLimit = 1u << 20;
-// s_sleep argument between polling rounds (units of 64 clocks)
-#ifndef FH_POLL_SLEEP
-#define FH_POLL_SLEEP 1
-#endif
-
-__device__ __forceinline__ unsigned long long tag(unsigned epoch, uint32_t bits) {
-  return ((unsigned long long)epoch << 32) | bits;
-}
-
-__device__ __forceinline__ void st_tagged(unsigned long long* p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Poll N tagged words until each carries `epoch`, keeping every load of a
-// round in flight together; out[i] gets word i's low 32 bits.  Words with
-// live[i] false are skipped.
-template <int N>
-__device__ __forceinline__ bool poll_tagged(unsigned long long* const (&p)[N],
-                                            const bool (&live)[N], unsigned epoch,
-                                            unsigned* err, uint32_t (&out)[N]) {
-  unsigned long long v[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i)
-    v[i] = live[i] ? __hip_atomic_load(p[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                   : tag(epoch, 0u);
-  for (unsigned n = 0;; ++n) {
-    bool done = true;
-#pragma unroll
-    for (int i = 0; i < N; ++i) done = done && (unsigned)(v[i] >> 32) == epoch;
-    if (done) break;
-    if (n >= kSpinLimit) {
-      __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int i = 0; i < N; ++i) out[i] = (uint32_t)v[i];
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(FH_POLL_SLEEP);
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-      if ((unsigned)(v[i] >> 32) != epoch)
-        v[i] = __hip_atomic_load(p[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) out[i] = (uint32_t)v[i];
-  return true;
-}
-
-// A stage-2 partial whose workgroup gave up a poll carries this id (never a
-// token id, nor part_empty's), so that the finisher can mark the outputs.
-constexpr int32_t kBadPart = -1;
-
 union Batch1Shared {
   SelShared sel;
   Part parts[1024];
   int probes[1024];
 };
+
+// What a stage-2 workgroup works on: rows [r_lo, r_hi) of one query's p b
+// retrieved rows, that query's tagged probe bitset, its outputs, and the
+// five words its partial goes to.
+struct Stage2Job {
+  const void* E;
+  const void* Ec;
+  const int32_t* c2t;
+  int c, bsz, d, p;
+  float tau;                     // adaptive count: the bitset's total is n (0: fixed p)
+  const void* h;                 // the query's hidden state
+  uint32_t row;                  // the query's index (its Philox row)
+  int token_sample;
+  float tprime;
+  uint64_t seed;
+  int64_t r_lo, r_hi;
+  unsigned long long* tsel;      // the query's ceil(c/32) tagged bitset words
+  unsigned long long* tpart;     // this workgroup's five partial words
+  unsigned epoch;
+  unsigned* err;
+  int32_t* out_clusters;         // the query's [p], or null
+  int32_t* out_ids;              // the query's [p b], or null
+  float* out_logits;
+};
+
+// The stage-2 role (all 1024 threads): find the probes of the rows from the
+// bitset (a prefix count over its words), score the rows, merge and publish
+// the partial.  `gave_up`: this thread already gave up a poll.
+template <typename T, int MAXM>
+__device__ __forceinline__ void stage2_role(const Stage2Job& a, Batch1Shared& sh, bool gave_up) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  FH_TRACE(4);
+  const int64_t r_lo = a.r_lo, r_hi = a.r_hi;
+  uint4 hv[1][MAXM];
+  load_hslice<T, MAXM>(static_cast<const T*>(a.h), a.d / Chunk<T>::kElems, lane, hv[0]);
+  // the probes this workgroup's rows come from: positions [pos0, pos0+npos)
+  // of the ascending probe list, read off the selector's bitset
+  const int pos0 = (int)(r_lo / a.bsz);
+  const int npos = r_hi > r_lo ? (int)((r_hi - 1) / a.bsz) - pos0 + 1 : 0;
+  int nkept = a.p;  // probes in the published bitset
+  if (npos > 0) {
+    const int nw = (a.c + 31) / 32;
+    const int t = threadIdx.x;
+    // every listed probe starts as a valid cluster: if a bitset word never
+    // arrives, the popcounts need not reach p and some positions stay unset
+    for (int i = t; i < npos; i += 1024) sh.probes[i] = 0;
+    uint32_t word = 0u;
+    if (t < nw) {
+      unsigned long long* const ptr[1] = {a.tsel + t};
+      const bool live[1] = {true};
+      uint32_t got[1];
+      if (!poll_tagged<1>(ptr, live, a.epoch, a.err, got)) gave_up = true;
+      word = got[0];
+      // bits past c (a stale or foreign word) name no cluster
+      if (t == nw - 1 && (a.c & 31)) word &= (1u << (a.c & 31)) - 1u;
+    }
+    int tot;
+    int pos = block_exclusive_scan(__popc(word), sh.sel.red_scan, &tot);
+    nkept = min(tot, a.p);
+    if (pos < pos0 + npos && pos + __popc(word) > pos0) {
+      for (uint32_t bitsleft = word; bitsleft; bitsleft &= bitsleft - 1, ++pos) {
+        if (pos < pos0 || pos >= pos0 + npos) continue;
+        const int k = 32 * t + __builtin_ctz(bitsleft);
+        sh.probes[pos - pos0] = k;
+        // the workgroup holding a probe's first row reports it
+        if (a.out_clusters && (int64_t)pos * a.bsz >= r_lo) a.out_clusters[pos] = k;
+      }
+    }
+  }
+  __syncthreads();
+  FH_TRACE(5);
+  int64_t r_end = r_hi;
+  if (a.tau > 0.f) {
+    // adaptive: only the n b rows of the n kept probes; the rest of this
+    // workgroup's range, and the probe positions past n it owns, are padding
+    const int64_t nr = (int64_t)nkept * a.bsz;
+    r_end = min(r_hi, nr);
+    for (int64_t r = max(r_lo, nr) + threadIdx.x; r < r_hi; r += 1024) {
+      if (a.out_ids) a.out_ids[r] = -1;
+      if (a.out_logits) a.out_logits[r] = -INFINITY;
+    }
+    if (a.out_clusters)
+      for (int pos = max(pos0, nkept) + (int)threadIdx.x; pos < pos0 + npos; pos += 1024)
+        if ((int64_t)pos * a.bsz >= r_lo) a.out_clusters[pos] = -1;
+  }
+  Part part[1] = {part_empty()};
+  // slot f of the clustering; with the cluster-contiguous copy of E it is
+  // also the row, else the row is the token C2T[f]
+  auto src_of = [&](int64_t r) -> int64_t {
+    const int64_t f = (int64_t)sh.probes[r / a.bsz - pos0] * a.bsz + r % a.bsz;
+    return a.Ec ? f : (int64_t)a.c2t[f];
+  };
+  auto tok_of = [&](int64_t src) -> int64_t { return a.Ec ? (int64_t)a.c2t[src] : src; };
+  auto sink = [&](int, int64_t r, int64_t src, float z) {
+    if (lane == 0) {
+      if (a.out_logits) a.out_logits[r] = z;
+      if (a.out_ids) a.out_ids[r] = (int32_t)src;
+    }
+    part[0] = part_merge(part[0], part_of(z, (int32_t)src, a.token_sample, a.tprime, a.seed, a.row));
+  };
+  // four rows in flight per wave when the register slice allows it
+  wave_rows<T, MAXM, 1, (MAXM <= 4 ? 4 : 2)>(static_cast<const T*>(a.Ec ? a.Ec : a.E), a.d, lane,
+                                             hv, 1, r_lo + wave, r_end, 16, src_of, tok_of, sink);
+  FH_TRACE(22);
+  // sh.probes is read above; sh.parts aliases it
+  const bool wg_bad = __syncthreads_or(gave_up);
+  Part wg = block_merge_parts<16, 1>(part, 1, sh.parts);
+  if (wg_bad) wg.id = kBadPart;
+  if (threadIdx.x == 0) publish_part(a.tpart, a.epoch, wg);
+  FH_TRACE(6);
+}
 
 template <typename T, int MAXM, int KP, int QB, int MAXG>
 __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
@@ -192,55 +253,10 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     // lanes merge as a DPP tree, and lane 0 writes the outputs.  The other
     // waves have nothing to do; no barrier follows.
     if (wave != 0) return;
-    Part acc = part_empty();
     bool bad = false;
-    constexpr int kU = 3;  // parts per lane per round, their 5 words in flight together
-    for (int i0 = 0; i0 < a.g2; i0 += 64 * kU) {
-      unsigned long long* base[kU];
-      bool lv[kU];
-      unsigned long long v[5 * kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int i = i0 + lane + 64 * u;
-        lv[u] = i < a.g2;
-        base[u] = a.tparts + 5 * (int64_t)(lv[u] ? i : 0);
-#pragma unroll
-        for (int f = 0; f < 5; ++f)
-          v[5 * u + f] = lv[u] ? __hip_atomic_load(base[u] + f, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT)
-                               : tag(a.epoch, 0u);
-      }
-      for (unsigned n = 0;; ++n) {
-        bool done = true;
-#pragma unroll
-        for (int e = 0; e < 5 * kU; ++e) done = done && (unsigned)(v[e] >> 32) == a.epoch;
-        if (done) break;
-        if (n >= kSpinLimit) {
-          __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          bad = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(FH_POLL_SLEEP);
-#pragma unroll
-        for (int e = 0; e < 5 * kU; ++e)
-          if ((unsigned)(v[e] >> 32) != a.epoch)
-            v[e] = __hip_atomic_load(base[e / 5] + e % 5, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (!lv[u]) continue;
-        if ((int32_t)(uint32_t)v[5 * u + 4] == kBadPart) bad = true;
-        acc = part_merge(acc, Part{__uint_as_float((uint32_t)v[5 * u]),
-                                   __uint_as_float((uint32_t)v[5 * u + 1]),
-                                   __uint_as_float((uint32_t)v[5 * u + 2]),
-                                   __uint_as_float((uint32_t)v[5 * u + 3]),
-                                   (int32_t)(uint32_t)v[5 * u + 4]});
-      }
-    }
+    const Part r = wave_merge_tagged_parts(a.tparts, a.g2, a.epoch, a.err, &bad);
     FH_TRACE(23);
-    const bool anybad = __ballot(bad) != 0ull;
-    const Part r = wave_merge_part(acc);  // fixed DPP pattern, then lanes 0, 16, 32, 48
+    const bool anybad = bad;
     if (lane == 0) {
       if (anybad) {
         if (a.out_token) a.out_token[0] = -1;
@@ -369,94 +385,17 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
   }
 
   // ---- stage 2
-  FH_TRACE(4);
-  const int64_t n2 = (int64_t)a.p * a.bsz;
-  const int64_t r_lo = (int64_t)j * a.rows2;
-  const int64_t r_hi = min(n2, r_lo + a.rows2);
-  uint4 hv[1][MAXM];
-  load_hslice<T, MAXM>(hp, a.d / Chunk<T>::kElems, lane, hv[0]);
-  // the probes this workgroup's rows come from: positions [pos0, pos0+npos)
-  // of the ascending probe list, read off the selector's bitset
-  const int pos0 = (int)(r_lo / a.bsz);
-  const int npos = r_hi > r_lo ? (int)((r_hi - 1) / a.bsz) - pos0 + 1 : 0;
-  int nkept = a.p;  // probes in the published bitset
-  if (npos > 0) {
-    const int nw = (a.c + 31) / 32;
-    const int t = threadIdx.x;
-    // every listed probe starts as a valid cluster: if a bitset word never
-    // arrives, the popcounts need not reach p and some positions stay unset
-    for (int i = t; i < npos; i += 1024) sh.probes[i] = 0;
-    uint32_t word = 0u;
-    if (t < nw) {
-      unsigned long long* const ptr[1] = {a.tsel + t};
-      const bool live[1] = {true};
-      uint32_t got[1];
-      if (!poll_tagged<1>(ptr, live, a.epoch, a.err, got)) gave_up = true;
-      word = got[0];
-      // bits past c (a stale or foreign word) name no cluster
-      if (t == nw - 1 && (a.c & 31)) word &= (1u << (a.c & 31)) - 1u;
-    }
-    int tot;
-    int pos = block_exclusive_scan(__popc(word), sh.sel.red_scan, &tot);
-    nkept = min(tot, a.p);
-    if (pos < pos0 + npos && pos + __popc(word) > pos0) {
-      for (uint32_t bitsleft = word; bitsleft; bitsleft &= bitsleft - 1, ++pos) {
-        if (pos < pos0 || pos >= pos0 + npos) continue;
-        const int k = 32 * t + __builtin_ctz(bitsleft);
-        sh.probes[pos - pos0] = k;
-        // the workgroup holding a probe's first row reports it
-        if (a.out_clusters && (int64_t)pos * a.bsz >= r_lo) a.out_clusters[pos] = k;
-      }
-    }
-  }
-  __syncthreads();
-  FH_TRACE(5);
-  int64_t r_end = r_hi;
-  if (a.tau > 0.f) {
-    // adaptive: only the n b rows of the n kept probes; the rest of this
-    // workgroup's range, and the probe positions past n it owns, are padding
-    const int64_t nr = (int64_t)nkept * a.bsz;
-    r_end = min(r_hi, nr);
-    for (int64_t r = max(r_lo, nr) + threadIdx.x; r < r_hi; r += 1024) {
-      if (a.out_ids) a.out_ids[r] = -1;
-      if (a.out_logits) a.out_logits[r] = -INFINITY;
-    }
-    if (a.out_clusters)
-      for (int pos = max(pos0, nkept) + (int)threadIdx.x; pos < pos0 + npos; pos += 1024)
-        if ((int64_t)pos * a.bsz >= r_lo) a.out_clusters[pos] = -1;
-  }
-  Part part[1] = {part_empty()};
-  // slot f of the clustering; with the cluster-contiguous copy of E it is
-  // also the row, else the row is the token C2T[f]
-  auto src_of = [&](int64_t r) -> int64_t {
-    const int64_t f = (int64_t)sh.probes[r / a.bsz - pos0] * a.bsz + r % a.bsz;
-    return a.Ec ? f : (int64_t)a.c2t[f];
-  };
-  auto tok_of = [&](int64_t src) -> int64_t { return a.Ec ? (int64_t)a.c2t[src] : src; };
-  auto sink = [&](int, int64_t r, int64_t src, float z) {
-    if (lane == 0) {
-      if (a.out_logits) a.out_logits[r] = z;
-      if (a.out_ids) a.out_ids[r] = (int32_t)src;
-    }
-    part[0] = part_merge(part[0], part_of(z, (int32_t)src, a.token_sample, a.tprime, a.seed, 0u));
-  };
-  // four rows in flight per wave when the register slice allows it
-  wave_rows<T, MAXM, 1, (MAXM <= 4 ? 4 : 2)>(static_cast<const T*>(a.Ec ? a.Ec : a.E), a.d, lane,
-                                             hv, 1, r_lo + wave, r_end, 16, src_of, tok_of, sink);
-  FH_TRACE(22);
-  // sh.probes is read above; sh.parts aliases it
-  const bool wg_bad = __syncthreads_or(gave_up);
-  Part wg = block_merge_parts<16, 1>(part, 1, sh.parts);
-  if (wg_bad) wg.id = kBadPart;
-  if (threadIdx.x == 0) {
-    unsigned long long* tp = a.tparts + 5 * (int64_t)j;
-    st_tagged(tp + 0, tag(a.epoch, __float_as_uint(wg.key)));
-    st_tagged(tp + 1, tag(a.epoch, __float_as_uint(wg.z)));
-    st_tagged(tp + 2, tag(a.epoch, __float_as_uint(wg.m)));
-    st_tagged(tp + 3, tag(a.epoch, __float_as_uint(wg.s)));
-    st_tagged(tp + 4, tag(a.epoch, (uint32_t)wg.id));
-  }
-  FH_TRACE(6);
+  Stage2Job s2{};
+  s2.E = a.E; s2.Ec = a.Ec; s2.c2t = a.c2t;
+  s2.c = a.c; s2.bsz = a.bsz; s2.d = a.d; s2.p = a.p; s2.tau = a.tau;
+  s2.h = a.h; s2.row = 0u;
+  s2.token_sample = a.token_sample; s2.tprime = a.tprime; s2.seed = a.seed;
+  s2.r_lo = (int64_t)j * a.rows2;
+  s2.r_hi = min((int64_t)a.p * a.bsz, s2.r_lo + a.rows2);
+  s2.tsel = a.tsel; s2.tpart = a.tparts + 5 * (int64_t)j;
+  s2.epoch = a.epoch; s2.err = a.err;
+  s2.out_clusters = a.out_clusters; s2.out_ids = a.out_ids; s2.out_logits = a.out_logits;
+  stage2_role<T, MAXM>(s2, sh, gave_up);
 }
 
 static FusedArgs fused_args(const FusedLaunch& f) {
@@ -527,6 +466,162 @@ hipError_t FH_BATCH1_ENTRY(const FusedLaunch& f) {
 }
 
 }  // namespace fh
+
+#if FH_BATCH1_QB == 0
+namespace fh {
+
+// ======================================================================
+// Batched calls after stage 1, in one launch (2 <= B <= 16 queries; stage 1
+// ran as its own launch and stored each query's selection keys).  Roles by
+// workgroup index, in dispatch order:
+//   [0, B)           selector q: reads query q's keys, selects its p probes
+//                    and publishes them as a tagged bitset;
+//   [B, B + B G2q)   stage 2: query q = (w - B) / G2q, rows of its p b
+//                    retrieved rows (stage2_role, as in the batch-1 kernel);
+//   B + B G2q        finisher: wave q merges query q's G2q partials.
+// Every workgroup waits only for lower-indexed ones (see fh_handover.hpp),
+// so each query's stage 2 starts as soon as its own selector is done.
+// ======================================================================
+struct BatchedArgs {
+  const void* E;
+  const void* Ec;
+  const int32_t* c2t;
+  int c, bsz, d;
+  const void* H;       // [B x d]
+  int B;
+  const float* keys;   // [B x c] stage 1's selection keys
+  int p;
+  float zq;
+  int token_sample;
+  float tprime;
+  uint64_t seed;
+  int g2, rows2;       // stage-2 workgroups per query and rows per workgroup
+  unsigned epoch;
+  unsigned long long* tsel;    // [B x ceil(c/32)]
+  unsigned long long* tparts;  // [B x g2 x 5]
+  int32_t* out_clusters;       // [B x p] or null
+  int32_t* out_ids;            // [B x p b] or null
+  float* out_logits;
+  int32_t* out_token;
+  float* out_logit;
+  float* out_lse;
+  unsigned* err;
+};
+
+template <typename T, int MAXM, int KP>
+__global__ __launch_bounds__(1024) void k_batched(BatchedArgs a) {
+  __shared__ Batch1Shared sh;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int w = blockIdx.x;
+  const int W = (a.c + 31) / 32;
+  if (w < a.B) {  // ---- selector of query w (the keys as k_select takes them)
+    FH_TRACE(16);
+    const float* kq = a.keys + (int64_t)w * a.c;
+    select_clear(sh.sel);
+    float x[KP];
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int k = (int)threadIdx.x + kSelThreads * i;
+      x[i] = k < a.c ? saturate_key(kq[k]) : -FLT_MAX;
+    }
+    __syncthreads();
+    select_bits<KP>(x, a.c, a.p, a.zq, sh.sel);
+    FH_TRACE(17);
+    for (int t = threadIdx.x; t < W; t += kSelThreads)
+      st_tagged(a.tsel + (int64_t)w * W + t, tag(a.epoch, sh.sel.selbits[t]));
+    FH_TRACE(3);
+    return;
+  }
+  if (w == a.B + a.B * a.g2) {  // ---- finisher: wave q merges query q's partials
+    if (wave >= a.B) return;
+    bool bad = false;
+    const Part r = wave_merge_tagged_parts(a.tparts + 5 * (int64_t)wave * a.g2, a.g2, a.epoch,
+                                           a.err, &bad);
+    FH_TRACE(23);
+    if (lane == 0) {
+      if (bad) {
+        if (a.out_token) a.out_token[wave] = -1;
+        if (a.out_logit) a.out_logit[wave] = __int_as_float(0x7FC00000);
+        if (a.out_lse) a.out_lse[wave] = __int_as_float(0x7FC00000);
+      } else {
+        write_outputs(r, wave, a.out_token, a.out_logit, a.out_lse);
+      }
+    }
+    return;
+  }
+  // ---- stage 2
+  const int j = w - a.B;
+  const int q = j / a.g2, jj = j - q * a.g2;
+  const int64_t nb = (int64_t)a.p * a.bsz;
+  Stage2Job s2{};
+  s2.E = a.E; s2.Ec = a.Ec; s2.c2t = a.c2t;
+  s2.c = a.c; s2.bsz = a.bsz; s2.d = a.d; s2.p = a.p; s2.tau = 0.f;
+  s2.h = static_cast<const T*>(a.H) + (int64_t)q * a.d;
+  s2.row = (uint32_t)q;
+  s2.token_sample = a.token_sample; s2.tprime = a.tprime; s2.seed = a.seed;
+  s2.r_lo = (int64_t)jj * a.rows2;
+  s2.r_hi = min(nb, s2.r_lo + a.rows2);
+  s2.tsel = a.tsel + (int64_t)q * W;
+  s2.tpart = a.tparts + 5 * ((int64_t)q * a.g2 + jj);
+  s2.epoch = a.epoch; s2.err = a.err;
+  s2.out_clusters = a.out_clusters ? a.out_clusters + (int64_t)q * a.p : nullptr;
+  s2.out_ids = a.out_ids ? a.out_ids + (int64_t)q * nb : nullptr;
+  s2.out_logits = a.out_logits ? a.out_logits + (int64_t)q * nb : nullptr;
+  stage2_role<T, MAXM>(s2, sh, false);
+}
+
+static BatchedArgs batched_args(const BatchedLaunch& f) {
+  const KernelCtx& k = *f.ctx;
+  BatchedArgs a{};
+  a.E = k.E; a.Ec = k.Ec; a.c2t = k.c2t;
+  a.c = (int)k.c; a.bsz = (int)k.b; a.d = k.d;
+  a.H = f.H; a.B = f.B; a.keys = f.keys; a.p = f.p;
+  a.zq = select_quantile(k.c, f.p);
+  a.token_sample = f.token_sample; a.tprime = f.tprime; a.seed = f.seed;
+  a.g2 = batched_stage2_blocks(f.p, k.b, f.B, f.cus);
+  a.rows2 = (int)batched_rows2(f.p, k.b, f.B, f.cus);
+  a.epoch = f.epoch;
+  a.tsel = f.tagged;
+  a.tparts = f.tagged + batched_off_parts(k.c, f.B);
+  a.out_clusters = f.out_clusters; a.out_ids = f.out_ids; a.out_logits = f.out_logits;
+  a.out_token = f.out_token; a.out_logit = f.out_logit; a.out_lse = f.out_lse;
+  a.err = f.err;
+  return a;
+}
+
+template <typename T, int MAXM, int KP>
+static hipError_t bt_go(const BatchedLaunch& f, const BatchedArgs& a) {
+  const unsigned grid = (unsigned)(a.B + a.B * a.g2 + 1);
+  hipLaunchKernelGGL((k_batched<T, MAXM, KP>), dim3(grid), dim3(1024), 0, f.ctx->stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int KP>
+static hipError_t bt_m(const BatchedLaunch& f, const BatchedArgs& a) {
+  switch ((f.ctx->d / Chunk<T>::kElems + 63) / 64) {
+    case 1: return bt_go<T, 1, KP>(f, a);
+    case 2: return bt_go<T, 2, KP>(f, a);
+    case 3: case 4: return bt_go<T, 4, KP>(f, a);
+    case 5: case 6: return bt_go<T, 6, KP>(f, a);
+    case 7: case 8: return bt_go<T, 8, KP>(f, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t FH_BATCHED_ENTRY(const BatchedLaunch& f) {
+  if (!batched_fits(f.p, f.ctx->b, f.B, f.cus)) return hipErrorInvalidValue;
+  const BatchedArgs a = batched_args(f);
+  switch (sel_keys_per_thread(f.ctx->c)) {
+    case 1: return bt_m<FH_BATCH1_T, 1>(f, a);
+    case 2: return bt_m<FH_BATCH1_T, 2>(f, a);
+    case 8: return bt_m<FH_BATCH1_T, 8>(f, a);
+    case 16: return bt_m<FH_BATCH1_T, 16>(f, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace fh
+#endif  // FH_BATCH1_QB == 0
 
 #ifdef FH_PHASE_TRACE
 // Trace builds only: copy this variant's phase timestamps to the host.

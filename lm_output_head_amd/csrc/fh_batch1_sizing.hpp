@@ -54,6 +54,29 @@ inline bool batch1_fits(int64_t p, int64_t b, int cus) {
 
 // Tagged words, in this order: scores [c]; the probe bitset [ceil(c / 32)];
 // five words per stage-2 partial [5 x batch1_slots2(cus)].
+// Batched calls after stage 1 (2 <= B <= kBatchedMaxB queries): one launch of
+// B selectors, B x G2q stage-2 workgroups and a finisher, all resident at one
+// workgroup per CU: the stage-2 slots CUs - 1 - B are shared by the queries.
+constexpr int kBatchedMaxB = 16;
+inline int64_t batched_slots2(int B, int cus) { return std::max<int64_t>(1, (cus - 1 - B) / B); }
+inline int64_t batched_rows2(int64_t p, int64_t b, int B, int cus) {
+  return batch1_rows(p * b, batched_slots2(B, cus));
+}
+inline int batched_stage2_blocks(int64_t p, int64_t b, int B, int cus) {
+  const int64_t r = batched_rows2(p, b, B, cus);
+  return (int)std::max<int64_t>(1, (p * b + r - 1) / r);
+}
+inline bool batched_fits(int64_t p, int64_t b, int B, int cus) {
+  return B >= 2 && B <= kBatchedMaxB && cus - 1 - B >= B &&
+         batched_rows2(p, b, B, cus) / b + 2 <= kBatch1MaxProbesPerWg;
+}
+// Tagged words of a batched launch: [B x ceil(c/32)] probe bitsets, then
+// [B x G2q x 5] stage-2 partials (at most 5 x (CUs - 1) words).
+inline int64_t batched_off_parts(int64_t c, int B) { return (int64_t)B * ((c + 31) / 32); }
+inline int64_t batched_tag_words(int64_t c, int max_batch, int cus) {
+  return (int64_t)std::min(max_batch, kBatchedMaxB) * ((c + 31) / 32) + 5 * (int64_t)std::max(1, cus - 1);
+}
+
 inline int64_t batch1_off_sel(int64_t c) { return c; }
 inline int64_t batch1_off_parts(int64_t c) { return c + (c + 31) / 32; }
 inline int64_t batch1_tag_words(int64_t c, int cus) {

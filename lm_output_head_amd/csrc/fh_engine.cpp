@@ -68,6 +68,7 @@ struct fh_engine {
   int64_t parts_per_q = 0;
   unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up
   unsigned long long* tagged = nullptr;  // batch-1 hand-over words (fh_batch1_sizing.hpp layout)
+  unsigned long long* btag = nullptr;    // batched launch's hand-over words (same header)
   unsigned epoch = 0;
   int cus = 0;                // compute units of the device
   int path = FH_PATH_AUTO;
@@ -150,6 +151,7 @@ void free_engine(fh_engine* e) {
   (void)hipFree(e->parts);
   (void)hipFree(e->sync);
   (void)hipFree(e->tagged);
+  (void)hipFree(e->btag);
   for (hipEvent_t ev : e->prof_ev) (void)hipEventDestroy(ev);
   delete e;
 }
@@ -374,6 +376,7 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   // batch-1 hand-over words: enough partials for the largest stage-2 grid of
   // any p (batch1_stage2_blocks never exceeds batch1_slots2)
   const int64_t ntag = fh::batch1_tag_words(c, e->cus);
+  const int64_t nbtag = fh::batched_tag_words(c, (int)std::min<int64_t>(max_batch, 65535), e->cus);
 
   e->parts_per_q = std::max<int64_t>(
       {fh::rows_blocks(v, fh::kGatherRPW), fh::rows_blocks(v, fh::kDenseRPW),
@@ -392,6 +395,7 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
       {(void**)&e->parts, sizeof(fh::Part) * (size_t)(max_batch * e->parts_per_q), "partials"},
       {(void**)&e->sync, 4 * sizeof(unsigned), "sync flags"},
       {(void**)&e->tagged, sizeof(unsigned long long) * (size_t)ntag, "tagged hand-over words"},
+      {(void**)&e->btag, sizeof(unsigned long long) * (size_t)nbtag, "batched hand-over words"},
   };
   for (const Alloc& a : allocs) {
     r = hipMalloc(a.p, a.bytes);
@@ -401,6 +405,8 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   if (r == hipSuccess) r = hipMemsetAsync(e->sync, 0, 4 * sizeof(unsigned), st);
   if (r == hipSuccess)
     r = hipMemsetAsync(e->tagged, 0, sizeof(unsigned long long) * (size_t)ntag, st);
+  if (r == hipSuccess)
+    r = hipMemsetAsync(e->btag, 0, sizeof(unsigned long long) * (size_t)nbtag, st);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "copy C2T"); }
   r = fh::launch_permute_rows(e->ctx(st), e->Ec);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "cluster-contiguous E"); }
@@ -518,6 +524,38 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
   // batches of bf16 queries that share probes: stage 2 cluster-major on the
   // matrix cores, each probed cluster's rows read once for all its queries
   const bool cm = e->dtype == FH_BF16 && fh::gather_cm_fits((int)B, p, e->c);
+  if (!cm && e->path == FH_PATH_AUTO && capture == hipStreamCaptureStatusNone &&
+      fh::batched_fits(p, e->b, (int)B, e->cus)) {
+    // small batches, query-major stage 2: stage 1, then the selection, stage 2
+    // and the finish in one launch (its epoch, like the batch-1 kernel's, is
+    // why captured calls take the per-stage launches)
+    fh::KeyXform kx;
+    kx.sample = probe_sample; kx.temperature = temperature; kx.seed = seed;
+    hipError_t r = launch_stage1(e, st, k, h, B, e->scores, kx);
+    if (r != hipSuccess) return hip_fail(r, "score launch");
+    fh::BatchedLaunch f{};
+    f.ctx = &k;
+    f.cus = e->cus;
+    f.H = h;
+    f.B = (int)B;
+    f.keys = e->scores;
+    f.p = (int)p;
+    f.token_sample = token_sample;
+    f.tprime = tprime;
+    f.seed = seed;
+    e->epoch = e->epoch == 0xFFFFFFFFu ? 1u : e->epoch + 1u;
+    f.epoch = e->epoch;
+    f.tagged = e->btag;
+    f.out_clusters = out_clusters;
+    f.out_ids = out_ids;
+    f.out_logits = out_logits;
+    f.out_token = out_token;
+    f.out_logit = out_token_logit;
+    f.out_lse = out_lse;
+    f.err = e->sync;
+    r = timed(e, st, "batched", [&] { return fh::launch_batched(f); });
+    return r == hipSuccess ? FH_OK : hip_fail(r, "batched launch");
+  }
   // with sampled probes stage 1 stores the selection keys (the Gumbel draws
   // spread over its grid) and the selection takes them as they are
   fh::KeyXform kx;

@@ -186,6 +186,33 @@ hipError_t launch_spec_verify(const KernelCtx& k, int cus, const int32_t* t2c, u
                               float* out_lse);
 
 hipError_t launch_batch1(const FusedLaunch& f);
+
+// Batched calls (2 <= B <= kBatchedMaxB) after stage 1: selection, stage 2
+// and the finish in one launch, handed over through tagged words
+// (fh_batch1.inl, sizing in fh_batch1_sizing.hpp).
+struct BatchedLaunch {
+  const KernelCtx* ctx;
+  int cus;
+  const void* H;                  // [B x d] queries
+  int B;
+  const float* keys;              // [B x c] stage 1's selection keys
+  int p;
+  int token_sample;
+  float tprime;
+  uint64_t seed;
+  unsigned epoch;                 // this call's tag, never 0
+  unsigned long long* tagged;     // batched_tag_words(c, max_batch, cus) words (zeroed at create)
+  int32_t* out_clusters;          // [B x p] or null
+  int32_t* out_ids;               // [B x p b] or null
+  float* out_logits;
+  int32_t* out_token;
+  float* out_logit;
+  float* out_lse;
+  unsigned* err;                  // sticky flag: a bounded poll gave up
+};
+hipError_t launch_batched(const BatchedLaunch& f);
+hipError_t launch_batched_bf16(const BatchedLaunch& f);
+hipError_t launch_batched_f32(const BatchedLaunch& f);
 // per storage variant, one translation unit each
 hipError_t launch_batch1_bf16(const FusedLaunch& f);
 hipError_t launch_batch1_bf16_int4(const FusedLaunch& f);

@@ -572,6 +572,10 @@ hipError_t launch_finish(const KernelCtx& k, const Part* parts, int B, int64_t n
 
 // ---- batch-1 path: one launch (sizing in fh_batch1_sizing.hpp)
 
+hipError_t launch_batched(const BatchedLaunch& f) {
+  return f.ctx->bf16 ? launch_batched_bf16(f) : launch_batched_f32(f);
+}
+
 hipError_t launch_batch1(const FusedLaunch& f) {
   switch (f.ctx->qbits) {
     case 0: return f.ctx->bf16 ? launch_batch1_bf16(f) : launch_batch1_f32(f);

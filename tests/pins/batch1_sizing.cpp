@@ -49,6 +49,29 @@ int main(int argc, char** argv) {
       if (npos > kBatch1MaxProbesPerWg) return fail("probe list exceeds LDS", v, c, cus, p);
     }
   }
-  std::printf("ok g1=%d rows1=%lld fits=%lld maxg2=%lld words=%lld\n", g1, r1, fits, maxg2, words);
+  // batched launches after stage 1: B selectors, B x g2q stage-2 workgroups
+  // and a finisher, all within the CUs; every tagged word inside the buffer
+  const long long bwords = batched_tag_words(c, kBatchedMaxB, cus);
+  long long bfits = 0;
+  for (int B = 2; B <= kBatchedMaxB; ++B) {
+    for (long long p = 1; p <= c; ++p) {
+      if (!batched_fits(p, b, B, cus)) continue;
+      ++bfits;
+      const long long r2 = batched_rows2(p, b, B, cus);
+      const long long g2 = batched_stage2_blocks(p, b, B, cus);
+      if (g2 * r2 < p * b) return fail("batched stage-2 cover", v, c, cus, p);
+      if (B + B * g2 + 1 > cus) return fail("batched grid exceeds the CUs", v, c, cus, p);
+      if (batched_off_parts(c, B) + 5 * B * g2 > bwords)
+        return fail("batched partials overflow", v, c, cus, p);
+      for (long long j = 0; j < g2; ++j) {
+        const long long lo = j * r2, hi = (lo + r2 < p * b) ? lo + r2 : p * b;
+        if (hi <= lo) continue;
+        if ((hi - 1) / b - lo / b + 1 > kBatch1MaxProbesPerWg)
+          return fail("batched probe list exceeds LDS", v, c, cus, p);
+      }
+    }
+  }
+  std::printf("ok g1=%d rows1=%lld fits=%lld maxg2=%lld words=%lld batched_fits=%lld\n", g1, r1,
+              fits, maxg2, words, bfits);
   return 0;
 }

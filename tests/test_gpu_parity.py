@@ -132,6 +132,34 @@ def test_tiny_batch1_single_launch_large_p(p):
     head.close()
 
 
+@pytest.mark.parametrize("shape,quant,B,p,mode", [
+    ("tiny", "none", 2, 16, 0), ("tiny", "none", 3, 100, 3), ("tiny", "none", 16, 255, 2),
+    ("llama32_1b", "none", 4, 512, 0), ("llama32_1b", "int4", 8, 512, 1),
+    ("llama32_1b", "int8", 3, 1024, 3), ("gemma3_1b", "none", 16, 512, 3),
+])
+def test_batched_launch_matches_per_stage(shape, quant, B, p, mode):
+    """Small query-major batches run the selection, stage 2 and the finish in
+    one launch after stage 1; the per-stage launches (FH_PATH_MULTI) give the
+    same probes, retrieved ids and logits and tokens bit for bit, the LSE to
+    rounding (the partials merge in another order), and both match the
+    oracle."""
+    pb = make_problem(shape) if shape == "tiny" else make_problem(shape, nq=16)
+    head, H = _engine(pb, quant=quant, max_batch=B)
+    say("batched launch", shape, quant, B, p, mode)
+    one = host(head.forward(H[:B], p, mode=mode, temperature=0.8, seed=29, want_clusters=True,
+                            want_retrieved=True))
+    head.set_path("multi")
+    per = host(head.forward(H[:B], p, mode=mode, temperature=0.8, seed=29, want_clusters=True,
+                            want_retrieved=True))
+    for k in ("clusters", "ids", "logits", "token", "token_logit"):
+        assert np.array_equal(one[k], per[k]), k
+    assert np.allclose(one["lse"], per["lse"], rtol=1e-5, atol=1e-6)
+    assert_report(parity.check_forward(_oracle(pb, quant), pb.H[:B], p, mode, 0.8, 29, one),
+                  f"batched {shape} {quant} B={B} p={p} mode={mode}")
+    head.sync_status()
+    head.close()
+
+
 # ------------------------------------------------------- ragged / edge cases --
 
 def _custom_problem(v, d, c, dtype, nq, seed=5):
