@@ -54,6 +54,7 @@ struct fh_engine {
   int32_t* c2t = nullptr;
   int32_t* t2c = nullptr;     // cluster of every token (speculative verification)
   void* Ec = nullptr;         // cluster-contiguous copy of E: Ec[f] = E[C2T[f]]
+  void* Ecm = nullptr;        // Ec in fragment order (bf16 engines taking batches)
   uint8_t* cq = nullptr;
   uint16_t* csig = nullptr;
   uint8_t* cq_mfma = nullptr;    // INT4 codes in the MFMA tile layout (bf16 engines)
@@ -64,8 +65,8 @@ struct fh_engine {
   int32_t* mpre = nullptr;    // [ceil(c/32) x max_batch] probes in earlier words
   float* sumscores = nullptr;  // [c] summed scores of a batch (shared probes)
   int32_t* nprobe = nullptr;   // [max_batch] adaptive probe counts
-  fh::Part* parts = nullptr;  // [max_batch x parts_per_q]
-  int64_t parts_per_q = 0;
+  fh::Part* parts = nullptr;  // partials: [B x parts per query] of the call's stage 2
+  int64_t parts_total = 0;
   unsigned* sync = nullptr;   // [0]: sticky flag, a batch-1 poll gave up
   unsigned long long* tagged = nullptr;  // batch-1 hand-over words (fh_batch1_sizing.hpp layout)
   unsigned long long* btag = nullptr;    // batched launch's hand-over words (same header)
@@ -83,6 +84,7 @@ struct fh_engine {
     k.bf16 = dtype == FH_BF16;
     k.E = E;
     k.Ec = Ec;
+    k.Ecm = Ecm;
     k.C = C;
     k.c2t = c2t;
     k.cq = cq;
@@ -137,6 +139,7 @@ void free_engine(fh_engine* e) {
   if (!e) return;
   (void)hipFree(e->c2t);
   (void)hipFree(e->Ec);
+  (void)hipFree(e->Ecm);
   (void)hipFree(e->t2c);
   (void)hipFree(e->sumscores);
   (void)hipFree(e->nprobe);
@@ -378,9 +381,15 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   const int64_t ntag = fh::batch1_tag_words(c, e->cus);
   const int64_t nbtag = fh::batched_tag_words(c, (int)std::min<int64_t>(max_batch, 65535), e->cus);
 
-  e->parts_per_q = std::max<int64_t>(
+  // partials per query: the row kernels' and the dense GEMMs' workgroups, or
+  // (cluster-major stage 2, at most gather_cm_max_batch queries) one per
+  // probe, p <= c
+  const int64_t parts_per_q = std::max<int64_t>(
       {fh::rows_blocks(v, fh::kGatherRPW), fh::rows_blocks(v, fh::kDenseRPW),
-       fh::gather_cm_blocks(c, e->cus), fh::mfma_blocks(v), fh::splitd_blocks(v), 4096});
+       fh::mfma_blocks(v), fh::splitd_blocks(v), 4096});
+  e->parts_total = std::max<int64_t>(
+      max_batch * parts_per_q,
+      std::min<int64_t>(max_batch, fh::gather_cm_max_batch()) * c * ((b + 15) / 16));
   struct Alloc { void** p; size_t bytes; const char* what; };
   const Alloc allocs[] = {
       {(void**)&e->c2t, sizeof(int32_t) * (size_t)v, "C2T"},
@@ -392,7 +401,7 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
       {(void**)&e->sel, sizeof(int32_t) * (size_t)(max_batch * c), "selection"},
       {(void**)&e->mbits, sizeof(uint32_t) * (size_t)(max_batch * ((c + 31) / 32)), "probe bitsets"},
       {(void**)&e->mpre, sizeof(int32_t) * (size_t)(max_batch * ((c + 31) / 32)), "probe prefix counts"},
-      {(void**)&e->parts, sizeof(fh::Part) * (size_t)(max_batch * e->parts_per_q), "partials"},
+      {(void**)&e->parts, sizeof(fh::Part) * (size_t)e->parts_total, "partials"},
       {(void**)&e->sync, 4 * sizeof(unsigned), "sync flags"},
       {(void**)&e->tagged, sizeof(unsigned long long) * (size_t)ntag, "tagged hand-over words"},
       {(void**)&e->btag, sizeof(unsigned long long) * (size_t)nbtag, "batched hand-over words"},
@@ -410,6 +419,11 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "copy C2T"); }
   r = fh::launch_permute_rows(e->ctx(st), e->Ec);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "cluster-contiguous E"); }
+  if (dtype == FH_BF16 && max_batch >= 2) {  // what the cluster-major stage 2 reads
+    r = hipMalloc(&e->Ecm, (size_t)fh::fragment_order_bytes(c, b, (int)d));
+    if (r == hipSuccess) r = fh::launch_fragment_order(e->ctx(st), e->Ecm);
+    if (r != hipSuccess) { free_engine(e); return hip_fail(r, "fragment-order E"); }
+  }
   r = fh::launch_t2c(e->ctx(st), e->t2c);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "token clusters"); }
 
@@ -523,7 +537,7 @@ fh_status fh_forward(fh_engine* e, const void* h, int64_t B, int64_t p, int mode
 
   // batches of bf16 queries that share probes: stage 2 cluster-major on the
   // matrix cores, each probed cluster's rows read once for all its queries
-  const bool cm = e->dtype == FH_BF16 && fh::gather_cm_fits((int)B, p, e->c);
+  const bool cm = e->dtype == FH_BF16 && e->Ecm && fh::gather_cm_fits((int)B, p, e->c);
   if (!cm && e->path == FH_PATH_AUTO && capture == hipStreamCaptureStatusNone &&
       fh::batched_fits(p, e->b, (int)B, e->cus)) {
     // small batches, query-major stage 2: stage 1, then the selection, stage 2
@@ -660,7 +674,7 @@ fh_status fh_forward_adaptive(fh_engine* e, const void* h, int64_t B, int64_t p_
   if (r != hipSuccess) return hip_fail(r, "select launch");
   // batches of bf16 queries: the cluster-major stage 2 over the kept probes'
   // bitsets, each kept cluster's rows read once for all queries keeping it
-  const bool cm = e->dtype == FH_BF16 && fh::gather_cm_fits((int)B, p_max, e->c);
+  const bool cm = e->dtype == FH_BF16 && e->Ecm && fh::gather_cm_fits((int)B, p_max, e->c);
   r = timed(e, st, "adapt", [&] {
     return fh::launch_adapt(k, e->scores, (int)B, (int)p_max, (int)p_min, tau, probe_sample,
                             temperature, seed, S, np, out_ids, out_logits,
@@ -680,8 +694,10 @@ fh_status fh_forward_adaptive(fh_engine* e, const void* h, int64_t B, int64_t p_
                                out_logits, e->parts, &nparts, -1, np);
     });
   if (r != hipSuccess) return hip_fail(r, "gather launch");
+  // the cluster-major partials of a query's ranks past its count are unwritten
   r = timed(e, st, "finish", [&] {
-    return fh::launch_finish(k, e->parts, (int)B, nparts, out_token, out_token_logit, out_lse);
+    return fh::launch_finish(k, e->parts, (int)B, nparts, out_token, out_token_logit, out_lse,
+                             cm ? np : nullptr, (int)((e->b + 15) / 16));
   });
   return r == hipSuccess ? FH_OK : hip_fail(r, "finish launch");
 }

@@ -30,6 +30,7 @@ struct KernelCtx {
   bool bf16;
   const void* E;
   const void* Ec;  // cluster-contiguous copy of E (Ec[f] = E[C2T[f]]), or null
+  const void* Ecm = nullptr;  // its fragment-order copy (cluster-major stage 2), or null
   const void* C;
   const int32_t* c2t;
   const uint8_t* cq;
@@ -108,8 +109,12 @@ hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, 
                              const KeyXform& kx = KeyXform{});
 // Cluster-major stage 2 on the matrix cores (bf16 engines, B >= 2): every
 // probed cluster's rows are read once for all queries that probe it.
-int64_t gather_cm_blocks(int64_t c, int cus);
 bool gather_cm_fits(int B, int64_t p, int64_t c);
+// The fragment-order copy of the cluster-contiguous E that the cluster-major
+// stage 2 reads (layout in fh_mfma.hip): its bytes, and the launch that
+// writes it from k.Ec (bf16).
+int64_t fragment_order_bytes(int64_t c, int64_t b, int d);
+hipError_t launch_fragment_order(const KernelCtx& k, void* out);
 int gather_cm_max_batch();  // queries the cluster-major stage 2 can take
 // stage 2 over one probe list shared by the batch, as the matrix-core GEMM
 // with a row map (bf16 engines with the cluster-contiguous E)
@@ -117,6 +122,11 @@ hipError_t launch_gather_shared_mfma(const KernelCtx& k, int cus, const void* h,
                                      const int32_t* S, int p, int token_sample, float tprime,
                                      uint64_t seed, int32_t* out_ids, float* out_logits,
                                      Part* parts, int64_t* nparts);
+// Partials [B x p nrt], nrt = ceil(b / 16) row tiles per cluster: query q's
+// partial over row tile t of its probe of rank r (ascending cluster id) at
+// parts[(q p + r) nrt + t]; *nparts = p nrt.  A query with fewer than p
+// probes in its bitset (the adaptive count n) leaves the partials past
+// n nrt unwritten: launch_finish then takes n (scaled by nrt) as its limit.
 hipError_t launch_gather_cm(const KernelCtx& k, int cus, const void* h, int B, int p,
                             const uint32_t* mbits,
                             const int32_t* mpre, int token_sample, float tprime, uint64_t seed,
@@ -130,8 +140,11 @@ hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, 
 hipError_t launch_probs_fp8(const float* logits, const float* lse, int64_t B, int64_t n,
                             float temperature, uint8_t* out, int32_t* out_k, hipStream_t stream);
 
+// Merge each query's partials parts[q nparts, q nparts + n_q) in order, n_q
+// = nparts, or min(nparts, nlimit[q] scale) with nlimit (device, [B]) non-null.
 hipError_t launch_finish(const KernelCtx& k, const Part* parts, int B, int64_t nparts,
-                         int32_t* out_token, float* out_logit, float* out_lse);
+                         int32_t* out_token, float* out_logit, float* out_lse,
+                         const int32_t* nlimit = nullptr, int scale = 1);
 
 // The single-launch batch-1 path (stage 1, selection, stage 2 and the
 // finish by workgroups in dispatch order, handed over through tagged words).

@@ -322,12 +322,14 @@ __global__ __launch_bounds__(kSelThreads) void k_adapt(
 }
 
 __global__ __launch_bounds__(256) void k_finish(const Part* __restrict__ parts, int nparts,
+                                                const int32_t* __restrict__ nlimit, int scale,
                                                 int32_t* __restrict__ out_token,
                                                 float* __restrict__ out_logit,
                                                 float* __restrict__ out_lse) {
   __shared__ Part sh[256];
   const int q = blockIdx.x;
-  const Part r = merge_parts_block<256>(parts + (int64_t)q * nparts, nparts, sh);
+  const int n = nlimit ? max(0, min(nparts, nlimit[q] * scale)) : nparts;
+  const Part r = merge_parts_block<256>(parts + (int64_t)q * nparts, n, sh);
   if (threadIdx.x == 0) write_outputs(r, q, out_token, out_logit, out_lse);
 }
 
@@ -564,9 +566,10 @@ hipError_t launch_dense(const KernelCtx& k, const void* h, int B, int token_samp
 }
 
 hipError_t launch_finish(const KernelCtx& k, const Part* parts, int B, int64_t nparts,
-                         int32_t* out_token, float* out_logit, float* out_lse) {
+                         int32_t* out_token, float* out_logit, float* out_lse,
+                         const int32_t* nlimit, int scale) {
   hipLaunchKernelGGL(k_finish, dim3((unsigned)B), dim3(256), 0, k.stream, parts, (int)nparts,
-                     out_token, out_logit, out_lse);
+                     nlimit, scale, out_token, out_logit, out_lse);
   return hipGetLastError();
 }
 

@@ -588,26 +588,35 @@ __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
 // query still takes only its own probes).  Workgroup x owns clusters
 // [8x, 8x + 8).  For each of them the workgroup lists the queries whose
 // probe bitset holds it (ballots over the bitset words, ascending query
-// order).  The work items -- (cluster, 16-slot row tile of the cluster's rows
-// Ec[k b + j] in the cluster-contiguous E, tile of 16 of its queries) -- are
-// taken round-robin by the four waves; each computes its 16 x 16 logits with
-// MFMA over d (the next 128-element block's loads in flight during the
-// current block's products), so a cluster's rows are read once for all its
-// queries and a much-probed cluster's query tiles run in parallel.  The epilogue
-// writes the optional outputs at the query's canonical position (probe rank
-// from the bitset and its word prefix counts, then slot) and folds
-// (z, token) into a per-wave, per-query partial in LDS; the workgroup's four
-// wave partials are merged in order into parts[q][x].
+// order).  The work items -- (cluster, tile of 16 of its rows, tile of 16 of
+// its queries) -- are taken round-robin by the four waves; each computes its
+// 16 x 16 logits with MFMA over d (the next 128-element block's loads in
+// flight during the current block's products), so a cluster's rows are read
+// once for all its queries and a much-probed cluster's query tiles run in
+// parallel.  The rows come from the fragment-order copy of E (Ecm, below),
+// so every row load is one contiguous 1 KB read.  The epilogue writes the
+// optional outputs at the query's canonical position (probe rank from the
+// bitset and its word prefix counts, then slot) and one partial per query,
+// probe rank and row tile at parts[(q p + rank) nrt + rt], so that every
+// query's partials are merged in ascending cluster order whichever
+// workgroup ran first.
+//
+// Ecm, the fragment-order copy of the cluster-contiguous E (bf16 engines
+// that take batches): row tile rt of cluster k is ns = ceil(d / 32) steps of
+// 1 KB at tile index k nrt + rt; step s holds, for lane group g and row col,
+// elements 32 s + 8 g .. + 7 of the cluster's row 16 rt + col at byte
+// ((4 s + g) 16 + col) 16 -- the fragment lane 16 g + col of the MFMA takes
+// -- and zeros past the cluster's rows and past d.  (Read from the
+// row-major copy, an instruction touches 16 rows x 64 B; measured on the
+// Qwen-3-4B shape's 778 MB, that order streams at 4.4 TB/s where 1 KB
+// pieces stream at 6.0 and a plain read at 6.9.)
 // ======================================================================
-// Clusters per workgroup (divides 32: a workgroup's clusters share one bitset
-// word).  Measured on the Qwen-3-4B shape at B = 128, p = 1024: 4 and 8 give
-// the same time, 16 is 16% slower.
-constexpr int kCmClusters = 8;
+constexpr int kCmClusters = 8;  // per workgroup; divides 32 (one bitset word)
 static_assert(32 % kCmClusters == 0, "a workgroup's clusters share one bitset word");
 constexpr int kCmMaxB = 256;    // queries the LDS lists hold
 
 struct GatherCmArgs {
-  const uint16_t* Ec;  // cluster-contiguous E [v x d]
+  const uint4* Ecm;    // fragment-order copy of E (above)
   const int32_t* c2t;
   int c, b, d;
   const uint16_t* H;  // [B x d]
@@ -619,7 +628,7 @@ struct GatherCmArgs {
   int token_sample;
   float tprime;
   uint64_t seed;
-  Part* parts;  // [B x gridDim.x]
+  Part* parts;  // [B x p nrt]
 };
 
 __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
@@ -627,7 +636,6 @@ __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
   __shared__ int s_pre[kCmMaxB];
   __shared__ short s_q[kCmClusters][kCmMaxB];
   __shared__ int s_n[kCmClusters];
-  __shared__ Part s_acc[4][kCmMaxB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int k0 = blockIdx.x * kCmClusters;
@@ -635,8 +643,6 @@ __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
   for (int q = threadIdx.x; q < a.B; q += 256) {
     s_word[q] = a.mbits[(int64_t)w * a.B + q];
     s_pre[q] = a.mpre[(int64_t)w * a.B + q];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) s_acc[v][q] = part_empty();
   }
   __syncthreads();
   // the queries probing each of the workgroup's clusters, ascending
@@ -661,7 +667,7 @@ __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
   // work items (cluster, row tile, query tile), in that order, taken round-
   // robin by the four waves: a cluster probed by many queries spreads its
   // query tiles over the waves
-  const int nrt = (a.b + 15) / 16;
+  const int nrt = (a.b + 15) / 16, ns = (a.d + 31) / 32;
   int total = 0;
 #pragma unroll
   for (int ci = 0; ci < kCmClusters; ++ci) total += nrt * ((s_n[ci] + 15) / 16);
@@ -678,8 +684,8 @@ __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
     const int rt = rem / nqt, qt = rem % nqt;
     const int k = k0 + ci;
     const int bit = k & 31;
-    const int64_t f = (int64_t)k * a.b + min(16 * rt + col, a.b - 1);
-    const uint16_t* Ar = a.Ec + f * a.d;
+    // step s of the tile: At[64 s], the lane's fragment
+    const uint4* At = a.Ecm + ((int64_t)k * nrt + rt) * ns * 64 + lane;
     // the tile's token ids, loaded ahead of the products
     int32_t tok[4];
 #pragma unroll
@@ -689,15 +695,14 @@ __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
     const uint16_t* Hr = a.H + (int64_t)q * a.d;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nblk = a.d / 128;
-    // ping-pong: the next 128-element block is in flight during the MFMAs
-    // (measured: rings of 3, 4 or 6 blocks are no faster)
+    // ping-pong: the next 128-element block (four steps) is in flight during
+    // the current block's products
     uint4 a0[4], b0[4], a1[4], b1[4];
     auto ld = [&](int blk, uint4 (&av)[4], uint4 (&bv)[4]) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {  // step s: elements 32 s + 8 g .. + 7 of the block
-        const int kk = 128 * blk + 32 * s + 8 * g;
-        av[s] = *reinterpret_cast<const uint4*>(Ar + kk);
-        bv[s] = *reinterpret_cast<const uint4*>(Hr + kk);
+      for (int s = 0; s < 4; ++s) {
+        av[s] = At[64 * (4 * blk + s)];
+        bv[s] = *reinterpret_cast<const uint4*>(Hr + 128 * blk + 32 * s + 8 * g);
       }
     };
     if (nblk > 0) ld(0, a0, b0);
@@ -711,12 +716,10 @@ __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
         for (int s = 0; s < 4; ++s) acc = mfma16(a1[s], b1[s], acc);
       }
     }
-    for (int kb = nblk * 128; kb < a.d; kb += 32) {
-      const int kk = kb + 8 * g;
-      const bool ok = kk < a.d;
-      const uint4 av = ok ? *reinterpret_cast<const uint4*>(Ar + kk) : uint4{0u, 0u, 0u, 0u};
-      const uint4 bv = ok ? *reinterpret_cast<const uint4*>(Hr + kk) : uint4{0u, 0u, 0u, 0u};
-      acc = mfma16(av, bv, acc);
+    for (int st = 4 * nblk; st < ns; ++st) {  // d % 128 != 0: the last steps (Ecm is zero past d)
+      const int kk = 32 * st + 8 * g;
+      const uint4 bv = kk < a.d ? *reinterpret_cast<const uint4*>(Hr + kk) : uint4{0u, 0u, 0u, 0u};
+      acc = mfma16(At[64 * st], bv, acc);
     }
     // lane: slots j = 16 rt + 4 g + i of cluster k for query q
     const bool qok = qi < n;
@@ -738,15 +741,26 @@ __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
                    __shfl_xor(pt.s, m), __shfl_xor(pt.id, m)};
       pt = (lane & m) ? part_merge(o, pt) : part_merge(pt, o);
     }
-    if (g == 0 && qok) s_acc[wave][q] = part_merge(s_acc[wave][q], pt);
+    if (g == 0 && qok) a.parts[((int64_t)q * a.p + pos) * nrt + rt] = pt;
   }
-  __syncthreads();
-  for (int q = threadIdx.x; q < a.B; q += 256) {
-    Part r = s_acc[0][q];
-#pragma unroll
-    for (int v = 1; v < 4; ++v) r = part_merge(r, s_acc[v][q]);
-    a.parts[(int64_t)q * gridDim.x + blockIdx.x] = r;
-  }
+}
+
+// Ecm from the cluster-contiguous E (layout above): one thread per 16-byte
+// fragment.
+__global__ __launch_bounds__(256) void k_fragment_order(const uint16_t* __restrict__ Ec, int64_t c,
+                                                        int b, int d, int nrt, int ns,
+                                                        uint4* __restrict__ out) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= c * nrt * ns * 64) return;
+  const int lane = (int)(o & 63);
+  const int64_t step = o >> 6;
+  const int s = (int)(step % ns);
+  const int64_t tile = step / ns;
+  const int64_t k = tile / nrt;
+  const int rt = (int)(tile % nrt);
+  const int r = 16 * rt + (lane & 15), e = 32 * s + 8 * (lane >> 4);
+  out[o] = r < b && e < d ? *reinterpret_cast<const uint4*>(Ec + (k * b + r) * d + e)
+                          : uint4{0u, 0u, 0u, 0u};
 }
 
 // Re-lay INT4 rows for the MFMA tiles: in every 64-byte block of four
@@ -894,7 +908,6 @@ hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, 
   return score_mfma_go<0>(a, cus, k.stream);
 }
 
-int64_t gather_cm_blocks(int64_t c, int) { return (c + kCmClusters - 1) / kCmClusters; }
 // Cluster-major pays off when clusters are shared: the expected number of
 // queries per probed cluster, B p / (c (1 - (1 - p/c)^B)), is at least 2.
 int gather_cm_max_batch() { return kCmMaxB; }
@@ -905,18 +918,35 @@ bool gather_cm_fits(int B, int64_t p, int64_t c) {
   return (double)B * (double)p >= 2.0 * u;
 }
 
+int64_t fragment_order_bytes(int64_t c, int64_t b, int d) {
+  return c * ((b + 15) / 16) * ((d + 31) / 32) * 1024;
+}
+
+hipError_t launch_fragment_order(const KernelCtx& k, void* out) {
+  const int nrt = (int)((k.b + 15) / 16), ns = (k.d + 31) / 32;
+  const int64_t n = k.c * nrt * ns * 64;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fragment_order, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, k.stream,
+                     static_cast<const uint16_t*>(k.Ec), k.c, (int)k.b, k.d, nrt, ns,
+                     static_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
 hipError_t launch_gather_cm(const KernelCtx& k, int cus, const void* h, int B, int p,
                             const uint32_t* mbits,
                             const int32_t* mpre, int token_sample, float tprime, uint64_t seed,
                             int32_t* out_ids, float* out_logits, Part* parts, int64_t* nparts) {
+  (void)cus;
+  if (!k.Ecm || B < 1 || B > kCmMaxB || p < 1) return hipErrorInvalidValue;
   GatherCmArgs a{};
-  a.Ec = static_cast<const uint16_t*>(k.Ec); a.c2t = k.c2t;
+  a.Ecm = static_cast<const uint4*>(k.Ecm); a.c2t = k.c2t;
   a.c = (int)k.c; a.b = (int)k.b; a.d = k.d;
   a.H = static_cast<const uint16_t*>(h); a.B = B; a.p = p;
   a.mbits = mbits; a.mpre = mpre; a.out_ids = out_ids; a.out_logits = out_logits;
   a.token_sample = token_sample; a.tprime = tprime; a.seed = seed; a.parts = parts;
-  const int64_t blocks = gather_cm_blocks(k.c, cus);
-  *nparts = blocks;
+  *nparts = (int64_t)p * ((k.b + 15) / 16);
+  const int64_t blocks = (k.c + kCmClusters - 1) / kCmClusters;
+  if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_gather_cm, dim3((unsigned)blocks), dim3(256), 0, k.stream, a);
   return hipGetLastError();
 }
