@@ -116,12 +116,18 @@ struct MfmaArgs {
   const int32_t* c2t;
   int32_t* out_ids;
   KeyXform key;  // stage 1 (not EPI): scores or selection keys into out
+  // dense passes (EPI) over the fragment-order copy of E (FRAG): row r is
+  // slot r of the clustering, its tile r / 16 at Afrag + (r / 16) ns 64; the
+  // token is c2t[r] and its cluster r / bsz
+  const uint4* Afrag;
+  int ns;
 };
 
 constexpr int kHRow = 128 + 8;  // LDS row of a staged h block (bf16), padded
 
-template <int NT, int MT, int QB, bool EPI>
+template <int NT, int MT, int QB, bool EPI, bool FRAG = false>
 __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
+  static_assert(!FRAG || (QB == 0 && EPI), "the fragment-order rows serve the dense bf16 passes");
   constexpr int QW = 16 * NT;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t sH[2][QW * kHRow];
   __shared__ Part sh[EPI ? 4 : 1][EPI ? QW : 1];
@@ -174,9 +180,15 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int k = 128 * kb + 32 * s + 8 * g;
-          dst[m][s] = k < a.d ? *reinterpret_cast<const uint4*>(A + ra[m] * a.d + k)
-                              : uint4{0u, 0u, 0u, 0u};
+          if constexpr (FRAG) {  // one contiguous 1 KB per instruction
+            const int64_t tile = min(rbase + 16 * m, a.R - 16) / 16;
+            dst[m][s] = 4 * kb + s < a.ns ? a.Afrag[(tile * a.ns + 4 * kb + s) * 64 + lane]
+                                          : uint4{0u, 0u, 0u, 0u};
+          } else {
+            const int k = 128 * kb + 32 * s + 8 * g;
+            dst[m][s] = k < a.d ? *reinterpret_cast<const uint4*>(A + ra[m] * a.d + k)
+                                : uint4{0u, 0u, 0u, 0u};
+          }
         }
     };
     auto compute = [&](int buf, const uint4 (&cur)[MT][4]) {
@@ -387,15 +399,16 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int64_t r = rbase + 16 * m + 4 * g + i;
         if (r < a.R && q < a.B) {
-          if (a.out) a.out[(int64_t)q * a.ld_out + r] = acc[m][n][i];
-          const int32_t tok = a.rows_map ? a.c2t[phys(r)] : (int32_t)r;
+          const int32_t tok = FRAG ? a.c2t[r] : a.rows_map ? a.c2t[phys(r)] : (int32_t)r;
+          // the dense logits at the token's position (slots under FRAG)
+          if (a.out) a.out[(int64_t)q * a.ld_out + (FRAG ? (int64_t)tok : r)] = acc[m][n][i];
           if (a.out_ids) a.out_ids[(int64_t)q * a.ld_out + r] = tok;
           Part pt = part_of(acc[m][n][i], tok, a.token_sample, a.tprime, a.seed, (uint32_t)q);
           if (a.bits) {
-            const int k = a.t2c[r];
+            const int k = FRAG ? (int)(r / a.bsz) : a.t2c[r];
             const bool probed = (a.bits[(int64_t)q * a.W + (k >> 5)] >> (k & 31)) & 1u;
             pt.key = probed ? -INFINITY
-                            : acc[m][n][i] / a.tprime + gumbel_at(a.seed, (uint32_t)q, (uint32_t)r, 3u);
+                            : acc[m][n][i] / a.tprime + gumbel_at(a.seed, (uint32_t)q, (uint32_t)tok, 3u);
           }
           p = part_merge(p, pt);
         }
@@ -432,8 +445,9 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
 // waves 1..3 hand their tiles to wave 0 through LDS and it adds them in wave
 // order.  Rows and scale layout as in k_mfma_gemm (MT = 1, no row map).
 // ======================================================================
-template <int QB, bool EPI>
+template <int QB, bool EPI, bool FRAG = false>
 __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
+  static_assert(!FRAG || (QB == 0 && EPI), "the fragment-order rows serve the dense bf16 passes");
   __shared__ f32x4 red[3][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -460,8 +474,14 @@ __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
     auto load = [&](int kb, Blk& x) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int k = 128 * kb + 32 * s + 8 * g;
-        x.v[s] = k < a.d ? *reinterpret_cast<const uint4*>(A + ra * a.d + k) : uint4{0u, 0u, 0u, 0u};
+        if constexpr (FRAG) {  // one contiguous 1 KB per instruction
+          const int64_t tile = min(rbase, a.R - 16) / 16;
+          x.v[s] = 4 * kb + s < a.ns ? a.Afrag[(tile * a.ns + 4 * kb + s) * 64 + lane]
+                                     : uint4{0u, 0u, 0u, 0u};
+        } else {
+          const int k = 128 * kb + 32 * s + 8 * g;
+          x.v[s] = k < a.d ? *reinterpret_cast<const uint4*>(A + ra * a.d + k) : uint4{0u, 0u, 0u, 0u};
+        }
       }
       load_h(kb, x.hb);
     };
@@ -553,13 +573,14 @@ __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int64_t r = rbase + 4 * g + i;
       if (qok && r < a.R) {
-        if (a.out) a.out[(int64_t)q * a.ld_out + r] = acc[i];
-        Part pt = part_of(acc[i], (int32_t)r, a.token_sample, a.tprime, a.seed, (uint32_t)q);
+        const int32_t tok = FRAG ? a.c2t[r] : (int32_t)r;  // slots under FRAG
+        if (a.out) a.out[(int64_t)q * a.ld_out + tok] = acc[i];
+        Part pt = part_of(acc[i], tok, a.token_sample, a.tprime, a.seed, (uint32_t)q);
         if (a.bits) {
-          const int k = a.t2c[r];
+          const int k = FRAG ? (int)(r / a.bsz) : a.t2c[r];
           const bool probed = (a.bits[(int64_t)q * a.W + (k >> 5)] >> (k & 31)) & 1u;
           pt.key = probed ? -INFINITY
-                          : acc[i] / a.tprime + gumbel_at(a.seed, (uint32_t)q, (uint32_t)r, 3u);
+                          : acc[i] / a.tprime + gumbel_at(a.seed, (uint32_t)q, (uint32_t)tok, 3u);
         }
         p = part_merge(p, pt);
       }
@@ -843,30 +864,30 @@ static GemmShape gemm_shape(int64_t R, int B, int cus) {
   return s;
 }
 
-template <int NT, int MT, int QB, bool EPI>
+template <int NT, int MT, int QB, bool EPI, bool FRAG>
 static hipError_t gemm_go(const MfmaArgs& a, hipStream_t st, int64_t* nblocks) {
   const dim3 grid((unsigned)((a.R + 64 * MT - 1) / (64 * MT)),
                   (unsigned)((a.B + 16 * NT - 1) / (16 * NT)));
   if (nblocks) *nblocks = grid.x;
-  hipLaunchKernelGGL((k_mfma_gemm<NT, MT, QB, EPI>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_mfma_gemm<NT, MT, QB, EPI, FRAG>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int MT, int QB, bool EPI>
+template <int MT, int QB, bool EPI, bool FRAG>
 static hipError_t gemm_nt(const MfmaArgs& a, int nt, hipStream_t st, int64_t* nblocks) {
   switch (nt) {
-    case 1: return gemm_go<1, MT, QB, EPI>(a, st, nblocks);
-    case 2: return gemm_go<2, MT, QB, EPI>(a, st, nblocks);
-    case 4: return gemm_go<4, MT, QB, EPI>(a, st, nblocks);
-    default: return gemm_go<8, MT, QB, EPI>(a, st, nblocks);
+    case 1: return gemm_go<1, MT, QB, EPI, FRAG>(a, st, nblocks);
+    case 2: return gemm_go<2, MT, QB, EPI, FRAG>(a, st, nblocks);
+    case 4: return gemm_go<4, MT, QB, EPI, FRAG>(a, st, nblocks);
+    default: return gemm_go<8, MT, QB, EPI, FRAG>(a, st, nblocks);
   }
 }
 
-template <int QB, bool EPI>
+template <int QB, bool EPI, bool FRAG = false>
 static hipError_t mfma_dispatch(const MfmaArgs& a, int cus, hipStream_t st, int64_t* nblocks) {
   const GemmShape s = gemm_shape(a.R, a.B, cus);
-  return s.mt == 2 ? gemm_nt<2, QB, EPI>(a, s.nt, st, nblocks)
-                   : gemm_nt<1, QB, EPI>(a, s.nt, st, nblocks);
+  return s.mt == 2 ? gemm_nt<2, QB, EPI, FRAG>(a, s.nt, st, nblocks)
+                   : gemm_nt<1, QB, EPI, FRAG>(a, s.nt, st, nblocks);
 }
 
 int64_t mfma_blocks(int64_t R) { return (R + 63) / 64; }
@@ -957,14 +978,28 @@ hipError_t launch_gather_cm(const KernelCtx& k, int cus, const void* h, int B, i
 // cache traffic grows with B: measured at the Llama-3.2-1B shape, B = 2 takes
 // 101 us against the GEMM's 116 us, but B = 8 122 us against 118 us.
 constexpr int kDenseSplitdMaxB = 4;
+template <bool FRAG>
 static hipError_t dense_mfma_go(const MfmaArgs& a, int cus, hipStream_t st, int64_t* nparts) {
   if (a.B <= kDenseSplitdMaxB) {
     const dim3 grid((unsigned)splitd_blocks(a.R), 1);
     *nparts = grid.x;
-    hipLaunchKernelGGL((k_mfma_stage1_splitd<0, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_mfma_stage1_splitd<0, true, FRAG>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  return mfma_dispatch<0, true>(a, cus, st, nparts);
+  return mfma_dispatch<0, true, FRAG>(a, cus, st, nparts);
+}
+
+// The dense passes read the fragment-order copy of E when the engine keeps
+// one and its 16-row tiles are consecutive slots (b a multiple of 16).
+static hipError_t dense_rows_go(const KernelCtx& k, MfmaArgs& a, int cus, int64_t* nparts) {
+  if (k.Ecm && k.b % 16 == 0) {
+    a.Afrag = static_cast<const uint4*>(k.Ecm);
+    a.ns = (k.d + 31) / 32;
+    a.c2t = k.c2t;
+    a.bsz = (int)k.b;
+    return dense_mfma_go<true>(a, cus, k.stream, nparts);
+  }
+  return dense_mfma_go<false>(a, cus, k.stream, nparts);
 }
 
 hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, int token_sample,
@@ -974,7 +1009,7 @@ hipError_t launch_dense_mfma(const KernelCtx& k, int cus, const void* h, int B, 
   a.A = k.E; a.R = k.v; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
   a.out = out_logits; a.ld_out = k.v;
   a.token_sample = token_sample; a.tprime = tprime; a.seed = seed; a.parts = parts;
-  return dense_mfma_go(a, cus, k.stream, nparts);
+  return dense_rows_go(k, a, cus, nparts);
 }
 
 hipError_t launch_gather_shared_mfma(const KernelCtx& k, int cus, const void* h, int B,
@@ -996,7 +1031,7 @@ hipError_t launch_spec_mfma(const KernelCtx& k, int cus, const void* h, int B, f
   a.A = k.E; a.R = k.v; a.d = k.d; a.H = static_cast<const uint16_t*>(h); a.B = B;
   a.token_sample = 0; a.tprime = T; a.seed = seed; a.parts = parts;
   a.t2c = t2c; a.bits = bits; a.W = W;
-  return dense_mfma_go(a, cus, k.stream, nparts);
+  return dense_rows_go(k, a, cus, nparts);
 }
 
 }  // namespace fh
