@@ -55,6 +55,7 @@ struct fh_engine {
   int32_t* t2c = nullptr;     // cluster of every token (speculative verification)
   void* Ec = nullptr;         // cluster-contiguous copy of E: Ec[f] = E[C2T[f]]
   void* Ecm = nullptr;        // Ec in fragment order (bf16 engines taking batches)
+  void* Cm = nullptr;         // C in fragment order (the same engines)
   uint8_t* cq = nullptr;
   uint16_t* csig = nullptr;
   uint8_t* cq_mfma = nullptr;    // INT4 codes in the MFMA tile layout (bf16 engines)
@@ -85,6 +86,7 @@ struct fh_engine {
     k.E = E;
     k.Ec = Ec;
     k.Ecm = Ecm;
+    k.Cm = Cm;
     k.C = C;
     k.c2t = c2t;
     k.cq = cq;
@@ -140,6 +142,7 @@ void free_engine(fh_engine* e) {
   (void)hipFree(e->c2t);
   (void)hipFree(e->Ec);
   (void)hipFree(e->Ecm);
+  (void)hipFree(e->Cm);
   (void)hipFree(e->t2c);
   (void)hipFree(e->sumscores);
   (void)hipFree(e->nprobe);
@@ -419,10 +422,14 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "copy C2T"); }
   r = fh::launch_permute_rows(e->ctx(st), e->Ec);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "cluster-contiguous E"); }
-  if (dtype == FH_BF16 && max_batch >= 2) {  // what the cluster-major stage 2 reads
+  if (dtype == FH_BF16 && max_batch >= 2) {  // what the batched matrix-core kernels read
     r = hipMalloc(&e->Ecm, (size_t)fh::fragment_order_bytes(c, b, (int)d));
-    if (r == hipSuccess) r = fh::launch_fragment_order(e->ctx(st), e->Ecm);
-    if (r != hipSuccess) { free_engine(e); return hip_fail(r, "fragment-order E"); }
+    if (r == hipSuccess) r = fh::launch_fragment_order(e->Ec, c, b, (int)d, e->Ecm, st);
+    if (r == hipSuccess && quant == FH_QUANT_NONE) {  // quantised centroids have their own layouts
+      r = hipMalloc(&e->Cm, (size_t)fh::fragment_order_bytes(1, c, (int)d));
+      if (r == hipSuccess) r = fh::launch_fragment_order(C, 1, c, (int)d, e->Cm, st);
+    }
+    if (r != hipSuccess) { free_engine(e); return hip_fail(r, "fragment-order E and C"); }
   }
   r = fh::launch_t2c(e->ctx(st), e->t2c);
   if (r != hipSuccess) { free_engine(e); return hip_fail(r, "token clusters"); }

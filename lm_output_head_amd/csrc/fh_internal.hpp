@@ -31,6 +31,7 @@ struct KernelCtx {
   const void* E;
   const void* Ec;  // cluster-contiguous copy of E (Ec[f] = E[C2T[f]]), or null
   const void* Ecm = nullptr;  // its fragment-order copy (cluster-major stage 2), or null
+  const void* Cm = nullptr;   // the centroids' fragment-order copy (batched bf16 stage 1), or null
   const void* C;
   const int32_t* c2t;
   const uint8_t* cq;
@@ -110,11 +111,14 @@ hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, 
 // Cluster-major stage 2 on the matrix cores (bf16 engines, B >= 2): every
 // probed cluster's rows are read once for all queries that probe it.
 bool gather_cm_fits(int B, int64_t p, int64_t c);
-// The fragment-order copy of the cluster-contiguous E that the cluster-major
-// stage 2 reads (layout in fh_mfma.hip): its bytes, and the launch that
-// writes it from k.Ec (bf16).
+// Fragment-order copies (layout in fh_mfma.hip) of c clusters of b
+// contiguous bf16 rows of d elements: the cluster-contiguous E (read by the
+// cluster-major stage 2 and the dense passes) and the centroids (c = 1,
+// b = their count; read by batched stage 1).  Their bytes, and the launch
+// that writes one.
 int64_t fragment_order_bytes(int64_t c, int64_t b, int d);
-hipError_t launch_fragment_order(const KernelCtx& k, void* out);
+hipError_t launch_fragment_order(const void* rows, int64_t c, int64_t b, int d, void* out,
+                                 hipStream_t st);
 int gather_cm_max_batch();  // queries the cluster-major stage 2 can take
 // stage 2 over one probe list shared by the batch, as the matrix-core GEMM
 // with a row map (bf16 engines with the cluster-contiguous E)

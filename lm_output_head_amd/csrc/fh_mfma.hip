@@ -116,9 +116,10 @@ struct MfmaArgs {
   const int32_t* c2t;
   int32_t* out_ids;
   KeyXform key;  // stage 1 (not EPI): scores or selection keys into out
-  // dense passes (EPI) over the fragment-order copy of E (FRAG): row r is
-  // slot r of the clustering, its tile r / 16 at Afrag + (r / 16) ns 64; the
-  // token is c2t[r] and its cluster r / bsz
+  // rows from a fragment-order copy (FRAG): row r's tile r / 16 at
+  // Afrag + (r / 16) ns 64.  Stage 1: the centroids.  The dense passes (EPI):
+  // the fragment-order E, row r is slot r of the clustering, its token c2t[r]
+  // and its cluster r / bsz
   const uint4* Afrag;
   int ns;
 };
@@ -127,7 +128,7 @@ constexpr int kHRow = 128 + 8;  // LDS row of a staged h block (bf16), padded
 
 template <int NT, int MT, int QB, bool EPI, bool FRAG = false>
 __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
-  static_assert(!FRAG || (QB == 0 && EPI), "the fragment-order rows serve the dense bf16 passes");
+  static_assert(!FRAG || QB == 0, "fragment-order rows are bf16");
   constexpr int QW = 16 * NT;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t sH[2][QW * kHRow];
   __shared__ Part sh[EPI ? 4 : 1][EPI ? QW : 1];
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           if constexpr (FRAG) {  // one contiguous 1 KB per instruction
-            const int64_t tile = min(rbase + 16 * m, a.R - 16) / 16;
+            const int64_t tile = min((rbase + 16 * m) / 16, (a.R + 15) / 16 - 1);
             dst[m][s] = 4 * kb + s < a.ns ? a.Afrag[(tile * a.ns + 4 * kb + s) * 64 + lane]
                                           : uint4{0u, 0u, 0u, 0u};
           } else {
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
 // ======================================================================
 template <int QB, bool EPI, bool FRAG = false>
 __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
-  static_assert(!FRAG || (QB == 0 && EPI), "the fragment-order rows serve the dense bf16 passes");
+  static_assert(!FRAG || QB == 0, "fragment-order rows are bf16");
   __shared__ f32x4 red[3][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if constexpr (FRAG) {  // one contiguous 1 KB per instruction
-          const int64_t tile = min(rbase, a.R - 16) / 16;
+          const int64_t tile = rbase / 16;  // the grid covers ceil(R / 16) tiles
           x.v[s] = 4 * kb + s < a.ns ? a.Afrag[(tile * a.ns + 4 * kb + s) * 64 + lane]
                                      : uint4{0u, 0u, 0u, 0u};
         } else {
@@ -766,8 +767,9 @@ __global__ __launch_bounds__(256) void k_gather_cm(GatherCmArgs a) {
   }
 }
 
-// Ecm from the cluster-contiguous E (layout above): one thread per 16-byte
-// fragment.
+// The fragment-order copy (layout above) of c clusters of b contiguous rows
+// each: one thread per 16-byte fragment.  With c = 1 and b = the row count it
+// is a plain matrix's tiles of 16 consecutive rows (the centroids).
 __global__ __launch_bounds__(256) void k_fragment_order(const uint16_t* __restrict__ Ec, int64_t c,
                                                         int b, int d, int nrt, int ns,
                                                         uint4* __restrict__ out) {
@@ -899,16 +901,16 @@ int64_t splitd_blocks(int64_t R) { return (R + 15) / 16; }
 // 21.4 / 23.2 us, B = 32 18.0 / 20.9 us against 22.3 / 24.3 us; at B = 64 the
 // GEMM is faster (22.8 / 30.8 us against 28.3 / 34.8 us), its rows being read
 // once per workgroup for more queries.
-template <int QB>
+template <int QB, bool FRAG = false>
 static hipError_t score_mfma_go(const MfmaArgs& a, int cus, hipStream_t st) {
   const GemmShape s = gemm_shape(a.R, a.B, cus);
   const bool splitd = a.B <= 32 && s.nt == 1 && s.mt == 1;
   if (splitd) {
     const dim3 grid((unsigned)((a.R + 15) / 16), (unsigned)((a.B + 15) / 16));
-    hipLaunchKernelGGL((k_mfma_stage1_splitd<QB, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_mfma_stage1_splitd<QB, false, FRAG>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  return mfma_dispatch<QB, false>(a, cus, st, nullptr);
+  return mfma_dispatch<QB, false, FRAG>(a, cus, st, nullptr);
 }
 
 hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, float* out,
@@ -926,6 +928,11 @@ hipError_t launch_score_mfma(const KernelCtx& k, int cus, const void* h, int B, 
     return score_mfma_go<8>(a, cus, k.stream);
   }
   a.A = k.C;
+  if (k.Cm) {  // the centroids' fragment-order copy: one contiguous 1 KB per load
+    a.Afrag = static_cast<const uint4*>(k.Cm);
+    a.ns = (k.d + 31) / 32;
+    return score_mfma_go<0, true>(a, cus, k.stream);
+  }
   return score_mfma_go<0>(a, cus, k.stream);
 }
 
@@ -943,12 +950,13 @@ int64_t fragment_order_bytes(int64_t c, int64_t b, int d) {
   return c * ((b + 15) / 16) * ((d + 31) / 32) * 1024;
 }
 
-hipError_t launch_fragment_order(const KernelCtx& k, void* out) {
-  const int nrt = (int)((k.b + 15) / 16), ns = (k.d + 31) / 32;
-  const int64_t n = k.c * nrt * ns * 64;
+hipError_t launch_fragment_order(const void* rows, int64_t c, int64_t b, int d, void* out,
+                                 hipStream_t st) {
+  const int nrt = (int)((b + 15) / 16), ns = (d + 31) / 32;
+  const int64_t n = c * nrt * ns * 64;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fragment_order, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, k.stream,
-                     static_cast<const uint16_t*>(k.Ec), k.c, (int)k.b, k.d, nrt, ns,
+  hipLaunchKernelGGL(k_fragment_order, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(rows), c, (int)b, d, nrt, ns,
                      static_cast<uint4*>(out));
   return hipGetLastError();
 }
