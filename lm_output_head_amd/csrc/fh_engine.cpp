@@ -449,7 +449,8 @@ fh_status fh_create(const void* E, const void* C, const int32_t* C2T, fh_dtype d
     if (r != hipSuccess) { free_engine(e); return hip_fail(r, "centroid quantisation"); }
     if (hbad) { free_engine(e); return fail(FH_EINVAL, "a centroid group's scale overflows fp16"); }
     if (dtype == FH_BF16) {  // the MFMA layouts for batched stage 1 (INT8 rows are read as stored)
-      if (bits == 4) r = hipMalloc((void**)&e->cq_mfma, (size_t)(c * fh::mfma_int4_row_bytes((int)d)));
+      if (bits == 4)  // fragment order: whole tiles of 16 rows
+        r = hipMalloc((void**)&e->cq_mfma, (size_t)((c + 15) / 16 * 16 * fh::mfma_int4_row_bytes((int)d)));
       if (r == hipSuccess)
         r = hipMalloc((void**)&e->sig_mfma,
                       sizeof(uint16_t) * (size_t)((d / 32) * fh::mfma_sig_ld(c)));

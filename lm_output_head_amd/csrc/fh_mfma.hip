@@ -238,7 +238,8 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
     auto load_a = [&](int kb, Blk& x) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        x.w[m] = *reinterpret_cast<const uint4*>(A + ra[m] * a.a_row_bytes + 64 * kb + 16 * g);
+        const int64_t tile = min((rbase + 16 * m) / 16, (a.R + 15) / 16 - 1);
+        x.w[m] = *reinterpret_cast<const uint4*>(A + ((tile * (a.a_row_bytes / 64) + kb) * 64 + lane) * 16);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int grp = min(4 * kb + s, G - 1);
@@ -511,8 +512,8 @@ __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
       uint4 hb[4];
     };
     auto load = [&](int kb, Blk& x) {
-      if constexpr (QB == 4)
-        x.w4 = *reinterpret_cast<const uint4*>(A + ra * a.a_row_bytes + 64 * kb + 16 * g);
+      if constexpr (QB == 4)  // fragment order: the grid covers ceil(R / 16) tiles
+        x.w4 = *reinterpret_cast<const uint4*>(A + ((rbase / 16 * (a.a_row_bytes / 64) + kb) * 64 + lane) * 16);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int grp = min(4 * kb + s, G - 1);
@@ -786,25 +787,28 @@ __global__ __launch_bounds__(256) void k_fragment_order(const uint16_t* __restri
                           : uint4{0u, 0u, 0u, 0u};
 }
 
-// Re-lay INT4 rows for the MFMA tiles: in every 64-byte block of four
-// groups, lane group g's four bytes of each group (elements 8g .. 8g+7)
-// become the 16 contiguous bytes [16 g, 16 g + 16).  Rows are padded to whole
-// blocks with zero codes.  One thread per 16-byte output chunk.
+// Re-lay INT4 rows for the MFMA tiles, in fragment order: tiles of 16 rows,
+// and in tile t, block kb (four groups, 128 elements) is 1 KB in which lane
+// 16 g + col's 16 bytes are lane group g's four bytes of each of the four
+// groups (elements 8g .. 8g+7) of row 16 t + col -- so one load instruction
+// reads 1 KB in one piece.  Zero codes past the row's groups and past c.
+// One thread per 16-byte output chunk.
 __global__ __launch_bounds__(256) void k_relayout_int4(const uint8_t* __restrict__ q, int64_t c,
                                                        int G, uint8_t* __restrict__ out,
                                                        int64_t row_bytes) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // output chunk
-  const int64_t per_row = row_bytes / 16;
-  if (i >= c * per_row) return;
-  const int64_t r = i / per_row;
-  const int blk = (int)((i % per_row) / 4), g = (int)(i % 4);
+  const int64_t nkb = row_bytes / 64;
+  if (i >= (c + 15) / 16 * 16 * (row_bytes / 16)) return;
+  const int lane = (int)(i & 63), g = lane >> 4;
+  const int64_t kb = (i >> 6) % nkb, t = (i >> 6) / nkb;
+  const int64_t r = 16 * t + (lane & 15);
   uint32_t w[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const int grp = 4 * blk + s;
-    w[s] = grp < G ? *reinterpret_cast<const uint32_t*>(q + r * (G * 16) + grp * 16 + 4 * g) : 0u;
+    const int64_t grp = 4 * kb + s;
+    w[s] = r < c && grp < G ? *reinterpret_cast<const uint32_t*>(q + r * (G * 16) + grp * 16 + 4 * g) : 0u;
   }
-  *reinterpret_cast<uint4*>(out + r * row_bytes + 16 * i % row_bytes) = uint4{w[0], w[1], w[2], w[3]};
+  *reinterpret_cast<uint4*>(out + 16 * i) = uint4{w[0], w[1], w[2], w[3]};
 }
 
 // Scales group-major: sigT[grp][r] = sig[r][grp] (rows past c are 0).
@@ -828,7 +832,7 @@ hipError_t launch_mfma_relayout(const KernelCtx& k, uint8_t* cq_mfma, uint16_t* 
   const int G = k.d / 32;
   if (k.qbits == 4) {  // INT8 rows are read as stored
     const int64_t rb = mfma_int4_row_bytes(k.d);
-    const int64_t chunks = k.c * (rb / 16);
+    const int64_t chunks = (k.c + 15) / 16 * 16 * (rb / 16);
     hipLaunchKernelGGL(k_relayout_int4, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
                        k.stream, k.cq, k.c, G, cq_mfma, rb);
     const hipError_t r = hipGetLastError();
