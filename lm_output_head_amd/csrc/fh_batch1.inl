@@ -177,7 +177,7 @@ __device__ __forceinline__ void stage2_role(const Stage2Job& a, Batch1Shared& sh
       for (int pos = max(pos0, nkept) + (int)threadIdx.x; pos < pos0 + npos; pos += 1024)
         if ((int64_t)pos * a.bsz >= r_lo) a.out_clusters[pos] = -1;
   }
-  Part part[1] = {part_empty()};
+  LaneParts lp = lane_parts_empty();
   // slot f of the clustering; with the cluster-contiguous copy of E it is
   // also the row, else the row is the token C2T[f]
   auto src_of = [&](int64_t r) -> int64_t {
@@ -190,12 +190,13 @@ __device__ __forceinline__ void stage2_role(const Stage2Job& a, Batch1Shared& sh
       if (a.out_logits) a.out_logits[r] = z;
       if (a.out_ids) a.out_ids[r] = (int32_t)src;
     }
-    part[0] = part_merge(part[0], part_of(z, (int32_t)src, a.token_sample, a.tprime, a.seed, a.row));
+    lane_parts_add(lp, z, (int32_t)src, a.token_sample, a.tprime, a.seed, a.row);
   };
   // four rows in flight per wave when the register slice allows it
   wave_rows<T, MAXM, 1, (MAXM <= 4 ? 4 : 2)>(static_cast<const T*>(a.Ec ? a.Ec : a.E), a.d, lane,
                                              hv, 1, r_lo + wave, r_end, 16, src_of, tok_of, sink);
   FH_TRACE(22);
+  const Part part[1] = {lane_parts_finish(lp, a.token_sample, a.tprime, a.seed, a.row)};
   // sh.probes is read above; sh.parts aliases it
   const bool wg_bad = __syncthreads_or(gave_up);
   Part wg = block_merge_parts<16, 1>(part, 1, sh.parts);

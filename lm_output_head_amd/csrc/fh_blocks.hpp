@@ -256,6 +256,50 @@ __device__ __forceinline__ Part part_of(float z, int32_t t, int token_sample, fl
   return Part{key, z, z / tprime, 1.f, t};
 }
 
+// A wave's running partial over rows whose (z, token) arrive one at a time,
+// uniform across the wave.  A sampled token's key needs its Gumbel noise (a
+// Philox block and two logarithms): drawn by the whole wave for each row it
+// costs as much as 64 draws.  So with token sampling row i is parked in lane
+// i % 64, and every 64 rows (and at the end) each lane draws for its own row
+// and merges it into its own running partial; the lanes are merged at the
+// end.  The token and its logit do not depend on the merge order; the LSE's
+// rounding does.  Without token sampling a row's partial is merged at once.
+struct LaneParts {
+  Part acc;  // this lane's running partial (sampling) or the wave's (greedy)
+  float z;   // the row parked in this lane
+  int32_t t;
+  int n;     // rows parked since the last draw (uniform)
+};
+
+__device__ __forceinline__ LaneParts lane_parts_empty() {
+  return LaneParts{part_empty(), 0.f, 0, 0};
+}
+
+__device__ __forceinline__ void lane_parts_add(LaneParts& lp, float z, int32_t t, int token_sample,
+                                               float tprime, uint64_t seed, uint32_t row) {
+  if (!token_sample) {
+    lp.acc = part_merge(lp.acc, part_of(z, t, 0, tprime, seed, row));
+    return;
+  }
+  if ((int)(threadIdx.x & 63) == lp.n) {
+    lp.z = z;
+    lp.t = t;
+  }
+  if (++lp.n == 64) {
+    lp.acc = part_merge(lp.acc, part_of(lp.z, lp.t, 1, tprime, seed, row));
+    lp.n = 0;
+  }
+}
+
+// The wave's partial (uniform).
+__device__ __forceinline__ Part lane_parts_finish(LaneParts& lp, int token_sample, float tprime,
+                                                  uint64_t seed, uint32_t row) {
+  if (!token_sample) return lp.acc;
+  if ((int)(threadIdx.x & 63) < lp.n) lp.acc = part_merge(lp.acc, part_of(lp.z, lp.t, 1, tprime, seed, row));
+  lp.n = 0;
+  return wave_merge_part(lp.acc);
+}
+
 // Merge the NWAVES per-wave Parts of each of nq queries held by lane 0s;
 // thread q (< nq) returns the workgroup Part of query q.
 template <int NWAVES, int NQ>

@@ -130,9 +130,9 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 #pragma unroll
   for (int q = 0; q < NQ; ++q)
     load_hslice<T, MAXM>(Hp + (int64_t)(q0 + min(q, nq - 1)) * a.d, nch, lane, hv[q]);
-  Part part[NQ];
+  LaneParts lp[NQ];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) part[q] = part_empty();
+  for (int q = 0; q < NQ; ++q) lp[q] = lane_parts_empty();
 
   const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
   int64_t nrows = a.nrows;
@@ -160,13 +160,15 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
                                          (uint32_t)oq, (uint32_t)r);
       if (GATHER && a.out_ids) a.out_ids[oq * a.ld_vals + r] = (int32_t)src;
     }
-    if (EPI)
-      part[q] = part_merge(part[q], part_of(z, (int32_t)src, a.token_sample, a.tprime, a.seed,
-                                            (uint32_t)oq));
+    if (EPI) lane_parts_add(lp[q], z, (int32_t)src, a.token_sample, a.tprime, a.seed, (uint32_t)oq);
   };
   wave_rows<T, MAXM, NQ>(static_cast<const T*>(a.M), a.d, lane, hv, nq, r0, r1, 1, src_of, tok_of,
                         sink);
   if (EPI) {
+    Part part[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      part[q] = lane_parts_finish(lp[q], a.token_sample, a.tprime, a.seed, (uint32_t)(q0 + q));
     const Part wg = block_merge_parts<4, NQ>(part, nq, sh);
     if ((int)threadIdx.x < nq) a.parts[(int64_t)(q0 + threadIdx.x) * gridDim.x + blockIdx.x] = wg;
   }
