@@ -222,12 +222,29 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
     // probe sampling: the Gumbel-perturbed key s/T + G is formed here, one
     // row per lane-0 store, so the selector only ranks (keys saturate as in
     // the selection)
+    // (with sampled probes a row's score is parked in lane i mod 64 of the
+    // wave's rows and the lanes draw their Gumbel noise together, as in
+    // lane_parts_add)
+    const bool draw = a.probe_sample && !(a.tau > 0.f);
+    float ps = 0.f;
+    int64_t pr = -1;
+    int np = 0;
+    auto publish_parked = [&]() {
+      if (lane < np)
+        st_tagged(a.tscores + pr, tag(a.epoch, __float_as_uint(saturate_key(
+                                          ps / a.temperature + gumbel_at(a.seed, 0u, (uint32_t)pr, 0u)))));
+      np = 0;
+    };
     auto sink = [&](int, int64_t r, int64_t, float s) {
-      if (lane == 0) {
-        if (a.probe_sample && !(a.tau > 0.f))
-          s = s / a.temperature + gumbel_at(a.seed, 0u, (uint32_t)r, 0u);
-        st_tagged(a.tscores + r, tag(a.epoch, __float_as_uint(saturate_key(s))));
+      if (!draw) {
+        if (lane == 0) st_tagged(a.tscores + r, tag(a.epoch, __float_as_uint(saturate_key(s))));
+        return;
       }
+      if (lane == np) {
+        ps = s;
+        pr = r;
+      }
+      if (++np == 64) publish_parked();
     };
     if constexpr (QB != 0) {
       HGroups<MAXG> hg[1];
@@ -240,6 +257,7 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
       wave_rows<T, MAXM, 1>(static_cast<const T*>(a.C), a.d, lane, hv, 1, r_lo + wave, r_hi, 16,
                             same, same, sink);
     }
+    if (draw) publish_parked();
     FH_TRACE(1);
 #ifdef FH_PHASE_TRACE
     __syncthreads();
