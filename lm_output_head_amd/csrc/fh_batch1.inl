@@ -181,7 +181,8 @@ __device__ __forceinline__ void stage2_role(const Stage2Job& a, Batch1Shared& sh
   // slot f of the clustering; with the cluster-contiguous copy of E it is
   // also the row, else the row is the token C2T[f]
   auto src_of = [&](int64_t r) -> int64_t {
-    const int64_t f = (int64_t)sh.probes[r / a.bsz - pos0] * a.bsz + r % a.bsz;
+    const int rr = (int)r;  // p b < 2^31
+    const int64_t f = (int64_t)sh.probes[rr / a.bsz - pos0] * a.bsz + rr % a.bsz;
     return a.Ec ? f : (int64_t)a.c2t[f];
   };
   auto tok_of = [&](int64_t src) -> int64_t { return a.Ec ? (int64_t)a.c2t[src] : src; };

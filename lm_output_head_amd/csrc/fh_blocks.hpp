@@ -61,6 +61,19 @@ __device__ __forceinline__ void load_hslice(const T* h, int nch, int lane, uint4
   }
 }
 
+// A 16-byte load of chunk ch of a row through a buffer resource whose range
+// is the row's nch chunks: chunks past the row read as zero, so no lane needs
+// an exec mask around the load, and the compiler can count the loads in
+// flight exactly (waiting for one row while later rows are still loading).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int nch) {
+  // word 3: raw (untyped) 32-bit dword access, as CDNA buffer loads take it
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, nch * 16, 0x00020000);
+}
+__device__ __forceinline__ uint4 row_chunk(__amdgpu_buffer_rsrc_t rs, int ch) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, ch * 16, 0, 0);
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+
 template <typename T, int MAXM, int NQ, int RPI = 2, typename SrcOf, typename TokOf,
           typename Sink>
 __device__ __forceinline__ void wave_rows(const T* __restrict__ M, int d, int lane,
@@ -77,29 +90,26 @@ __device__ __forceinline__ void wave_rows(const T* __restrict__ M, int d, int la
 #pragma unroll
     for (int i = 0; i < RPI; ++i) {
       ok[i] = i == 0 || r + i * stride < r_end;
-      src[i] = ok[i] ? src_of(r + i * stride) : src[0];
-      tk[i] = ok[i] ? tok_of(src[i]) : tk[0];
-      const uint4* rp = reinterpret_cast<const uint4*>(M + src[i] * d);
+      // a row past the end stands in as row r (read twice, from cache), so
+      // that no index or load is conditional on another row's loaded value
+      src[i] = src_of(ok[i] ? r + i * stride : r);
+      tk[i] = tok_of(src[i]);
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(M + src[i] * d, nch);
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m) {
-        const int ch = lane + 64 * m;
-        mr[i][m] = (ok[i] && ch < nch) ? rp[ch] : uint4{0u, 0u, 0u, 0u};
-      }
+      for (int m = 0; m < MAXM; ++m) mr[i][m] = row_chunk(rs, lane + 64 * m);
     }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       if (q >= nq) break;
-      float acc[RPI];
+      // each row's dot product as soon as its own loads are in
 #pragma unroll
       for (int i = 0; i < RPI; ++i) {
-        acc[i] = 0.f;
+        if (!ok[i]) break;
+        float acc = 0.f;
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m) acc[i] = Chunk<T>::dot(mr[i][m], hv[q][m], acc[i]);
-        acc[i] = wave_sum(acc[i]);
+        for (int m = 0; m < MAXM; ++m) acc = Chunk<T>::dot(mr[i][m], hv[q][m], acc);
+        sink(q, r + i * stride, tk[i], wave_sum(acc));
       }
-#pragma unroll
-      for (int i = 0; i < RPI; ++i)
-        if (ok[i]) sink(q, r + i * stride, tk[i], acc[i]);
     }
   }
 }

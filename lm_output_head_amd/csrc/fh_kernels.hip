@@ -144,7 +144,8 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   // the token C2T[f]
   auto src_of = [&](int64_t r) -> int64_t {
     if (!GATHER) return r;
-    const int64_t f = (int64_t)Sq[r / a.bsz] * a.bsz + r % a.bsz;
+    const int rr = (int)r;  // p b < 2^31
+    const int64_t f = (int64_t)Sq[rr / a.bsz] * a.bsz + rr % a.bsz;
     return a.contiguous ? f : (int64_t)a.c2t[f];
   };
   auto tok_of = [&](int64_t src) -> int64_t {
