@@ -255,8 +255,9 @@ __global__ __launch_bounds__(1024) void k_batch1(FusedArgs a) {
       uint4 hv[1][MAXM];
       load_hslice<T, MAXM>(hp, a.d / Chunk<T>::kElems, lane, hv[0]);
       auto same = [](int64_t r) { return r; };
-      wave_rows<T, MAXM, 1>(static_cast<const T*>(a.C), a.d, lane, hv, 1, r_lo + wave, r_hi, 16,
-                            same, same, sink);
+      // C is streamed once per call: non-temporal loads
+      wave_rows<T, MAXM, 1, 2, kLoadStream>(static_cast<const T*>(a.C), a.d, lane, hv, 1,
+                                            r_lo + wave, r_hi, 16, same, same, sink);
     }
     if (draw) publish_parked();
     FH_TRACE(1);

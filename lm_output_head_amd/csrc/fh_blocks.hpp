@@ -47,9 +47,10 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t 
 // stride, ... < r_end and NQ queries.  Lane l owns the 16-byte chunks l,
 // l+64, ... of a row (MAXM of them at most), so a row is read as fully
 // coalesced 16-byte loads and the lane's slice of each h stays in registers
-// (hv) for all rows.  Two rows' loads are issued before any math.  `sink` is
-// called by every lane with the wave-uniform result of each (row, query) and
-// the token id tok_of(src(r)).
+// (hv) for all rows.  RPI rows' loads are issued before any math; AUX is the
+// loads' cache policy (kLoadStream for rows read once).  `sink` is called by
+// every lane with the wave-uniform result of each (row, query) and the token
+// id tok_of(src(r)).
 // ======================================================================
 template <typename T, int MAXM>
 __device__ __forceinline__ void load_hslice(const T* h, int nch, int lane, uint4 (&hv)[MAXM]) {
@@ -69,13 +70,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int 
   // word 3: raw (untyped) 32-bit dword access, as CDNA buffer loads take it
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, nch * 16, 0x00020000);
 }
+// Cache-policy argument of a buffer load: the non-temporal (nt) hint, for
+// rows streamed once per call.
+constexpr int kLoadStream = 2;
+template <int AUX = 0>
 __device__ __forceinline__ uint4 row_chunk(__amdgpu_buffer_rsrc_t rs, int ch) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, ch * 16, 0, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, ch * 16, 0, AUX);
   return uint4{v[0], v[1], v[2], v[3]};
 }
 
-template <typename T, int MAXM, int NQ, int RPI = 2, typename SrcOf, typename TokOf,
-          typename Sink>
+template <typename T, int MAXM, int NQ, int RPI = 2, int AUX = 0, typename SrcOf,
+          typename TokOf, typename Sink>
 __device__ __forceinline__ void wave_rows(const T* __restrict__ M, int d, int lane,
                                           const uint4 (&hv)[NQ][MAXM], int nq, int64_t r_begin,
                                           int64_t r_end, int64_t stride, SrcOf src_of,
@@ -96,7 +101,7 @@ __device__ __forceinline__ void wave_rows(const T* __restrict__ M, int d, int la
       tk[i] = tok_of(src[i]);
       const __amdgpu_buffer_rsrc_t rs = row_rsrc(M + src[i] * d, nch);
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m) mr[i][m] = row_chunk(rs, lane + 64 * m);
+      for (int m = 0; m < MAXM; ++m) mr[i][m] = row_chunk<AUX>(rs, lane + 64 * m);
     }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {

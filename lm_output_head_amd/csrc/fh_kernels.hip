@@ -163,8 +163,10 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
     }
     if (EPI) lane_parts_add(lp[q], z, (int32_t)src, a.token_sample, a.tprime, a.seed, (uint32_t)oq);
   };
-  wave_rows<T, MAXM, NQ>(static_cast<const T*>(a.M), a.d, lane, hv, nq, r0, r1, 1, src_of, tok_of,
-                        sink);
+  // rows streamed in order (dense head, scores) take non-temporal loads;
+  // gathered rows do not (measured slower with them)
+  wave_rows<T, MAXM, NQ, 2, (GATHER ? 0 : kLoadStream)>(static_cast<const T*>(a.M), a.d, lane, hv,
+                                                       nq, r0, r1, 1, src_of, tok_of, sink);
   if (EPI) {
     Part part[NQ];
 #pragma unroll

@@ -48,6 +48,16 @@ namespace fh {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// A 16-byte load with the non-temporal hint, for the bf16 operand streams
+// read in order (the fragment-order copies of C and E).  Gathered rows and
+// the INT4 codes keep ordinary loads: the hint measured slower on both.
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(256) void k_mfma_gemm(MfmaArgs a) {
         for (int s = 0; s < 4; ++s) {
           if constexpr (FRAG) {  // one contiguous 1 KB per instruction
             const int64_t tile = min((rbase + 16 * m) / 16, (a.R + 15) / 16 - 1);
-            dst[m][s] = 4 * kb + s < a.ns ? a.Afrag[(tile * a.ns + 4 * kb + s) * 64 + lane]
+            dst[m][s] = 4 * kb + s < a.ns ? ld_stream(a.Afrag + (tile * a.ns + 4 * kb + s) * 64 + lane)
                                           : uint4{0u, 0u, 0u, 0u};
           } else {
             const int k = 128 * kb + 32 * s + 8 * g;
@@ -478,7 +488,7 @@ __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
       for (int s = 0; s < 4; ++s) {
         if constexpr (FRAG) {  // one contiguous 1 KB per instruction
           const int64_t tile = rbase / 16;  // the grid covers ceil(R / 16) tiles
-          x.v[s] = 4 * kb + s < a.ns ? a.Afrag[(tile * a.ns + 4 * kb + s) * 64 + lane]
+          x.v[s] = 4 * kb + s < a.ns ? ld_stream(a.Afrag + (tile * a.ns + 4 * kb + s) * 64 + lane)
                                      : uint4{0u, 0u, 0u, 0u};
         } else {
           const int k = 128 * kb + 32 * s + 8 * g;
