@@ -645,7 +645,11 @@ __global__ __launch_bounds__(256) void k_mfma_stage1_splitd(MfmaArgs a) {
 // Qwen-3-4B shape's 778 MB, that order streams at 4.4 TB/s where 1 KB
 // pieces stream at 6.0 and a plain read at 6.9.)
 // ======================================================================
-constexpr int kCmClusters = 8;  // per workgroup; divides 32 (one bitset word)
+// Clusters per workgroup; divides 32 (one bitset word).  Small workgroups
+// balance best: measured at 8 / 4 / 2 / 1 clusters, Qwen-3-4B INT4 B = 128
+// 236.8 / 234.0 / 224.7 / 223.9 us per call, Llama INT4 B = 32
+// 106.7 / 103.5 / 102.0 / 100.5 us.
+constexpr int kCmClusters = 1;
 static_assert(32 % kCmClusters == 0, "a workgroup's clusters share one bitset word");
 constexpr int kCmMaxB = 256;    // queries the LDS lists hold
 
